@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Decode throughput of one Nemotron-H-like SSM layer on one MI355X.
+
+Workload (one "step"): one decode token for every request of the batch through
+one SSM layer -- the fused causal conv1d state update (conv state 3072 x 3 bf16,
+width 4, SiLU) followed by ReplaySSM append-decode (batch 256, 32 heads, head dim
+64, state 128, 8 groups, ring capacity 16: step size and decay, ring append,
+decay-prefix weights, shared k.q inner products, checkpoint read S_0 q, output
+combine, and the fused flush on every 16th step).  Inputs are seeded synthetic
+tensors with the workload's distributions, resident in device memory before the
+timed region; consecutive steps rotate over several independent layer instances
+(checkpoint + ring + conv state each) so the working set exceeds the 256 MB
+Infinity Cache and the state is streamed from HBM.
+
+Prints ONE JSON line.  `value` is decode tokens/s of the layer (batch x steps /
+time).  `roofline` is for the dominant kernel, replay_append_decode: algorithmic
+bytes per launch / its average launch duration measured with HIP events on its
+stream, against the 8 TB/s HBM peak.  `cpu_baseline` is the CPU oracle (ReplaySSM
+bookkeeping in float64 numpy) timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def _args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1024)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--layers", type=int, default=4, help="layer instances rotated per step")
+    ap.add_argument("--pool", type=int, default=32, help="distinct pre-generated step inputs")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-standard", action="store_true", help="skip the standard-step comparator")
+    ap.add_argument("--cpu-steps", type=int, default=32)
+    return ap.parse_args(argv)
+
+
+def _cpu_baseline(steps: int):
+    """The CPU oracle (ReplaySSM standard mode, float64) on the full batch of the
+    same workload for `steps` decode steps; single-threaded numpy elementwise code."""
+    import numpy as np
+
+    from oracle import replay as o_rep
+    from ssm_recurrent_decode_amd import synth
+    wl = synth.WORKLOADS[1]
+    sh, seed = wl.shape, wl.cfg_seed
+    A, bias = synth.mamba2_head_params(sh, seed, 1)
+    S0 = synth.state0(sh, seed, 1).astype(np.float64)
+    seq = []
+    for t in range(steps):
+        st = synth.mamba2_step_inputs(sh, seed, 1, t)
+        seq.append({"v": synth.bf16_bits_to_f64(st["v"]), "k": synth.bf16_bits_to_f64(st["k"]),
+                    "q": synth.bf16_bits_to_f64(st["q"]), "dt": st["dt"].astype(np.float64)})
+    t0 = time.perf_counter()
+    o_rep.run_standard(S0, seq, bias.astype(np.float64), A.astype(np.float64), sh.capacity, sh.ngroups)
+    dt = time.perf_counter() - t0
+    return {"value": sh.batch * steps / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"ReplaySSM standard-mode oracle, full batch {sh.batch}, {steps} decode steps "
+                      f"({steps // sh.capacity} flushes), float64 numpy, {dt:.1f} s"}
+
+
+def main(argv=None) -> int:
+    a = _args(argv)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the decode path has no cross-GPU step "
+              "(requests shard across GPUs with no exchange); run with --gpus 1",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import ssm_recurrent_decode_amd as rd
+    from ssm_recurrent_decode_amd import synth, traffic
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = synth.WORKLOADS[1]
+    sh, seed = wl.shape, wl.cfg_seed
+    B, H, D, N, G, L = sh.batch, sh.nheads, sh.head_dim, sh.state_dim, sh.ngroups, sh.capacity
+    C, W = wl.conv_channels, wl.conv_width
+    NL, P = a.layers, a.pool
+    dims = rd.Dims(B, H, D, N, G, L)
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    # ---- layer instances: checkpoint, ring, per-head params, conv state and taps
+    gen = torch.Generator(device=dev)
+    layers = []
+    for l in range(NL):
+        gen.manual_seed(seed * 100 + l)
+        S0 = torch.randn((B, H, D, N), generator=gen, device=dev) * math.sqrt(0.1)
+        A, bias = synth.mamba2_head_params(sh, seed, 1, layer=l)
+        cst, cw = synth.conv_layer(B, C, W, seed, 1, layer=l)
+        layers.append({"S0": S0, "ring": rd.Ring(dims, device=dev), "A": torch.from_numpy(A).to(dev),
+                       "bias": torch.from_numpy(bias).to(dev), "conv_state": bf(cst), "conv_w": bf(cw)})
+    # ---- pool of step inputs (cycled; values do not change the work done)
+    pool = []
+    for p in range(P):
+        st = synth.mamba2_step_inputs(sh, seed, 1, p)
+        pool.append({"v": bf(st["v"]), "k": bf(st["k"]), "q": bf(st["q"]),
+                     "dt": torch.from_numpy(st["dt"]).to(dev),
+                     "x": bf(synth.conv_step_input(B, C, seed, 1, p))})
+    y = torch.empty((B, H, D), device=dev)
+    conv_out = torch.empty((B, C), device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    calls = []
+    for l in range(NL):
+        Ly = layers[l]
+        per = []
+        for p in range(P):
+            ip = pool[p]
+            conv = rd.prepare_causal_conv1d_update(Ly["conv_state"], ip["x"], Ly["conv_w"], conv_out,
+                                                   stream=stream)
+            app = rd.prepare_replay_append_decode(dims, Ly["S0"], Ly["ring"], ip["v"], ip["k"], ip["q"],
+                                                  ip["dt"], Ly["bias"], Ly["A"], y, stream=stream)
+            per.append((conv, app))
+        calls.append(per)
+
+    def step_calls(t):
+        return calls[t % NL][(t // NL) % P]
+
+    # ---- warmup
+    for t in range(a.warmup):
+        conv, app = step_calls(t)
+        conv()
+        app()
+    torch.cuda.synchronize()
+
+    # ring fill level before each timed launch, from the integer schedule of each layer
+    def cached_before(step_index):
+        layer_step = step_index // NL            # steps this layer has taken before
+        return layer_step % L
+
+    K = a.steps
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(K):
+        t = a.warmup + i
+        conv, app = step_calls(t)
+        conv()
+        ev_a[i].record(stream)
+        app()
+        ev_b[i].record(stream)
+    end.record(stream)
+    end.synchronize()
+    total_ms = start.elapsed_time(end)
+    kern_ms = [ev_a[i].elapsed_time(ev_b[i]) for i in range(K)]
+    errs = [int(Ly["ring"].err.item()) for Ly in layers]
+    if any(errs):
+        raise RuntimeError(f"ring anomaly bits set: {errs}")
+
+    alg_bytes = 0
+    nflush = 0
+    for i in range(K):
+        h = cached_before(a.warmup + i)
+        fl = (h == L - 1)
+        nflush += fl
+        alg_bytes += traffic.replay_append(B, H, D, N, G, h, fl)
+    kern_total_s = sum(kern_ms) / 1e3
+    achieved = alg_bytes / kern_total_s / 1e9
+    ms_per_step = total_ms / K
+    value = B * K / (total_ms / 1e3)
+
+    out = {
+        "metric": "SSM decode tokens/s at batch 256 (Mamba-2 shape); achieved HBM GB/s vs peak",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
+        "config": {"workload": "Nemotron-H-like SSM layer decode step: causal conv1d update (3072x3 "
+                               "bf16, width 4) + ReplaySSM append-decode, batch 256, 32 heads, "
+                               "head dim 64, state 128, 8 groups, ring capacity 16",
+                   "batch": B, "nheads": H, "head_dim": D, "state_dim": N, "ngroups": G,
+                   "capacity": L, "conv_channels": C, "layer_instances_rotated": NL,
+                   "flush_steps_timed": nflush},
+        "roofline": {"bound": "hbm", "kernel": "replay_append_decode",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel_avg_us": round(1e3 * sum(kern_ms) / K, 3),
+                     "alg_bytes_per_launch": round(alg_bytes / K)},
+    }
+
+    if not a.no_standard:
+        # comparator: the baseline that writes the state back every step
+        std_calls = []
+        for l in range(NL):
+            Ly = layers[l]
+            std_calls.append([rd.prepare_ssm_decode_step(dims, Ly["S0"], pool[p]["v"], pool[p]["k"],
+                                                         pool[p]["q"], pool[p]["dt"], Ly["bias"],
+                                                         Ly["A"], y, stream=stream) for p in range(P)])
+        for t in range(32):
+            std_calls[t % NL][(t // NL) % P]()
+        s_a = torch.cuda.Event(enable_timing=True)
+        s_b = torch.cuda.Event(enable_timing=True)
+        Ks = min(K, 512)
+        torch.cuda.synchronize()
+        s_a.record(stream)
+        for t in range(Ks):
+            std_calls[t % NL][(t // NL) % P]()
+        s_b.record(stream)
+        s_b.synchronize()
+        std_us = 1e3 * s_a.elapsed_time(s_b) / Ks
+        std_bytes = traffic.standard_step(B, H, D, N, G)
+        out["standard_step"] = {"kernel": "ssm_decode_step", "us_per_step": round(std_us, 3),
+                                "achieved_GBs": round(std_bytes / (std_us * 1e-6) / 1e9, 1),
+                                "alg_bytes": std_bytes,
+                                "replay_speedup": round(std_us / (1e3 * sum(kern_ms) / K), 3)}
+
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = _cpu_baseline(a.cpu_steps)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,255 @@
+/*
+ * ssm_recurrent_decode.h -- C ABI of the MI355X (gfx950) batched single-token SSM
+ * decode library (libssm_recurrent_decode.so).
+ *
+ * What is computed comes from "ReplaySSM: Cache SSM Inputs, Not State" (a summary
+ * of Tri Dao's blog post); each entry point names the section it follows.  The
+ * conv state layout comes from the vLLM page on disaggregated prefill/decode for
+ * hybrid SSM models, section "DS Layout".
+ *
+ * General rules
+ * -------------
+ *  - Every pointer argument is a DEVICE pointer (hipMalloc'd or equivalent) owned
+ *    by the caller, unless stated otherwise.  The library never allocates, frees,
+ *    copies to the host or synchronises; a call validates its arguments on the
+ *    host, enqueues its kernels on `stream` and returns.  Every call is therefore
+ *    safe to capture in a HIP graph (no memset nodes are recorded).
+ *  - `stream` is a hipStream_t passed as void* (NULL = the legacy default stream).
+ *  - Return value: 0 = enqueued.  Negative = rejected on the host before anything
+ *    was enqueued: RSSM_EINVAL (null pointer, non-positive or inconsistent size,
+ *    H % G != 0, T < 1, L < 2T for a verify), RSSM_ENOTSUP (a (d, n, L, T) the
+ *    library was not built for), RSSM_ELAUNCH (the HIP launch itself failed).
+ *  - Device-side anomalies in the ring pointers (head/count/pending out of range,
+ *    accepted > pending, drafts left uncommitted) never fault: the kernels clamp
+ *    the value into range, proceed, and OR a bit into *ring->err (when err is not
+ *    NULL).  The caller reads that word whenever it chooses.
+ *  - Dense row-major layouts, innermost index last.  bf16 is passed as its
+ *    uint16_t bit pattern.  fp32 is IEEE binary32.
+ *  - Outputs must not alias inputs.  Different requests are independent, so two
+ *    calls on disjoint buffers may run on different streams concurrently; two
+ *    calls on the same ring must be ordered (same stream or events).
+ *
+ * Symbols: B batch, H nheads, d head_dim, n state_dim, G ngroups (head h reads
+ * the k/q of group h / (H / G)), L ring capacity, T draft window.
+ * Supported: d in {64, 128}; n = 128; 1 <= L <= 32; 1 <= T <= 8 with 2T <= L for
+ * the verify calls; any B >= 1, H >= 1 with H % G == 0.
+ */
+#ifndef SSM_RECURRENT_DECODE_H
+#define SSM_RECURRENT_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RSSM_ABI_VERSION 1
+
+#define RSSM_OK 0
+#define RSSM_EINVAL (-22)
+#define RSSM_ENOTSUP (-95)
+#define RSSM_ELAUNCH (-5)
+
+/* bits OR-ed into *ring->err by the kernels */
+#define RSSM_ERR_POINTERS 1  /* head/count/pending out of range on entry (clamped)       */
+#define RSSM_ERR_ACCEPTED 2  /* accepted[b] outside [0, pending[b]] (clamped)            */
+#define RSSM_ERR_PENDING 4   /* decode/verify called with uncommitted drafts (dropped)   */
+
+typedef struct rssm_dims {
+  int32_t batch;      /* B */
+  int32_t nheads;     /* H */
+  int32_t head_dim;   /* d: value / output length, rows of the per-head state */
+  int32_t state_dim;  /* n: key / query length, columns of the per-head state  */
+  int32_t ngroups;    /* G: k and q are shared by the H/G heads of a group     */
+  int32_t capacity;   /* L: ring capacity (ignored by the standard-step calls) */
+} rssm_dims;
+
+/*
+ * Per-request ReplaySSM decode memory besides the checkpoint state S_0.
+ * (Method, "core idea" and "three advantages"; kernel design, "ring buffer".)
+ * The ring holds the most recent inputs since the checkpoint, addressed modulo L
+ * from `head`, so a rollback only moves a pointer.  Physical slot of logical
+ * entry j (0 = oldest) of request b is (head[b] + j) % L.
+ *
+ * Caller allocates every array and zero-fills head, count, pending, arrive and
+ * err once before the first call; afterwards only the library writes them
+ * (rssm_ring_reset re-zeroes a subset of requests).
+ */
+typedef struct rssm_ring {
+  void* vu;          /* Mamba-2: v  bf16 [B, H, L, d];  GDN: u fp32 [B, H, L, d]     */
+  uint16_t* k;       /* bf16 [B, G, L, n]                                           */
+  float* dt;         /* Mamba-2: Delta fp32 [B, H, L] (after softplus);  GDN: unused */
+  float* decay;      /* Mamba-2: a = exp(A Delta);  GDN: alpha = exp(g);  fp32 [B,H,L] */
+  int32_t* head;     /* [B] physical slot of the oldest entry since the checkpoint */
+  int32_t* count;    /* [B] committed entries since the checkpoint                 */
+  int32_t* pending;  /* [B] uncommitted draft entries that follow them             */
+  int32_t* arrive;   /* [B] work-group arrival counters; zero between calls         */
+  int32_t* err;      /* [1] anomaly bits (RSSM_ERR_*), may be NULL                  */
+} rssm_ring;
+
+int rssm_abi_version(void);
+const char* rssm_strerror(int code);
+
+/* Bytes of each ring array for the given dims: writes 9 sizes in the order of
+ * the rssm_ring fields (vu, k, dt, decay, head, count, pending, arrive, err).
+ * is_gdn selects fp32 u instead of bf16 v and no dt array.  Host-only. */
+int rssm_ring_sizes(const rssm_dims* dims, int is_gdn, size_t out_bytes[9]);
+
+/* Zero head/count/pending for requests with mask[b] != 0 (mask NULL = all) and
+ * clear err.  The ring contents are left as they are: with count = 0 they are
+ * never read.  Use after an explicit replay_flush to recycle a request slot, or
+ * to start a new request from a checkpoint state. */
+int rssm_ring_reset(const rssm_dims* dims, rssm_ring* ring, const int32_t* mask, void* stream);
+
+/* ---------------------------------------------------------------- Mamba-2 */
+
+/*
+ * Standard Mamba-2 decode step with state write-back (the baseline).
+ * Background, "memory-bound": S_t = a_t S_{t-1} + Delta_t v_t k_t^T, y_t = S_t q_t,
+ * a_t = exp(A Delta_t); algorithms, "Mamba-2 standard decode", baseline bullet.
+ *   state   fp32 [B, H, d, n]  in/out
+ *   v       bf16 [B, H, d];  k, q bf16 [B, G, n]
+ *   dt      fp32 [B, H] raw step; Delta = softplus(dt + dt_bias[h])
+ *   dt_bias fp32 [H];  A fp32 [H] (negative)
+ *   y       fp32 [B, H, d]  out
+ */
+int ssm_decode_step(const rssm_dims* dims, float* state, const uint16_t* v, const uint16_t* k,
+                    const uint16_t* q, const float* dt, const float* dt_bias, const float* A,
+                    float* y, void* stream);
+
+/*
+ * ReplaySSM append-decode for one token per request.
+ * Algorithms, "Mamba-2 standard decode", ReplaySSM bullet; method, "output-only
+ * decode": append (v, Delta, k) and the decay a to the ring; with the c entries
+ * since the checkpoint (this one included),
+ *     y = abar (S_0 q) + sum_j s_j (k_j^T q) v_j,
+ *     abar = prod_i a_i,  s_j = Delta_j prod_{i>j} a_i;
+ * S_0 is only read.  When the append fills the ring (c == L) the same call
+ * flushes: S_0 <- abar S_0 + sum_j s_j v_j k_j^T, head advances by L, count = 0.
+ * The flush decision is per request, read from count at run time.
+ *   state0  fp32 [B, H, d, n] checkpoint, read (written on flush steps)
+ *   ring    Mamba-2 ring; requires pending == 0 and count < L on entry
+ *   v, k, q, dt, dt_bias, A, y  as ssm_decode_step
+ *   flushed int32 [B] out (1 = this request flushed), may be NULL
+ */
+int replay_append_decode(const rssm_dims* dims, float* state0, rssm_ring* ring,
+                         const uint16_t* v, const uint16_t* k, const uint16_t* q,
+                         const float* dt, const float* dt_bias, const float* A, float* y,
+                         int32_t* flushed, void* stream);
+
+/*
+ * Explicit flush of the committed entries (method, "core idea": summarise the
+ * buffered inputs into the state and clear the buffer).  For requests with
+ * mask[b] != 0 (mask NULL = all) and count > 0:
+ *     S_0 <- abar S_0 + sum_{j<count} s_j v_j k_j^T ;  head += count ;  count = 0.
+ * Pending drafts stay cached after the new head.
+ */
+int replay_flush(const rssm_dims* dims, float* state0, rssm_ring* ring, const int32_t* mask,
+                 void* stream);
+
+/*
+ * ReplaySSM speculative verify of T drafts per request.
+ * Algorithms, "speculative decoding", ReplaySSM bullet and the flush-decision
+ * rule: drafts go to the slots after the c committed entries; draft s (0-based)
+ * sees p_s = c + s + 1 entries:
+ *     y_s = abar_s (S_0 q_s) + sum_{j<p_s} w_{j,s} (k_j^T q_s) v_j,
+ *     abar_s = prod_{i<p_s} a_i,  w_{j,s} = Delta_j prod_{j<i<p_s} a_i.
+ * If c + 2T > L the c committed entries (never the drafts) are folded into S_0
+ * in the same call (head += c, count = 0), so at least T slots stay free for the
+ * next window.  pending becomes T; replay_rollback commits the accepted prefix.
+ *   v bf16 [B, T, H, d];  k, q bf16 [B, T, G, n];  dt fp32 [B, T, H] raw
+ *   y fp32 [B, T, H, d] out (every draft position, rejected ones included)
+ *   flushed int32 [B] out, may be NULL
+ * Requires 1 <= T, 2T <= L; on entry pending == 0 and count + T <= L.
+ */
+int replay_verify_T(const rssm_dims* dims, int32_t T, float* state0, rssm_ring* ring,
+                    const uint16_t* v, const uint16_t* k, const uint16_t* q, const float* dt,
+                    const float* dt_bias, const float* A, float* y, int32_t* flushed,
+                    void* stream);
+
+/*
+ * Device-side commit / rollback (method, "rollback becomes a buffer operation";
+ * CUDA-Graph notes, "device-side commit and rollback"): for every request
+ *     count += clamp(accepted[b], 0, pending[b]);  pending = 0.
+ * Rejected drafts are simply left beyond count.  No host synchronisation.
+ * Shared by the Mamba-2 and GDN rings (it touches pointers only).
+ *   accepted int32 [B] (device)
+ */
+int replay_rollback(const rssm_dims* dims, rssm_ring* ring, const int32_t* accepted,
+                    void* stream);
+
+/* ---------------------------------------------------------- Gated DeltaNet */
+
+/*
+ * Standard GDN decode step with state write-back (baseline).
+ * Background: S_t = e^{g_t} S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ * y_t = S_t q_t; computed as u = beta (v - e^g S k), S <- e^g S + u k^T.
+ *   state fp32 [B, H, d, n] in/out;  v bf16 [B, H, d];  k, q bf16 [B, G, n]
+ *   g, beta fp32 [B, H] (already activated: g <= 0, 0 < beta < 1)
+ *   y fp32 [B, H, d] out
+ */
+int gdn_decode_step(const rssm_dims* dims, float* state, const uint16_t* v, const uint16_t* k,
+                    const uint16_t* q, const float* g, const float* beta, float* y,
+                    void* stream);
+
+/*
+ * ReplaySSM GDN speculative verify (appendix, "GDN speculative decoding" and
+ * "GDN standard decode").  The ring caches the corrections u (fp32) with k and
+ * alpha = e^g.  With the committed state S_h = abar S_0 + sum_j w_j u_j k_j^T
+ * read only through products with the 2T draft vectors, gamma_s = prod_{i<=s}
+ * alpha_i over the window:
+ *     R_s = beta_s (v_s - gamma_s S_h k_s),
+ *     A_{s,s'} = beta_s (gamma_s / gamma_s') (k_s . k_s')   (s' < s),
+ *     (I + A) U = R  (strictly lower-triangular T x T solve),
+ *     y_s = gamma_s S_h q_s + sum_{s'<=s} (gamma_s / gamma_s') (k_s' . q_s) u_s'.
+ * (u_s, k_s, alpha_s) are written after the committed entries; early flush of
+ * the committed entries when c + 2T > L, as replay_verify_T; pending = T.
+ *   v bf16 [B, T, H, d];  k, q bf16 [B, T, G, n];  g, beta fp32 [B, T, H]
+ *   y fp32 [B, T, H, d] out;  flushed int32 [B] out, may be NULL
+ */
+int gdn_replay_verify_T(const rssm_dims* dims, int32_t T, float* state0, rssm_ring* ring,
+                        const uint16_t* v, const uint16_t* k, const uint16_t* q, const float* g,
+                        const float* beta, float* y, int32_t* flushed, void* stream);
+
+/*
+ * Explicit GDN flush (appendix, state-and-output route): for requests with
+ * mask[b] != 0 (NULL = all) and count > 0,
+ *     S_0 <- abar S_0 + sum_{j<count} w_j u_j k_j^T,  w_j = prod_{j<i<count} alpha_i,
+ * head += count, count = 0.
+ */
+int gdn_replay_flush(const rssm_dims* dims, float* state0, rssm_ring* ring, const int32_t* mask,
+                     void* stream);
+
+/* ---------------------------------------------------------- causal conv1d */
+
+/*
+ * Fused causal depthwise conv1d state update with SiLU, one token per request.
+ * The conv state is stored channel-major with the time axis fastest, the
+ * (dim, state_len) "DS" layout of the vLLM disaggregation page.  With
+ * window = [state[b,c,0..W-2], x[b,c]]:
+ *     out[b,c] = SiLU(sum_w weight[c,w] window[w]);  state[b,c,:] <- window[1..W-1].
+ *   conv_state bf16 [B, C, W-1] in/out;  x bf16 [B, C];  weight bf16 [C, W]
+ *   out fp32 [B, C]
+ * Supported: W = 4.
+ */
+int causal_conv1d_update(int32_t batch, int32_t channels, int32_t width, uint16_t* conv_state,
+                         const uint16_t* x, const uint16_t* weight, float* out, void* stream);
+
+/* ---------------------------------------------------------- measurement aid */
+
+/*
+ * Streaming HBM probes used to calibrate traffic counters and to record the
+ * achievable bandwidth: rssm_probe_copy copies `bytes` (multiple of 16) from
+ * src to dst; rssm_probe_read reads `bytes` and writes one fp32 checksum per
+ * work-group into sink (sink holds at least rssm_probe_read_sink_floats(bytes)).
+ */
+int rssm_probe_copy(void* dst, const void* src, size_t bytes, void* stream);
+int rssm_probe_read(const void* src, size_t bytes, float* sink, void* stream);
+size_t rssm_probe_read_sink_floats(size_t bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_RECURRENT_DECODE_H */

@@ -198,3 +198,38 @@ def run_spec(S0, rounds, dt_bias, A, L, G, accepted):
         fl.append(np.array(fb))
         starts.append(np.array(cb))
     return ys, fl, starts, reqs
+
+
+def pointer_schedule_standard(L: int, steps: int, head0: int = 0, count0: int = 0):
+    """Integer bookkeeping of standard decode alone: per step (head, count,
+    flushed) after the call.  Append adds one entry; the step that fills the ring
+    folds all L entries and moves head past them."""
+    head, count = head0, count0
+    out = []
+    for _ in range(steps):
+        count += 1
+        flushed = count == L
+        if flushed:
+            head = (head + count) % L
+            count = 0
+        out.append((head, count, flushed))
+    return out
+
+
+def pointer_schedule_spec(L: int, T: int, accepted):
+    """Integer bookkeeping of speculative rounds alone, for one request:
+    per round (count at round start, flushed, head after verify, count after
+    verify, count after commit).  The verify folds the committed entries when
+    c + 2T > L; the commit keeps ``accepted[r]`` drafts."""
+    head, count = 0, 0
+    out = []
+    for a in accepted:
+        c = count
+        flushed = c + 2 * T > L
+        if flushed:
+            head = (head + c) % L
+            count = 0
+        after_verify = (head, count)
+        count += int(a)
+        out.append((c, flushed, after_verify[0], after_verify[1], count))
+    return out

@@ -1,0 +1,280 @@
+"""Thin PyTorch binding of the C ABI: the same entry-point names, tensors instead of
+raw pointers.  Every function only checks dtypes, shapes, contiguity and device,
+then passes data pointers and the current HIP stream to the library; all compute
+happens in the HIP kernels.  Non-zero return codes raise RuntimeError.
+
+bf16 arguments may be torch.bfloat16 tensors or int16/uint16 tensors holding the
+bit patterns.  PyTorch is used for device memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+_F32 = (torch.float32,)
+_I32 = (torch.int32,)
+
+
+@dataclass(frozen=True)
+class Dims:
+    batch: int
+    nheads: int
+    head_dim: int
+    state_dim: int
+    ngroups: int
+    capacity: int = 1
+
+    def c(self) -> _lib.rssm_dims:
+        return _lib.rssm_dims(self.batch, self.nheads, self.head_dim, self.state_dim,
+                              self.ngroups, self.capacity)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _p(t, name, dtypes, shape, allow_none=False):
+    if t is None:
+        if allow_none:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if t.data_ptr() % 16 != 0:
+        raise ValueError(f"{name} must be 16-byte aligned (the kernels use 16-byte vector loads)")
+    return t.data_ptr()
+
+
+class Ring:
+    """Device arrays of one layer's ReplaySSM ring (see rssm_ring in the header).
+
+    Allocated zero-filled with torch on ``device``; ``gdn`` selects fp32
+    corrections u instead of bf16 values v and no step-size array."""
+
+    def __init__(self, dims: Dims, gdn: bool = False, device="cuda"):
+        B, H, G, L = dims.batch, dims.nheads, dims.ngroups, dims.capacity
+        D, N = dims.head_dim, dims.state_dim
+        self.dims, self.gdn = dims, gdn
+        z = dict(device=device)
+        self.vu = torch.zeros((B, H, L, D), dtype=torch.float32 if gdn else torch.bfloat16, **z)
+        self.k = torch.zeros((B, G, L, N), dtype=torch.bfloat16, **z)
+        self.dt = None if gdn else torch.zeros((B, H, L), dtype=torch.float32, **z)
+        self.decay = torch.zeros((B, H, L), dtype=torch.float32, **z)
+        self.head = torch.zeros((B,), dtype=torch.int32, **z)
+        self.count = torch.zeros((B,), dtype=torch.int32, **z)
+        self.pending = torch.zeros((B,), dtype=torch.int32, **z)
+        self.arrive = torch.zeros((B,), dtype=torch.int32, **z)
+        self.err = torch.zeros((1,), dtype=torch.int32, **z)
+
+    def c(self) -> _lib.rssm_ring:
+        return _lib.rssm_ring(self.vu.data_ptr(), self.k.data_ptr(),
+                              None if self.dt is None else self.dt.data_ptr(),
+                              self.decay.data_ptr(), self.head.data_ptr(), self.count.data_ptr(),
+                              self.pending.data_ptr(), self.arrive.data_ptr(), self.err.data_ptr())
+
+    def tensors(self):
+        return {k: getattr(self, k) for k in ("vu", "k", "dt", "decay", "head", "count",
+                                              "pending", "arrive", "err")}
+
+
+def ring_sizes(dims: Dims, gdn: bool = False):
+    out = (ctypes.c_size_t * 9)()
+    d = dims.c()
+    _lib.check(_lib.load().rssm_ring_sizes(ctypes.byref(d), int(gdn), out), "rssm_ring_sizes")
+    return list(out)
+
+
+def rssm_ring_reset(dims: Dims, ring: Ring, mask=None, stream=None):
+    d, rc = dims.c(), ring.c()
+    m = _p(mask, "mask", _I32, (dims.batch,), allow_none=True)
+    _lib.check(_lib.load().rssm_ring_reset(ctypes.byref(d), ctypes.byref(rc), m, _stream(stream)),
+               "rssm_ring_reset")
+
+
+# ------------------------------------------------------------------ Mamba-2
+def ssm_decode_step(dims: Dims, state, v, k, q, dt, dt_bias, A, y, stream=None):
+    B, H, D, N, G = dims.batch, dims.nheads, dims.head_dim, dims.state_dim, dims.ngroups
+    d = dims.c()
+    args = (_p(state, "state", _F32, (B, H, D, N)), _p(v, "v", _BF16, (B, H, D)),
+            _p(k, "k", _BF16, (B, G, N)), _p(q, "q", _BF16, (B, G, N)),
+            _p(dt, "dt", _F32, (B, H)), _p(dt_bias, "dt_bias", _F32, (H,)),
+            _p(A, "A", _F32, (H,)), _p(y, "y", _F32, (B, H, D)))
+    _lib.check(_lib.load().ssm_decode_step(ctypes.byref(d), *args, _stream(stream)), "ssm_decode_step")
+
+
+def _ring_args(dims: Dims, ring: Ring, gdn: bool):
+    if ring.gdn != gdn:
+        raise ValueError("ring kind does not match the call (Mamba-2 vs GDN)")
+    if ring.dims != dims:
+        raise ValueError("ring was allocated for different dims")
+    return ring.c()
+
+
+def replay_append_decode(dims: Dims, state0, ring: Ring, v, k, q, dt, dt_bias, A, y,
+                         flushed=None, stream=None):
+    B, H, D, N, G = dims.batch, dims.nheads, dims.head_dim, dims.state_dim, dims.ngroups
+    d, rc = dims.c(), _ring_args(dims, ring, False)
+    args = (_p(state0, "state0", _F32, (B, H, D, N)), ctypes.byref(rc),
+            _p(v, "v", _BF16, (B, H, D)), _p(k, "k", _BF16, (B, G, N)),
+            _p(q, "q", _BF16, (B, G, N)), _p(dt, "dt", _F32, (B, H)),
+            _p(dt_bias, "dt_bias", _F32, (H,)), _p(A, "A", _F32, (H,)),
+            _p(y, "y", _F32, (B, H, D)), _p(flushed, "flushed", _I32, (B,), allow_none=True))
+    _lib.check(_lib.load().replay_append_decode(ctypes.byref(d), *args, _stream(stream)),
+               "replay_append_decode")
+
+
+def replay_flush(dims: Dims, state0, ring: Ring, mask=None, stream=None):
+    B, H, D, N = dims.batch, dims.nheads, dims.head_dim, dims.state_dim
+    d, rc = dims.c(), _ring_args(dims, ring, False)
+    _lib.check(_lib.load().replay_flush(
+        ctypes.byref(d), _p(state0, "state0", _F32, (B, H, D, N)), ctypes.byref(rc),
+        _p(mask, "mask", _I32, (B,), allow_none=True), _stream(stream)), "replay_flush")
+
+
+def replay_verify_T(dims: Dims, T: int, state0, ring: Ring, v, k, q, dt, dt_bias, A, y,
+                    flushed=None, stream=None):
+    B, H, D, N, G = dims.batch, dims.nheads, dims.head_dim, dims.state_dim, dims.ngroups
+    d, rc = dims.c(), _ring_args(dims, ring, False)
+    args = (_p(state0, "state0", _F32, (B, H, D, N)), ctypes.byref(rc),
+            _p(v, "v", _BF16, (B, T, H, D)), _p(k, "k", _BF16, (B, T, G, N)),
+            _p(q, "q", _BF16, (B, T, G, N)), _p(dt, "dt", _F32, (B, T, H)),
+            _p(dt_bias, "dt_bias", _F32, (H,)), _p(A, "A", _F32, (H,)),
+            _p(y, "y", _F32, (B, T, H, D)), _p(flushed, "flushed", _I32, (B,), allow_none=True))
+    _lib.check(_lib.load().replay_verify_T(ctypes.byref(d), int(T), *args, _stream(stream)),
+               "replay_verify_T")
+
+
+def replay_rollback(dims: Dims, ring: Ring, accepted, stream=None):
+    d, rc = dims.c(), ring.c()
+    _lib.check(_lib.load().replay_rollback(
+        ctypes.byref(d), ctypes.byref(rc), _p(accepted, "accepted", _I32, (dims.batch,)),
+        _stream(stream)), "replay_rollback")
+
+
+# ------------------------------------------------------------------ Gated DeltaNet
+def gdn_decode_step(dims: Dims, state, v, k, q, g, beta, y, stream=None):
+    B, H, D, N, G = dims.batch, dims.nheads, dims.head_dim, dims.state_dim, dims.ngroups
+    d = dims.c()
+    args = (_p(state, "state", _F32, (B, H, D, N)), _p(v, "v", _BF16, (B, H, D)),
+            _p(k, "k", _BF16, (B, G, N)), _p(q, "q", _BF16, (B, G, N)),
+            _p(g, "g", _F32, (B, H)), _p(beta, "beta", _F32, (B, H)), _p(y, "y", _F32, (B, H, D)))
+    _lib.check(_lib.load().gdn_decode_step(ctypes.byref(d), *args, _stream(stream)), "gdn_decode_step")
+
+
+def gdn_replay_verify_T(dims: Dims, T: int, state0, ring: Ring, v, k, q, g, beta, y,
+                        flushed=None, stream=None):
+    B, H, D, N, G = dims.batch, dims.nheads, dims.head_dim, dims.state_dim, dims.ngroups
+    d, rc = dims.c(), _ring_args(dims, ring, True)
+    args = (_p(state0, "state0", _F32, (B, H, D, N)), ctypes.byref(rc),
+            _p(v, "v", _BF16, (B, T, H, D)), _p(k, "k", _BF16, (B, T, G, N)),
+            _p(q, "q", _BF16, (B, T, G, N)), _p(g, "g", _F32, (B, T, H)),
+            _p(beta, "beta", _F32, (B, T, H)), _p(y, "y", _F32, (B, T, H, D)),
+            _p(flushed, "flushed", _I32, (B,), allow_none=True))
+    _lib.check(_lib.load().gdn_replay_verify_T(ctypes.byref(d), int(T), *args, _stream(stream)),
+               "gdn_replay_verify_T")
+
+
+def gdn_replay_flush(dims: Dims, state0, ring: Ring, mask=None, stream=None):
+    B, H, D, N = dims.batch, dims.nheads, dims.head_dim, dims.state_dim
+    d, rc = dims.c(), _ring_args(dims, ring, True)
+    _lib.check(_lib.load().gdn_replay_flush(
+        ctypes.byref(d), _p(state0, "state0", _F32, (B, H, D, N)), ctypes.byref(rc),
+        _p(mask, "mask", _I32, (B,), allow_none=True), _stream(stream)), "gdn_replay_flush")
+
+
+# ------------------------------------------------------------------ conv1d
+def causal_conv1d_update(conv_state, x, weight, out, stream=None):
+    if conv_state.dim() != 3:
+        raise ValueError("conv_state must be [B, C, W-1]")
+    B, C, Wm1 = conv_state.shape
+    W = Wm1 + 1
+    args = (_p(conv_state, "conv_state", _BF16, (B, C, Wm1)), _p(x, "x", _BF16, (B, C)),
+            _p(weight, "weight", _BF16, (C, W)), _p(out, "out", _F32, (B, C)))
+    _lib.check(_lib.load().causal_conv1d_update(B, C, W, *args, _stream(stream)),
+               "causal_conv1d_update")
+
+
+# ------------------------------------------------------------------ probes
+def rssm_probe_copy(dst, src, stream=None):
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < n:
+        raise ValueError("dst smaller than src")
+    _lib.check(_lib.load().rssm_probe_copy(dst.data_ptr(), src.data_ptr(), n, _stream(stream)),
+               "rssm_probe_copy")
+
+
+def rssm_probe_read(src, sink, stream=None):
+    n = src.numel() * src.element_size()
+    need = _lib.load().rssm_probe_read_sink_floats(n)
+    if sink.dtype != torch.float32 or sink.numel() < need:
+        raise ValueError(f"sink must be fp32 with >= {need} elements")
+    _lib.check(_lib.load().rssm_probe_read(src.data_ptr(), n, sink.data_ptr(), _stream(stream)),
+               "rssm_probe_read")
+
+
+def probe_read_sink_floats(nbytes: int) -> int:
+    return int(_lib.load().rssm_probe_read_sink_floats(nbytes))
+
+
+# ------------------------------------------------------------------ prepared calls
+class Prepared:
+    """A library call with every pointer argument resolved once.
+
+    Calling it re-issues the same C call (same buffers, same stream) with no
+    per-call marshalling, for tight timing loops and graph capture."""
+
+    def __init__(self, fn, *args, keep=()):
+        self._fn, self._args, self._keep = fn, args, keep
+
+    def __call__(self):
+        rc = self._fn(*self._args)
+        if rc != 0:
+            _lib.check(rc, self._fn.__name__)
+
+
+def prepare_replay_append_decode(dims: Dims, state0, ring: Ring, v, k, q, dt, dt_bias, A, y,
+                                 flushed=None, stream=None) -> Prepared:
+    B, H, D, N, G = dims.batch, dims.nheads, dims.head_dim, dims.state_dim, dims.ngroups
+    d, rc = dims.c(), _ring_args(dims, ring, False)
+    args = (ctypes.byref(d), _p(state0, "state0", _F32, (B, H, D, N)), ctypes.byref(rc),
+            _p(v, "v", _BF16, (B, H, D)), _p(k, "k", _BF16, (B, G, N)),
+            _p(q, "q", _BF16, (B, G, N)), _p(dt, "dt", _F32, (B, H)),
+            _p(dt_bias, "dt_bias", _F32, (H,)), _p(A, "A", _F32, (H,)),
+            _p(y, "y", _F32, (B, H, D)), _p(flushed, "flushed", _I32, (B,), allow_none=True),
+            _stream(stream))
+    return Prepared(_lib.load().replay_append_decode, *args, keep=(d, rc))
+
+
+def prepare_ssm_decode_step(dims: Dims, state, v, k, q, dt, dt_bias, A, y, stream=None) -> Prepared:
+    B, H, D, N, G = dims.batch, dims.nheads, dims.head_dim, dims.state_dim, dims.ngroups
+    d = dims.c()
+    args = (ctypes.byref(d), _p(state, "state", _F32, (B, H, D, N)), _p(v, "v", _BF16, (B, H, D)),
+            _p(k, "k", _BF16, (B, G, N)), _p(q, "q", _BF16, (B, G, N)),
+            _p(dt, "dt", _F32, (B, H)), _p(dt_bias, "dt_bias", _F32, (H,)),
+            _p(A, "A", _F32, (H,)), _p(y, "y", _F32, (B, H, D)), _stream(stream))
+    return Prepared(_lib.load().ssm_decode_step, *args, keep=(d,))
+
+
+def prepare_causal_conv1d_update(conv_state, x, weight, out, stream=None) -> Prepared:
+    B, C, Wm1 = conv_state.shape
+    args = (B, C, Wm1 + 1, _p(conv_state, "conv_state", _BF16, (B, C, Wm1)),
+            _p(x, "x", _BF16, (B, C)), _p(weight, "weight", _BF16, (C, Wm1 + 1)),
+            _p(out, "out", _F32, (B, C)), _stream(stream))
+    return Prepared(_lib.load().causal_conv1d_update, *args)

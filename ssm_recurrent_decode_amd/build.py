@@ -1,0 +1,101 @@
+"""Build libssm_recurrent_decode.so for gfx950 in-tree with hipcc.
+
+    python -m ssm_recurrent_decode_amd.build [--jobs N]
+
+Each csrc/*.hip file is compiled to an object under _build/ (in parallel), then the
+objects are linked into ssm_recurrent_decode_amd/libssm_recurrent_decode.so.  The
+device assembly of every object is kept next to it and scanned for instructions
+this library must never contain (see isa_check.py, when present).
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import glob
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB_NAME = "libssm_recurrent_decode.so"
+LIB_PATH = os.path.join(PKG, LIB_NAME)
+ARCH = "gfx950"
+
+HIPCC_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    # keep hipcc from forming packed fp32 arithmetic on its own
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # one plain atomic per work-group: no wave-level rewrite, so its return value is
+    # only waited for where it is used
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
+    "-I", INCLUDE, "-I", CSRC,
+    "-Wall", "-Wno-unused-result",
+]
+
+
+def _hipcc() -> str:
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: the HIP toolchain (ROCm) is required to build")
+
+
+def _compile(src: str) -> tuple[str, str]:
+    name = os.path.splitext(os.path.basename(src))[0]
+    obj = os.path.join(BUILD, name + ".o")
+    asm = os.path.join(BUILD, name + f"-{ARCH}.s")
+    hipcc = _hipcc()
+    cmd = [hipcc, *HIPCC_FLAGS, "-c", src, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+    # device assembly of the same translation unit, for the instruction scan
+    cmd_s = [hipcc, *HIPCC_FLAGS, "--cuda-device-only", "-S", src, "-o", asm]
+    r = subprocess.run(cmd_s, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed for {src}:\n{r.stdout}\n{r.stderr}")
+    return obj, asm
+
+
+def build(jobs: int | None = None, verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    if not srcs:
+        raise RuntimeError("no HIP sources found")
+    jobs = jobs or min(len(srcs), max(1, os.cpu_count() or 1))
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        results = list(ex.map(_compile, srcs))
+    objs = [o for o, _ in results]
+    asms = [a for _, a in results]
+    try:
+        from . import isa_check  # not shipped to every machine; building happens here
+    except ImportError:
+        isa_check = None
+    if isa_check is not None:
+        isa_check.check(asms)
+    tmp = LIB_PATH + ".tmp"
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, LIB_PATH)
+    if verbose:
+        print(f"built {LIB_PATH}")
+    return LIB_PATH
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--jobs", type=int, default=None)
+    a = ap.parse_args(argv)
+    build(a.jobs, verbose=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,88 @@
+// Library-wide C ABI helpers (version, error strings, ring sizing) and the
+// streaming HBM probes used to calibrate traffic counters.
+#include "common.hpp"
+
+namespace rssm {
+
+struct CopyParams {
+  float4* dst;
+  const float4* src;
+  size_t n16;
+};
+
+// Grid-stride float4 copy: one read and one write of every byte.
+__global__ __launch_bounds__(kBlock) void probe_copy_kernel(CopyParams p) {
+  const size_t stride = (size_t)gridDim.x * kBlock;
+  for (size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x; i < p.n16; i += stride)
+    p.dst[i] = p.src[i];
+}
+
+struct ReadParams {
+  const float4* src;
+  float* sink;
+  size_t n16;
+};
+
+constexpr int kProbeBlocks = 4096;
+
+// Grid-stride float4 read; one checksum per work-group keeps the loads live.
+__global__ __launch_bounds__(kBlock) void probe_read_kernel(ReadParams p) {
+  __shared__ float red[kBlock / kWave];
+  const size_t stride = (size_t)gridDim.x * kBlock;
+  float acc = 0.f;
+  for (size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x; i < p.n16; i += stride) {
+    const float4 v = p.src[i];
+    acc += (v.x + v.y) + (v.z + v.w);
+  }
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, kWave);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) p.sink[blockIdx.x] = red[0] + red[1] + red[2] + red[3];
+}
+
+}  // namespace rssm
+
+extern "C" int rssm_abi_version(void) { return RSSM_ABI_VERSION; }
+
+extern "C" const char* rssm_strerror(int code) {
+  switch (code) {
+    case RSSM_OK: return "ok";
+    case RSSM_EINVAL: return "invalid argument (null pointer, bad or inconsistent size)";
+    case RSSM_ENOTSUP: return "shape not supported by this build (d in {64,128}, n = 128, L <= 32, T <= 8)";
+    case RSSM_ELAUNCH: return "HIP kernel launch failed";
+    default: return "unknown error code";
+  }
+}
+
+extern "C" int rssm_ring_sizes(const rssm_dims* d, int is_gdn, size_t out[9]) {
+  if (!rssm_host::dims_ok(d) || d->capacity < 1 || out == nullptr) return RSSM_EINVAL;
+  const size_t B = d->batch, H = d->nheads, G = d->ngroups, L = d->capacity;
+  const size_t D = d->head_dim, N = d->state_dim;
+  out[0] = B * H * L * D * (is_gdn ? 4 : 2);
+  out[1] = B * G * L * N * 2;
+  out[2] = is_gdn ? 0 : B * H * L * 4;
+  out[3] = B * H * L * 4;
+  out[4] = out[5] = out[6] = out[7] = B * 4;
+  out[8] = 4;
+  return RSSM_OK;
+}
+
+extern "C" int rssm_probe_copy(void* dst, const void* src, size_t bytes, void* stream) {
+  if (!dst || !src || bytes == 0 || bytes % 16 != 0) return RSSM_EINVAL;
+  rssm::CopyParams p{static_cast<float4*>(dst), static_cast<const float4*>(src), bytes / 16};
+  const size_t want = (p.n16 + rssm::kBlock - 1) / rssm::kBlock;
+  const dim3 grid((unsigned)(want < rssm::kProbeBlocks ? want : rssm::kProbeBlocks));
+  return rssm_host::launch(rssm::probe_copy_kernel, grid, dim3(rssm::kBlock), stream, p);
+}
+
+extern "C" size_t rssm_probe_read_sink_floats(size_t bytes) {
+  const size_t want = (bytes / 16 + rssm::kBlock - 1) / rssm::kBlock;
+  return want < (size_t)rssm::kProbeBlocks ? (want ? want : 1) : (size_t)rssm::kProbeBlocks;
+}
+
+extern "C" int rssm_probe_read(const void* src, size_t bytes, float* sink, void* stream) {
+  if (!src || !sink || bytes == 0 || bytes % 16 != 0) return RSSM_EINVAL;
+  rssm::ReadParams p{static_cast<const float4*>(src), sink, bytes / 16};
+  const dim3 grid((unsigned)rssm_probe_read_sink_floats(bytes));
+  return rssm_host::launch(rssm::probe_read_kernel, grid, dim3(rssm::kBlock), stream, p);
+}

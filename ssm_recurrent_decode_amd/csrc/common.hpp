@@ -1,0 +1,197 @@
+// Shared device/host helpers for the gfx950 decode kernels.
+//
+// Lane layout used by every state-streaming kernel ("tile layout")
+// ------------------------------------------------------------------
+// A per-head state is a d x n fp32 matrix stored row-major (n fastest).  It is cut
+// into 16 x 16 tiles.  In a wave of 64 lanes, lane l owns row r = l & 15 of a row
+// tile and the four consecutive columns 4*(l >> 4) .. +3 of every 16-column tile,
+// loaded as one float4 per tile.  This is exactly the accumulator layout of
+// v_mfma_f32_16x16x4_f32 when the MFMA computes the transposed tile (state columns
+// on the M axis, state rows on the N axis), so a rank-c update S += V diag(w) K^T
+// runs on the matrix cores straight from the registers the state was loaded into,
+// and a row's dot product with a vector needs only a two-step reduction over the
+// four lanes l, l^16, l^32, l^48 that share the row.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ssm_recurrent_decode.h"
+
+namespace rssm {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;          // four waves per work-group
+constexpr int kWavesPerBlock = kBlock / kWave;
+constexpr int kMaxL = 32;            // ring capacity limit (entries fit one wave)
+constexpr int kMaxT = 8;             // draft window limit
+constexpr int kNumXcd = 8;           // MI355X: eight accelerator dies, one L2 each
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// softplus in fp32; above 20 the correction log1p(e^-x) is below fp32 resolution.
+__device__ __forceinline__ float softplus_f32(float x) { return x > 20.f ? x : log1pf(expf(x)); }
+
+// Work-groups are dispatched round-robin over the XCDs (block i -> XCD i % 8).
+// Renumber so that each XCD receives a contiguous range of logical work-groups:
+// neighbouring heads of one request (which share k/q and the group's ring keys)
+// then meet in the same L2.  Blocks past the largest multiple of 8 keep their id.
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  const int per = nblocks / kNumXcd;
+  const int full = per * kNumXcd;
+  if (bid >= full) return bid;
+  return (bid % kNumXcd) * per + bid / kNumXcd;
+}
+
+// Physical slot of logical ring entry j (0 <= j < L) when the oldest entry sits in
+// slot head (0 <= head < L): head + j wraps at most once.
+__device__ __forceinline__ int ring_slot(int head, int j, int L) {
+  const int s = head + j;
+  return s >= L ? s - L : s;
+}
+
+// Exclusive suffix product across the lanes of a wave, for values that are 1 on
+// every lane >= 32: returns prod_{i > lane} x_i and sets *all = prod_i x_i.  Five
+// log-steps instead of a serial chain; products only, never a division, so an
+// underflow to zero stays zero.
+__device__ __forceinline__ float suffix_product_excl(float x, int lane, float* all) {
+  float v = x;
+#pragma unroll
+  for (int off = 1; off < 32; off <<= 1) {
+    const float o = __shfl_down(v, off, kWave);
+    v = (lane + off < kWave) ? v * o : v;
+  }
+  *all = __shfl(v, 0, kWave);
+  const float ex = __shfl_down(v, 1, kWave);
+  return (lane + 1 < kWave) ? ex : 1.f;
+}
+
+// Sum over the four lanes that share a row in the tile layout.
+__device__ __forceinline__ float reduce_row4(float v) {
+  v += __shfl_xor(v, 16, kWave);
+  v += __shfl_xor(v, 32, kWave);
+  return v;
+}
+
+// Sum over the 16 consecutive lanes of a quarter-wave.
+__device__ __forceinline__ float reduce_quarter(float v) {
+  v += __shfl_xor(v, 1, kWave);
+  v += __shfl_xor(v, 2, kWave);
+  v += __shfl_xor(v, 4, kWave);
+  v += __shfl_xor(v, 8, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float4 ld_f4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ void st_f4(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
+__device__ __forceinline__ uint2 ld_u2(const uint16_t* p) { return *reinterpret_cast<const uint2*>(p); }
+__device__ __forceinline__ uint4 ld_u4(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+__device__ __forceinline__ float dot4_bf16(float4 s, uint2 q) {
+  return s.x * bf16_lo(q.x) + s.y * bf16_hi(q.x) + s.z * bf16_lo(q.y) + s.w * bf16_hi(q.y);
+}
+
+__device__ __forceinline__ float dot8_bf16(uint4 a, uint4 b) {
+  return bf16_lo(a.x) * bf16_lo(b.x) + bf16_hi(a.x) * bf16_hi(b.x) + bf16_lo(a.y) * bf16_lo(b.y) +
+         bf16_hi(a.y) * bf16_hi(b.y) + bf16_lo(a.z) * bf16_lo(b.z) + bf16_hi(a.z) * bf16_hi(b.z) +
+         bf16_lo(a.w) * bf16_lo(b.w) + bf16_hi(a.w) * bf16_hi(b.w);
+}
+
+// Work-group arrival count for the ring-pointer update.  Every work-group of a
+// request calls this once, after its copies of the pointers are in registers (the
+// asm consumes them, so the atomic cannot be issued before those loads have
+// returned).  The caller whose arrival completes the count (return value ==
+// nblocks - 1) is the last reader of the old pointers and may overwrite them; it
+// also resets the counter for the next launch.  No fence is needed: the new
+// pointers are only read by later launches.
+__device__ __forceinline__ int arrive_after_reading(int32_t* counter, int a, int b, int c) {
+  int one = 1;
+  asm volatile("; arrival after pointer reads %1 %2 %3" : "+v"(one) : "v"(a), "v"(b), "v"(c));
+  return atomicAdd(counter, one);
+}
+
+__device__ __forceinline__ void flag_error(int32_t* err, int bits) {
+  if (err != nullptr && bits != 0) atomicOr(err, bits);
+}
+
+// One fp32 MFMA step of the transposed tile product: acc[m][nn] += sum_k a[m][k] b[k][nn]
+// with lane l supplying a[l & 15][l >> 4] and b[l >> 4][l & 15].
+__device__ __forceinline__ v4f mfma4(float a, float b, v4f acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+}
+
+// Per-lane slice of the entries used in the output combine and the fold: lane
+// (r, cq) handles entries j = cq + 4m, m < kMaxL / 4.
+constexpr int kVJ = kMaxL / 4;
+
+// Fold F cached entries into the checkpoint tiles held in registers and store them:
+//   S_0 <- fabar S_0 + sum_{j<F} fw_j x_j k_j^T   (x = v for Mamba-2, u for GDN)
+// on the matrix cores (transposed tile product, K axis = ring entries).
+// sk: keys of entries 0..F-1 in LDS, row-major [j][N] bf16; fw: weights in LDS;
+// vj[rt][m] = x_{cq+4m}[row of tile rt] for this lane.
+template <int D, int N, int RT, int NCT>
+__device__ __forceinline__ void fold_and_store(float* S0, float4 (&s)[RT][NCT], float fab,
+                                               const uint16_t* sk, const float* fw,
+                                               const float (&vj)[RT][kVJ], int F, int wave,
+                                               int r, int cq) {
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int rowbase = (wave * RT + rt) * 16;
+    float bop[kVJ];
+#pragma unroll
+    for (int ks = 0; ks < kVJ; ++ks) {
+      const int j = 4 * ks + cq;
+      bop[ks] = (j < F) ? fw[j] * vj[rt][ks] : 0.f;
+    }
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      v4f acc = {fab * s[rt][ct].x, fab * s[rt][ct].y, fab * s[rt][ct].z, fab * s[rt][ct].w};
+#pragma unroll
+      for (int ks = 0; ks < kVJ; ++ks) {
+        if (4 * ks >= F) break;  // uniform across the work-group
+        const int j = 4 * ks + cq;
+        const float aop = (j < F) ? bf16_to_f32(sk[j * N + ct * 16 + r]) : 0.f;
+        acc = mfma4(aop, bop[ks], acc);
+      }
+      st_f4(S0 + (rowbase + r) * N + ct * 16 + cq * 4, make_float4(acc[0], acc[1], acc[2], acc[3]));
+    }
+  }
+}
+
+}  // namespace rssm
+
+// ---------------------------------------------------------------- host side
+namespace rssm_host {
+
+template <typename P>
+inline int launch(void (*kern)(P), dim3 grid, dim3 block, void* stream, const P& params) {
+  void* args[] = {const_cast<P*>(&params)};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, args, 0,
+                                 reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? RSSM_OK : RSSM_ELAUNCH;
+}
+
+inline bool dims_ok(const rssm_dims* d) {
+  if (d == nullptr) return false;
+  if (d->batch < 1 || d->nheads < 1 || d->ngroups < 1 || d->head_dim < 1 || d->state_dim < 1)
+    return false;
+  if (d->nheads % d->ngroups != 0) return false;
+  if ((long long)d->batch * d->nheads > (1LL << 30)) return false;
+  return true;
+}
+
+inline bool shape_supported(const rssm_dims* d) {
+  return (d->head_dim == 64 || d->head_dim == 128) && d->state_dim == 128;
+}
+
+inline bool ring_ok(const rssm_ring* r, bool need_dt) {
+  return r != nullptr && r->vu != nullptr && r->k != nullptr && r->decay != nullptr &&
+         (!need_dt || r->dt != nullptr) && r->head != nullptr && r->count != nullptr &&
+         r->pending != nullptr && r->arrive != nullptr;
+}
+
+}  // namespace rssm_host

@@ -1,0 +1,81 @@
+"""Algorithmic HBM bytes of each decode kernel launch (the minimum traffic the
+operation needs, every byte counted once), for roofline reporting.
+
+The per-head model follows the traffic paragraph of "ReplaySSM: Cache SSM Inputs,
+Not State" (method, "three advantages"): the baseline moves 8dn bytes of state
+plus the step inputs; ReplaySSM with h cached entries moves 4dn bytes of
+checkpoint, the h cached (v, Delta, k) entries, the current inputs and the new
+entry.  Here it is counted with this library's dtypes -- fp32 state, bf16 v/k/q,
+fp32 step size and decay in the ring, fp32 y, fp32 GDN corrections -- and with k/q
+counted once per group (they are shared by the heads of a group).
+"""
+from __future__ import annotations
+
+F32, BF16, I32 = 4, 2, 4
+
+
+def standard_step(B, H, d, n, G) -> int:
+    """ssm_decode_step: state read + write, v, k, q, dt in, y out, per-head params."""
+    return B * (2 * F32 * H * d * n + BF16 * H * d + 2 * BF16 * G * n + F32 * H + F32 * H * d) \
+        + 2 * F32 * H
+
+
+def replay_slot(H, d, n, G) -> int:
+    """Bytes of one cached entry of one request: v (bf16, all heads), k (bf16, per
+    group), step size and decay (fp32 per head)."""
+    return BF16 * H * d + BF16 * G * n + 2 * F32 * H
+
+
+def replay_append(B, H, d, n, G, h, flush: bool) -> int:
+    """replay_append_decode with h entries cached before the call.  A flush step
+    writes the checkpoint back instead of caching the new entry."""
+    per_req = (F32 * H * d * n                       # checkpoint read
+               + h * replay_slot(H, d, n, G)         # cached entries read
+               + BF16 * H * d + 2 * BF16 * G * n + F32 * H   # v, k, q, dt in
+               + F32 * H * d                         # y out
+               + 3 * I32 * 2)                        # head/count/pending read+write
+    per_req += F32 * H * d * n if flush else replay_slot(H, d, n, G)
+    return B * per_req + 2 * F32 * H
+
+
+def replay_verify(B, H, d, n, G, T, c, flush: bool) -> int:
+    """replay_verify_T with c committed entries: checkpoint read, c cached entries,
+    T drafts in, T outputs, T new entries cached, checkpoint write on a flush."""
+    per_req = (F32 * H * d * n + c * replay_slot(H, d, n, G)
+               + T * (BF16 * H * d + 2 * BF16 * G * n + F32 * H)
+               + T * F32 * H * d + T * replay_slot(H, d, n, G) + 3 * I32 * 2)
+    if flush:
+        per_req += F32 * H * d * n
+    return B * per_req + 2 * F32 * H
+
+
+def gdn_slot(H, d, n, G) -> int:
+    """One cached GDN entry: u (fp32), k (bf16 per group), alpha (fp32)."""
+    return F32 * H * d + BF16 * G * n + F32 * H
+
+
+def gdn_verify(B, H, d, n, G, T, c, flush: bool) -> int:
+    per_req = (F32 * H * d * n + c * gdn_slot(H, d, n, G)
+               + T * (BF16 * H * d + 2 * BF16 * G * n + 2 * F32 * H)
+               + T * F32 * H * d + T * gdn_slot(H, d, n, G) + 3 * I32 * 2)
+    if flush:
+        per_req += F32 * H * d * n
+    return B * per_req
+
+
+def gdn_standard_step(B, H, d, n, G) -> int:
+    return B * (2 * F32 * H * d * n + BF16 * H * d + 2 * BF16 * G * n + 2 * F32 * H + F32 * H * d)
+
+
+def conv1d(B, C, W) -> int:
+    """conv state read + write (bf16), x in (bf16), out (fp32), taps (bf16, shared)."""
+    return B * C * (2 * BF16 * (W - 1) + BF16 + F32) + C * W * BF16
+
+
+def pages_traffic_per_head(d, n, h=None) -> int:
+    """The page's per-head formula, with 2 bytes per vector element and scalar:
+    baseline 8dn + 2(d + 2n + 1); ReplaySSM 4dn + 2h(d + n + 1) + 2(d + 2n + 1)
+    + 2(d + n + 1)."""
+    if h is None:
+        return 8 * d * n + 2 * (d + 2 * n + 1)
+    return 4 * d * n + 2 * h * (d + n + 1) + 2 * (d + 2 * n + 1) + 2 * (d + n + 1)

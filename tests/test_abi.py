@@ -1,0 +1,118 @@
+"""The C ABI without a GPU: the library loads, exports every function the header
+declares (and the binding prototypes exactly those), and rejects bad arguments on
+the host with the documented codes before anything is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from ssm_recurrent_decode_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssm_recurrent_decode.h")
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation returns first
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_0-9]+\s*\**\s*([A-Za-z_0-9]+)\s*\(", text, re.M)))
+
+
+def test_every_declared_function_is_exported_and_prototyped():
+    names = _declared()
+    assert "replay_append_decode" in names and "gdn_replay_verify_T" in names
+    lib = _lib.load()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES), set(names) ^ set(_lib.SIGNATURES)
+
+
+def test_abi_version_and_strerror():
+    lib = _lib.load()
+    assert lib.rssm_abi_version() == 1
+    assert "invalid" in _lib.strerror(_lib.RSSM_EINVAL)
+    assert "not supported" in _lib.strerror(_lib.RSSM_ENOTSUP)
+
+
+def _dims(B=4, H=8, d=64, n=128, G=1, L=8):
+    return _lib.rssm_dims(B, H, d, n, G, L)
+
+
+def _ring():
+    return _lib.rssm_ring(*([FAKE.value] * 9))
+
+
+def test_ring_sizes():
+    lib = _lib.load()
+    out = (ctypes.c_size_t * 9)()
+    d = _dims(B=256, H=32, d=64, n=128, G=8, L=16)
+    assert lib.rssm_ring_sizes(ctypes.byref(d), 0, out) == 0
+    assert list(out) == [256 * 32 * 16 * 64 * 2, 256 * 8 * 16 * 128 * 2, 256 * 32 * 16 * 4,
+                         256 * 32 * 16 * 4, 1024, 1024, 1024, 1024, 4]
+    assert lib.rssm_ring_sizes(ctypes.byref(d), 1, out) == 0
+    assert out[0] == 256 * 32 * 16 * 64 * 4 and out[2] == 0
+
+
+def test_host_validation_codes():
+    lib = _lib.load()
+    P = FAKE
+    d = _dims()
+    r = _ring()
+    EINVAL, ENOTSUP = _lib.RSSM_EINVAL, _lib.RSSM_ENOTSUP
+    # null pointers
+    assert lib.ssm_decode_step(ctypes.byref(d), None, P, P, P, P, P, P, P, None) == EINVAL
+    assert lib.replay_append_decode(ctypes.byref(d), P, None, P, P, P, P, P, P, P, None, None) == EINVAL
+    # H % G != 0
+    bad = _dims(H=6, G=4)
+    assert lib.ssm_decode_step(ctypes.byref(bad), P, P, P, P, P, P, P, P, None) == EINVAL
+    # unsupported head/state dims
+    for dd in (_dims(d=96), _dims(n=64), _dims(d=256)):
+        assert lib.ssm_decode_step(ctypes.byref(dd), P, P, P, P, P, P, P, P, None) == ENOTSUP
+        assert lib.replay_append_decode(ctypes.byref(dd), P, ctypes.byref(r), P, P, P, P, P, P, P,
+                                        None, None) == ENOTSUP
+    # capacity limits
+    assert lib.replay_append_decode(ctypes.byref(_dims(L=0)), P, ctypes.byref(r), P, P, P, P, P, P,
+                                    P, None, None) == EINVAL
+    assert lib.replay_append_decode(ctypes.byref(_dims(L=33)), P, ctypes.byref(r), P, P, P, P, P,
+                                    P, P, None, None) == ENOTSUP
+    # verify window: T < 1, L < 2T, T > 8
+    for T, L, code in ((0, 8, EINVAL), (5, 8, EINVAL), (9, 32, ENOTSUP)):
+        dd = _dims(L=L)
+        assert lib.replay_verify_T(ctypes.byref(dd), T, P, ctypes.byref(r), P, P, P, P, P, P, P,
+                                   None, None) == code
+        assert lib.gdn_replay_verify_T(ctypes.byref(dd), T, P, ctypes.byref(r), P, P, P, P, P, P,
+                                       None, None) == code
+    # GDN ring needs no dt; Mamba-2 ring does
+    r_nodt = _ring()
+    r_nodt.dt = None
+    assert lib.replay_flush(ctypes.byref(d), P, ctypes.byref(r_nodt), None, None) == EINVAL
+    # conv1d: only W = 4 and C % 4 == 0
+    assert lib.causal_conv1d_update(4, 3072, 3, P, P, P, P, None) == ENOTSUP
+    assert lib.causal_conv1d_update(4, 3070, 4, P, P, P, P, None) == ENOTSUP
+    assert lib.causal_conv1d_update(0, 3072, 4, P, P, P, P, None) == EINVAL
+    # rollback needs accepted
+    assert lib.replay_rollback(ctypes.byref(d), ctypes.byref(r), None, None) == EINVAL
+    # probes
+    assert lib.rssm_probe_copy(P, P, 15, None) == EINVAL
+
+
+def test_binding_rejects_host_tensors_and_wrong_shapes():
+    torch = pytest.importorskip("torch")
+    from ssm_recurrent_decode_amd import binding
+    dims = binding.Dims(2, 4, 64, 128, 2, 8)
+    st = torch.zeros(2, 4, 64, 128)
+    with pytest.raises(ValueError):
+        binding._p(st, "state", binding._F32, (2, 4, 64, 128))        # host tensor
+    with pytest.raises(ValueError):
+        binding._p(torch.zeros(3), "x", binding._F32, (2,))
+    with pytest.raises(TypeError):
+        binding._p(torch.zeros(2, dtype=torch.float64), "x", binding._F32, (2,))
+    assert dims.c().capacity == 8
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(ImportError):
+        _lib.load(str(tmp_path / "nope.so"))

@@ -128,3 +128,26 @@ def test_spec_window_never_truncated_and_flush_as_late_as_possible():
 def test_spec_config0_shape_with_rollbacks():
     """Config-0 sizes (d=64, n=128) with T=4, L=16 and random acceptance."""
     _spec_check(2, 8, 64, 128, 1, 16, 4, 12, seed=9, s0_scale=np.sqrt(0.1))
+
+
+def test_integer_schedules_match_full_oracle():
+    rng = np.random.default_rng(55)
+    L, T, R = 16, 4, 60
+    S0, rounds, dt_bias, A = tiny_mamba2(rng, 1, 1, 2, 3, 1, R, T=T)
+    acc = rng.integers(0, T + 1, size=R)
+    r = replay.ReplayRequest(S0[0], L, 1)
+    sched = replay.pointer_schedule_spec(L, T, acc)
+    for i, rd in enumerate(rounds):
+        delta, a = mamba2.step_size_and_decay(rd["dt"], dt_bias, A)
+        c0 = r.count
+        _, f = r.verify_round(rd["v"][0], rd["k"][0], rd["q"][0], delta[0], a[0])
+        assert sched[i][:4] == (c0, f, r.head, r.count)
+        r.commit(int(acc[i]))
+        assert sched[i][4] == r.count
+    S0, seq, dt_bias, A = tiny_mamba2(rng, 1, 1, 2, 3, 1, 40)
+    r = replay.ReplayRequest(S0[0], 8, 1)
+    sched = replay.pointer_schedule_standard(8, 40)
+    for t, st in enumerate(seq):
+        delta, a = mamba2.step_size_and_decay(st["dt"], dt_bias, A)
+        _, f = r.decode_step(st["v"][0], st["k"][0], st["q"][0], delta[0], a[0])
+        assert sched[t] == (r.head, r.count, f)
