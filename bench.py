@@ -44,7 +44,26 @@ def _args(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-standard", action="store_true", help="skip the standard-step comparator")
     ap.add_argument("--cpu-steps", type=int, default=32)
+    ap.add_argument("--no-graph", action="store_true", help="time the step eagerly only")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run the 1 GiB copy probe (for scaling traffic counters) and exit")
     return ap.parse_args(argv)
+
+
+def _calibrate_copy():
+    """Eight launches of the streaming copy probe over 1 GiB: each reads and writes
+    exactly 2^30 bytes, so FETCH_SIZE / WRITE_SIZE of these dispatches give the
+    counters' scale."""
+    import torch
+    import ssm_recurrent_decode_amd as rd
+    n = 1 << 30
+    src = torch.empty(n // 4, dtype=torch.float32, device="cuda").uniform_()
+    dst = torch.empty_like(src)
+    for _ in range(8):
+        rd.rssm_probe_copy(dst, src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "rssm_probe_copy", "bytes_read_per_launch": n,
+                      "bytes_written_per_launch": n, "launches": 8}))
 
 
 def _cpu_baseline(steps: int):
@@ -80,11 +99,15 @@ def main(argv=None) -> int:
               file=sys.stderr)
         return 2
 
+    if a.calibrate_copy:
+        _calibrate_copy()
+        return 0
+
     import numpy as np
     import torch
 
     import ssm_recurrent_decode_amd as rd
-    from ssm_recurrent_decode_amd import synth, traffic
+    from ssm_recurrent_decode_amd import profiling, synth, traffic
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -117,7 +140,8 @@ def main(argv=None) -> int:
                      "x": bf(synth.conv_step_input(B, C, seed, 1, p))})
     y = torch.empty((B, H, D), device=dev)
     conv_out = torch.empty((B, C), device=dev)
-    stream = torch.cuda.current_stream(dev)
+    side = torch.cuda.Stream(device=dev)          # default priority
+    stream = side
 
     calls = []
     for l in range(NL):
@@ -136,6 +160,7 @@ def main(argv=None) -> int:
         return calls[t % NL][(t // NL) % P]
 
     # ---- warmup
+    torch.cuda.synchronize()
     for t in range(a.warmup):
         conv, app = step_calls(t)
         conv()
@@ -163,8 +188,33 @@ def main(argv=None) -> int:
         ev_b[i].record(stream)
     end.record(stream)
     end.synchronize()
-    total_ms = start.elapsed_time(end)
+    eager_ms = start.elapsed_time(end)
     kern_ms = [ev_a[i].elapsed_time(ev_b[i]) for i in range(K)]
+    total_ms = eager_ms
+    graph_info = None
+    if not a.no_graph:
+        # the same step sequence captured once per ring cycle of every layer and
+        # replayed: no host launch cost between kernels
+        GS = NL * L
+        t0 = a.warmup + K
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for j in range(GS):
+                conv, app = step_calls(t0 + j)
+                conv()
+                app()
+        reps = max(1, K // GS)
+        with torch.cuda.stream(side):
+            g.replay()                              # warm replay
+            torch.cuda.synchronize()
+            start.record(side)
+            for _ in range(reps):
+                g.replay()
+            end.record(side)
+        end.synchronize()
+        total_ms = start.elapsed_time(end) * K / (reps * GS)
+        graph_info = {"steps_per_graph": GS, "replays": reps,
+                      "ms_per_step": round(start.elapsed_time(end) / (reps * GS), 5)}
     errs = [int(Ly["ring"].err.item()) for Ly in layers]
     if any(errs):
         raise RuntimeError(f"ring anomaly bits set: {errs}")
@@ -180,6 +230,7 @@ def main(argv=None) -> int:
     achieved = alg_bytes / kern_total_s / 1e9
     ms_per_step = total_ms / K
     value = B * K / (total_ms / 1e3)
+    traffic_bytes, traffic_note = profiling.stored_traffic("replay_append_decode")
 
     out = {
         "metric": "SSM decode tokens/s at batch 256 (Mamba-2 shape); achieved HBM GB/s vs peak",
@@ -194,9 +245,13 @@ def main(argv=None) -> int:
                    "flush_steps_timed": nflush},
         "roofline": {"bound": "hbm", "kernel": "replay_append_decode",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_bytes,
+                     "traffic_note": traffic_note,
                      "kernel_avg_us": round(1e3 * sum(kern_ms) / K, 3),
                      "alg_bytes_per_launch": round(alg_bytes / K)},
+        "timing": {"step": "hip graph replay" if graph_info else "eager launches",
+                   "eager_ms_per_step": round(eager_ms / K, 5), "graph": graph_info,
+                   "kernel": "HIP events around every replay_append_decode launch (eager pass)"},
     }
 
     if not a.no_standard:

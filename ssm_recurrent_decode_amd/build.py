@@ -45,21 +45,21 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP toolchain (ROCm) is required to build")
 
 
-def _compile(src: str) -> tuple[str, str]:
+def _run(cmd, what):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"{what} failed:\n{r.stdout}\n{r.stderr}")
+
+
+def _jobs(src: str):
+    """The object file and, separately, the device assembly of the same
+    translation unit (for the instruction scan); the two run in parallel."""
     name = os.path.splitext(os.path.basename(src))[0]
     obj = os.path.join(BUILD, name + ".o")
     asm = os.path.join(BUILD, name + f"-{ARCH}.s")
     hipcc = _hipcc()
-    cmd = [hipcc, *HIPCC_FLAGS, "-c", src, "-o", obj]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
-    # device assembly of the same translation unit, for the instruction scan
-    cmd_s = [hipcc, *HIPCC_FLAGS, "--cuda-device-only", "-S", src, "-o", asm]
-    r = subprocess.run(cmd_s, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc -S failed for {src}:\n{r.stdout}\n{r.stderr}")
-    return obj, asm
+    return (obj, [hipcc, *HIPCC_FLAGS, "-c", src, "-o", obj]), \
+           (asm, [hipcc, *HIPCC_FLAGS, "--cuda-device-only", "-S", src, "-o", asm])
 
 
 def build(jobs: int | None = None, verbose: bool = False) -> str:
@@ -67,11 +67,12 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     if not srcs:
         raise RuntimeError("no HIP sources found")
-    jobs = jobs or min(len(srcs), max(1, os.cpu_count() or 1))
+    work = [j for src in srcs for j in _jobs(src)]
+    jobs = jobs or min(len(work), max(1, os.cpu_count() or 1))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        results = list(ex.map(_compile, srcs))
-    objs = [o for o, _ in results]
-    asms = [a for _, a in results]
+        list(ex.map(lambda j: _run(j[1], f"hipcc ({os.path.basename(j[0])})"), work))
+    objs = [out for out, _ in work if out.endswith(".o")]
+    asms = [out for out, _ in work if out.endswith(".s")]
     try:
         from . import isa_check  # not shipped to every machine; building happens here
     except ImportError:

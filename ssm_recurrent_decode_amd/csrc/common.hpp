@@ -133,17 +133,17 @@ constexpr int kVJ = kMaxL / 4;
 // on the matrix cores (transposed tile product, K axis = ring entries).
 // sk: keys of entries 0..F-1 in LDS, row-major [j][N] bf16; fw: weights in LDS;
 // vj[rt][m] = x_{cq+4m}[row of tile rt] for this lane.
-template <int D, int N, int RT, int NCT>
+template <int D, int N, int RT, int NCT, int VJ>
 __device__ __forceinline__ void fold_and_store(float* S0, float4 (&s)[RT][NCT], float fab,
                                                const uint16_t* sk, const float* fw,
-                                               const float (&vj)[RT][kVJ], int F, int wave,
+                                               const float (&vj)[RT][VJ], int F, int wave,
                                                int r, int cq) {
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int rowbase = (wave * RT + rt) * 16;
-    float bop[kVJ];
+    float bop[VJ];
 #pragma unroll
-    for (int ks = 0; ks < kVJ; ++ks) {
+    for (int ks = 0; ks < VJ; ++ks) {
       const int j = 4 * ks + cq;
       bop[ks] = (j < F) ? fw[j] * vj[rt][ks] : 0.f;
     }
@@ -151,7 +151,7 @@ __device__ __forceinline__ void fold_and_store(float* S0, float4 (&s)[RT][NCT], 
     for (int ct = 0; ct < NCT; ++ct) {
       v4f acc = {fab * s[rt][ct].x, fab * s[rt][ct].y, fab * s[rt][ct].z, fab * s[rt][ct].w};
 #pragma unroll
-      for (int ks = 0; ks < kVJ; ++ks) {
+      for (int ks = 0; ks < VJ; ++ks) {
         if (4 * ks >= F) break;  // uniform across the work-group
         const int j = 4 * ks + cq;
         const float aop = (j < F) ? bf16_to_f32(sk[j * N + ct * 16 + r]) : 0.f;

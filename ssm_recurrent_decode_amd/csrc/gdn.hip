@@ -303,7 +303,7 @@ __global__ __launch_bounds__(kBlock) void gdn_verify_kernel(GdnReplayParams p) {
   }
 
   // ---- early flush of the committed entries
-  if (F > 0) fold_and_store<D, N, RT, NCT>(S0, s, s_abar, s_k, s_w, uf, F, wave, r, cq);
+  if (F > 0) fold_and_store<D, N, RT, NCT, kVJ>(S0, s, s_abar, s_k, s_w, uf, F, wave, r, cq);
 
   // ---- draft keys cached by the group's owner head
   if (h % hpg == 0) {
@@ -402,7 +402,7 @@ __global__ __launch_bounds__(kBlock) void gdn_flush_kernel(GdnReplayParams p) {
         ld_u4(p.ring_k + (((size_t)b * G + g) * L + (head + j) % L) * N + o);
   }
   __syncthreads();
-  fold_and_store<D, N, RT, NCT>(S0, s, s_abar, s_k, s_w, uf, F, wave, r, cq);
+  fold_and_store<D, N, RT, NCT, kVJ>(S0, s, s_abar, s_k, s_w, uf, F, wave, r, cq);
 
   if (tid == 0) {
     if (h == 0) flag_error(p.err, bad);
