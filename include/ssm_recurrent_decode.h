@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define RSSM_ABI_VERSION 1
+#define RSSM_ABI_VERSION 2
 
 #define RSSM_OK 0
 #define RSSM_EINVAL (-22)
@@ -70,36 +70,51 @@ typedef struct rssm_dims {
  * (Method, "core idea" and "three advantages"; kernel design, "ring buffer".)
  * The ring holds the most recent inputs since the checkpoint, addressed modulo L
  * from `head`, so a rollback only moves a pointer.  Physical slot of logical
- * entry j (0 = oldest) of request b is (head[b] + j) % L.
+ * entry j (0 = oldest) of request b is (head + j) % L.
  *
- * Caller allocates every array and zero-fills head, count, pending, arrive and
- * err once before the first call; afterwards only the library writes them
- * (rssm_ring_reset re-zeroes a subset of requests).
+ * The pointers of request b live in one 64-bit word ptr[b] (RSSM_PTR_* below):
+ * head, count (committed entries since the checkpoint), pending (uncommitted
+ * drafts that follow them) and the arrival count of the call in flight.  A
+ * work-group takes the word with one atomic add of 1, which reads the pointers
+ * and counts it in at once; the work-group that finds the arrival field at
+ * (work-groups of the request - 1) is the last reader and writes the new
+ * pointers with the field back at zero.  The field is zero between calls.
+ *
+ * Caller allocates every array and zero-fills ptr and err once before the first
+ * call; afterwards only the library writes them (rssm_ring_reset re-zeroes a
+ * subset of requests).  Unsigned fields: a head >= L or a count above the
+ * largest legal value is clamped and flagged (RSSM_ERR_POINTERS).
  */
+#define RSSM_PTR_ARRIVE(w) ((uint32_t)((w) & 0xFFFFu))
+#define RSSM_PTR_HEAD(w) ((uint32_t)(((w) >> 16) & 0xFFFFu))
+#define RSSM_PTR_COUNT(w) ((uint32_t)(((w) >> 32) & 0xFFFFu))
+#define RSSM_PTR_PENDING(w) ((uint32_t)(((w) >> 48) & 0xFFFFu))
+#define RSSM_PTR_PACK(head, count, pending)                                      \
+  ((((uint64_t)(head) & 0xFFFFu) << 16) | (((uint64_t)(count) & 0xFFFFu) << 32) | \
+   (((uint64_t)(pending) & 0xFFFFu) << 48))
+
 typedef struct rssm_ring {
   void* vu;          /* Mamba-2: v  bf16 [B, H, L, d];  GDN: u fp32 [B, H, L, d]     */
   uint16_t* k;       /* bf16 [B, G, L, n]                                           */
   float* dt;         /* Mamba-2: Delta fp32 [B, H, L] (after softplus);  GDN: unused */
   float* decay;      /* Mamba-2: a = exp(A Delta);  GDN: alpha = exp(g);  fp32 [B,H,L] */
-  int32_t* head;     /* [B] physical slot of the oldest entry since the checkpoint */
-  int32_t* count;    /* [B] committed entries since the checkpoint                 */
-  int32_t* pending;  /* [B] uncommitted draft entries that follow them             */
-  int32_t* arrive;   /* [B] work-group arrival counters; zero between calls         */
+  uint64_t* ptr;     /* [B] packed pointer words (RSSM_PTR_*), 8-byte aligned        */
   int32_t* err;      /* [1] anomaly bits (RSSM_ERR_*), may be NULL                  */
 } rssm_ring;
 
 int rssm_abi_version(void);
 const char* rssm_strerror(int code);
 
-/* Bytes of each ring array for the given dims: writes 9 sizes in the order of
- * the rssm_ring fields (vu, k, dt, decay, head, count, pending, arrive, err).
+/* Bytes of each ring array for the given dims: writes 6 sizes in the order of
+ * the rssm_ring fields (vu, k, dt, decay, ptr, err).
  * is_gdn selects fp32 u instead of bf16 v and no dt array.  Host-only. */
-int rssm_ring_sizes(const rssm_dims* dims, int is_gdn, size_t out_bytes[9]);
+int rssm_ring_sizes(const rssm_dims* dims, int is_gdn, size_t out_bytes[6]);
 
-/* Zero head/count/pending for requests with mask[b] != 0 (mask NULL = all) and
- * clear err.  The ring contents are left as they are: with count = 0 they are
- * never read.  Use after an explicit replay_flush to recycle a request slot, or
- * to start a new request from a checkpoint state. */
+/* Zero the pointer word (head, count, pending, arrivals) of requests with
+ * mask[b] != 0 (mask NULL = all) and clear err.  The ring contents are left as
+ * they are: with count = 0 they are never read.  Use after an explicit
+ * replay_flush to recycle a request slot, or to start a new request from a
+ * checkpoint state. */
 int rssm_ring_reset(const rssm_dims* dims, rssm_ring* ring, const int32_t* mask, void* stream);
 
 /* ---------------------------------------------------------------- Mamba-2 */

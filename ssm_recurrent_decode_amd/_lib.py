@@ -19,6 +19,7 @@ RSSM_ELAUNCH = -5
 RSSM_ERR_POINTERS = 1
 RSSM_ERR_ACCEPTED = 2
 RSSM_ERR_PENDING = 4
+ABI_VERSION = 2  # RSSM_ABI_VERSION of the header this binding follows
 
 
 class rssm_dims(ctypes.Structure):
@@ -28,8 +29,7 @@ class rssm_dims(ctypes.Structure):
 
 class rssm_ring(ctypes.Structure):
     _fields_ = [("vu", c_void_p), ("k", c_void_p), ("dt", c_void_p), ("decay", c_void_p),
-                ("head", c_void_p), ("count", c_void_p), ("pending", c_void_p),
-                ("arrive", c_void_p), ("err", c_void_p)]
+                ("ptr", c_void_p), ("err", c_void_p)]
 
 
 _D = POINTER(rssm_dims)
@@ -79,7 +79,7 @@ def load(path: str = LIB_PATH):
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    if lib.rssm_abi_version() != 1:
+    if lib.rssm_abi_version() != ABI_VERSION:
         raise ImportError("libssm_recurrent_decode.so ABI version mismatch")
     if path == LIB_PATH:
         _lib = lib

@@ -66,7 +66,10 @@ class Ring:
     """Device arrays of one layer's ReplaySSM ring (see rssm_ring in the header).
 
     Allocated zero-filled with torch on ``device``; ``gdn`` selects fp32
-    corrections u instead of bf16 values v and no step-size array."""
+    corrections u instead of bf16 values v and no step-size array.  The pointers
+    of request b are packed in the 64-bit word ``ptr[b]`` (arrivals in bits
+    0-15, head 16-31, count 32-47, pending 48-63); ``head``, ``count``,
+    ``pending`` and ``arrive`` are read-only int32 views decoded from it."""
 
     def __init__(self, dims: Dims, gdn: bool = False, device="cuda"):
         B, H, G, L = dims.batch, dims.nheads, dims.ngroups, dims.capacity
@@ -77,25 +80,50 @@ class Ring:
         self.k = torch.zeros((B, G, L, N), dtype=torch.bfloat16, **z)
         self.dt = None if gdn else torch.zeros((B, H, L), dtype=torch.float32, **z)
         self.decay = torch.zeros((B, H, L), dtype=torch.float32, **z)
-        self.head = torch.zeros((B,), dtype=torch.int32, **z)
-        self.count = torch.zeros((B,), dtype=torch.int32, **z)
-        self.pending = torch.zeros((B,), dtype=torch.int32, **z)
-        self.arrive = torch.zeros((B,), dtype=torch.int32, **z)
+        self.ptr = torch.zeros((B,), dtype=torch.int64, **z)
         self.err = torch.zeros((1,), dtype=torch.int32, **z)
+
+    def _field(self, shift: int):
+        return ((self.ptr >> shift) & 0xFFFF).to(torch.int32)
+
+    @property
+    def arrive(self):
+        return self._field(0)
+
+    @property
+    def head(self):
+        return self._field(16)
+
+    @property
+    def count(self):
+        return self._field(32)
+
+    @property
+    def pending(self):
+        return self._field(48)
+
+    def set_pointers(self, head=None, count=None, pending=None):
+        """Overwrite pointer fields (sequences of B ints, or None to keep); each
+        value is stored modulo 2^16 as the packed word holds it.  Arrivals are
+        zeroed."""
+        cur = [self.head.cpu().tolist(), self.count.cpu().tolist(), self.pending.cpu().tolist()]
+        new = [list(x) if x is not None else c for x, c in zip((head, count, pending), cur)]
+        words = [((h & 0xFFFF) << 16) | ((c & 0xFFFF) << 32) | ((p & 0xFFFF) << 48)
+                 for h, c, p in zip(*new)]
+        words = [w - (1 << 64) if w >= (1 << 63) else w for w in words]
+        self.ptr.copy_(torch.tensor(words, dtype=torch.int64))
 
     def c(self) -> _lib.rssm_ring:
         return _lib.rssm_ring(self.vu.data_ptr(), self.k.data_ptr(),
                               None if self.dt is None else self.dt.data_ptr(),
-                              self.decay.data_ptr(), self.head.data_ptr(), self.count.data_ptr(),
-                              self.pending.data_ptr(), self.arrive.data_ptr(), self.err.data_ptr())
+                              self.decay.data_ptr(), self.ptr.data_ptr(), self.err.data_ptr())
 
     def tensors(self):
-        return {k: getattr(self, k) for k in ("vu", "k", "dt", "decay", "head", "count",
-                                              "pending", "arrive", "err")}
+        return {k: getattr(self, k) for k in ("vu", "k", "dt", "decay", "ptr", "err")}
 
 
 def ring_sizes(dims: Dims, gdn: bool = False):
-    out = (ctypes.c_size_t * 9)()
+    out = (ctypes.c_size_t * 6)()
     d = dims.c()
     _lib.check(_lib.load().rssm_ring_sizes(ctypes.byref(d), int(gdn), out), "rssm_ring_sizes")
     return list(out)

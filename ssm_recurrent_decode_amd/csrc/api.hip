@@ -54,7 +54,7 @@ extern "C" const char* rssm_strerror(int code) {
   }
 }
 
-extern "C" int rssm_ring_sizes(const rssm_dims* d, int is_gdn, size_t out[9]) {
+extern "C" int rssm_ring_sizes(const rssm_dims* d, int is_gdn, size_t out[6]) {
   if (!rssm_host::dims_ok(d) || d->capacity < 1 || out == nullptr) return RSSM_EINVAL;
   const size_t B = d->batch, H = d->nheads, G = d->ngroups, L = d->capacity;
   const size_t D = d->head_dim, N = d->state_dim;
@@ -62,8 +62,8 @@ extern "C" int rssm_ring_sizes(const rssm_dims* d, int is_gdn, size_t out[9]) {
   out[1] = B * G * L * N * 2;
   out[2] = is_gdn ? 0 : B * H * L * 4;
   out[3] = B * H * L * 4;
-  out[4] = out[5] = out[6] = out[7] = B * 4;
-  out[8] = 4;
+  out[4] = B * 8;
+  out[5] = 4;
   return RSSM_OK;
 }
 

@@ -101,17 +101,44 @@ __device__ __forceinline__ float dot8_bf16(uint4 a, uint4 b) {
          bf16_lo(a.w) * bf16_lo(b.w) + bf16_hi(a.w) * bf16_hi(b.w);
 }
 
-// Work-group arrival count for the ring-pointer update.  Every work-group of a
-// request calls this once, after its copies of the pointers are in registers (the
-// asm consumes them, so the atomic cannot be issued before those loads have
-// returned).  The caller whose arrival completes the count (return value ==
-// nblocks - 1) is the last reader of the old pointers and may overwrite them; it
-// also resets the counter for the next launch.  No fence is needed: the new
-// pointers are only read by later launches.
-__device__ __forceinline__ int arrive_after_reading(int32_t* counter, int a, int b, int c) {
-  int one = 1;
-  asm volatile("; arrival after pointer reads %1 %2 %3" : "+v"(one) : "v"(a), "v"(b), "v"(c));
-  return atomicAdd(counter, one);
+// Ring pointer word of one request: arrivals of the call in flight in bits
+// 0-15, head 16-31, count 32-47, pending 48-63.
+struct RingPtr {
+  int head, count, pending, arrive;
+};
+
+__device__ __forceinline__ RingPtr unpack_ptr(unsigned long long w) {
+  return {int((w >> 16) & 0xFFFFu), int((w >> 32) & 0xFFFFu), int((w >> 48) & 0xFFFFu),
+          int(w & 0xFFFFu)};
+}
+
+__device__ __forceinline__ unsigned long long pack_ptr(int head, int count, int pending) {
+  return ((unsigned long long)(head & 0xFFFF) << 16) | ((unsigned long long)(count & 0xFFFF) << 32) |
+         ((unsigned long long)(pending & 0xFFFF) << 48);
+}
+
+// Work-group arrival.  Each work-group of a request adds 1 to the word once;
+// the returned old value is its copy of the pointers, so the read and the
+// arrival are one operation.  The work-group whose arrival field reads
+// nblocks - 1 comes after every other work-group's read and alone writes the
+// new pointers (arrival field zero) with put_pointers.  No fence is needed:
+// the new pointers are only read by later launches.
+__device__ __forceinline__ unsigned long long take_pointers(unsigned long long* word) {
+  return atomicAdd(word, 1ull);
+}
+
+__device__ __forceinline__ void put_pointers(unsigned long long* word, unsigned long long w) {
+  atomicExch(word, w);
+}
+
+// Plain access for the single-thread-per-request pointer kernels (rollback,
+// reset), device scope so no stale cached copy is read.
+__device__ __forceinline__ unsigned long long load_pointers(const unsigned long long* word) {
+  return __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void store_pointers(unsigned long long* word, unsigned long long w) {
+  __hip_atomic_store(word, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ void flag_error(int32_t* err, int bits) {
@@ -188,10 +215,19 @@ inline bool shape_supported(const rssm_dims* d) {
   return (d->head_dim == 64 || d->head_dim == 128) && d->state_dim == 128;
 }
 
+// The arrival field of a pointer word is 16 bits wide and counts the
+// work-groups of one request (at most one per head).
+inline bool ring_shape_supported(const rssm_dims* d) {
+  return shape_supported(d) && d->capacity <= rssm::kMaxL && d->nheads <= 0xFFFF;
+}
+
+inline bool ptr_ok(const rssm_ring* r) {
+  return r != nullptr && r->ptr != nullptr && reinterpret_cast<uintptr_t>(r->ptr) % 8 == 0;
+}
+
 inline bool ring_ok(const rssm_ring* r, bool need_dt) {
-  return r != nullptr && r->vu != nullptr && r->k != nullptr && r->decay != nullptr &&
-         (!need_dt || r->dt != nullptr) && r->head != nullptr && r->count != nullptr &&
-         r->pending != nullptr && r->arrive != nullptr;
+  return ptr_ok(r) && r->vu != nullptr && r->k != nullptr && r->decay != nullptr &&
+         (!need_dt || r->dt != nullptr);
 }
 
 }  // namespace rssm_host

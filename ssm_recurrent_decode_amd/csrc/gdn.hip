@@ -89,10 +89,7 @@ struct GdnReplayParams {
   float* ring_u;       // [B, H, L, D] fp32
   uint16_t* ring_k;    // [B, G, L, N]
   float* ring_alpha;   // [B, H, L]
-  int32_t* head;
-  int32_t* count;
-  int32_t* pending;
-  int32_t* arrive;
+  unsigned long long* ptr;  // [B] packed ring pointer words
   int32_t* err;
   const uint16_t* v;   // [B, T, H, D]
   const uint16_t* k;   // [B, T, G, N]
@@ -126,28 +123,13 @@ __global__ __launch_bounds__(kBlock) void gdn_verify_kernel(GdnReplayParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, cq = lane >> 4;
 
-  int head = p.head[b], cnt = p.count[b];
-  const int pend = p.pending[b];
-  int bad = 0;
-  if (head < 0 || head >= L) {
-    head = ((head % L) + L) % L;
-    bad |= RSSM_ERR_POINTERS;
-  }
-  if (cnt < 0 || cnt > L - T) {
-    cnt = cnt < 0 ? 0 : L - T;
-    bad |= RSSM_ERR_POINTERS;
-  }
-  if (pend != 0) bad |= RSSM_ERR_PENDING;
-  const int c = cnt;
-  const int E = c + T;
-  const bool do_flush = (c + 2 * T > L);
-  const int F = do_flush ? c : 0;
-
+  // ---- the pointer word (one atomic: read + arrival) and the checkpoint tiles,
+  //      which need no pointer, in flight together
+  __shared__ unsigned long long s_word;
+  unsigned long long word = 0;
+  if (tid == 0) word = take_pointers(&p.ptr[b]);
   const size_t bh = (size_t)b * H + h;
   float* S0 = p.state0 + bh * D * N;
-
-  // ---- long-latency loads: checkpoint tiles; this lane's readout vector at the
-  //      tile columns; per-row ring corrections; fold operands
   float4 s[RT][NCT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -155,8 +137,27 @@ __global__ __launch_bounds__(kBlock) void gdn_verify_kernel(GdnReplayParams p) {
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) s[rt][ct] = ld_f4(S0 + row * N + ct * 16 + cq * 4);
   }
-  int arrival = 0;
-  if (tid == 0) arrival = arrive_after_reading(&p.arrive[b], head, cnt, pend);
+  if (tid == 0) s_word = word;
+  __syncthreads();
+  const RingPtr rp = unpack_ptr(s_word);
+  int head = rp.head, cnt = rp.count;
+  int bad = 0;
+  if (head >= L) {
+    head %= L;
+    bad |= RSSM_ERR_POINTERS;
+  }
+  if (cnt > L - T) {
+    cnt = L - T;
+    bad |= RSSM_ERR_POINTERS;
+  }
+  if (rp.pending != 0) bad |= RSSM_ERR_PENDING;
+  const int c = cnt;
+  const int E = c + T;
+  const bool do_flush = (c + 2 * T > L);
+  const int F = do_flush ? c : 0;
+
+  // ---- long-latency loads: this lane's readout vector at the tile columns;
+  //      per-row ring corrections; fold operands
   uint2 xv[NCT];
   {
     const int vsel = r;  // MFMA M index = readout vector
@@ -320,12 +321,8 @@ __global__ __launch_bounds__(kBlock) void gdn_verify_kernel(GdnReplayParams p) {
       flag_error(p.err, bad);
       if (p.flushed != nullptr) p.flushed[b] = do_flush ? 1 : 0;
     }
-    if (arrival == H - 1) {
-      p.arrive[b] = 0;
-      p.head[b] = do_flush ? (head + c) % L : head;
-      p.count[b] = do_flush ? 0 : c;
-      p.pending[b] = T;
-    }
+    if (rp.arrive == H - 1)
+      put_pointers(&p.ptr[b], pack_ptr(do_flush ? (head + c) % L : head, do_flush ? 0 : c, T));
   }
 }
 
@@ -345,35 +342,33 @@ __global__ __launch_bounds__(kBlock) void gdn_flush_kernel(GdnReplayParams p) {
   const int r = lane & 15, cq = lane >> 4;
 
   if (p.mask != nullptr && p.mask[b] == 0) return;
-  int head = p.head[b], cnt = p.count[b];
-  const int pend = p.pending[b];
+  __shared__ unsigned long long s_word;
+  if (tid == 0) s_word = take_pointers(&p.ptr[b]);
+  __syncthreads();
+  const RingPtr rp = unpack_ptr(s_word);
+  int head = rp.head, cnt = rp.count;
   int bad = 0;
-  if (head < 0 || head >= L) {
-    head = ((head % L) + L) % L;
+  if (head >= L) {
+    head %= L;
     bad |= RSSM_ERR_POINTERS;
   }
-  if (cnt < 0 || cnt > L) {
-    cnt = cnt < 0 ? 0 : L;
+  if (cnt > L) {
+    cnt = L;
     bad |= RSSM_ERR_POINTERS;
   }
-  if (pend < 0 || cnt + pend > L) bad |= RSSM_ERR_POINTERS;
-  if (cnt == 0) {
-    if (h == 0 && tid == 0) flag_error(p.err, bad);
-    return;
-  }
+  if (cnt + rp.pending > L) bad |= RSSM_ERR_POINTERS;
   const int F = cnt;
   const size_t bh = (size_t)b * H + h;
   float* S0 = p.state0 + bh * D * N;
-
   float4 s[RT][NCT];
+  if (F > 0) {
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int row = (wave * RT + rt) * 16 + r;
+    for (int rt = 0; rt < RT; ++rt) {
+      const int row = (wave * RT + rt) * 16 + r;
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) s[rt][ct] = ld_f4(S0 + row * N + ct * 16 + cq * 4);
+      for (int ct = 0; ct < NCT; ++ct) s[rt][ct] = ld_f4(S0 + row * N + ct * 16 + cq * 4);
+    }
   }
-  int arrival = 0;
-  if (tid == 0) arrival = arrive_after_reading(&p.arrive[b], head, cnt, pend);
   float uf[RT][kVJ];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -402,15 +397,13 @@ __global__ __launch_bounds__(kBlock) void gdn_flush_kernel(GdnReplayParams p) {
         ld_u4(p.ring_k + (((size_t)b * G + g) * L + (head + j) % L) * N + o);
   }
   __syncthreads();
-  fold_and_store<D, N, RT, NCT, kVJ>(S0, s, s_abar, s_k, s_w, uf, F, wave, r, cq);
+  if (F > 0) fold_and_store<D, N, RT, NCT, kVJ>(S0, s, s_abar, s_k, s_w, uf, F, wave, r, cq);
 
   if (tid == 0) {
     if (h == 0) flag_error(p.err, bad);
-    if (arrival == H - 1) {
-      p.arrive[b] = 0;
-      p.head[b] = (head + F) % L;
-      p.count[b] = 0;
-    }
+    // every work-group arrives, also with nothing to fold, so the last one can
+    // reset the arrival field
+    if (rp.arrive == H - 1) put_pointers(&p.ptr[b], pack_ptr((head + F) % L, 0, rp.pending));
   }
 }
 
@@ -427,10 +420,7 @@ GdnReplayParams make_gdn_params(const rssm_dims* d, float* state0, rssm_ring* ri
   p.ring_u = static_cast<float*>(ring->vu);
   p.ring_k = ring->k;
   p.ring_alpha = ring->decay;
-  p.head = ring->head;
-  p.count = ring->count;
-  p.pending = ring->pending;
-  p.arrive = ring->arrive;
+  p.ptr = reinterpret_cast<unsigned long long*>(ring->ptr);
   p.err = ring->err;
   p.H = d->nheads;
   p.G = d->ngroups;
@@ -465,7 +455,7 @@ extern "C" int gdn_replay_verify_T(const rssm_dims* dims, int32_t T, float* stat
       !g || !beta || !y)
     return RSSM_EINVAL;
   if (T < 1 || dims->capacity < 2 * T) return RSSM_EINVAL;
-  if (!rssm_host::shape_supported(dims) || dims->capacity > kMaxL || T > kMaxT) return RSSM_ENOTSUP;
+  if (!rssm_host::ring_shape_supported(dims) || T > kMaxT) return RSSM_ENOTSUP;
   GdnReplayParams p = make_gdn_params(dims, state0, ring);
   p.v = v;
   p.k = k;
@@ -492,7 +482,7 @@ extern "C" int gdn_replay_flush(const rssm_dims* dims, float* state0, rssm_ring*
                                 const int32_t* mask, void* stream) {
   if (!rssm_host::dims_ok(dims) || !rssm_host::ring_ok(ring, false) || !state0) return RSSM_EINVAL;
   if (dims->capacity < 1) return RSSM_EINVAL;
-  if (!rssm_host::shape_supported(dims) || dims->capacity > kMaxL) return RSSM_ENOTSUP;
+  if (!rssm_host::ring_shape_supported(dims)) return RSSM_ENOTSUP;
   GdnReplayParams p = make_gdn_params(dims, state0, ring);
   p.mask = mask;
   const dim3 grid(dims->batch * dims->nheads);

@@ -97,35 +97,33 @@ __global__ __launch_bounds__(kBlock) void replay_flush_kernel(ReplayParams p) {
   const int r = lane & 15, cq = lane >> 4;
 
   if (p.mask != nullptr && p.mask[b] == 0) return;
-  int head = p.head[b], cnt = p.count[b];
-  const int pend = p.pending[b];
+  __shared__ unsigned long long s_word;
+  if (tid == 0) s_word = take_pointers(&p.ptr[b]);
+  __syncthreads();
+  const RingPtr rp = unpack_ptr(s_word);
+  int head = rp.head, cnt = rp.count;
   int bad = 0;
-  if (head < 0 || head >= L) {
-    head = ((head % L) + L) % L;
+  if (head >= L) {
+    head %= L;
     bad |= RSSM_ERR_POINTERS;
   }
-  if (cnt < 0 || cnt > L) {
-    cnt = cnt < 0 ? 0 : L;
+  if (cnt > L) {
+    cnt = L;
     bad |= RSSM_ERR_POINTERS;
   }
-  if (pend < 0 || cnt + pend > L) bad |= RSSM_ERR_POINTERS;
-  if (cnt == 0) {
-    if (h == 0 && tid == 0) flag_error(p.err, bad);
-    return;
-  }
+  if (cnt + rp.pending > L) bad |= RSSM_ERR_POINTERS;
   const int F = cnt;
   const size_t bh = (size_t)b * H + h;
   float* S0 = p.state0 + bh * D * N;
-
   float4 s[RT][NCT];
+  if (F > 0) {
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int row = (wave * RT + rt) * 16 + r;
+    for (int rt = 0; rt < RT; ++rt) {
+      const int row = (wave * RT + rt) * 16 + r;
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) s[rt][ct] = ld_f4(S0 + row * N + ct * 16 + cq * 4);
+      for (int ct = 0; ct < NCT; ++ct) s[rt][ct] = ld_f4(S0 + row * N + ct * 16 + cq * 4);
+    }
   }
-  int arrival = 0;
-  if (tid == 0) arrival = arrive_after_reading(&p.arrive[b], head, cnt, pend);
   float vj[RT][kVJ];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -159,22 +157,18 @@ __global__ __launch_bounds__(kBlock) void replay_flush_kernel(ReplayParams p) {
         ld_u4(p.ring_k + (((size_t)b * G + g) * L + (head + j) % L) * N + o);
   }
   __syncthreads();
-  fold_and_store<D, N, RT, NCT, kVJ>(S0, s, s_fabar, s_k, s_fw, vj, F, wave, r, cq);
+  if (F > 0) fold_and_store<D, N, RT, NCT, kVJ>(S0, s, s_fabar, s_k, s_fw, vj, F, wave, r, cq);
 
   if (tid == 0) {
     if (h == 0) flag_error(p.err, bad);
-    if (arrival == H - 1) {
-      p.arrive[b] = 0;
-      p.head[b] = (head + F) % L;
-      p.count[b] = 0;
-    }
+    // every work-group of the request arrives (also when there is nothing to
+    // fold) so the last one can reset the arrival field
+    if (rp.arrive == H - 1) put_pointers(&p.ptr[b], pack_ptr((head + F) % L, 0, rp.pending));
   }
 }
 
 struct PtrParams {
-  int32_t* head;
-  int32_t* count;
-  int32_t* pending;
+  unsigned long long* ptr;
   int32_t* err;
   const int32_t* accepted;
   const int32_t* mask;
@@ -185,22 +179,26 @@ struct PtrParams {
 __global__ __launch_bounds__(kBlock) void rollback_kernel(PtrParams p) {
   const int b = blockIdx.x * kBlock + threadIdx.x;
   if (b >= p.B) return;
-  int cnt = p.count[b], pend = p.pending[b], acc = p.accepted[b];
+  const RingPtr rp = unpack_ptr(load_pointers(&p.ptr[b]));
+  int head = rp.head, cnt = rp.count, pend = rp.pending, acc = p.accepted[b];
   int bad = 0;
-  if (pend < 0 || pend > p.L) {
-    pend = pend < 0 ? 0 : p.L;
+  if (head >= p.L) {
+    head %= p.L;
     bad |= RSSM_ERR_POINTERS;
   }
-  if (cnt < 0 || cnt + pend > p.L) {
-    cnt = cnt < 0 ? 0 : (p.L - pend < 0 ? 0 : p.L - pend);
+  if (pend > p.L) {
+    pend = p.L;
+    bad |= RSSM_ERR_POINTERS;
+  }
+  if (cnt + pend > p.L) {
+    cnt = p.L - pend;
     bad |= RSSM_ERR_POINTERS;
   }
   if (acc < 0 || acc > pend) {
     acc = acc < 0 ? 0 : pend;
     bad |= RSSM_ERR_ACCEPTED;
   }
-  p.count[b] = cnt + acc;
-  p.pending[b] = 0;
+  store_pointers(&p.ptr[b], pack_ptr(head, cnt + acc, 0));
   flag_error(p.err, bad);
 }
 
@@ -208,11 +206,7 @@ __global__ __launch_bounds__(kBlock) void ring_reset_kernel(PtrParams p) {
   const int b = blockIdx.x * kBlock + threadIdx.x;
   if (b == 0 && p.err != nullptr) *p.err = 0;
   if (b >= p.B) return;
-  if (p.mask == nullptr || p.mask[b] != 0) {
-    p.head[b] = 0;
-    p.count[b] = 0;
-    p.pending[b] = 0;
-  }
+  if (p.mask == nullptr || p.mask[b] != 0) store_pointers(&p.ptr[b], 0ull);
 }
 
 }  // namespace rssm
@@ -230,10 +224,7 @@ ReplayParams make_replay_params(const rssm_dims* d, float* state0, rssm_ring* ri
   p.ring_k = ring->k;
   p.ring_dt = ring->dt;
   p.ring_decay = ring->decay;
-  p.head = ring->head;
-  p.count = ring->count;
-  p.pending = ring->pending;
-  p.arrive = ring->arrive;
+  p.ptr = reinterpret_cast<unsigned long long*>(ring->ptr);
   p.err = ring->err;
   p.H = d->nheads;
   p.G = d->ngroups;
@@ -263,7 +254,7 @@ extern "C" int replay_append_decode(const rssm_dims* dims, float* state0, rssm_r
       !dt || !dt_bias || !A || !y)
     return RSSM_EINVAL;
   if (dims->capacity < 1) return RSSM_EINVAL;
-  if (!rssm_host::shape_supported(dims) || dims->capacity > kMaxL) return RSSM_ENOTSUP;
+  if (!rssm_host::ring_shape_supported(dims)) return RSSM_ENOTSUP;
   ReplayParams p = make_replay_params(dims, state0, ring);
   p.v = v;
   p.k = k;
@@ -281,7 +272,7 @@ extern "C" int replay_flush(const rssm_dims* dims, float* state0, rssm_ring* rin
                             const int32_t* mask, void* stream) {
   if (!rssm_host::dims_ok(dims) || !rssm_host::ring_ok(ring, true) || !state0) return RSSM_EINVAL;
   if (dims->capacity < 1) return RSSM_EINVAL;
-  if (!rssm_host::shape_supported(dims) || dims->capacity > kMaxL) return RSSM_ENOTSUP;
+  if (!rssm_host::ring_shape_supported(dims)) return RSSM_ENOTSUP;
   ReplayParams p = make_replay_params(dims, state0, ring);
   p.mask = mask;
   const dim3 grid(dims->batch * dims->nheads);
@@ -297,7 +288,7 @@ extern "C" int replay_verify_T(const rssm_dims* dims, int32_t T, float* state0, 
       !dt || !dt_bias || !A || !y)
     return RSSM_EINVAL;
   if (T < 1 || dims->capacity < 2 * T) return RSSM_EINVAL;
-  if (!rssm_host::shape_supported(dims) || dims->capacity > kMaxL || T > kMaxT) return RSSM_ENOTSUP;
+  if (!rssm_host::ring_shape_supported(dims) || T > kMaxT) return RSSM_ENOTSUP;
   ReplayParams p = make_replay_params(dims, state0, ring);
   p.v = v;
   p.k = k;
@@ -314,10 +305,9 @@ extern "C" int replay_verify_T(const rssm_dims* dims, int32_t T, float* state0, 
 
 extern "C" int replay_rollback(const rssm_dims* dims, rssm_ring* ring, const int32_t* accepted,
                                void* stream) {
-  if (!rssm_host::dims_ok(dims) || ring == nullptr || !ring->count || !ring->pending || !accepted)
-    return RSSM_EINVAL;
+  if (!rssm_host::dims_ok(dims) || !rssm_host::ptr_ok(ring) || !accepted) return RSSM_EINVAL;
   if (dims->capacity < 1) return RSSM_EINVAL;
-  PtrParams p{ring->head, ring->count, ring->pending, ring->err, accepted, nullptr,
+  PtrParams p{reinterpret_cast<unsigned long long*>(ring->ptr), ring->err, accepted, nullptr,
               dims->batch, dims->capacity};
   const dim3 grid((dims->batch + kBlock - 1) / kBlock);
   return launch(rollback_kernel, grid, dim3(kBlock), stream, p);
@@ -325,10 +315,9 @@ extern "C" int replay_rollback(const rssm_dims* dims, rssm_ring* ring, const int
 
 extern "C" int rssm_ring_reset(const rssm_dims* dims, rssm_ring* ring, const int32_t* mask,
                                void* stream) {
-  if (!rssm_host::dims_ok(dims) || ring == nullptr || !ring->head || !ring->count || !ring->pending)
-    return RSSM_EINVAL;
-  PtrParams p{ring->head, ring->count, ring->pending, ring->err, nullptr, mask, dims->batch,
-              dims->capacity};
+  if (!rssm_host::dims_ok(dims) || !rssm_host::ptr_ok(ring)) return RSSM_EINVAL;
+  PtrParams p{reinterpret_cast<unsigned long long*>(ring->ptr), ring->err, nullptr, mask,
+              dims->batch, dims->capacity};
   const dim3 grid((dims->batch + kBlock - 1) / kBlock);
   return launch(ring_reset_kernel, grid, dim3(kBlock), stream, p);
 }

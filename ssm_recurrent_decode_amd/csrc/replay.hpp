@@ -18,10 +18,7 @@ struct ReplayParams {
   uint16_t* ring_k;
   float* ring_dt;
   float* ring_decay;
-  int32_t* head;
-  int32_t* count;
-  int32_t* pending;
-  int32_t* arrive;
+  unsigned long long* ptr;  // [B] packed ring pointer words
   int32_t* err;
   const uint16_t* v;   // [B, T, H, D]
   const uint16_t* k;   // [B, T, G, N]
@@ -47,255 +44,252 @@ __device__ __forceinline__ void load_tiles(float4 (&s)[RT][NCT], const float* S0
   }
 }
 
-// One kernel for both decode modes.
+// One kernel for both decode modes, one work-group of four waves per (request,
+// head).
 //  APPEND (T == 1): append the token; it is entry c of E = c + 1; flush all E
 //    entries when E == L (flush-when-full).  count <- E or 0.
 //  VERIFY (T drafts): drafts are entries c .. c+T-1; draft s reads p_s = c+s+1
 //    entries; if c + 2T > L fold the c committed entries only.  pending <- T.
-// A work-group serves HPW consecutive heads of one group: the queries, the ring
-// keys and the inner products k_j . q_s are shared by them and computed once.  With
-// DB the checkpoints of two heads are in flight at a time (two register buffers);
-// without it the next head is fetched into the one buffer once it is consumed.  LCAP (16 or 32) bounds L and sizes the per-lane entry
-// arrays.  Every global load is issued unconditionally with clamped indices
-// (results selected afterwards), so loads go out back to back and the first wait
-// comes at the first use.
-template <int D, int N, int T, bool APPEND, int LCAP, int HPW, bool DB>
+//
+// Nothing waits for the checkpoint until it is needed.  The pointer word (one
+// atomic: read and arrival), the queries and drafts, the step sizes and decays,
+// the group's ring keys and the head's ring values of all L physical slots are
+// requested first, the checkpoint tiles last.  Loads complete in issue order, so
+// the weights (wave 0), the inner products k . q (all waves) and the ring writes
+// of the new entries go ahead while the checkpoint is still streaming in; only the
+// output combine and the fold wait for it.  Ring values arrive 16 bytes per lane
+// and are kept in LDS, where the new entries' values are written into their
+// slots, so the combine and the fold read every value from one array.  The ring
+// is read by physical slot; the pointers only decide which logical entry a slot
+// holds (j = slot - head mod L).  Weights are computed in logical order and
+// stored by physical slot.  LCAP (16 or 32) bounds L and sizes the arrays.
+template <int D, int N, int T, bool APPEND, int LCAP>
 __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
   static_assert(N == 128, "key/query staging assumes n = 128 (16 lanes x 8 values)");
   static_assert(LCAP == 16 || LCAP == 32, "ring capacity bound");
-  static_assert(HPW >= 1 && HPW <= kWavesPerBlock, "one weight scan per wave");
   constexpr int NCT = N / 16;
   constexpr int RT = D / (16 * kWavesPerBlock);
-  constexpr int VJ = LCAP / 4;         // entries per lane in the combine and fold
-  constexpr int PASSES = LCAP / 16;    // inner-product passes of 16 entries
-  constexpr int NEWV = T * D / 8;      // 16-byte chunks of one head's new v
+  constexpr int VJ = LCAP / 4;         // physical slots per lane in the combine and fold
+  constexpr int PASSES = LCAP / 16;    // inner-product passes of 16 slots
+  constexpr int NEWV = T * D / 8;      // 16-byte chunks of the head's new v
   constexpr int NEWK = T * N / 8;      // ... of the group's new k
-  constexpr int NCH = HPW * NEWV + NEWK;
-  constexpr int NCP = (NCH + kBlock - 1) / kBlock;  // new-entry chunks per thread
-  __shared__ float s_w[HPW][T][LCAP];  // w_{j,s} per head, zero where j >= p_s
-  __shared__ float s_M[T][LCAP];       // k_j . q_s (shared by the group)
-  __shared__ float s_abar[HPW][T];
-  __shared__ float s_fw[HPW][LCAP];
-  __shared__ float s_fabar[HPW];
+  constexpr int NCH = NEWV + NEWK;
+  constexpr int NCP = (NCH + kBlock - 1) / kBlock;
+  constexpr int RVC = LCAP * D / 8;    // 16-byte chunks of the head's ring values
+  constexpr int RVP = (RVC + kBlock - 1) / kBlock;
+  __shared__ float s_w[T][LCAP];       // w_{j,s} by physical slot, zero where not read
+  __shared__ float s_M[T][LCAP];       // k . q_s by physical slot
+  __shared__ float s_abar[T];
+  __shared__ float s_fw[LCAP];         // fold weights by physical slot
+  __shared__ float s_fabar;
   __shared__ __attribute__((aligned(16))) uint16_t s_q[T * N];
-  __shared__ __attribute__((aligned(16))) uint16_t s_k[LCAP * N];
+  __shared__ __attribute__((aligned(16))) uint16_t s_k[LCAP * N];  // keys to fold by slot
+  __shared__ __attribute__((aligned(16))) uint16_t s_v[LCAP * D];  // values by slot
+  __shared__ unsigned long long s_word;
 
   const int H = p.H, G = p.G, L = p.L;
-  const int wpr = H / HPW;  // work-groups per request
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
-  const int b = wg / wpr, h0 = (wg - b * wpr) * HPW, hpg = H / G, g = h0 / hpg;
+  const int b = wg / H, h = wg - b * H, hpg = H / G, g = h / hpg;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, cq = lane >> 4, sub = lane & 15;
-  const size_t bh0 = (size_t)b * H + h0;
+  const size_t bh = (size_t)b * H + h;
 
-  // ---- checkpoint tiles of the first two heads: no ring pointer needed
-  float4 sa[RT][NCT], sb[RT][NCT];
-  load_tiles<D, N, RT, NCT>(sa, p.state0 + bh0 * D * N, wave, r, cq);
-  if (DB && HPW > 1) load_tiles<D, N, RT, NCT>(sb, p.state0 + (bh0 + 1) * D * N, wave, r, cq);
-  // queries (8 columns per lane) and the new entries' v / k, all pointer-free
-  uint4 qm[T];
+  // ---- 1. the pointer word and every small operand
+  unsigned long long word = 0;
+  if (tid == 0) word = take_pointers(&p.ptr[b]);
+  uint4 qm[T], kin[T];
 #pragma unroll
-  for (int sd = 0; sd < T; ++sd) qm[sd] = ld_u4(p.q + (((size_t)b * T + sd) * G + g) * N + sub * 8);
-  const bool k_owner = (h0 % hpg) == 0;
-  // chunk t < HPW*NEWV: v of head h0 + t / NEWV; then NEWK chunks of the group's k
-  uint4 newc[NCP];
+  for (int sd = 0; sd < T; ++sd) {
+    qm[sd] = ld_u4(p.q + (((size_t)b * T + sd) * G + g) * N + sub * 8);
+    kin[sd] = ld_u4(p.k + (((size_t)b * T + sd) * G + g) * N + sub * 8);
+  }
+  uint4 newc[NCP];  // chunks of the new entries: the head's v, then the group's k
 #pragma unroll
   for (int i = 0; i < NCP; ++i) {
     const int t = min(tid + i * kBlock, NCH - 1);
     const uint16_t* src;
-    if (t < HPW * NEWV) {
-      const int hh = t / NEWV, tv = t - hh * NEWV;
-      src = p.v + (((size_t)b * T + tv / (D / 8)) * H + h0 + hh) * D + (tv % (D / 8)) * 8;
+    if (t < NEWV) {
+      src = p.v + (((size_t)b * T + t / (D / 8)) * H + h) * D + (t % (D / 8)) * 8;
     } else {
-      const int tk = t - HPW * NEWV;
+      const int tk = t - NEWV;
       src = p.k + (((size_t)b * T + tk / (N / 8)) * G + g) * N + (tk % (N / 8)) * 8;
     }
     newc[i] = ld_u4(src);
   }
+  float dt_slot = 0.f, dc_slot = 1.f, dt_draft = 0.f, dt_bias = 0.f, A_h = 0.f;
+  if (wave == 0) {  // step sizes and decays of every slot, the drafts' raw dt
+    const int sl = min(lane, L - 1);
+    dt_slot = p.ring_dt[bh * L + sl];
+    dc_slot = p.ring_decay[bh * L + sl];
+    dt_draft = p.dt[((size_t)b * T + min(lane, T - 1)) * H + h];
+    dt_bias = p.dt_bias[h];
+    A_h = p.A[h];
+  }
+  uint4 kr[PASSES];  // ring key of slot ps*16 + wave*4 + lane/16, 8 columns per lane
+#pragma unroll
+  for (int ps = 0; ps < PASSES; ++ps)
+    kr[ps] = ld_u4(p.ring_k + (((size_t)b * G + g) * L + min(ps * 16 + wave * 4 + (lane >> 4), L - 1)) * N + sub * 8);
+  uint4 rv[RVP];  // ring values, 16 bytes per lane, slot-major as in memory
+#pragma unroll
+  for (int i = 0; i < RVP; ++i)
+    rv[i] = ld_u4(p.ring_v + bh * L * D + min(tid + i * kBlock, L * D / 8 - 1) * 8);
 
-  // ---- ring pointers (uniform per request), clamped into range
-  int head = p.head[b], cnt = p.count[b];
-  const int pend = p.pending[b];
+  // ---- 2. the checkpoint, last
+  float4 st[RT][NCT];
+  load_tiles<D, N, RT, NCT>(st, p.state0 + bh * D * N, wave, r, cq);
+
+  // ---- 3. ring pointers (uniform per request), clamped into range
+  if (tid == 0) s_word = word;
+#pragma unroll
+  for (int i = 0; i < RVP; ++i) {
+    const int t = tid + i * kBlock;
+    if (t < L * D / 8) *reinterpret_cast<uint4*>(&s_v[t * 8]) = rv[i];
+  }
+  __syncthreads();
+  const RingPtr rp = unpack_ptr(s_word);
+  int head = rp.head, cnt = rp.count;
   int bad = 0;
-  if (head < 0 || head >= L) {
-    head = ((head % L) + L) % L;
+  if (head >= L) {
+    head %= L;
     bad |= RSSM_ERR_POINTERS;
   }
   const int cmax = APPEND ? L - 1 : L - T;
-  if (cnt < 0 || cnt > cmax) {
-    cnt = cnt < 0 ? 0 : cmax;
+  if (cnt > cmax) {
+    cnt = cmax;
     bad |= RSSM_ERR_POINTERS;
   }
-  if (pend != 0) bad |= RSSM_ERR_PENDING;
+  if (rp.pending != 0) bad |= RSSM_ERR_PENDING;
   const int c = cnt;
   const int E = c + T;
   const bool do_flush = APPEND ? (E == L) : (c + 2 * T > L);
   const int F = do_flush ? (APPEND ? E : c) : 0;
   const bool write_new = !(APPEND && do_flush);
-  int arrival = 0;
-  if (tid == 0) arrival = arrive_after_reading(&p.arrive[b], head, cnt, pend);
+  // logical entry held by physical slot sl (0 <= sl < L)
+  auto logical = [&](int sl) { const int j = sl - head; return j < 0 ? j + L : j; };
 
-  // ---- v_j[row] of the first two heads for the entries this lane combines
-  //      (j = cq + 4m); later heads are fetched with their checkpoint tiles
-  float va[RT][VJ], vb[RT][VJ];
-  auto load_v = [&](float (&vj)[RT][VJ], int i) {
+  // ---- 4. the new entries: values into their LDS slots; v (this head) and k
+  //      (group owner head only) cached in the ring unless this call empties it
+  const bool k_owner = (h % hpg) == 0;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const int row = (wave * RT + rt) * 16 + r;
-#pragma unroll
-      for (int m = 0; m < VJ; ++m) {
-        const int j = cq + 4 * m;
-        const int jj = min(j, E - 1);
-        const uint16_t* src = (jj < c) ? p.ring_v + ((bh0 + i) * L + ring_slot(head, jj, L)) * D
-                                       : p.v + (((size_t)b * T + max(jj - c, 0)) * H + h0 + i) * D;
-        const float val = bf16_to_f32(src[row]);
-        vj[rt][m] = (j < E) ? val : 0.f;
-      }
+  for (int i = 0; i < NCP; ++i) {
+    const int t = tid + i * kBlock;
+    if (t < NEWV) {
+      const int sd = t / (D / 8), o = (t % (D / 8)) * 8;
+      const int sl = ring_slot(head, c + sd, L);
+      *reinterpret_cast<uint4*>(&s_v[sl * D + o]) = newc[i];
+      if (write_new) *reinterpret_cast<uint4*>(p.ring_v + (bh * L + sl) * D + o) = newc[i];
+    } else if (write_new && k_owner && t < NCH) {
+      const int tk = t - NEWV;
+      const int sd = tk / (N / 8), o = (tk % (N / 8)) * 8;
+      *reinterpret_cast<uint4*>(p.ring_k + (((size_t)b * G + g) * L + ring_slot(head, c + sd, L)) * N + o) = newc[i];
     }
-  };
-  load_v(va, 0);
-  if (DB && HPW > 1) load_v(vb, 1);
-  // ---- keys of the entries for the shared inner products (16 lanes per entry)
-  uint4 kj[PASSES];
-#pragma unroll
-  for (int ps = 0; ps < PASSES; ++ps) {
-    const int j = ps * 16 + wave * 4 + (lane >> 4);
-    const int jj = min(j, E - 1);
-    const uint16_t* src = (jj < c)
-        ? p.ring_k + (((size_t)b * G + g) * L + ring_slot(head, jj, L)) * N
-        : p.k + (((size_t)b * T + max(jj - c, 0)) * G + g) * N;
-    kj[ps] = ld_u4(src + sub * 8);
   }
 
-  // ---- wave i: step sizes and decays of head h0+i, then its weights by
-  //      suffix-product scans (one per draft boundary, one for the fold)
-  if (wave < HPW) {
-    const int i = wave, hh = h0 + wave;
-    const size_t bh = bh0 + i;
-    const int j = lane;
-    const int jj = min(j, E - 1);
-    const size_t o = bh * L + ring_slot(head, max(min(jj, c - 1), 0), L);
-    const float dl_ring = p.ring_dt[o], al_ring = p.ring_decay[o];
-    const int sdj = max(jj - c, 0);
-    const float dl_new = softplus_f32(p.dt[((size_t)b * T + sdj) * H + hh] + p.dt_bias[hh]);
-    const float al_new = expf(p.A[hh] * dl_new);
-    const bool valid = j < E, cached = jj < c;
+  // ---- 5. wave 0: decay weights in logical order, stored by physical slot
+  if (wave == 0) {
+    const int j = lane;                                // logical entry
+    const int sj = ring_slot(head, min(j, L - 1), L);  // its physical slot
+    const float dl_ring = __shfl(dt_slot, sj, kWave);
+    const float al_ring = __shfl(dc_slot, sj, kWave);
+    const float dtd = __shfl(dt_draft, min(max(j - c, 0), T - 1), kWave);
+    const float dl_new = softplus_f32(dtd + dt_bias);
+    const float al_new = expf(A_h * dl_new);
+    const bool valid = j < E, cached = j < c;
     const float dl = valid ? (cached ? dl_ring : dl_new) : 0.f;
     const float al = valid ? (cached ? al_ring : al_new) : 1.f;
+    const int wi = (j < L) ? sj : j;  // physical index this lane writes
 #pragma unroll
     for (int sd = 0; sd < T; ++sd) {
       const int m = c + sd;  // last entry seen by draft sd
       float all;
       const float ex = suffix_product_excl(j <= m ? al : 1.f, lane, &all);
-      if (j < LCAP) s_w[i][sd][j] = (j <= m) ? dl * ex : 0.f;
-      if (lane == 0) s_abar[i][sd] = all;
+      if (j < LCAP) s_w[sd][wi] = (j <= m) ? dl * ex : 0.f;
+      if (lane == 0) s_abar[sd] = all;
     }
     {
       float all;
       const float ex = suffix_product_excl(j < F ? al : 1.f, lane, &all);
-      if (j < LCAP) s_fw[i][j] = (j < F) ? dl * ex : 0.f;
-      if (lane == 0) s_fabar[i] = all;
+      if (j < LCAP) s_fw[wi] = (j < F) ? dl * ex : 0.f;
+      if (lane == 0) s_fabar = all;
     }
     if (write_new && j >= c && j < E) {  // cache the new entries' step size and decay
-      const size_t on = bh * L + ring_slot(head, j, L);
-      p.ring_dt[on] = dl;
-      p.ring_decay[on] = al;
+      p.ring_dt[bh * L + sj] = dl;
+      p.ring_decay[bh * L + sj] = al;
+    }
+    if (lane < 16) {
+#pragma unroll
+      for (int sd = 0; sd < T; ++sd) *reinterpret_cast<uint4*>(&s_q[sd * N + sub * 8]) = qm[sd];
     }
   }
-  if (wave == 0 && lane < 16) {
-#pragma unroll
-    for (int sd = 0; sd < T; ++sd) *reinterpret_cast<uint4*>(&s_q[sd * N + sub * 8]) = qm[sd];
-  }
 
-  // ---- all waves: inner products and staging of the keys to fold
+  // ---- 6. all waves: k . q_s for every physical slot (16 lanes per slot); keys
+  //      to fold staged by slot (zero rows for slots not folded)
 #pragma unroll
   for (int ps = 0; ps < PASSES; ++ps) {
-    const int j = ps * 16 + wave * 4 + (lane >> 4);
-    const uint4 kv = (j < E) ? kj[ps] : make_uint4(0, 0, 0, 0);
-    if (j < F) *reinterpret_cast<uint4*>(&s_k[j * N + sub * 8]) = kv;
+    const int sl = ps * 16 + wave * 4 + (lane >> 4);
+    const bool in_ring = sl < L;
+    const int j = logical(min(sl, L - 1));
+    uint4 kv = (in_ring && j < c) ? kr[ps] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int sd = 0; sd < T; ++sd)
+      if (in_ring && j == c + sd) kv = kin[sd];
+    if (in_ring) *reinterpret_cast<uint4*>(&s_k[sl * N + sub * 8]) = (j < F) ? kv : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int sd = 0; sd < T; ++sd) {
       const float dv = reduce_quarter(dot8_bf16(kv, qm[sd]));
-      if (sub == 0) s_M[sd][j] = dv;
+      if (sub == 0) s_M[sd][sl] = dv;
     }
   }
   __syncthreads();
 
-  // ---- per head: output-only route y_s = abar_s (S_0 q_s) + sum_j w_{j,s} M_{j,s} v_j,
-  //      then the fold when flushing; the next-but-one head is loaded into the
-  //      buffer just consumed
+  // ---- 7. output-only route, fold when flushing (the checkpoint is needed here)
+  float vj[RT][VJ];  // value of slot cq + 4m at this lane's rows, zero if not read
 #pragma unroll
-  for (int i = 0; i < HPW; ++i) {
-    float4 (&s)[RT][NCT] = (DB && (i & 1)) ? sb : sa;
-    float (&vj)[RT][VJ] = (DB && (i & 1)) ? vb : va;
-    const size_t bh = bh0 + i;
-    float* S0 = p.state0 + bh * D * N;
+  for (int m = 0; m < VJ; ++m) {
+    const int sl = cq + 4 * m;
+    const bool used = sl < L && logical(min(sl, L - 1)) < E;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const int row = (wave * RT + rt) * 16 + r;
-      float dots[T];
-#pragma unroll
-      for (int sd = 0; sd < T; ++sd) dots[sd] = 0.f;
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-        for (int sd = 0; sd < T; ++sd)
-          dots[sd] += dot4_bf16(s[rt][ct], *reinterpret_cast<const uint2*>(&s_q[sd * N + ct * 16 + cq * 4]));
-#pragma unroll
-      for (int sd = 0; sd < T; ++sd) {
-        float part = s_abar[i][sd] * dots[sd];
-#pragma unroll
-        for (int m = 0; m < VJ; ++m) {
-          const int j = cq + 4 * m;
-          part += s_w[i][sd][j] * s_M[sd][j] * vj[rt][m];  // both zero beyond p_s
-        }
-        part = reduce_row4(part);
-        if ((sd & 3) == cq) p.y[(((size_t)b * T + sd) * H + h0 + i) * D + row] = part;
-      }
-    }
-    if (F > 0)
-      fold_and_store<D, N, RT, NCT, VJ>(S0, s, s_fabar[i], s_k, s_fw[i], vj, F, wave, r, cq);
-    constexpr int ahead = DB ? 2 : 1;  // the buffer just consumed takes head i + ahead
-    if (i + ahead < HPW) {
-      load_tiles<D, N, RT, NCT>(s, p.state0 + (bh + ahead) * D * N, wave, r, cq);
-      load_v(vj, i + ahead);
+      vj[rt][m] = used ? bf16_to_f32(s_v[min(sl, LCAP - 1) * D + row]) : 0.f;
     }
   }
-
-  // ---- cache the new entries' v (every head here) and k (group owner only)
-  if (write_new) {
 #pragma unroll
-    for (int i = 0; i < NCP; ++i) {
-      const int t = tid + i * kBlock;
-      if (t < HPW * NEWV) {
-        const int hh = t / NEWV, tv = t - hh * NEWV;
-        const int sd = tv / (D / 8), o = (tv % (D / 8)) * 8;
-        *reinterpret_cast<uint4*>(p.ring_v + ((bh0 + hh) * L + ring_slot(head, c + sd, L)) * D + o) = newc[i];
-      } else if (k_owner && t < NCH) {
-        const int tk = t - HPW * NEWV;
-        const int sd = tk / (N / 8), o = (tk % (N / 8)) * 8;
-        *reinterpret_cast<uint4*>(p.ring_k + (((size_t)b * G + g) * L + ring_slot(head, c + sd, L)) * N + o) = newc[i];
+  for (int rt = 0; rt < RT; ++rt) {
+    const int row = (wave * RT + rt) * 16 + r;
+    float dots[T];
+#pragma unroll
+    for (int sd = 0; sd < T; ++sd) dots[sd] = 0.f;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int sd = 0; sd < T; ++sd)
+        dots[sd] += dot4_bf16(st[rt][ct], *reinterpret_cast<const uint2*>(&s_q[sd * N + ct * 16 + cq * 4]));
+#pragma unroll
+    for (int sd = 0; sd < T; ++sd) {
+      float part = s_abar[sd] * dots[sd];
+#pragma unroll
+      for (int m = 0; m < VJ; ++m) {
+        const int sl = cq + 4 * m;
+        part += s_w[sd][sl] * s_M[sd][sl] * vj[rt][m];  // zero for slots not read
       }
+      part = reduce_row4(part);
+      if ((sd & 3) == cq) p.y[(((size_t)b * T + sd) * H + h) * D + row] = part;
     }
   }
+  if (F > 0)
+    fold_and_store<D, N, RT, NCT, VJ>(p.state0 + bh * D * N, st, s_fabar, s_k, s_fw, vj, L, wave, r, cq);
 
-  // ---- pointer update by the last work-group of the request to read them
+  // ---- 8. pointer update by the last work-group of the request to read them
   if (tid == 0) {
-    if (h0 == 0) {
+    if (h == 0) {
       flag_error(p.err, bad);
       if (p.flushed != nullptr) p.flushed[b] = do_flush ? 1 : 0;
     }
-    if (arrival == wpr - 1) {
-      p.arrive[b] = 0;
-      if (APPEND) {
-        p.head[b] = do_flush ? ring_slot(head, E % L, L) : head;
-        p.count[b] = do_flush ? 0 : E;
-        p.pending[b] = 0;
-      } else {
-        p.head[b] = do_flush ? ring_slot(head, c % L, L) : head;
-        p.count[b] = do_flush ? 0 : c;
-        p.pending[b] = T;
-      }
+    if (rp.arrive == H - 1) {
+      const int keep = APPEND ? E : c;  // entries that stay committed unless flushed
+      put_pointers(&p.ptr[b], pack_ptr(do_flush ? ring_slot(head, F % L, L) : head,
+                                       do_flush ? keep - F : keep, APPEND ? 0 : T));
     }
   }
 }
@@ -306,33 +300,11 @@ namespace rssm_host {
 
 using rssm::ReplayParams;
 
-// Work-group shape: heads per work-group and double buffering.  Four heads with two
-// state buffers in flight when the group size allows it (measured best on the
-// 32-head, 8-group layer; 1, 2 or 4 heads with one or two buffers all stream within
-// 3% of each other there), else one head per work-group.
-struct WindowShape {
-  int hpw;
-  bool db;
-};
-
-inline WindowShape window_shape(const ReplayParams& p) {
-  const int hpg = p.H / p.G;
-  if (hpg % 4 == 0) return {4, true};
-  return {1, false};
-}
-
-template <int D, int T, bool APPEND, int LCAP>
-int launch_window_cap(const ReplayParams& p, WindowShape sh, int B, void* stream) {
-  const dim3 grid(B * (p.H / sh.hpw)), block(rssm::kBlock);
-  if (sh.hpw == 4) return launch(rssm::replay_window_kernel<D, 128, T, APPEND, LCAP, 4, true>, grid, block, stream, p);
-  return launch(rssm::replay_window_kernel<D, 128, T, APPEND, LCAP, 1, false>, grid, block, stream, p);
-}
-
 template <int D, int T, bool APPEND>
 int launch_window(const ReplayParams& p, int B, void* stream) {
-  const WindowShape sh = window_shape(p);
-  if (p.L <= 16) return launch_window_cap<D, T, APPEND, 16>(p, sh, B, stream);
-  return launch_window_cap<D, T, APPEND, 32>(p, sh, B, stream);
+  const dim3 grid(B * p.H), block(rssm::kBlock);
+  if (p.L <= 16) return launch(rssm::replay_window_kernel<D, 128, T, APPEND, 16>, grid, block, stream, p);
+  return launch(rssm::replay_window_kernel<D, 128, T, APPEND, 32>, grid, block, stream, p);
 }
 
 // Verify launchers for T = 1..4 and T = 5..8 live in their own translation units.

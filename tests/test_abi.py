@@ -32,7 +32,7 @@ def test_every_declared_function_is_exported_and_prototyped():
 
 def test_abi_version_and_strerror():
     lib = _lib.load()
-    assert lib.rssm_abi_version() == 1
+    assert lib.rssm_abi_version() == _lib.ABI_VERSION == 2
     assert "invalid" in _lib.strerror(_lib.RSSM_EINVAL)
     assert "not supported" in _lib.strerror(_lib.RSSM_ENOTSUP)
 
@@ -42,16 +42,16 @@ def _dims(B=4, H=8, d=64, n=128, G=1, L=8):
 
 
 def _ring():
-    return _lib.rssm_ring(*([FAKE.value] * 9))
+    return _lib.rssm_ring(*([FAKE.value] * 6))
 
 
 def test_ring_sizes():
     lib = _lib.load()
-    out = (ctypes.c_size_t * 9)()
+    out = (ctypes.c_size_t * 6)()
     d = _dims(B=256, H=32, d=64, n=128, G=8, L=16)
     assert lib.rssm_ring_sizes(ctypes.byref(d), 0, out) == 0
     assert list(out) == [256 * 32 * 16 * 64 * 2, 256 * 8 * 16 * 128 * 2, 256 * 32 * 16 * 4,
-                         256 * 32 * 16 * 4, 1024, 1024, 1024, 1024, 4]
+                         256 * 32 * 16 * 4, 256 * 8, 4]
     assert lib.rssm_ring_sizes(ctypes.byref(d), 1, out) == 0
     assert out[0] == 256 * 32 * 16 * 64 * 4 and out[2] == 0
 
@@ -95,6 +95,15 @@ def test_host_validation_codes():
     assert lib.causal_conv1d_update(0, 3072, 4, P, P, P, P, None) == EINVAL
     # rollback needs accepted
     assert lib.replay_rollback(ctypes.byref(d), ctypes.byref(r), None, None) == EINVAL
+    # pointer words must be 8-byte aligned
+    r_odd = _ring()
+    r_odd.ptr = FAKE.value + 4
+    assert lib.replay_rollback(ctypes.byref(d), ctypes.byref(r_odd), P, None) == EINVAL
+    assert lib.rssm_ring_reset(ctypes.byref(d), ctypes.byref(r_odd), None, None) == EINVAL
+    # the 16-bit arrival field bounds the heads per request
+    big = _dims(H=1 << 16, G=1)
+    assert lib.replay_append_decode(ctypes.byref(big), P, ctypes.byref(r), P, P, P, P, P, P, P,
+                                    None, None) == ENOTSUP
     # probes
     assert lib.rssm_probe_copy(P, P, 15, None) == EINVAL
 

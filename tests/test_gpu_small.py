@@ -203,7 +203,7 @@ def test_pointer_anomalies_are_clamped_and_flagged():
     assert int(ring.err.item()) & 2
     assert ring.count.cpu().tolist() == [4, 0, 4, 2]
     ring.err.zero_()
-    ring.count.copy_(dev_i32(np.array([40, 3, -2, 1])))       # corrupt count
+    ring.set_pointers(count=[40, 3, -2, 1])                   # corrupt count
     rd.replay_verify_T(dims, 4, state0, ring, dev_bf16(st["v"]), dev_bf16(st["k"]),
                        dev_bf16(st["q"]), dev_f32(st["dt"]), dev_f32(dt_bias), dev_f32(A), y)
     torch.cuda.synchronize()
