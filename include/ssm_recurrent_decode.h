@@ -72,33 +72,32 @@ typedef struct rssm_dims {
  * from `head`, so a rollback only moves a pointer.  Physical slot of logical
  * entry j (0 = oldest) of request b is (head + j) % L.
  *
- * The pointers of request b live in one 64-bit word ptr[b] (RSSM_PTR_* below):
- * head, count (committed entries since the checkpoint), pending (uncommitted
- * drafts that follow them) and the arrival count of the call in flight.  A
- * work-group takes the word with one atomic add of 1, which reads the pointers
- * and counts it in at once; the work-group that finds the arrival field at
- * (work-groups of the request - 1) is the last reader and writes the new
- * pointers with the field back at zero.  The field is zero between calls.
+ * The pointers of request b (head, count = committed entries since the
+ * checkpoint, pending = uncommitted drafts that follow them) are packed in a
+ * 64-bit word (RSSM_PTR_* below) kept once per head: ptr[b * H + h] is request
+ * b's word as head h keeps it.  Every call moves all H copies of a request the
+ * same way, so they stay equal; the work of head h reads and writes only copy h,
+ * so no two work-groups share a word and no atomics are needed.
  *
  * Caller allocates every array and zero-fills ptr and err once before the first
  * call; afterwards only the library writes them (rssm_ring_reset re-zeroes a
  * subset of requests).  Unsigned fields: a head >= L or a count above the
- * largest legal value is clamped and flagged (RSSM_ERR_POINTERS).
+ * largest legal value is clamped and flagged (RSSM_ERR_POINTERS).  Bits 48-63
+ * are zero.
  */
-#define RSSM_PTR_ARRIVE(w) ((uint32_t)((w) & 0xFFFFu))
-#define RSSM_PTR_HEAD(w) ((uint32_t)(((w) >> 16) & 0xFFFFu))
-#define RSSM_PTR_COUNT(w) ((uint32_t)(((w) >> 32) & 0xFFFFu))
-#define RSSM_PTR_PENDING(w) ((uint32_t)(((w) >> 48) & 0xFFFFu))
-#define RSSM_PTR_PACK(head, count, pending)                                      \
-  ((((uint64_t)(head) & 0xFFFFu) << 16) | (((uint64_t)(count) & 0xFFFFu) << 32) | \
-   (((uint64_t)(pending) & 0xFFFFu) << 48))
+#define RSSM_PTR_HEAD(w) ((uint32_t)((w) & 0xFFFFu))
+#define RSSM_PTR_COUNT(w) ((uint32_t)(((w) >> 16) & 0xFFFFu))
+#define RSSM_PTR_PENDING(w) ((uint32_t)(((w) >> 32) & 0xFFFFu))
+#define RSSM_PTR_PACK(head, count, pending)                                \
+  (((uint64_t)(head) & 0xFFFFu) | (((uint64_t)(count) & 0xFFFFu) << 16) | \
+   (((uint64_t)(pending) & 0xFFFFu) << 32))
 
 typedef struct rssm_ring {
   void* vu;          /* Mamba-2: v  bf16 [B, H, L, d];  GDN: u fp32 [B, H, L, d]     */
   uint16_t* k;       /* bf16 [B, G, L, n]                                           */
   float* dt;         /* Mamba-2: Delta fp32 [B, H, L] (after softplus);  GDN: unused */
   float* decay;      /* Mamba-2: a = exp(A Delta);  GDN: alpha = exp(g);  fp32 [B,H,L] */
-  uint64_t* ptr;     /* [B] packed pointer words (RSSM_PTR_*), 8-byte aligned        */
+  uint64_t* ptr;     /* [B, H] packed pointer words (RSSM_PTR_*), one per head       */
   int32_t* err;      /* [1] anomaly bits (RSSM_ERR_*), may be NULL                  */
 } rssm_ring;
 
@@ -110,7 +109,7 @@ const char* rssm_strerror(int code);
  * is_gdn selects fp32 u instead of bf16 v and no dt array.  Host-only. */
 int rssm_ring_sizes(const rssm_dims* dims, int is_gdn, size_t out_bytes[6]);
 
-/* Zero the pointer word (head, count, pending, arrivals) of requests with
+/* Zero the pointer words (head, count, pending) of requests with
  * mask[b] != 0 (mask NULL = all) and clear err.  The ring contents are left as
  * they are: with count = 0 they are never read.  Use after an explicit
  * replay_flush to recycle a request slot, or to start a new request from a

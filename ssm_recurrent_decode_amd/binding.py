@@ -67,9 +67,10 @@ class Ring:
 
     Allocated zero-filled with torch on ``device``; ``gdn`` selects fp32
     corrections u instead of bf16 values v and no step-size array.  The pointers
-    of request b are packed in the 64-bit word ``ptr[b]`` (arrivals in bits
-    0-15, head 16-31, count 32-47, pending 48-63); ``head``, ``count``,
-    ``pending`` and ``arrive`` are read-only int32 views decoded from it."""
+    of request b are packed in 64-bit words (head in bits 0-15, count 16-31,
+    pending 32-47), one copy per head in ``ptr[b, h]``; ``head``, ``count`` and
+    ``pending`` are int32 views decoded from head 0's copy, and ``copies_agree``
+    checks that every head's copy is the same."""
 
     def __init__(self, dims: Dims, gdn: bool = False, device="cuda"):
         B, H, G, L = dims.batch, dims.nheads, dims.ngroups, dims.capacity
@@ -80,38 +81,36 @@ class Ring:
         self.k = torch.zeros((B, G, L, N), dtype=torch.bfloat16, **z)
         self.dt = None if gdn else torch.zeros((B, H, L), dtype=torch.float32, **z)
         self.decay = torch.zeros((B, H, L), dtype=torch.float32, **z)
-        self.ptr = torch.zeros((B,), dtype=torch.int64, **z)
+        self.ptr = torch.zeros((B, H), dtype=torch.int64, **z)
         self.err = torch.zeros((1,), dtype=torch.int32, **z)
 
     def _field(self, shift: int):
-        return ((self.ptr >> shift) & 0xFFFF).to(torch.int32)
-
-    @property
-    def arrive(self):
-        return self._field(0)
+        return ((self.ptr[:, 0] >> shift) & 0xFFFF).to(torch.int32)
 
     @property
     def head(self):
-        return self._field(16)
+        return self._field(0)
 
     @property
     def count(self):
-        return self._field(32)
+        return self._field(16)
 
     @property
     def pending(self):
-        return self._field(48)
+        return self._field(32)
+
+    def copies_agree(self) -> bool:
+        return bool(torch.all(self.ptr == self.ptr[:, :1]))
 
     def set_pointers(self, head=None, count=None, pending=None):
-        """Overwrite pointer fields (sequences of B ints, or None to keep); each
-        value is stored modulo 2^16 as the packed word holds it.  Arrivals are
-        zeroed."""
+        """Overwrite pointer fields of every head's copy (sequences of B ints, or
+        None to keep head 0's value); each value is stored modulo 2^16 as the
+        packed word holds it."""
         cur = [self.head.cpu().tolist(), self.count.cpu().tolist(), self.pending.cpu().tolist()]
         new = [list(x) if x is not None else c for x, c in zip((head, count, pending), cur)]
-        words = [((h & 0xFFFF) << 16) | ((c & 0xFFFF) << 32) | ((p & 0xFFFF) << 48)
-                 for h, c, p in zip(*new)]
-        words = [w - (1 << 64) if w >= (1 << 63) else w for w in words]
-        self.ptr.copy_(torch.tensor(words, dtype=torch.int64))
+        words = [(h & 0xFFFF) | ((c & 0xFFFF) << 16) | ((p & 0xFFFF) << 32) for h, c, p in zip(*new)]
+        col = torch.tensor(words, dtype=torch.int64).to(self.ptr.device)
+        self.ptr.copy_(col[:, None].expand_as(self.ptr))
 
     def c(self) -> _lib.rssm_ring:
         return _lib.rssm_ring(self.vu.data_ptr(), self.k.data_ptr(),

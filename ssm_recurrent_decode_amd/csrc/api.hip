@@ -62,7 +62,7 @@ extern "C" int rssm_ring_sizes(const rssm_dims* d, int is_gdn, size_t out[6]) {
   out[1] = B * G * L * N * 2;
   out[2] = is_gdn ? 0 : B * H * L * 4;
   out[3] = B * H * L * 4;
-  out[4] = B * 8;
+  out[4] = B * H * 8;
   out[5] = 4;
   return RSSM_OK;
 }

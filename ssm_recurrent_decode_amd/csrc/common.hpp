@@ -54,35 +54,60 @@ __device__ __forceinline__ int ring_slot(int head, int j, int L) {
   return s >= L ? s - L : s;
 }
 
-// Exclusive suffix product across the lanes of a wave, for values that are 1 on
-// every lane >= 32: returns prod_{i > lane} x_i and sets *all = prod_i x_i.  Five
-// log-steps instead of a serial chain; products only, never a division, so an
-// underflow to zero stays zero.
-__device__ __forceinline__ float suffix_product_excl(float x, int lane, float* all) {
+// ---- cross-lane steps in registers (DPP and the gfx950 lane swaps, no LDS)
+// DPP controls of the gfx9 encoding.
+constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppRowShr1 = 0x111;   // row_shr:n = 0x110 + n
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
+constexpr int kDppRowRor4 = 0x124;   // row_ror:n = 0x120 + n
+constexpr int kDppRowRor8 = 0x128;
+constexpr int kDppWaveShr1 = 0x138;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
+// src moved by the DPP pattern CTRL; lanes with no source, and lanes of rows not
+// in ROW_MASK, get `old`.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_move(float old, float src) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src), CTRL,
+                                                    ROW_MASK, 0xF, false));
+}
+
+// Exclusive prefix product over the 64 lanes of a wave: returns
+// prod_{l' < lane} x_{l'} and sets *all = prod over all lanes (every lane).
+// Hillis-Steele steps inside each row of 16 lanes, then the row totals are
+// carried across rows; products only, never a division, so an underflow to zero
+// stays zero.  All lanes of the wave must be active.
+__device__ __forceinline__ float prefix_product_excl(float x, float* all) {
   float v = x;
-#pragma unroll
-  for (int off = 1; off < 32; off <<= 1) {
-    const float o = __shfl_down(v, off, kWave);
-    v = (lane + off < kWave) ? v * o : v;
-  }
-  *all = __shfl(v, 0, kWave);
-  const float ex = __shfl_down(v, 1, kWave);
-  return (lane + 1 < kWave) ? ex : 1.f;
+  v *= dpp_move<kDppRowShr1>(1.f, v);
+  v *= dpp_move<kDppRowShr2>(1.f, v);
+  v *= dpp_move<kDppRowShr4>(1.f, v);
+  v *= dpp_move<kDppRowShr8>(1.f, v);
+  v *= dpp_move<kDppRowBcast15, 0xA>(1.f, v);  // rows 1, 3 take lane 15 of rows 0, 2
+  v *= dpp_move<kDppRowBcast31, 0xC>(1.f, v);  // rows 2, 3 take lane 31
+  *all = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
+  return dpp_move<kDppWaveShr1>(1.f, v);
 }
 
-// Sum over the four lanes that share a row in the tile layout.
+// Sum over the four lanes that share a row in the tile layout (lanes l, l^16,
+// l^32, l^48), every lane receiving the sum.
 __device__ __forceinline__ float reduce_row4(float v) {
-  v += __shfl_xor(v, 16, kWave);
-  v += __shfl_xor(v, 32, kWave);
-  return v;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+  v = __int_as_float(a[0]) + __int_as_float(a[1]);  // v_l + v_{l^16}
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return __int_as_float(c[0]) + __int_as_float(c[1]);  // ... + the same from l^32
 }
 
-// Sum over the 16 consecutive lanes of a quarter-wave.
+// Sum over the 16 lanes of a row, every lane of the row receiving the sum.
 __device__ __forceinline__ float reduce_quarter(float v) {
-  v += __shfl_xor(v, 1, kWave);
-  v += __shfl_xor(v, 2, kWave);
-  v += __shfl_xor(v, 4, kWave);
-  v += __shfl_xor(v, 8, kWave);
+  v += dpp_move<kDppRowRor8>(0.f, v);
+  v += dpp_move<kDppRowRor4>(0.f, v);
+  v += dpp_move<kDppQuadXor2>(0.f, v);
+  v += dpp_move<kDppQuadXor1>(0.f, v);
   return v;
 }
 
@@ -101,44 +126,20 @@ __device__ __forceinline__ float dot8_bf16(uint4 a, uint4 b) {
          bf16_lo(a.w) * bf16_lo(b.w) + bf16_hi(a.w) * bf16_hi(b.w);
 }
 
-// Ring pointer word of one request: arrivals of the call in flight in bits
-// 0-15, head 16-31, count 32-47, pending 48-63.
+// Ring pointer word of one request as one head keeps it: head in bits 0-15,
+// count 16-31, pending 32-47.  Each head has its own copy and every call moves
+// all copies alike, so the work of head h reads and writes only copy h.
 struct RingPtr {
-  int head, count, pending, arrive;
+  int head, count, pending;
 };
 
 __device__ __forceinline__ RingPtr unpack_ptr(unsigned long long w) {
-  return {int((w >> 16) & 0xFFFFu), int((w >> 32) & 0xFFFFu), int((w >> 48) & 0xFFFFu),
-          int(w & 0xFFFFu)};
+  return {int(w & 0xFFFFu), int((w >> 16) & 0xFFFFu), int((w >> 32) & 0xFFFFu)};
 }
 
 __device__ __forceinline__ unsigned long long pack_ptr(int head, int count, int pending) {
-  return ((unsigned long long)(head & 0xFFFF) << 16) | ((unsigned long long)(count & 0xFFFF) << 32) |
-         ((unsigned long long)(pending & 0xFFFF) << 48);
-}
-
-// Work-group arrival.  Each work-group of a request adds 1 to the word once;
-// the returned old value is its copy of the pointers, so the read and the
-// arrival are one operation.  The work-group whose arrival field reads
-// nblocks - 1 comes after every other work-group's read and alone writes the
-// new pointers (arrival field zero) with put_pointers.  No fence is needed:
-// the new pointers are only read by later launches.
-__device__ __forceinline__ unsigned long long take_pointers(unsigned long long* word) {
-  return atomicAdd(word, 1ull);
-}
-
-__device__ __forceinline__ void put_pointers(unsigned long long* word, unsigned long long w) {
-  atomicExch(word, w);
-}
-
-// Plain access for the single-thread-per-request pointer kernels (rollback,
-// reset), device scope so no stale cached copy is read.
-__device__ __forceinline__ unsigned long long load_pointers(const unsigned long long* word) {
-  return __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ void store_pointers(unsigned long long* word, unsigned long long w) {
-  __hip_atomic_store(word, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return (unsigned long long)(head & 0xFFFF) | ((unsigned long long)(count & 0xFFFF) << 16) |
+         ((unsigned long long)(pending & 0xFFFF) << 32);
 }
 
 __device__ __forceinline__ void flag_error(int32_t* err, int bits) {
@@ -215,10 +216,8 @@ inline bool shape_supported(const rssm_dims* d) {
   return (d->head_dim == 64 || d->head_dim == 128) && d->state_dim == 128;
 }
 
-// The arrival field of a pointer word is 16 bits wide and counts the
-// work-groups of one request (at most one per head).
 inline bool ring_shape_supported(const rssm_dims* d) {
-  return shape_supported(d) && d->capacity <= rssm::kMaxL && d->nheads <= 0xFFFF;
+  return shape_supported(d) && d->capacity <= rssm::kMaxL;
 }
 
 inline bool ptr_ok(const rssm_ring* r) {

@@ -89,7 +89,7 @@ struct GdnReplayParams {
   float* ring_u;       // [B, H, L, D] fp32
   uint16_t* ring_k;    // [B, G, L, N]
   float* ring_alpha;   // [B, H, L]
-  unsigned long long* ptr;  // [B] packed ring pointer words
+  unsigned long long* ptr;  // [B, H] packed ring pointer words, one copy per head
   int32_t* err;
   const uint16_t* v;   // [B, T, H, D]
   const uint16_t* k;   // [B, T, G, N]
@@ -123,12 +123,10 @@ __global__ __launch_bounds__(kBlock) void gdn_verify_kernel(GdnReplayParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, cq = lane >> 4;
 
-  // ---- the pointer word (one atomic: read + arrival) and the checkpoint tiles,
-  //      which need no pointer, in flight together
-  __shared__ unsigned long long s_word;
-  unsigned long long word = 0;
-  if (tid == 0) word = take_pointers(&p.ptr[b]);
+  // ---- this head's copy of the pointer word and the checkpoint tiles, which
+  //      need no pointer, in flight together
   const size_t bh = (size_t)b * H + h;
+  const unsigned long long word = p.ptr[bh];
   float* S0 = p.state0 + bh * D * N;
   float4 s[RT][NCT];
 #pragma unroll
@@ -137,9 +135,7 @@ __global__ __launch_bounds__(kBlock) void gdn_verify_kernel(GdnReplayParams p) {
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) s[rt][ct] = ld_f4(S0 + row * N + ct * 16 + cq * 4);
   }
-  if (tid == 0) s_word = word;
-  __syncthreads();
-  const RingPtr rp = unpack_ptr(s_word);
+  const RingPtr rp = unpack_ptr(word);
   int head = rp.head, cnt = rp.count;
   int bad = 0;
   if (head >= L) {
@@ -321,8 +317,7 @@ __global__ __launch_bounds__(kBlock) void gdn_verify_kernel(GdnReplayParams p) {
       flag_error(p.err, bad);
       if (p.flushed != nullptr) p.flushed[b] = do_flush ? 1 : 0;
     }
-    if (rp.arrive == H - 1)
-      put_pointers(&p.ptr[b], pack_ptr(do_flush ? (head + c) % L : head, do_flush ? 0 : c, T));
+    p.ptr[bh] = pack_ptr(do_flush ? (head + c) % L : head, do_flush ? 0 : c, T);
   }
 }
 
@@ -342,10 +337,8 @@ __global__ __launch_bounds__(kBlock) void gdn_flush_kernel(GdnReplayParams p) {
   const int r = lane & 15, cq = lane >> 4;
 
   if (p.mask != nullptr && p.mask[b] == 0) return;
-  __shared__ unsigned long long s_word;
-  if (tid == 0) s_word = take_pointers(&p.ptr[b]);
-  __syncthreads();
-  const RingPtr rp = unpack_ptr(s_word);
+  const size_t bh = (size_t)b * H + h;
+  const RingPtr rp = unpack_ptr(p.ptr[bh]);
   int head = rp.head, cnt = rp.count;
   int bad = 0;
   if (head >= L) {
@@ -358,7 +351,6 @@ __global__ __launch_bounds__(kBlock) void gdn_flush_kernel(GdnReplayParams p) {
   }
   if (cnt + rp.pending > L) bad |= RSSM_ERR_POINTERS;
   const int F = cnt;
-  const size_t bh = (size_t)b * H + h;
   float* S0 = p.state0 + bh * D * N;
   float4 s[RT][NCT];
   if (F > 0) {
@@ -401,9 +393,7 @@ __global__ __launch_bounds__(kBlock) void gdn_flush_kernel(GdnReplayParams p) {
 
   if (tid == 0) {
     if (h == 0) flag_error(p.err, bad);
-    // every work-group arrives, also with nothing to fold, so the last one can
-    // reset the arrival field
-    if (rp.arrive == H - 1) put_pointers(&p.ptr[b], pack_ptr((head + F) % L, 0, rp.pending));
+    p.ptr[bh] = pack_ptr((head + F) % L, 0, rp.pending);
   }
 }
 

@@ -97,10 +97,8 @@ __global__ __launch_bounds__(kBlock) void replay_flush_kernel(ReplayParams p) {
   const int r = lane & 15, cq = lane >> 4;
 
   if (p.mask != nullptr && p.mask[b] == 0) return;
-  __shared__ unsigned long long s_word;
-  if (tid == 0) s_word = take_pointers(&p.ptr[b]);
-  __syncthreads();
-  const RingPtr rp = unpack_ptr(s_word);
+  const size_t bh = (size_t)b * H + h;
+  const RingPtr rp = unpack_ptr(p.ptr[bh]);
   int head = rp.head, cnt = rp.count;
   int bad = 0;
   if (head >= L) {
@@ -113,7 +111,6 @@ __global__ __launch_bounds__(kBlock) void replay_flush_kernel(ReplayParams p) {
   }
   if (cnt + rp.pending > L) bad |= RSSM_ERR_POINTERS;
   const int F = cnt;
-  const size_t bh = (size_t)b * H + h;
   float* S0 = p.state0 + bh * D * N;
   float4 s[RT][NCT];
   if (F > 0) {
@@ -161,9 +158,7 @@ __global__ __launch_bounds__(kBlock) void replay_flush_kernel(ReplayParams p) {
 
   if (tid == 0) {
     if (h == 0) flag_error(p.err, bad);
-    // every work-group of the request arrives (also when there is nothing to
-    // fold) so the last one can reset the arrival field
-    if (rp.arrive == H - 1) put_pointers(&p.ptr[b], pack_ptr((head + F) % L, 0, rp.pending));
+    p.ptr[bh] = pack_ptr((head + F) % L, 0, rp.pending);
   }
 }
 
@@ -172,15 +167,16 @@ struct PtrParams {
   int32_t* err;
   const int32_t* accepted;
   const int32_t* mask;
-  int B, L;
+  int B, H, L;
 };
 
+// One thread per (request, head) copy of the pointer word:
 // count += clamp(accepted, 0, pending); pending = 0.
 __global__ __launch_bounds__(kBlock) void rollback_kernel(PtrParams p) {
-  const int b = blockIdx.x * kBlock + threadIdx.x;
-  if (b >= p.B) return;
-  const RingPtr rp = unpack_ptr(load_pointers(&p.ptr[b]));
-  int head = rp.head, cnt = rp.count, pend = rp.pending, acc = p.accepted[b];
+  const int i = blockIdx.x * kBlock + threadIdx.x;
+  if (i >= p.B * p.H) return;
+  const RingPtr rp = unpack_ptr(p.ptr[i]);
+  int head = rp.head, cnt = rp.count, pend = rp.pending, acc = p.accepted[i / p.H];
   int bad = 0;
   if (head >= p.L) {
     head %= p.L;
@@ -198,15 +194,15 @@ __global__ __launch_bounds__(kBlock) void rollback_kernel(PtrParams p) {
     acc = acc < 0 ? 0 : pend;
     bad |= RSSM_ERR_ACCEPTED;
   }
-  store_pointers(&p.ptr[b], pack_ptr(head, cnt + acc, 0));
+  p.ptr[i] = pack_ptr(head, cnt + acc, 0);
   flag_error(p.err, bad);
 }
 
 __global__ __launch_bounds__(kBlock) void ring_reset_kernel(PtrParams p) {
-  const int b = blockIdx.x * kBlock + threadIdx.x;
-  if (b == 0 && p.err != nullptr) *p.err = 0;
-  if (b >= p.B) return;
-  if (p.mask == nullptr || p.mask[b] != 0) store_pointers(&p.ptr[b], 0ull);
+  const int i = blockIdx.x * kBlock + threadIdx.x;
+  if (i == 0 && p.err != nullptr) *p.err = 0;
+  if (i >= p.B * p.H) return;
+  if (p.mask == nullptr || p.mask[i / p.H] != 0) p.ptr[i] = 0ull;
 }
 
 }  // namespace rssm
@@ -308,8 +304,8 @@ extern "C" int replay_rollback(const rssm_dims* dims, rssm_ring* ring, const int
   if (!rssm_host::dims_ok(dims) || !rssm_host::ptr_ok(ring) || !accepted) return RSSM_EINVAL;
   if (dims->capacity < 1) return RSSM_EINVAL;
   PtrParams p{reinterpret_cast<unsigned long long*>(ring->ptr), ring->err, accepted, nullptr,
-              dims->batch, dims->capacity};
-  const dim3 grid((dims->batch + kBlock - 1) / kBlock);
+              dims->batch, dims->nheads, dims->capacity};
+  const dim3 grid((dims->batch * dims->nheads + kBlock - 1) / kBlock);
   return launch(rollback_kernel, grid, dim3(kBlock), stream, p);
 }
 
@@ -317,7 +313,7 @@ extern "C" int rssm_ring_reset(const rssm_dims* dims, rssm_ring* ring, const int
                                void* stream) {
   if (!rssm_host::dims_ok(dims) || !rssm_host::ptr_ok(ring)) return RSSM_EINVAL;
   PtrParams p{reinterpret_cast<unsigned long long*>(ring->ptr), ring->err, nullptr, mask,
-              dims->batch, dims->capacity};
-  const dim3 grid((dims->batch + kBlock - 1) / kBlock);
+              dims->batch, dims->nheads, dims->capacity};
+  const dim3 grid((dims->batch * dims->nheads + kBlock - 1) / kBlock);
   return launch(ring_reset_kernel, grid, dim3(kBlock), stream, p);
 }

@@ -18,7 +18,7 @@ struct ReplayParams {
   uint16_t* ring_k;
   float* ring_dt;
   float* ring_decay;
-  unsigned long long* ptr;  // [B] packed ring pointer words
+  unsigned long long* ptr;  // [B, H] packed ring pointer words, one copy per head
   int32_t* err;
   const uint16_t* v;   // [B, T, H, D]
   const uint16_t* k;   // [B, T, G, N]
@@ -51,8 +51,8 @@ __device__ __forceinline__ void load_tiles(float4 (&s)[RT][NCT], const float* S0
 //  VERIFY (T drafts): drafts are entries c .. c+T-1; draft s reads p_s = c+s+1
 //    entries; if c + 2T > L fold the c committed entries only.  pending <- T.
 //
-// Nothing waits for the checkpoint until it is needed.  The pointer word (one
-// atomic: read and arrival), the queries and drafts, the step sizes and decays,
+// Nothing waits for the checkpoint until it is needed.  This head's copy of the
+// pointer word, the queries and drafts, the step sizes and decays,
 // the group's ring keys and the head's ring values of all L physical slots are
 // requested first, the checkpoint tiles last.  Loads complete in issue order, so
 // the weights (wave 0), the inner products k . q (all waves) and the ring writes
@@ -85,7 +85,6 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t s_q[T * N];
   __shared__ __attribute__((aligned(16))) uint16_t s_k[LCAP * N];  // keys to fold by slot
   __shared__ __attribute__((aligned(16))) uint16_t s_v[LCAP * D];  // values by slot
-  __shared__ unsigned long long s_word;
 
   const int H = p.H, G = p.G, L = p.L;
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
@@ -94,9 +93,8 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
   const int r = lane & 15, cq = lane >> 4, sub = lane & 15;
   const size_t bh = (size_t)b * H + h;
 
-  // ---- 1. the pointer word and every small operand
-  unsigned long long word = 0;
-  if (tid == 0) word = take_pointers(&p.ptr[b]);
+  // ---- 1. this head's copy of the pointer word and every small operand
+  const unsigned long long word = p.ptr[bh];
   uint4 qm[T], kin[T];
 #pragma unroll
   for (int sd = 0; sd < T; ++sd) {
@@ -134,19 +132,19 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
   for (int i = 0; i < RVP; ++i)
     rv[i] = ld_u4(p.ring_v + bh * L * D + min(tid + i * kBlock, L * D / 8 - 1) * 8);
 
-  // ---- 2. the checkpoint, last
+  // ---- 2. the checkpoint, last (the scheduler may not hoist it above the rest)
+  __builtin_amdgcn_sched_barrier(0);
   float4 st[RT][NCT];
   load_tiles<D, N, RT, NCT>(st, p.state0 + bh * D * N, wave, r, cq);
 
   // ---- 3. ring pointers (uniform per request), clamped into range
-  if (tid == 0) s_word = word;
 #pragma unroll
   for (int i = 0; i < RVP; ++i) {
     const int t = tid + i * kBlock;
     if (t < L * D / 8) *reinterpret_cast<uint4*>(&s_v[t * 8]) = rv[i];
   }
   __syncthreads();
-  const RingPtr rp = unpack_ptr(s_word);
+  const RingPtr rp = unpack_ptr(word);
   int head = rp.head, cnt = rp.count;
   int bad = 0;
   if (head >= L) {
@@ -185,9 +183,11 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
     }
   }
 
-  // ---- 5. wave 0: decay weights in logical order, stored by physical slot
+  // ---- 5. wave 0: decay weights, stored by physical slot.  Lane l takes logical
+  //      entry j = 63 - l, so products over the entries after j are prefix
+  //      products over the lanes before l.
   if (wave == 0) {
-    const int j = lane;                                // logical entry
+    const int j = kWave - 1 - lane;                    // logical entry
     const int sj = ring_slot(head, min(j, L - 1), L);  // its physical slot
     const float dl_ring = __shfl(dt_slot, sj, kWave);
     const float al_ring = __shfl(dc_slot, sj, kWave);
@@ -202,13 +202,13 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
     for (int sd = 0; sd < T; ++sd) {
       const int m = c + sd;  // last entry seen by draft sd
       float all;
-      const float ex = suffix_product_excl(j <= m ? al : 1.f, lane, &all);
+      const float ex = prefix_product_excl(j <= m ? al : 1.f, &all);
       if (j < LCAP) s_w[sd][wi] = (j <= m) ? dl * ex : 0.f;
       if (lane == 0) s_abar[sd] = all;
     }
     {
       float all;
-      const float ex = suffix_product_excl(j < F ? al : 1.f, lane, &all);
+      const float ex = prefix_product_excl(j < F ? al : 1.f, &all);
       if (j < LCAP) s_fw[wi] = (j < F) ? dl * ex : 0.f;
       if (lane == 0) s_fabar = all;
     }
@@ -280,17 +280,15 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
   if (F > 0)
     fold_and_store<D, N, RT, NCT, VJ>(p.state0 + bh * D * N, st, s_fabar, s_k, s_fw, vj, L, wave, r, cq);
 
-  // ---- 8. pointer update by the last work-group of the request to read them
+  // ---- 8. this head's copy of the new pointers
   if (tid == 0) {
     if (h == 0) {
       flag_error(p.err, bad);
       if (p.flushed != nullptr) p.flushed[b] = do_flush ? 1 : 0;
     }
-    if (rp.arrive == H - 1) {
-      const int keep = APPEND ? E : c;  // entries that stay committed unless flushed
-      put_pointers(&p.ptr[b], pack_ptr(do_flush ? ring_slot(head, F % L, L) : head,
-                                       do_flush ? keep - F : keep, APPEND ? 0 : T));
-    }
+    const int keep = APPEND ? E : c;  // entries that stay committed unless flushed
+    p.ptr[bh] = pack_ptr(do_flush ? ring_slot(head, F % L, L) : head, do_flush ? keep - F : keep,
+                         APPEND ? 0 : T);
   }
 }
 

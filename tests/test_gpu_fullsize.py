@@ -107,6 +107,7 @@ def test_config1_standard_and_replay_full():
         worst[0] = max(worst[0], er, es)
         head, count, fl = sched[t]
         assert bool(torch.all(ring.head == head)) and bool(torch.all(ring.count == count)), t
+        assert ring.copies_agree(), t
         assert bool(torch.all(flushed == int(fl))), t
         if fl:
             e = rel_err(state_r[tb, th].cpu().numpy(), S[:, 0])
@@ -158,6 +159,7 @@ def test_config2_speculative_verify_full():
         assert np.array_equal(ring.count.cpu().numpy(), sched_arr[:, r, 3]), r
         rd.replay_rollback(dims, ring, dacc[r])
         assert np.array_equal(ring.count.cpu().numpy(), sched_arr[:, r, 4]), r
+        assert ring.copies_agree(), r
     assert int(ring.err.item()) == 0
     rd.replay_flush(dims, state0, ring)
     e = rel_err(state0[tb, th].cpu().numpy(), S[:, 0])
@@ -197,6 +199,7 @@ def test_config3_capacity_sweep_full(L):
         head, count, fl = sched[t]
         if t % 64 == 0 or fl:
             assert bool(torch.all(ring.head == head)) and bool(torch.all(ring.count == count)), t
+            assert ring.copies_agree(), t
             assert bool(torch.all(flushed == int(fl))), t
         if fl and (t // L) % 8 == 0:
             es = rel_err(state0[tb, th].cpu().numpy(), S[:, 0])
@@ -242,6 +245,7 @@ def test_config4_gdn_verify_full():
         assert e <= Y_TOL, (r, e)
         assert np.array_equal(flushed.cpu().numpy(), scheds[:, r, 1].astype(np.int32)), r
         assert np.array_equal(ring.count.cpu().numpy(), scheds[:, r, 3]), r
+        assert ring.copies_agree(), r
         rd.replay_rollback(dims, ring, dacc[r])
     assert int(ring.err.item()) == 0
     rd.gdn_replay_flush(dims, state0, ring)

@@ -83,7 +83,7 @@ def test_replay_append_decode_small(d, G, L, ring_dominant):
         assert e <= Y_TOL, (t, e)
         head, count, fl = sched[t]
         assert torch.all(ring.head == head) and torch.all(ring.count == count), t
-        assert torch.all(ring.pending == 0) and torch.all(ring.arrive == 0)
+        assert torch.all(ring.pending == 0) and ring.copies_agree()
         assert torch.all(flushed == int(fl)), t
         if fl:
             nflush += 1
