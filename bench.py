@@ -45,6 +45,8 @@ def _args(argv=None):
     ap.add_argument("--no-standard", action="store_true", help="skip the standard-step comparator")
     ap.add_argument("--cpu-steps", type=int, default=32)
     ap.add_argument("--no-graph", action="store_true", help="time the step eagerly only")
+    ap.add_argument("--no-rows", action="store_true",
+                    help="skip the other measured rows (verify, GDN verify, capacity sweep)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run the 1 GiB copy probe (for scaling traffic counters) and exit")
     return ap.parse_args(argv)
@@ -88,6 +90,204 @@ def _cpu_baseline(steps: int):
     return {"value": sh.batch * steps / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"ReplaySSM standard-mode oracle, full batch {sh.batch}, {steps} decode steps "
                       f"({steps // sh.capacity} flushes), float64 numpy, {dt:.1f} s"}
+
+
+# ------------------------------------------------------------------ other rows
+def _events(torch, n):
+    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(n)]
+
+
+def _verify_bytes(traffic, gdn, H, D, N, G, T, L, counts):
+    """Algorithmic bytes of one verify launch from the committed counts the
+    kernel saw (one per request)."""
+    fn = traffic.gdn_verify if gdn else traffic.replay_verify
+    tot = 0
+    for c in set(int(x) for x in counts):
+        nb = int((counts == c).sum())
+        tot += fn(nb, H, D, N, G, T, c, c + 2 * T > L)
+    return tot
+
+
+def _row_verify(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, rounds=64, warm=16):
+    """Speculative verify rounds (verify kernel + device-side rollback) on two
+    rotated layer instances.  A first pass records the committed count every
+    request had before each round; the rings are reset and the same sequence is
+    replayed with HIP events around every launch."""
+    wl = synth.WORKLOADS[cfg_id]
+    sh, seed = wl.shape, wl.cfg_seed
+    B, H, D, N, G, L, T = sh.batch, sh.nheads, sh.head_dim, sh.state_dim, sh.ngroups, sh.capacity, sh.T
+    NLr, P, R = 2, 8, warm + rounds
+    dims = rd.Dims(B, H, D, N, G, L)
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    gen = torch.Generator(device=dev)
+    layers = []
+    for l in range(NLr):
+        gen.manual_seed(seed * 100 + l)
+        Ly = {"S0": torch.randn((B, H, D, N), generator=gen, device=dev) * math.sqrt(0.1),
+              "ring": rd.Ring(dims, gdn=gdn, device=dev)}
+        if not gdn:
+            A, bias = synth.mamba2_head_params(sh, seed, cfg_id, layer=l)
+            Ly["A"], Ly["bias"] = torch.from_numpy(A).to(dev), torch.from_numpy(bias).to(dev)
+        layers.append(Ly)
+    pool = []
+    for p in range(P):
+        if gdn:
+            st = synth.gdn_round_inputs(sh, seed, cfg_id, p)
+            pool.append({"v": bf(st["v"]), "k": bf(st["k"]), "q": bf(st["q"]),
+                         "g": torch.from_numpy(st["g"]).to(dev), "beta": torch.from_numpy(st["beta"]).to(dev)})
+        else:
+            st = synth.mamba2_step_inputs(sh, seed, cfg_id, p)
+            pool.append({"v": bf(st["v"]), "k": bf(st["k"]), "q": bf(st["q"]),
+                         "dt": torch.from_numpy(st["dt"]).to(dev)})
+    acc = synth.accept_draws(seed, cfg_id, R, B, T)
+    dacc = [torch.from_numpy(acc[r]).to(dev) for r in range(R)]
+    y = torch.empty((B, T, H, D), device=dev)
+    flushed = torch.zeros((B,), dtype=torch.int32, device=dev)
+
+    def verify(r):
+        Ly, ip = layers[r % NLr], pool[r % P]
+        if gdn:
+            rd.gdn_replay_verify_T(dims, T, Ly["S0"], Ly["ring"], ip["v"], ip["k"], ip["q"], ip["g"],
+                                   ip["beta"], y, flushed, stream=stream)
+        else:
+            rd.replay_verify_T(dims, T, Ly["S0"], Ly["ring"], ip["v"], ip["k"], ip["q"], ip["dt"],
+                               Ly["bias"], Ly["A"], y, flushed, stream=stream)
+
+    def rollback(r):
+        rd.replay_rollback(dims, layers[r % NLr]["ring"], dacc[r], stream=stream)
+
+    counts = []
+    for r in range(R):                       # pass 1: pointers each round saw
+        torch.cuda.synchronize()
+        counts.append(layers[r % NLr]["ring"].count.cpu().numpy().copy())
+        verify(r)
+        rollback(r)
+    torch.cuda.synchronize()
+    for Ly in layers:
+        rd.rssm_ring_reset(dims, Ly["ring"], stream=stream)
+    ev_v, ev_r = _events(torch, R), _events(torch, R)
+    torch.cuda.synchronize()
+    for r in range(R):                       # pass 2: the same rounds, timed
+        ev_v[r][0].record(stream)
+        verify(r)
+        ev_v[r][1].record(stream)
+        rollback(r)
+        ev_r[r][1].record(stream)
+    torch.cuda.synchronize()
+    errs = [int(Ly["ring"].err.item()) for Ly in layers]
+    if any(errs):
+        raise RuntimeError(f"ring anomaly bits set: {errs}")
+    v_us = [1e3 * ev_v[r][0].elapsed_time(ev_v[r][1]) for r in range(warm, R)]
+    r_us = [1e3 * ev_v[r][1].elapsed_time(ev_r[r][1]) for r in range(warm, R)]
+    byts = [_verify_bytes(traffic, gdn, H, D, N, G, T, L, counts[r]) for r in range(warm, R)]
+    fl = np.array([counts[r] + 2 * T > L for r in range(warm, R)])
+    round_s = (sum(v_us) + sum(r_us)) * 1e-6
+    gbs = sum(byts) / (sum(v_us) * 1e-6) / 1e9
+    return {"workload": ("Gated DeltaNet" if gdn else "Mamba-2") +
+                        f" speculative verify, batch {B}, {H} heads, head dim {D}, state {N}, "
+                        f"{G} group(s), ring capacity {L}, T={T}; two layer instances rotated",
+            "kernel": "gdn_replay_verify_T" if gdn else "replay_verify_T",
+            "rounds_timed": rounds, "verify_us": round(sum(v_us) / rounds, 3),
+            "rollback_us": round(sum(r_us) / rounds, 3),
+            "verified_positions_per_s": round(B * T * rounds / round_s, 1),
+            "accepted_tokens_per_s": round(float(acc[warm:].sum()) / round_s, 1),
+            "achieved_GBs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "alg_bytes_per_round": round(sum(byts) / rounds),
+            "flush_rate": round(float(fl.mean()), 4),
+            "mean_committed_before": round(float(np.mean([counts[r] for r in range(warm, R)])), 3)}
+
+
+def _row_sweep(torch, np, rd, synth, traffic, dev, stream, capacities=(4, 8, 16, 32)):
+    """Append-decode at every ring capacity of the large-layer workload, flush
+    and non-flush steps reported separately, plus the standard step."""
+    wl = synth.WORKLOADS[3]
+    base, seed = wl.shape, wl.cfg_seed
+    B, H, D, N, G = base.batch, base.nheads, base.head_dim, base.state_dim, base.ngroups
+    NLs, P = 2, 4
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    gen = torch.Generator(device=dev)
+    S0s, params = [], []
+    for l in range(NLs):
+        gen.manual_seed(seed * 100 + l)
+        S0s.append(torch.randn((B, H, D, N), generator=gen, device=dev) * math.sqrt(0.1))
+        A, bias = synth.mamba2_head_params(base, seed, 3, layer=l)
+        params.append((torch.from_numpy(A).to(dev), torch.from_numpy(bias).to(dev)))
+    pool = []
+    for p in range(P):
+        st = synth.mamba2_step_inputs(base, seed, 3, p)
+        pool.append({"v": bf(st["v"]), "k": bf(st["k"]), "q": bf(st["q"]),
+                     "dt": torch.from_numpy(st["dt"]).to(dev)})
+    y = torch.empty((B, H, D), device=dev)
+    res = {"workload": f"Mamba-2 append-decode, batch {B}, {H} heads, head dim {D}, state {N}, "
+                       f"{G} groups; two layer instances rotated", "kernel": "replay_append_decode"}
+    for L in capacities:
+        dims = rd.Dims(B, H, D, N, G, L)
+        rings = [rd.Ring(dims, device=dev) for _ in range(NLs)]
+        calls = [[rd.prepare_replay_append_decode(dims, S0s[l], rings[l], pool[p]["v"], pool[p]["k"],
+                                                  pool[p]["q"], pool[p]["dt"], params[l][1],
+                                                  params[l][0], y, stream=stream)
+                  for p in range(P)] for l in range(NLs)]
+        warm, K = NLs * L, NLs * L * max(2, 64 // L)
+        for t in range(warm):
+            calls[t % NLs][(t // NLs) % P]()
+        ev = _events(torch, K)
+        torch.cuda.synchronize()
+        for i in range(K):
+            t = warm + i
+            ev[i][0].record(stream)
+            calls[t % NLs][(t // NLs) % P]()
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        us = np.array([1e3 * a_.elapsed_time(b_) for a_, b_ in ev])
+        h = np.array([((warm + i) // NLs) % L for i in range(K)])
+        fl = h == L - 1
+        byts = np.array([traffic.replay_append(B, H, D, N, G, int(x), bool(x == L - 1)) for x in h])
+        nf, f = ~fl, fl
+        res[f"L{L}"] = {
+            "nonflush_us": round(float(us[nf].mean()), 3),
+            "nonflush_GBs": round(float(byts[nf].sum() / (us[nf].sum() * 1e-6) / 1e9), 1),
+            "nonflush_bytes_per_step": round(float(byts[nf].mean())),
+            "flush_us": round(float(us[f].mean()), 3),
+            "flush_GBs": round(float(byts[f].sum() / (us[f].sum() * 1e-6) / 1e9), 1),
+            "flush_bytes_per_step": round(float(byts[f].mean())),
+            "avg_us": round(float(us.mean()), 3),
+            "avg_GBs": round(float(byts.sum() / (us.sum() * 1e-6) / 1e9), 1),
+            "tokens_per_s": round(float(B / (us.mean() * 1e-6)), 1), "steps_timed": K}
+        errs = [int(r.err.item()) for r in rings]
+        if any(errs):
+            raise RuntimeError(f"ring anomaly bits set: {errs}")
+        del rings, calls
+    dims = rd.Dims(B, H, D, N, G, 16)
+    std = [[rd.prepare_ssm_decode_step(dims, S0s[l], pool[p]["v"], pool[p]["k"], pool[p]["q"],
+                                       pool[p]["dt"], params[l][1], params[l][0], y, stream=stream)
+            for p in range(P)] for l in range(NLs)]
+    for t in range(8):
+        std[t % NLs][(t // NLs) % P]()
+    ev = _events(torch, 32)
+    torch.cuda.synchronize()
+    for i in range(32):
+        ev[i][0].record(stream)
+        std[i % NLs][(i // NLs) % P]()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    su = float(np.mean([1e3 * a_.elapsed_time(b_) for a_, b_ in ev]))
+    sb = traffic.standard_step(B, H, D, N, G)
+    res["standard_step"] = {"kernel": "ssm_decode_step", "us": round(su, 3),
+                            "GBs": round(sb / (su * 1e-6) / 1e9, 1), "tokens_per_s": round(B / (su * 1e-6), 1)}
+    return res
+
+
+def _rows(torch, np, rd, synth, traffic, dev, stream):
+    return {"speculative_verify": _row_verify(torch, np, rd, synth, traffic, dev, stream, 2, False),
+            "gdn_speculative_verify": _row_verify(torch, np, rd, synth, traffic, dev, stream, 4, True),
+            "capacity_sweep": _row_sweep(torch, np, rd, synth, traffic, dev, stream)}
 
 
 def main(argv=None) -> int:
@@ -173,30 +373,35 @@ def main(argv=None) -> int:
         return layer_step % L
 
     K = a.steps
-    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    # eager pass: the step as launched (conv, then replay), timed as a whole
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(K):
-        t = a.warmup + i
-        conv, app = step_calls(t)
+        conv, app = step_calls(a.warmup + i)
         conv()
-        ev_a[i].record(stream)
         app()
-        ev_b[i].record(stream)
     end.record(stream)
     end.synchronize()
     eager_ms = start.elapsed_time(end)
-    kern_ms = [ev_a[i].elapsed_time(ev_b[i]) for i in range(K)]
+    # the dominant kernel alone: the next K replay launches back to back on its
+    # stream, HIP events around the whole run (average launch duration)
+    t_kern = a.warmup + K
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(K):
+        step_calls(t_kern + i)[1]()
+    end.record(stream)
+    end.synchronize()
+    kern_avg_ms = start.elapsed_time(end) / K
     total_ms = eager_ms
     graph_info = None
     if not a.no_graph:
         # the same step sequence captured once per ring cycle of every layer and
         # replayed: no host launch cost between kernels
         GS = NL * L
-        t0 = a.warmup + K
+        t0 = a.warmup + 2 * K
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=side):
             for j in range(GS):
@@ -222,12 +427,11 @@ def main(argv=None) -> int:
     alg_bytes = 0
     nflush = 0
     for i in range(K):
-        h = cached_before(a.warmup + i)
+        h = cached_before(t_kern + i)
         fl = (h == L - 1)
         nflush += fl
         alg_bytes += traffic.replay_append(B, H, D, N, G, h, fl)
-    kern_total_s = sum(kern_ms) / 1e3
-    achieved = alg_bytes / kern_total_s / 1e9
+    achieved = alg_bytes / K / (kern_avg_ms * 1e-3) / 1e9
     ms_per_step = total_ms / K
     value = B * K / (total_ms / 1e3)
     traffic_bytes, traffic_note = profiling.stored_traffic("replay_append_decode")
@@ -247,11 +451,12 @@ def main(argv=None) -> int:
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_bytes,
                      "traffic_note": traffic_note,
-                     "kernel_avg_us": round(1e3 * sum(kern_ms) / K, 3),
+                     "kernel_avg_us": round(1e3 * kern_avg_ms, 3),
                      "alg_bytes_per_launch": round(alg_bytes / K)},
         "timing": {"step": "hip graph replay" if graph_info else "eager launches",
                    "eager_ms_per_step": round(eager_ms / K, 5), "graph": graph_info,
-                   "kernel": "HIP events around every replay_append_decode launch (eager pass)"},
+                   "kernel": "HIP events around K back-to-back replay_append_decode launches on "
+                             "their stream"},
     }
 
     if not a.no_standard:
@@ -278,7 +483,12 @@ def main(argv=None) -> int:
         out["standard_step"] = {"kernel": "ssm_decode_step", "us_per_step": round(std_us, 3),
                                 "achieved_GBs": round(std_bytes / (std_us * 1e-6) / 1e9, 1),
                                 "alg_bytes": std_bytes,
-                                "replay_speedup": round(std_us / (1e3 * sum(kern_ms) / K), 3)}
+                                "replay_speedup": round(std_us / (1e3 * kern_avg_ms), 3)}
+
+    if not a.no_rows:
+        del calls, layers
+        torch.cuda.empty_cache()
+        out["rows"] = _rows(torch, np, rd, synth, traffic, dev, stream)
 
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = _cpu_baseline(a.cpu_steps)

@@ -11,7 +11,8 @@ counted once per group (they are shared by the heads of a group).
 """
 from __future__ import annotations
 
-F32, BF16, I32 = 4, 2, 4
+F32, BF16 = 4, 2
+PTR = 8  # one packed pointer word per request, read and written once
 
 
 def standard_step(B, H, d, n, G) -> int:
@@ -33,7 +34,7 @@ def replay_append(B, H, d, n, G, h, flush: bool) -> int:
                + h * replay_slot(H, d, n, G)         # cached entries read
                + BF16 * H * d + 2 * BF16 * G * n + F32 * H   # v, k, q, dt in
                + F32 * H * d                         # y out
-               + 3 * I32 * 2)                        # head/count/pending read+write
+               + 2 * PTR)                            # pointer word read + write
     per_req += F32 * H * d * n if flush else replay_slot(H, d, n, G)
     return B * per_req + 2 * F32 * H
 
@@ -43,7 +44,7 @@ def replay_verify(B, H, d, n, G, T, c, flush: bool) -> int:
     T drafts in, T outputs, T new entries cached, checkpoint write on a flush."""
     per_req = (F32 * H * d * n + c * replay_slot(H, d, n, G)
                + T * (BF16 * H * d + 2 * BF16 * G * n + F32 * H)
-               + T * F32 * H * d + T * replay_slot(H, d, n, G) + 3 * I32 * 2)
+               + T * F32 * H * d + T * replay_slot(H, d, n, G) + 2 * PTR)
     if flush:
         per_req += F32 * H * d * n
     return B * per_req + 2 * F32 * H
@@ -57,7 +58,7 @@ def gdn_slot(H, d, n, G) -> int:
 def gdn_verify(B, H, d, n, G, T, c, flush: bool) -> int:
     per_req = (F32 * H * d * n + c * gdn_slot(H, d, n, G)
                + T * (BF16 * H * d + 2 * BF16 * G * n + 2 * F32 * H)
-               + T * F32 * H * d + T * gdn_slot(H, d, n, G) + 3 * I32 * 2)
+               + T * F32 * H * d + T * gdn_slot(H, d, n, G) + 2 * PTR)
     if flush:
         per_req += F32 * H * d * n
     return B * per_req
