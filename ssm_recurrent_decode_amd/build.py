@@ -30,8 +30,8 @@ HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # keep hipcc from forming packed fp32 arithmetic on its own
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # one plain atomic per work-group: no wave-level rewrite, so its return value is
-    # only waited for where it is used
+    # the only atomics (error-flag ORs, taken on anomalies) stay plain per-lane
+    # operations: no wave-level rewrite with its extra waits
     "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-I", INCLUDE, "-I", CSRC,
     "-Wall", "-Wno-unused-result",
