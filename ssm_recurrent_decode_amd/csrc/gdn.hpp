@@ -1,0 +1,321 @@
+// Gated DeltaNet ReplaySSM verify kernel and its launcher, shared by the
+// translation units that instantiate it.
+//
+// Method: "ReplaySSM: Cache SSM Inputs, Not State" -- appendix, GDN standard
+// decode (the correction u is cached so the update becomes S_t = alpha_t S_{t-1}
+// + u_t k_t^T) and GDN speculative decoding (all T corrections of a window from
+// one strictly lower-triangular T x T solve).
+#pragma once
+
+#include "common.hpp"
+
+namespace rssm {
+
+struct GdnReplayParams {
+  float* state0;
+  float* ring_u;       // [B, H, L, D] fp32
+  uint16_t* ring_k;    // [B, G, L, N]
+  float* ring_alpha;   // [B, H, L]
+  unsigned long long* ptr;  // [B, H] packed ring pointer words, one copy per head
+  int32_t* err;
+  const uint16_t* v;   // [B, T, H, D]
+  const uint16_t* k;   // [B, T, G, N]
+  const uint16_t* q;   // [B, T, G, N]
+  const float* g;      // [B, T, H]
+  const float* beta;   // [B, T, H]
+  float* y;            // [B, T, H, D]
+  int32_t* flushed;
+  const int32_t* mask;
+  int H, G, L;
+};
+
+// One verify round of T drafts, one work-group of four waves per (request, head).
+// Entries in logical order: the c committed ones (ring), then the T drafts.
+//   committed-state readouts  S_c x = abar S_0 x + sum_{j<c} w_j u_j (k_j . x),
+//     abar = prod_{i<c} alpha_i,  w_j = prod_{j<i<c} alpha_i,  x in {k_s, q_s};
+//   R_s = beta_s (v_s - gamma_s S_c k_s),  gamma_s = prod_{s'<=s} alpha'_s';
+//   u_s = R_s - sum_{s'<s} beta_s (prod_{s'<i<=s} alpha'_i) (k_s . k_s') u_s'
+//     (forward substitution of the strictly lower-triangular system);
+//   y_s = gamma_s S_c q_s + sum_{s'<=s} (prod_{s'<i<=s} alpha'_i) (k_s' . q_s) u_s';
+//   the drafts' (u, k, alpha') are cached in their ring slots; when c + 2T > L
+//   the committed entries are folded first: S_0 <- abar S_0 + sum_j w_j u_j k_j^T.
+//
+// As in the Mamba-2 window kernel, the pointer word and every small operand --
+// the 2T readout vectors and the draft values (16 bytes per lane into LDS), the
+// decays of all L slots, the gates and betas, the ring keys and the ring
+// corrections of all L physical slots (16 bytes per lane into LDS) -- are
+// requested before the checkpoint tiles, so the weights and the inner products
+// k . x proceed while the checkpoint is in flight.  The 2T readouts S_0 x run on
+// the matrix cores from the state registers; the fold (when flushing) follows
+// from the same registers; the per-row solve runs one thread per row after that.
+template <int D, int N, int T, int LCAP>
+__global__ __launch_bounds__(kBlock) void gdn_verify_kernel(GdnReplayParams p) {
+  static_assert(N == 128, "key staging assumes n = 128");
+  static_assert(2 * T <= 16, "readout vectors must fit one MFMA M axis");
+  static_assert(D <= kBlock, "one thread per state row in the solve");
+  static_assert(LCAP == 16 || LCAP == 32, "ring capacity bound");
+  constexpr int NCT = N / 16;
+  constexpr int RT = D / (16 * kWavesPerBlock);
+  constexpr int NV = 2 * T;               // readout vectors: k_0..k_{T-1}, q_0..q_{T-1}
+  constexpr int VJ = LCAP / 4;            // physical slots per lane in the fold
+  constexpr int PASSES = LCAP / 16;       // inner-product passes of 16 slots
+  constexpr int XC = NV * N / 8;          // 16-byte chunks of the readout vectors
+  constexpr int VC = T * D / 8;           // ... of the draft values
+  constexpr int XVP = (XC + VC + kBlock - 1) / kBlock;
+  constexpr int UC = LCAP * D / 4;        // ... of the ring corrections (fp32)
+  constexpr int UP = (UC + kBlock - 1) / kBlock;
+  __shared__ float s_Z[NV][D];            // (S_0 x_v)[row]
+  __shared__ float s_M[NV][LCAP];         // k_slot . x_v by physical slot
+  __shared__ float s_w[LCAP];             // w_j by physical slot, zero if not committed
+  __shared__ float s_abar;
+  __shared__ float s_alpha_d[T];          // draft decays alpha'_s
+  __shared__ float s_beta[T];
+  __shared__ __attribute__((aligned(16))) uint16_t s_x[NV * N];     // readout vectors
+  __shared__ __attribute__((aligned(16))) uint16_t s_vd[T * D];     // draft values
+  __shared__ __attribute__((aligned(16))) uint16_t s_k[LCAP * N];   // keys to fold by slot
+  __shared__ __attribute__((aligned(16))) float s_u[LCAP * D];      // corrections by slot
+
+  const int H = p.H, G = p.G, L = p.L;
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int b = wg / H, h = wg - b * H, hpg = H / G, g = h / hpg;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, cq = lane >> 4, sub = lane & 15;
+  const size_t bh = (size_t)b * H + h;
+
+  // ---- 1. this head's copy of the pointer word and every small operand
+  const unsigned long long word = p.ptr[bh];
+  uint4 xvc[XVP];  // readout vectors (k drafts, then q drafts), then the draft values
+#pragma unroll
+  for (int i = 0; i < XVP; ++i) {
+    const int t = min(tid + i * kBlock, XC + VC - 1);
+    const uint16_t* src;
+    if (t < XC) {
+      const int v = t / (N / 8), o = (t % (N / 8)) * 8;
+      src = (v < T) ? p.k + (((size_t)b * T + v) * G + g) * N + o
+                    : p.q + (((size_t)b * T + (v - T)) * G + g) * N + o;
+    } else {
+      const int tv = t - XC;
+      src = p.v + (((size_t)b * T + tv / (D / 8)) * H + h) * D + (tv % (D / 8)) * 8;
+    }
+    xvc[i] = ld_u4(src);
+  }
+  float al_slot = 1.f, gd = 0.f, bt = 0.f;
+  if (wave == 0) {
+    al_slot = p.ring_alpha[bh * L + min(lane, L - 1)];
+    gd = p.g[((size_t)b * T + min(lane, T - 1)) * H + h];
+    bt = p.beta[((size_t)b * T + min(lane, T - 1)) * H + h];
+  }
+  uint4 kr[PASSES];  // ring key of slot ps*16 + wave*4 + lane/16, 8 columns per lane
+#pragma unroll
+  for (int ps = 0; ps < PASSES; ++ps)
+    kr[ps] = ld_u4(p.ring_k + (((size_t)b * G + g) * L + min(ps * 16 + wave * 4 + (lane >> 4), L - 1)) * N + sub * 8);
+  float4 uc[UP];  // ring corrections, 16 bytes per lane, slot-major as in memory
+#pragma unroll
+  for (int i = 0; i < UP; ++i)
+    uc[i] = ld_f4(p.ring_u + bh * L * D + min(tid + i * kBlock, L * D / 4 - 1) * 4);
+
+  // ---- 2. the checkpoint, last (the scheduler may not hoist it above the rest)
+  __builtin_amdgcn_sched_barrier(0);
+  float* S0 = p.state0 + bh * D * N;
+  float4 st[RT][NCT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int row = (wave * RT + rt) * 16 + r;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) st[rt][ct] = ld_f4(S0 + row * N + ct * 16 + cq * 4);
+  }
+
+  // ---- 3. small operands into LDS; pointers, clamped into range
+#pragma unroll
+  for (int i = 0; i < XVP; ++i) {
+    const int t = tid + i * kBlock;
+    if (t < XC) *reinterpret_cast<uint4*>(&s_x[t * 8]) = xvc[i];
+    else if (t < XC + VC) *reinterpret_cast<uint4*>(&s_vd[(t - XC) * 8]) = xvc[i];
+  }
+#pragma unroll
+  for (int i = 0; i < UP; ++i) {
+    const int t = tid + i * kBlock;
+    if (t < L * D / 4) *reinterpret_cast<float4*>(&s_u[t * 4]) = uc[i];
+  }
+  const RingPtr rp = unpack_ptr(word);
+  int head = rp.head, cnt = rp.count;
+  int bad = 0;
+  if (head >= L) {
+    head %= L;
+    bad |= RSSM_ERR_POINTERS;
+  }
+  if (cnt > L - T) {
+    cnt = L - T;
+    bad |= RSSM_ERR_POINTERS;
+  }
+  if (rp.pending != 0) bad |= RSSM_ERR_PENDING;
+  const int c = cnt;
+  const bool do_flush = (c + 2 * T > L);
+  // logical entry held by physical slot sl (0 <= sl < L)
+  auto logical = [&](int sl) { const int j = sl - head; return j < 0 ? j + L : j; };
+
+  // ---- 4. wave 0: decay weights of the committed entries (lane l takes logical
+  //      entry 63 - l, so products over later entries are prefix products), the
+  //      draft decays and betas, the drafts' decays cached in the ring
+  if (wave == 0) {
+    const int j = kWave - 1 - lane;
+    const int sj = ring_slot(head, min(j, L - 1), L);
+    const float al = __shfl(al_slot, sj, kWave);
+    float all;
+    const float ex = prefix_product_excl(j < c ? al : 1.f, &all);
+    if (j < LCAP) s_w[(j < L) ? sj : j] = (j < c) ? ex : 0.f;
+    if (lane == 0) s_abar = all;
+    if (lane < T) {
+      const float ad = expf(gd);
+      s_alpha_d[lane] = ad;
+      s_beta[lane] = bt;
+      p.ring_alpha[bh * L + ring_slot(head, c + lane, L)] = ad;
+    }
+  }
+  __syncthreads();
+
+  // ---- 5. all waves: k_slot . x_v for every physical slot (16 lanes per slot);
+  //      keys to fold staged by slot; the drafts' keys cached by the group owner
+#pragma unroll
+  for (int ps = 0; ps < PASSES; ++ps) {
+    const int sl = ps * 16 + wave * 4 + (lane >> 4);
+    const bool in_ring = sl < L;
+    const int j = logical(min(sl, L - 1));
+    uint4 kv = (in_ring && j < c) ? kr[ps] : make_uint4(0, 0, 0, 0);
+    const int sd = j - c;
+    if (in_ring && sd >= 0 && sd < T) kv = *reinterpret_cast<const uint4*>(&s_x[sd * N + sub * 8]);
+    if (in_ring)
+      *reinterpret_cast<uint4*>(&s_k[sl * N + sub * 8]) =
+          (do_flush && j < c) ? kv : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const float d = reduce_quarter(dot8_bf16(kv, *reinterpret_cast<const uint4*>(&s_x[v * N + sub * 8])));
+      if (sub == 0) s_M[v][sl] = d;
+    }
+  }
+  if (h % hpg == 0) {
+    for (int t = tid; t < T * (N / 8); t += kBlock) {
+      const int sd = t / (N / 8), o = (t % (N / 8)) * 8;
+      *reinterpret_cast<uint4*>(p.ring_k + (((size_t)b * G + g) * L + ring_slot(head, c + sd, L)) * N + o) =
+          *reinterpret_cast<const uint4*>(&s_x[sd * N + o]);
+    }
+  }
+  __syncthreads();
+
+  // ---- 6. readouts Z = S_0 [K|Q] on the matrix cores: A[m][k] = x_m[col], B[k][nn]
+  //      = S_0[row nn][col]; lane (r, cq) ends with Z[4cq+i][row r of the tile]
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const uint2 xv = (r < NV) ? *reinterpret_cast<const uint2*>(&s_x[r * N + ct * 16 + cq * 4])
+                                : make_uint2(0, 0);
+      acc = mfma4(bf16_lo(xv.x), st[rt][ct].x, acc);
+      acc = mfma4(bf16_hi(xv.x), st[rt][ct].y, acc);
+      acc = mfma4(bf16_lo(xv.y), st[rt][ct].z, acc);
+      acc = mfma4(bf16_hi(xv.y), st[rt][ct].w, acc);
+    }
+    const int row = (wave * RT + rt) * 16 + r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (4 * cq + i < NV) s_Z[4 * cq + i][row] = acc[i];
+  }
+
+  // ---- 7. early flush of the committed entries (from the same registers)
+  if (do_flush) {
+    float uf[RT][VJ];  // correction of slot cq + 4m at this lane's rows, zero if not folded
+#pragma unroll
+    for (int m = 0; m < VJ; ++m) {
+      const int sl = cq + 4 * m;
+      const bool used = sl < L && logical(min(sl, L - 1)) < c;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        uf[rt][m] = used ? s_u[min(sl, LCAP - 1) * D + (wave * RT + rt) * 16 + r] : 0.f;
+    }
+    fold_and_store<D, N, RT, NCT, VJ>(S0, st, s_abar, s_k, s_w, uf, L, wave, r, cq);
+  }
+  __syncthreads();
+
+  // ---- 8. per row: committed-state readouts, corrections by forward
+  //      substitution, outputs, the corrections cached in the ring
+  const int rho = tid;
+  if (rho < D) {
+    const float abar = s_abar;
+    float sh[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) sh[v] = abar * s_Z[v][rho];
+#pragma unroll
+    for (int sl = 0; sl < LCAP; ++sl) {
+      if (sl < L && logical(sl) < c) {
+        const float wu = s_w[sl] * s_u[sl * D + rho];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) sh[v] += wu * s_M[v][sl];
+      }
+    }
+    int dslot[T];  // physical slots of the drafts
+#pragma unroll
+    for (int sd = 0; sd < T; ++sd) dslot[sd] = ring_slot(head, c + sd, L);
+    float gamma[T];
+    {
+      float gm = 1.f;
+#pragma unroll
+      for (int sd = 0; sd < T; ++sd) {
+        gm *= s_alpha_d[sd];
+        gamma[sd] = gm;
+      }
+    }
+    float u[T];
+#pragma unroll
+    for (int sd = 0; sd < T; ++sd) {
+      const float bs = s_beta[sd];
+      float acc = bs * (bf16_to_f32(s_vd[sd * D + rho]) - gamma[sd] * sh[sd]);  // R_s
+      float ratio = 1.f;                                                       // prod_{s'<i<=s} alpha'_i
+#pragma unroll
+      for (int sp = sd - 1; sp >= 0; --sp) {
+        ratio *= s_alpha_d[sp + 1];
+        acc -= bs * ratio * s_M[sd][dslot[sp]] * u[sp];  // A_{s,s'} u_{s'}
+      }
+      u[sd] = acc;
+    }
+#pragma unroll
+    for (int sd = 0; sd < T; ++sd) {
+      float acc = gamma[sd] * sh[T + sd];
+      float ratio = 1.f;
+#pragma unroll
+      for (int sp = sd; sp >= 0; --sp) {
+        if (sp < sd) ratio *= s_alpha_d[sp + 1];
+        acc += ratio * s_M[T + sd][dslot[sp]] * u[sp];
+      }
+      p.y[(((size_t)b * T + sd) * H + h) * D + rho] = acc;
+      p.ring_u[(bh * L + dslot[sd]) * D + rho] = u[sd];
+    }
+  }
+
+  if (tid == 0) {
+    if (h == 0) {
+      flag_error(p.err, bad);
+      if (p.flushed != nullptr) p.flushed[b] = do_flush ? 1 : 0;
+    }
+    p.ptr[bh] = pack_ptr(do_flush ? (head + c) % L : head, do_flush ? 0 : c, T);
+  }
+}
+
+}  // namespace rssm
+
+namespace rssm_host {
+
+using rssm::GdnReplayParams;
+
+template <int D, int T>
+int launch_gdn_window(const GdnReplayParams& p, int B, void* stream) {
+  const dim3 grid(B * p.H), block(rssm::kBlock);
+  if (p.L <= 16) return launch(rssm::gdn_verify_kernel<D, 128, T, 16>, grid, block, stream, p);
+  return launch(rssm::gdn_verify_kernel<D, 128, T, 32>, grid, block, stream, p);
+}
+
+// Verify launchers for T = 1..4 and T = 5..8 live in their own translation units.
+__attribute__((visibility("hidden"))) int launch_gdn_verify_lo(int T, int D, const GdnReplayParams& p, int B, void* stream);
+__attribute__((visibility("hidden"))) int launch_gdn_verify_hi(int T, int D, const GdnReplayParams& p, int B, void* stream);
+
+}  // namespace rssm_host

@@ -148,7 +148,8 @@ def _spec_inputs(sh, seed, cfg_id, rounds):
     return [synth.mamba2_step_inputs(sh, seed, cfg_id, r) for r in range(rounds)]
 
 
-@pytest.mark.parametrize("d,G,L,T", [(64, 1, 16, 4), (64, 2, 8, 2), (128, 4, 16, 3), (64, 1, 8, 4)])
+@pytest.mark.parametrize("d,G,L,T", [(64, 1, 16, 4), (64, 2, 8, 2), (128, 4, 16, 3), (64, 1, 8, 4),
+                                     (64, 2, 32, 8), (128, 1, 20, 5), (64, 4, 12, 6)])
 def test_replay_verify_rollback_small(d, G, L, T):
     """Speculative rounds: every draft's y (rejected included) against the
     per-draft snapshot semantics; pointers and early-flush flags bit-exact; the
@@ -234,7 +235,8 @@ def test_gdn_decode_step_small():
     assert rel_err(state.cpu().numpy(), S) <= S_TOL
 
 
-@pytest.mark.parametrize("d,G,L,T", [(128, 32, 16, 4), (64, 8, 8, 2), (128, 16, 16, 1)])
+@pytest.mark.parametrize("d,G,L,T", [(128, 32, 16, 4), (64, 8, 8, 2), (128, 16, 16, 1),
+                                     (64, 8, 32, 8), (128, 32, 24, 5), (64, 4, 14, 7)])
 def test_gdn_replay_verify_small(d, G, L, T):
     base = synth.WORKLOADS[4]
     sh = base.shape.with_(batch=3, head_dim=d, ngroups=G, capacity=L, T=T)
