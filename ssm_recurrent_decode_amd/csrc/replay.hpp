@@ -55,9 +55,9 @@ __device__ __forceinline__ void load_tiles(float4 (&s)[RT][NCT], const float* S0
 // pointer word, the queries and drafts, the step sizes and decays,
 // the group's ring keys and the head's ring values of all L physical slots are
 // requested first, the checkpoint tiles last.  Loads complete in issue order, so
-// the weights (wave 0), the inner products k . q (all waves) and the ring writes
-// of the new entries go ahead while the checkpoint is still streaming in; only the
-// output combine and the fold wait for it.  Ring values arrive 16 bytes per lane
+// the weights (wave 0) and the inner products k . q (all waves) go ahead while the
+// checkpoint is still streaming in; only the output combine and the fold wait for
+// it.  The new entries are cached in the ring by the last stores of the kernel.  Ring values arrive 16 bytes per lane
 // and are kept in LDS, where the new entries' values are written into their
 // slots, so the combine and the fold read every value from one array.  The ring
 // is read by physical slot; the pointers only decide which logical entry a slot
@@ -82,6 +82,7 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
   __shared__ float s_abar[T];
   __shared__ float s_fw[LCAP];         // fold weights by physical slot
   __shared__ float s_fabar;
+  __shared__ float s_dtn[T], s_dcn[T];  // the new entries' step size and decay
   __shared__ __attribute__((aligned(16))) uint16_t s_q[T * N];
   __shared__ __attribute__((aligned(16))) uint16_t s_k[LCAP * N];  // keys to fold by slot
   __shared__ __attribute__((aligned(16))) uint16_t s_v[LCAP * D];  // values by slot
@@ -165,21 +166,14 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
   // logical entry held by physical slot sl (0 <= sl < L)
   auto logical = [&](int sl) { const int j = sl - head; return j < 0 ? j + L : j; };
 
-  // ---- 4. the new entries: values into their LDS slots; v (this head) and k
-  //      (group owner head only) cached in the ring unless this call empties it
-  const bool k_owner = (h % hpg) == 0;
+  // ---- 4. the new entries' values into their LDS slots (they are cached in the
+  //      ring at the end)
 #pragma unroll
   for (int i = 0; i < NCP; ++i) {
     const int t = tid + i * kBlock;
     if (t < NEWV) {
       const int sd = t / (D / 8), o = (t % (D / 8)) * 8;
-      const int sl = ring_slot(head, c + sd, L);
-      *reinterpret_cast<uint4*>(&s_v[sl * D + o]) = newc[i];
-      if (write_new) *reinterpret_cast<uint4*>(p.ring_v + (bh * L + sl) * D + o) = newc[i];
-    } else if (write_new && k_owner && t < NCH) {
-      const int tk = t - NEWV;
-      const int sd = tk / (N / 8), o = (tk % (N / 8)) * 8;
-      *reinterpret_cast<uint4*>(p.ring_k + (((size_t)b * G + g) * L + ring_slot(head, c + sd, L)) * N + o) = newc[i];
+      *reinterpret_cast<uint4*>(&s_v[ring_slot(head, c + sd, L) * D + o]) = newc[i];
     }
   }
 
@@ -212,9 +206,9 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
       if (j < LCAP) s_fw[wi] = (j < F) ? dl * ex : 0.f;
       if (lane == 0) s_fabar = all;
     }
-    if (write_new && j >= c && j < E) {  // cache the new entries' step size and decay
-      p.ring_dt[bh * L + sj] = dl;
-      p.ring_decay[bh * L + sj] = al;
+    if (write_new && j >= c && j < E) {  // the new entries' step size and decay
+      s_dtn[j - c] = dl;
+      s_dcn[j - c] = al;
     }
     if (lane < 16) {
 #pragma unroll
@@ -280,7 +274,31 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
   if (F > 0)
     fold_and_store<D, N, RT, NCT, VJ>(p.state0 + bh * D * N, st, s_fabar, s_k, s_fw, vj, L, wave, r, cq);
 
-  // ---- 8. this head's copy of the new pointers
+  // ---- 8. the new entries cached in the ring unless this call empties it: v of
+  //      this head, k by the group's first head, step size and decay.  Stores are
+  //      issued last (measured slightly faster than in the middle phase).
+  if (write_new) {
+    const bool k_owner = (h % hpg) == 0;
+#pragma unroll
+    for (int i = 0; i < NCP; ++i) {
+      const int t = tid + i * kBlock;
+      if (t < NEWV) {
+        const int sd = t / (D / 8), o = (t % (D / 8)) * 8;
+        *reinterpret_cast<uint4*>(p.ring_v + (bh * L + ring_slot(head, c + sd, L)) * D + o) = newc[i];
+      } else if (k_owner && t < NCH) {
+        const int tk = t - NEWV;
+        const int sd = tk / (N / 8), o = (tk % (N / 8)) * 8;
+        *reinterpret_cast<uint4*>(p.ring_k + (((size_t)b * G + g) * L + ring_slot(head, c + sd, L)) * N + o) = newc[i];
+      }
+    }
+    if (tid < T) {
+      const int sl = ring_slot(head, c + tid, L);
+      p.ring_dt[bh * L + sl] = s_dtn[tid];
+      p.ring_decay[bh * L + sl] = s_dcn[tid];
+    }
+  }
+
+  // ---- 9. this head's copy of the new pointers
   if (tid == 0) {
     if (h == 0) {
       flag_error(p.err, bad);
