@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define RSSM_ABI_VERSION 2
+#define RSSM_ABI_VERSION 3
 
 #define RSSM_OK 0
 #define RSSM_EINVAL (-22)
@@ -72,19 +72,30 @@ typedef struct rssm_dims {
  * from `head`, so a rollback only moves a pointer.  Physical slot of logical
  * entry j (0 = oldest) of request b is (head + j) % L.
  *
- * The pointers of request b (head, count = committed entries since the
- * checkpoint, pending = uncommitted drafts that follow them) are packed in a
- * 64-bit word (RSSM_PTR_* below) kept once per head: ptr[b * H + h] is request
- * b's word as head h keeps it.  Every call moves all H copies of a request the
- * same way, so they stay equal; the work of head h reads and writes only copy h,
- * so no two work-groups share a word and no atomics are needed.
+ * Everything else a call needs about request b's ring as head h sees it sits in
+ * one record of RSSM_META_WORDS(L) 32-bit words (one or two 128-byte lines),
+ * meta[(b * H + h) * RSSM_META_WORDS(L) + ...]:
+ *   words 0-1   the pointer word (uint64, RSSM_PTR_* below): head, count =
+ *               committed entries since the checkpoint, pending = uncommitted
+ *               drafts that follow them;
+ *   word  2     Mamba-2: the head's A of the cached entries (so a flush needs no
+ *               parameters); GDN: unused;
+ *   words 3..   per physical slot s < L, word 3 + s: Mamba-2 Delta (after
+ *               softplus; the decay is a = exp(A Delta)); GDN alpha = exp(g);
+ *   the rest    unused.
+ * A call writes each record it moves as whole lines, so the per-step bookkeeping
+ * costs one full-line write per head instead of several partial ones.  Every
+ * call moves all H records of a request the same way, so their pointer words
+ * stay equal; the work of head h reads and writes only record h, so no two
+ * work-groups share one and no atomics are needed.
  *
- * Caller allocates every array and zero-fills ptr and err once before the first
- * call; afterwards only the library writes them (rssm_ring_reset re-zeroes a
- * subset of requests).  Unsigned fields: a head >= L or a count above the
- * largest legal value is clamped and flagged (RSSM_ERR_POINTERS).  Bits 48-63
- * are zero.
+ * Caller allocates every array (meta 128-byte aligned) and zero-fills meta and
+ * err once before the first call; afterwards only the library writes them
+ * (rssm_ring_reset re-zeroes the pointer words of a subset of requests).
+ * Unsigned fields: a head >= L or a count above the largest legal value is
+ * clamped and flagged (RSSM_ERR_POINTERS).  Bits 48-63 of the word are zero.
  */
+#define RSSM_META_WORDS(L) ((L) + 3 <= 32 ? 32 : 64)
 #define RSSM_PTR_HEAD(w) ((uint32_t)((w) & 0xFFFFu))
 #define RSSM_PTR_COUNT(w) ((uint32_t)(((w) >> 16) & 0xFFFFu))
 #define RSSM_PTR_PENDING(w) ((uint32_t)(((w) >> 32) & 0xFFFFu))
@@ -95,19 +106,18 @@ typedef struct rssm_dims {
 typedef struct rssm_ring {
   void* vu;          /* Mamba-2: v  bf16 [B, H, L, d];  GDN: u fp32 [B, H, L, d]     */
   uint16_t* k;       /* bf16 [B, G, L, n]                                           */
-  float* dt;         /* Mamba-2: Delta fp32 [B, H, L] (after softplus);  GDN: unused */
-  float* decay;      /* Mamba-2: a = exp(A Delta);  GDN: alpha = exp(g);  fp32 [B,H,L] */
-  uint64_t* ptr;     /* [B, H] packed pointer words (RSSM_PTR_*), one per head       */
+  float* meta;       /* [B, H, RSSM_META_WORDS(L)] records: pointer word, A, Delta or
+                        alpha per slot (see above)                                   */
   int32_t* err;      /* [1] anomaly bits (RSSM_ERR_*), may be NULL                  */
 } rssm_ring;
 
 int rssm_abi_version(void);
 const char* rssm_strerror(int code);
 
-/* Bytes of each ring array for the given dims: writes 6 sizes in the order of
- * the rssm_ring fields (vu, k, dt, decay, ptr, err).
- * is_gdn selects fp32 u instead of bf16 v and no dt array.  Host-only. */
-int rssm_ring_sizes(const rssm_dims* dims, int is_gdn, size_t out_bytes[6]);
+/* Bytes of each ring array for the given dims: writes 4 sizes in the order of
+ * the rssm_ring fields (vu, k, meta, err).  is_gdn selects fp32 u instead of
+ * bf16 v.  Host-only. */
+int rssm_ring_sizes(const rssm_dims* dims, int is_gdn, size_t out_bytes[4]);
 
 /* Zero the pointer words (head, count, pending) of requests with
  * mask[b] != 0 (mask NULL = all) and clear err.  The ring contents are left as
@@ -135,7 +145,8 @@ int ssm_decode_step(const rssm_dims* dims, float* state, const uint16_t* v, cons
 /*
  * ReplaySSM append-decode for one token per request.
  * Algorithms, "Mamba-2 standard decode", ReplaySSM bullet; method, "output-only
- * decode": append (v, Delta, k) and the decay a to the ring; with the c entries
+ * decode": append (v, Delta, k) to the ring (the decay a = exp(A Delta) is
+ * recomputed from Delta and the A kept in the record); with the c entries
  * since the checkpoint (this one included),
  *     y = abar (S_0 q) + sum_j s_j (k_j^T q) v_j,
  *     abar = prod_i a_i,  s_j = Delta_j prod_{i>j} a_i;
@@ -157,7 +168,8 @@ int replay_append_decode(const rssm_dims* dims, float* state0, rssm_ring* ring,
  * buffered inputs into the state and clear the buffer).  For requests with
  * mask[b] != 0 (mask NULL = all) and count > 0:
  *     S_0 <- abar S_0 + sum_{j<count} s_j v_j k_j^T ;  head += count ;  count = 0.
- * Pending drafts stay cached after the new head.
+ * Pending drafts stay cached after the new head.  The decays come from the Delta
+ * and A kept in each record by the calls that cached the entries.
  */
 int replay_flush(const rssm_dims* dims, float* state0, rssm_ring* ring, const int32_t* mask,
                  void* stream);

@@ -19,7 +19,7 @@ RSSM_ELAUNCH = -5
 RSSM_ERR_POINTERS = 1
 RSSM_ERR_ACCEPTED = 2
 RSSM_ERR_PENDING = 4
-ABI_VERSION = 2  # RSSM_ABI_VERSION of the header this binding follows
+ABI_VERSION = 3  # RSSM_ABI_VERSION of the header this binding follows
 
 
 class rssm_dims(ctypes.Structure):
@@ -28,8 +28,7 @@ class rssm_dims(ctypes.Structure):
 
 
 class rssm_ring(ctypes.Structure):
-    _fields_ = [("vu", c_void_p), ("k", c_void_p), ("dt", c_void_p), ("decay", c_void_p),
-                ("ptr", c_void_p), ("err", c_void_p)]
+    _fields_ = [("vu", c_void_p), ("k", c_void_p), ("meta", c_void_p), ("err", c_void_p)]
 
 
 _D = POINTER(rssm_dims)

@@ -62,15 +62,21 @@ def _p(t, name, dtypes, shape, allow_none=False):
     return t.data_ptr()
 
 
+def meta_words(L: int) -> int:
+    """32-bit words of one per-head ring record (RSSM_META_WORDS)."""
+    return 32 if L + 3 <= 32 else 64
+
+
 class Ring:
     """Device arrays of one layer's ReplaySSM ring (see rssm_ring in the header).
 
     Allocated zero-filled with torch on ``device``; ``gdn`` selects fp32
-    corrections u instead of bf16 values v and no step-size array.  The pointers
-    of request b are packed in 64-bit words (head in bits 0-15, count 16-31,
-    pending 32-47), one copy per head in ``ptr[b, h]``; ``head``, ``count`` and
-    ``pending`` are int32 views decoded from head 0's copy, and ``copies_agree``
-    checks that every head's copy is the same."""
+    corrections u instead of bf16 values v.  ``meta`` holds one record per
+    (request, head): the packed pointer word (head in bits 0-15, count 16-31,
+    pending 32-47) in words 0-1, then A and the per-slot step sizes (Mamba-2) or
+    decays (GDN).  ``head``, ``count`` and ``pending`` are int32 views decoded
+    from head 0's record, and ``copies_agree`` checks that every head's pointer
+    word is the same."""
 
     def __init__(self, dims: Dims, gdn: bool = False, device="cuda"):
         B, H, G, L = dims.batch, dims.nheads, dims.ngroups, dims.capacity
@@ -79,10 +85,13 @@ class Ring:
         z = dict(device=device)
         self.vu = torch.zeros((B, H, L, D), dtype=torch.float32 if gdn else torch.bfloat16, **z)
         self.k = torch.zeros((B, G, L, N), dtype=torch.bfloat16, **z)
-        self.dt = None if gdn else torch.zeros((B, H, L), dtype=torch.float32, **z)
-        self.decay = torch.zeros((B, H, L), dtype=torch.float32, **z)
-        self.ptr = torch.zeros((B, H), dtype=torch.int64, **z)
+        self.meta = torch.zeros((B, H, meta_words(L)), dtype=torch.float32, **z)
         self.err = torch.zeros((1,), dtype=torch.int32, **z)
+
+    @property
+    def ptr(self):
+        """Pointer words [B, H] (int64 view into the records)."""
+        return self.meta.view(torch.int64)[:, :, 0]
 
     def _field(self, shift: int):
         return ((self.ptr[:, 0] >> shift) & 0xFFFF).to(torch.int32)
@@ -100,29 +109,29 @@ class Ring:
         return self._field(32)
 
     def copies_agree(self) -> bool:
-        return bool(torch.all(self.ptr == self.ptr[:, :1]))
+        w = self.ptr
+        return bool(torch.all(w == w[:, :1]))
 
     def set_pointers(self, head=None, count=None, pending=None):
-        """Overwrite pointer fields of every head's copy (sequences of B ints, or
+        """Overwrite pointer fields of every head's record (sequences of B ints, or
         None to keep head 0's value); each value is stored modulo 2^16 as the
         packed word holds it."""
         cur = [self.head.cpu().tolist(), self.count.cpu().tolist(), self.pending.cpu().tolist()]
         new = [list(x) if x is not None else c for x, c in zip((head, count, pending), cur)]
         words = [(h & 0xFFFF) | ((c & 0xFFFF) << 16) | ((p & 0xFFFF) << 32) for h, c, p in zip(*new)]
-        col = torch.tensor(words, dtype=torch.int64).to(self.ptr.device)
-        self.ptr.copy_(col[:, None].expand_as(self.ptr))
+        col = torch.tensor(words, dtype=torch.int64).to(self.meta.device)
+        self.meta.view(torch.int64)[:, :, 0] = col[:, None]
 
     def c(self) -> _lib.rssm_ring:
-        return _lib.rssm_ring(self.vu.data_ptr(), self.k.data_ptr(),
-                              None if self.dt is None else self.dt.data_ptr(),
-                              self.decay.data_ptr(), self.ptr.data_ptr(), self.err.data_ptr())
+        return _lib.rssm_ring(self.vu.data_ptr(), self.k.data_ptr(), self.meta.data_ptr(),
+                              self.err.data_ptr())
 
     def tensors(self):
-        return {k: getattr(self, k) for k in ("vu", "k", "dt", "decay", "ptr", "err")}
+        return {k: getattr(self, k) for k in ("vu", "k", "meta", "err")}
 
 
 def ring_sizes(dims: Dims, gdn: bool = False):
-    out = (ctypes.c_size_t * 6)()
+    out = (ctypes.c_size_t * 4)()
     d = dims.c()
     _lib.check(_lib.load().rssm_ring_sizes(ctypes.byref(d), int(gdn), out), "rssm_ring_sizes")
     return list(out)

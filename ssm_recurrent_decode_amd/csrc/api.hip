@@ -54,16 +54,15 @@ extern "C" const char* rssm_strerror(int code) {
   }
 }
 
-extern "C" int rssm_ring_sizes(const rssm_dims* d, int is_gdn, size_t out[6]) {
+extern "C" int rssm_ring_sizes(const rssm_dims* d, int is_gdn, size_t out[4]) {
   if (!rssm_host::dims_ok(d) || d->capacity < 1 || out == nullptr) return RSSM_EINVAL;
+  if (d->capacity > rssm::kMaxL) return RSSM_ENOTSUP;
   const size_t B = d->batch, H = d->nheads, G = d->ngroups, L = d->capacity;
   const size_t D = d->head_dim, N = d->state_dim;
   out[0] = B * H * L * D * (is_gdn ? 4 : 2);
   out[1] = B * G * L * N * 2;
-  out[2] = is_gdn ? 0 : B * H * L * 4;
-  out[3] = B * H * L * 4;
-  out[4] = B * H * 8;
-  out[5] = 4;
+  out[2] = B * H * (size_t)rssm::meta_words((int)L) * 4;
+  out[3] = 4;
   return RSSM_OK;
 }
 

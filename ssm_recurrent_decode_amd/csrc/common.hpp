@@ -126,9 +126,13 @@ __device__ __forceinline__ float dot8_bf16(uint4 a, uint4 b) {
          bf16_lo(a.w) * bf16_lo(b.w) + bf16_hi(a.w) * bf16_hi(b.w);
 }
 
-// Ring pointer word of one request as one head keeps it: head in bits 0-15,
-// count 16-31, pending 32-47.  Each head has its own copy and every call moves
-// all copies alike, so the work of head h reads and writes only copy h.
+// Per-(request, head) ring record: words 0-1 the pointer word (head in bits
+// 0-15, count 16-31, pending 32-47), word 2 the head's A (Mamba-2), word 3 + s
+// the step size (Mamba-2) or decay (GDN) of physical slot s.  Each head has its
+// own record and every call moves all of a request's records alike, so the work
+// of head h reads and writes only record h.
+constexpr int kMetaPtr = 0, kMetaA = 2, kMetaSlot = 3;
+__host__ __device__ constexpr int meta_words(int L) { return L + kMetaSlot <= 32 ? 32 : 64; }
 struct RingPtr {
   int head, count, pending;
 };
@@ -220,13 +224,12 @@ inline bool ring_shape_supported(const rssm_dims* d) {
   return shape_supported(d) && d->capacity <= rssm::kMaxL;
 }
 
-inline bool ptr_ok(const rssm_ring* r) {
-  return r != nullptr && r->ptr != nullptr && reinterpret_cast<uintptr_t>(r->ptr) % 8 == 0;
+inline bool meta_ok(const rssm_ring* r) {
+  return r != nullptr && r->meta != nullptr && reinterpret_cast<uintptr_t>(r->meta) % 128 == 0;
 }
 
-inline bool ring_ok(const rssm_ring* r, bool need_dt) {
-  return ptr_ok(r) && r->vu != nullptr && r->k != nullptr && r->decay != nullptr &&
-         (!need_dt || r->dt != nullptr);
+inline bool ring_ok(const rssm_ring* r) {
+  return meta_ok(r) && r->vu != nullptr && r->k != nullptr;
 }
 
 }  // namespace rssm_host

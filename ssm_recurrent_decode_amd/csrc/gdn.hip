@@ -99,7 +99,8 @@ __global__ __launch_bounds__(kBlock) void gdn_flush_kernel(GdnReplayParams p) {
 
   if (p.mask != nullptr && p.mask[b] == 0) return;
   const size_t bh = (size_t)b * H + h;
-  const RingPtr rp = unpack_ptr(p.ptr[bh]);
+  float* rec = p.meta + bh * meta_words(L);  // this head's ring record
+  const RingPtr rp = unpack_ptr(*reinterpret_cast<const unsigned long long*>(rec + kMetaPtr));
   int head = rp.head, cnt = rp.count;
   int bad = 0;
   if (head >= L) {
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(kBlock) void gdn_flush_kernel(GdnReplayParams p) {
   }
   if (wave == 0) {
     const int j = lane;
-    const float al = (j < F) ? p.ring_alpha[bh * L + (head + j) % L] : 1.f;
+    const float al = (j < F) ? rec[kMetaSlot + (head + j) % L] : 1.f;
     float R = 1.f, P = 1.f;
     for (int m = 0; m < F; ++m) {
       const float am = __shfl(al, m, kWave);
@@ -154,7 +155,7 @@ __global__ __launch_bounds__(kBlock) void gdn_flush_kernel(GdnReplayParams p) {
 
   if (tid == 0) {
     if (h == 0) flag_error(p.err, bad);
-    p.ptr[bh] = pack_ptr((head + F) % L, 0, rp.pending);
+    *reinterpret_cast<unsigned long long*>(rec + kMetaPtr) = pack_ptr((head + F) % L, 0, rp.pending);
   }
 }
 
@@ -170,8 +171,7 @@ GdnReplayParams make_gdn_params(const rssm_dims* d, float* state0, rssm_ring* ri
   p.state0 = state0;
   p.ring_u = static_cast<float*>(ring->vu);
   p.ring_k = ring->k;
-  p.ring_alpha = ring->decay;
-  p.ptr = reinterpret_cast<unsigned long long*>(ring->ptr);
+  p.meta = ring->meta;
   p.err = ring->err;
   p.H = d->nheads;
   p.G = d->ngroups;
@@ -196,7 +196,7 @@ extern "C" int gdn_replay_verify_T(const rssm_dims* dims, int32_t T, float* stat
                                    const uint16_t* v, const uint16_t* k, const uint16_t* q,
                                    const float* g, const float* beta, float* y, int32_t* flushed,
                                    void* stream) {
-  if (!rssm_host::dims_ok(dims) || !rssm_host::ring_ok(ring, false) || !state0 || !v || !k || !q ||
+  if (!rssm_host::dims_ok(dims) || !rssm_host::ring_ok(ring) || !state0 || !v || !k || !q ||
       !g || !beta || !y)
     return RSSM_EINVAL;
   if (T < 1 || dims->capacity < 2 * T) return RSSM_EINVAL;
@@ -215,7 +215,7 @@ extern "C" int gdn_replay_verify_T(const rssm_dims* dims, int32_t T, float* stat
 
 extern "C" int gdn_replay_flush(const rssm_dims* dims, float* state0, rssm_ring* ring,
                                 const int32_t* mask, void* stream) {
-  if (!rssm_host::dims_ok(dims) || !rssm_host::ring_ok(ring, false) || !state0) return RSSM_EINVAL;
+  if (!rssm_host::dims_ok(dims) || !rssm_host::ring_ok(ring) || !state0) return RSSM_EINVAL;
   if (dims->capacity < 1) return RSSM_EINVAL;
   if (!rssm_host::ring_shape_supported(dims)) return RSSM_ENOTSUP;
   GdnReplayParams p = make_gdn_params(dims, state0, ring);

@@ -15,8 +15,7 @@ struct GdnReplayParams {
   float* state0;
   float* ring_u;       // [B, H, L, D] fp32
   uint16_t* ring_k;    // [B, G, L, N]
-  float* ring_alpha;   // [B, H, L]
-  unsigned long long* ptr;  // [B, H] packed ring pointer words, one copy per head
+  float* meta;         // [B, H, meta_words(L)] per-head ring records (alpha per slot)
   int32_t* err;
   const uint16_t* v;   // [B, T, H, D]
   const uint16_t* k;   // [B, T, G, N]
@@ -83,7 +82,9 @@ __global__ __launch_bounds__(kBlock) void gdn_verify_kernel(GdnReplayParams p) {
   const size_t bh = (size_t)b * H + h;
 
   // ---- 1. this head's copy of the pointer word and every small operand
-  const unsigned long long word = p.ptr[bh];
+  const int MS = meta_words(L);
+  float* rec = p.meta + bh * MS;  // this head's ring record
+  const unsigned long long word = *reinterpret_cast<const unsigned long long*>(rec + kMetaPtr);
   uint4 xvc[XVP];  // readout vectors (k drafts, then q drafts), then the draft values
 #pragma unroll
   for (int i = 0; i < XVP; ++i) {
@@ -99,9 +100,9 @@ __global__ __launch_bounds__(kBlock) void gdn_verify_kernel(GdnReplayParams p) {
     }
     xvc[i] = ld_u4(src);
   }
-  float al_slot = 1.f, gd = 0.f, bt = 0.f;
-  if (wave == 0) {
-    al_slot = p.ring_alpha[bh * L + min(lane, L - 1)];
+  float rec_l = 0.f, gd = 0.f, bt = 0.f;
+  if (wave == 0) {  // the whole record (decays of every slot), the drafts' gates and betas
+    rec_l = rec[min(lane, MS - 1)];
     gd = p.g[((size_t)b * T + min(lane, T - 1)) * H + h];
     bt = p.beta[((size_t)b * T + min(lane, T - 1)) * H + h];
   }
@@ -160,16 +161,14 @@ __global__ __launch_bounds__(kBlock) void gdn_verify_kernel(GdnReplayParams p) {
   if (wave == 0) {
     const int j = kWave - 1 - lane;
     const int sj = ring_slot(head, min(j, L - 1), L);
-    const float al = __shfl(al_slot, sj, kWave);
+    const float al = __shfl(rec_l, kMetaSlot + sj, kWave);
     float all;
     const float ex = prefix_product_excl(j < c ? al : 1.f, &all);
     if (j < LCAP) s_w[(j < L) ? sj : j] = (j < c) ? ex : 0.f;
     if (lane == 0) s_abar = all;
     if (lane < T) {
-      const float ad = expf(gd);
-      s_alpha_d[lane] = ad;
+      s_alpha_d[lane] = expf(gd);
       s_beta[lane] = bt;
-      p.ring_alpha[bh * L + ring_slot(head, c + lane, L)] = ad;
     }
   }
   __syncthreads();
@@ -292,12 +291,21 @@ __global__ __launch_bounds__(kBlock) void gdn_verify_kernel(GdnReplayParams p) {
     }
   }
 
-  if (tid == 0) {
-    if (h == 0) {
+  // ---- 9. this head's record rewritten as whole lines by wave 0: the new pointer
+  //      word and the decays with the drafts' in their slots
+  if (wave == 0) {
+    if (lane == 0 && h == 0) {
       flag_error(p.err, bad);
       if (p.flushed != nullptr) p.flushed[b] = do_flush ? 1 : 0;
     }
-    p.ptr[bh] = pack_ptr(do_flush ? (head + c) % L : head, do_flush ? 0 : c, T);
+    const unsigned long long nw = pack_ptr(do_flush ? (head + c) % L : head, do_flush ? 0 : c, T);
+    const int sl = lane - kMetaSlot;
+    const int sd = (sl >= 0 && sl < L) ? logical(sl) - c : -1;
+    float x = rec_l;
+    if (lane == kMetaPtr) x = __uint_as_float(uint32_t(nw));
+    if (lane == kMetaPtr + 1) x = __uint_as_float(uint32_t(nw >> 32));
+    if (sd >= 0 && sd < T) x = s_alpha_d[min(max(sd, 0), T - 1)];
+    if (lane < MS) rec[lane] = x;
   }
 }
 

@@ -98,7 +98,8 @@ __global__ __launch_bounds__(kBlock) void replay_flush_kernel(ReplayParams p) {
 
   if (p.mask != nullptr && p.mask[b] == 0) return;
   const size_t bh = (size_t)b * H + h;
-  const RingPtr rp = unpack_ptr(p.ptr[bh]);
+  float* rec = p.meta + bh * meta_words(L);  // this head's ring record
+  const RingPtr rp = unpack_ptr(*reinterpret_cast<const unsigned long long*>(rec + kMetaPtr));
   int head = rp.head, cnt = rp.count;
   int bad = 0;
   if (head >= L) {
@@ -135,9 +136,8 @@ __global__ __launch_bounds__(kBlock) void replay_flush_kernel(ReplayParams p) {
     const int j = lane;
     float dl = 0.f, al = 1.f;
     if (j < F) {
-      const size_t o = bh * L + (head + j) % L;
-      dl = p.ring_dt[o];
-      al = p.ring_decay[o];
+      dl = rec[kMetaSlot + (head + j) % L];
+      al = expf(rec[kMetaA] * dl);
     }
     float R = 1.f, P = 1.f;
     for (int m = 0; m < F; ++m) {
@@ -158,24 +158,29 @@ __global__ __launch_bounds__(kBlock) void replay_flush_kernel(ReplayParams p) {
 
   if (tid == 0) {
     if (h == 0) flag_error(p.err, bad);
-    p.ptr[bh] = pack_ptr((head + F) % L, 0, rp.pending);
+    *reinterpret_cast<unsigned long long*>(rec + kMetaPtr) = pack_ptr((head + F) % L, 0, rp.pending);
   }
 }
 
 struct PtrParams {
-  unsigned long long* ptr;
+  float* meta;
   int32_t* err;
   const int32_t* accepted;
   const int32_t* mask;
   int B, H, L;
 };
 
-// One thread per (request, head) copy of the pointer word:
-// count += clamp(accepted, 0, pending); pending = 0.
+__device__ __forceinline__ unsigned long long* ptr_word(const PtrParams& p, int i) {
+  return reinterpret_cast<unsigned long long*>(p.meta + (size_t)i * meta_words(p.L) + kMetaPtr);
+}
+
+// One thread per (request, head) record: count += clamp(accepted, 0, pending);
+// pending = 0.
 __global__ __launch_bounds__(kBlock) void rollback_kernel(PtrParams p) {
   const int i = blockIdx.x * kBlock + threadIdx.x;
   if (i >= p.B * p.H) return;
-  const RingPtr rp = unpack_ptr(p.ptr[i]);
+  unsigned long long* w = ptr_word(p, i);
+  const RingPtr rp = unpack_ptr(*w);
   int head = rp.head, cnt = rp.count, pend = rp.pending, acc = p.accepted[i / p.H];
   int bad = 0;
   if (head >= p.L) {
@@ -194,7 +199,7 @@ __global__ __launch_bounds__(kBlock) void rollback_kernel(PtrParams p) {
     acc = acc < 0 ? 0 : pend;
     bad |= RSSM_ERR_ACCEPTED;
   }
-  p.ptr[i] = pack_ptr(head, cnt + acc, 0);
+  *w = pack_ptr(head, cnt + acc, 0);
   flag_error(p.err, bad);
 }
 
@@ -202,7 +207,7 @@ __global__ __launch_bounds__(kBlock) void ring_reset_kernel(PtrParams p) {
   const int i = blockIdx.x * kBlock + threadIdx.x;
   if (i == 0 && p.err != nullptr) *p.err = 0;
   if (i >= p.B * p.H) return;
-  if (p.mask == nullptr || p.mask[i / p.H] != 0) p.ptr[i] = 0ull;
+  if (p.mask == nullptr || p.mask[i / p.H] != 0) *ptr_word(p, i) = 0ull;
 }
 
 }  // namespace rssm
@@ -218,9 +223,7 @@ ReplayParams make_replay_params(const rssm_dims* d, float* state0, rssm_ring* ri
   p.state0 = state0;
   p.ring_v = static_cast<uint16_t*>(ring->vu);
   p.ring_k = ring->k;
-  p.ring_dt = ring->dt;
-  p.ring_decay = ring->decay;
-  p.ptr = reinterpret_cast<unsigned long long*>(ring->ptr);
+  p.meta = ring->meta;
   p.err = ring->err;
   p.H = d->nheads;
   p.G = d->ngroups;
@@ -246,7 +249,7 @@ extern "C" int replay_append_decode(const rssm_dims* dims, float* state0, rssm_r
                                     const uint16_t* v, const uint16_t* k, const uint16_t* q,
                                     const float* dt, const float* dt_bias, const float* A,
                                     float* y, int32_t* flushed, void* stream) {
-  if (!rssm_host::dims_ok(dims) || !rssm_host::ring_ok(ring, true) || !state0 || !v || !k || !q ||
+  if (!rssm_host::dims_ok(dims) || !rssm_host::ring_ok(ring) || !state0 || !v || !k || !q ||
       !dt || !dt_bias || !A || !y)
     return RSSM_EINVAL;
   if (dims->capacity < 1) return RSSM_EINVAL;
@@ -266,7 +269,7 @@ extern "C" int replay_append_decode(const rssm_dims* dims, float* state0, rssm_r
 
 extern "C" int replay_flush(const rssm_dims* dims, float* state0, rssm_ring* ring,
                             const int32_t* mask, void* stream) {
-  if (!rssm_host::dims_ok(dims) || !rssm_host::ring_ok(ring, true) || !state0) return RSSM_EINVAL;
+  if (!rssm_host::dims_ok(dims) || !rssm_host::ring_ok(ring) || !state0) return RSSM_EINVAL;
   if (dims->capacity < 1) return RSSM_EINVAL;
   if (!rssm_host::ring_shape_supported(dims)) return RSSM_ENOTSUP;
   ReplayParams p = make_replay_params(dims, state0, ring);
@@ -280,7 +283,7 @@ extern "C" int replay_verify_T(const rssm_dims* dims, int32_t T, float* state0, 
                                const uint16_t* v, const uint16_t* k, const uint16_t* q,
                                const float* dt, const float* dt_bias, const float* A, float* y,
                                int32_t* flushed, void* stream) {
-  if (!rssm_host::dims_ok(dims) || !rssm_host::ring_ok(ring, true) || !state0 || !v || !k || !q ||
+  if (!rssm_host::dims_ok(dims) || !rssm_host::ring_ok(ring) || !state0 || !v || !k || !q ||
       !dt || !dt_bias || !A || !y)
     return RSSM_EINVAL;
   if (T < 1 || dims->capacity < 2 * T) return RSSM_EINVAL;
@@ -301,19 +304,20 @@ extern "C" int replay_verify_T(const rssm_dims* dims, int32_t T, float* state0, 
 
 extern "C" int replay_rollback(const rssm_dims* dims, rssm_ring* ring, const int32_t* accepted,
                                void* stream) {
-  if (!rssm_host::dims_ok(dims) || !rssm_host::ptr_ok(ring) || !accepted) return RSSM_EINVAL;
+  if (!rssm_host::dims_ok(dims) || !rssm_host::meta_ok(ring) || !accepted) return RSSM_EINVAL;
   if (dims->capacity < 1) return RSSM_EINVAL;
-  PtrParams p{reinterpret_cast<unsigned long long*>(ring->ptr), ring->err, accepted, nullptr,
-              dims->batch, dims->nheads, dims->capacity};
+  if (dims->capacity > kMaxL) return RSSM_ENOTSUP;
+  PtrParams p{ring->meta, ring->err, accepted, nullptr, dims->batch, dims->nheads, dims->capacity};
   const dim3 grid((dims->batch * dims->nheads + kBlock - 1) / kBlock);
   return launch(rollback_kernel, grid, dim3(kBlock), stream, p);
 }
 
 extern "C" int rssm_ring_reset(const rssm_dims* dims, rssm_ring* ring, const int32_t* mask,
                                void* stream) {
-  if (!rssm_host::dims_ok(dims) || !rssm_host::ptr_ok(ring)) return RSSM_EINVAL;
-  PtrParams p{reinterpret_cast<unsigned long long*>(ring->ptr), ring->err, nullptr, mask,
-              dims->batch, dims->nheads, dims->capacity};
+  if (!rssm_host::dims_ok(dims) || !rssm_host::meta_ok(ring)) return RSSM_EINVAL;
+  if (dims->capacity < 1) return RSSM_EINVAL;
+  if (dims->capacity > kMaxL) return RSSM_ENOTSUP;
+  PtrParams p{ring->meta, ring->err, nullptr, mask, dims->batch, dims->nheads, dims->capacity};
   const dim3 grid((dims->batch * dims->nheads + kBlock - 1) / kBlock);
   return launch(ring_reset_kernel, grid, dim3(kBlock), stream, p);
 }

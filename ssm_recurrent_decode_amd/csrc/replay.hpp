@@ -16,9 +16,7 @@ struct ReplayParams {
   float* state0;
   uint16_t* ring_v;
   uint16_t* ring_k;
-  float* ring_dt;
-  float* ring_decay;
-  unsigned long long* ptr;  // [B, H] packed ring pointer words, one copy per head
+  float* meta;         // [B, H, meta_words(L)] per-head ring records
   int32_t* err;
   const uint16_t* v;   // [B, T, H, D]
   const uint16_t* k;   // [B, T, G, N]
@@ -82,7 +80,7 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
   __shared__ float s_abar[T];
   __shared__ float s_fw[LCAP];         // fold weights by physical slot
   __shared__ float s_fabar;
-  __shared__ float s_dtn[T], s_dcn[T];  // the new entries' step size and decay
+  __shared__ float s_dtn[T];  // the new entries' step sizes
   __shared__ __attribute__((aligned(16))) uint16_t s_q[T * N];
   __shared__ __attribute__((aligned(16))) uint16_t s_k[LCAP * N];  // keys to fold by slot
   __shared__ __attribute__((aligned(16))) uint16_t s_v[LCAP * D];  // values by slot
@@ -95,7 +93,9 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
   const size_t bh = (size_t)b * H + h;
 
   // ---- 1. this head's copy of the pointer word and every small operand
-  const unsigned long long word = p.ptr[bh];
+  const int MS = meta_words(L);
+  float* rec = p.meta + bh * MS;  // this head's ring record
+  const unsigned long long word = *reinterpret_cast<const unsigned long long*>(rec + kMetaPtr);
   uint4 qm[T], kin[T];
 #pragma unroll
   for (int sd = 0; sd < T; ++sd) {
@@ -115,11 +115,9 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
     }
     newc[i] = ld_u4(src);
   }
-  float dt_slot = 0.f, dc_slot = 1.f, dt_draft = 0.f, dt_bias = 0.f, A_h = 0.f;
-  if (wave == 0) {  // step sizes and decays of every slot, the drafts' raw dt
-    const int sl = min(lane, L - 1);
-    dt_slot = p.ring_dt[bh * L + sl];
-    dc_slot = p.ring_decay[bh * L + sl];
+  float rec_l = 0.f, dt_draft = 0.f, dt_bias = 0.f, A_h = 0.f;
+  if (wave == 0) {  // the whole record (step sizes of every slot), the drafts' raw dt
+    rec_l = rec[min(lane, MS - 1)];
     dt_draft = p.dt[((size_t)b * T + min(lane, T - 1)) * H + h];
     dt_bias = p.dt_bias[h];
     A_h = p.A[h];
@@ -183,8 +181,8 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
   if (wave == 0) {
     const int j = kWave - 1 - lane;                    // logical entry
     const int sj = ring_slot(head, min(j, L - 1), L);  // its physical slot
-    const float dl_ring = __shfl(dt_slot, sj, kWave);
-    const float al_ring = __shfl(dc_slot, sj, kWave);
+    const float dl_ring = __shfl(rec_l, kMetaSlot + sj, kWave);
+    const float al_ring = expf(A_h * dl_ring);
     const float dtd = __shfl(dt_draft, min(max(j - c, 0), T - 1), kWave);
     const float dl_new = softplus_f32(dtd + dt_bias);
     const float al_new = expf(A_h * dl_new);
@@ -206,10 +204,7 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
       if (j < LCAP) s_fw[wi] = (j < F) ? dl * ex : 0.f;
       if (lane == 0) s_fabar = all;
     }
-    if (write_new && j >= c && j < E) {  // the new entries' step size and decay
-      s_dtn[j - c] = dl;
-      s_dcn[j - c] = al;
-    }
+    if (j >= c && j < E) s_dtn[j - c] = dl;  // the new entries' step sizes
     if (lane < 16) {
 #pragma unroll
       for (int sd = 0; sd < T; ++sd) *reinterpret_cast<uint4*>(&s_q[sd * N + sub * 8]) = qm[sd];
@@ -275,8 +270,8 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
     fold_and_store<D, N, RT, NCT, VJ>(p.state0 + bh * D * N, st, s_fabar, s_k, s_fw, vj, L, wave, r, cq);
 
   // ---- 8. the new entries cached in the ring unless this call empties it: v of
-  //      this head, k by the group's first head, step size and decay.  Stores are
-  //      issued last (measured slightly faster than in the middle phase).
+  //      this head, k by the group's first head.  Stores are issued last
+  //      (measured slightly faster than in the middle phase).
   if (write_new) {
     const bool k_owner = (h % hpg) == 0;
 #pragma unroll
@@ -291,22 +286,26 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
         *reinterpret_cast<uint4*>(p.ring_k + (((size_t)b * G + g) * L + ring_slot(head, c + sd, L)) * N + o) = newc[i];
       }
     }
-    if (tid < T) {
-      const int sl = ring_slot(head, c + tid, L);
-      p.ring_dt[bh * L + sl] = s_dtn[tid];
-      p.ring_decay[bh * L + sl] = s_dcn[tid];
-    }
   }
 
-  // ---- 9. this head's copy of the new pointers
-  if (tid == 0) {
-    if (h == 0) {
+  // ---- 9. this head's record rewritten as whole lines by wave 0: the new
+  //      pointer word, A, and the step sizes with the new entries' in their slots
+  if (wave == 0) {
+    if (lane == 0 && h == 0) {
       flag_error(p.err, bad);
       if (p.flushed != nullptr) p.flushed[b] = do_flush ? 1 : 0;
     }
     const int keep = APPEND ? E : c;  // entries that stay committed unless flushed
-    p.ptr[bh] = pack_ptr(do_flush ? ring_slot(head, F % L, L) : head, do_flush ? keep - F : keep,
-                         APPEND ? 0 : T);
+    const unsigned long long nw =
+        pack_ptr(do_flush ? ring_slot(head, F % L, L) : head, do_flush ? keep - F : keep, APPEND ? 0 : T);
+    const int sl = lane - kMetaSlot;
+    const int sd = (sl >= 0 && sl < L) ? logical(sl) - c : -1;
+    float x = rec_l;
+    if (lane == kMetaPtr) x = __uint_as_float(uint32_t(nw));
+    if (lane == kMetaPtr + 1) x = __uint_as_float(uint32_t(nw >> 32));
+    if (lane == kMetaA) x = A_h;
+    if (write_new && sd >= 0 && sd < T) x = s_dtn[min(max(sd, 0), T - 1)];
+    if (lane < MS) rec[lane] = x;
   }
 }
 

@@ -32,7 +32,7 @@ def test_every_declared_function_is_exported_and_prototyped():
 
 def test_abi_version_and_strerror():
     lib = _lib.load()
-    assert lib.rssm_abi_version() == _lib.ABI_VERSION == 2
+    assert lib.rssm_abi_version() == _lib.ABI_VERSION == 3
     assert "invalid" in _lib.strerror(_lib.RSSM_EINVAL)
     assert "not supported" in _lib.strerror(_lib.RSSM_ENOTSUP)
 
@@ -42,18 +42,23 @@ def _dims(B=4, H=8, d=64, n=128, G=1, L=8):
 
 
 def _ring():
-    return _lib.rssm_ring(*([FAKE.value] * 6))
+    return _lib.rssm_ring(*([FAKE.value] * 4))
 
 
 def test_ring_sizes():
     lib = _lib.load()
-    out = (ctypes.c_size_t * 6)()
+    out = (ctypes.c_size_t * 4)()
     d = _dims(B=256, H=32, d=64, n=128, G=8, L=16)
     assert lib.rssm_ring_sizes(ctypes.byref(d), 0, out) == 0
-    assert list(out) == [256 * 32 * 16 * 64 * 2, 256 * 8 * 16 * 128 * 2, 256 * 32 * 16 * 4,
-                         256 * 32 * 16 * 4, 256 * 32 * 8, 4]
+    assert list(out) == [256 * 32 * 16 * 64 * 2, 256 * 8 * 16 * 128 * 2, 256 * 32 * 32 * 4, 4]
     assert lib.rssm_ring_sizes(ctypes.byref(d), 1, out) == 0
-    assert out[0] == 256 * 32 * 16 * 64 * 4 and out[2] == 0
+    assert out[0] == 256 * 32 * 16 * 64 * 4
+    # a record is one 128-byte line up to L = 29, two lines above
+    for L, words in ((29, 32), (30, 64), (32, 64)):
+        d = _dims(B=2, H=4, L=L)
+        assert lib.rssm_ring_sizes(ctypes.byref(d), 0, out) == 0
+        assert out[2] == 2 * 4 * words * 4
+    assert lib.rssm_ring_sizes(ctypes.byref(_dims(L=33)), 0, out) == _lib.RSSM_ENOTSUP
 
 
 def test_host_validation_codes():
@@ -85,19 +90,18 @@ def test_host_validation_codes():
                                    None, None) == code
         assert lib.gdn_replay_verify_T(ctypes.byref(dd), T, P, ctypes.byref(r), P, P, P, P, P, P,
                                        None, None) == code
-    # GDN ring needs no dt; Mamba-2 ring does
-    r_nodt = _ring()
-    r_nodt.dt = None
-    assert lib.replay_flush(ctypes.byref(d), P, ctypes.byref(r_nodt), None, None) == EINVAL
+    # ring records must be present and 128-byte aligned
+    r_nometa = _ring()
+    r_nometa.meta = None
+    assert lib.replay_flush(ctypes.byref(d), P, ctypes.byref(r_nometa), None, None) == EINVAL
     # conv1d: only W = 4 and C % 4 == 0
     assert lib.causal_conv1d_update(4, 3072, 3, P, P, P, P, None) == ENOTSUP
     assert lib.causal_conv1d_update(4, 3070, 4, P, P, P, P, None) == ENOTSUP
     assert lib.causal_conv1d_update(0, 3072, 4, P, P, P, P, None) == EINVAL
     # rollback needs accepted
     assert lib.replay_rollback(ctypes.byref(d), ctypes.byref(r), None, None) == EINVAL
-    # pointer words must be 8-byte aligned
     r_odd = _ring()
-    r_odd.ptr = FAKE.value + 4
+    r_odd.meta = FAKE.value + 64
     assert lib.replay_rollback(ctypes.byref(d), ctypes.byref(r_odd), P, None) == EINVAL
     assert lib.rssm_ring_reset(ctypes.byref(d), ctypes.byref(r_odd), None, None) == EINVAL
 
