@@ -39,12 +39,12 @@ struct GdnReplayParams {
 //   the drafts' (u, k, alpha') are cached in their ring slots; when c + 2T > L
 //   the committed entries are folded first: S_0 <- abar S_0 + sum_j w_j u_j k_j^T.
 //
-// As in the Mamba-2 window kernel, the pointer word and every small operand --
-// the 2T readout vectors and the draft values (16 bytes per lane into LDS), the
-// decays of all L slots, the gates and betas, the ring keys and the ring
-// corrections of all L physical slots (16 bytes per lane into LDS) -- are
-// requested before the checkpoint tiles, so the weights and the inner products
-// k . x proceed while the checkpoint is in flight.  The 2T readouts S_0 x run on
+// As in the Mamba-2 window kernel, the ring record (pointer word and the decays
+// of all L slots) and every small operand -- the 2T readout vectors and the draft
+// values (16 bytes per lane into LDS), the gates and betas -- are requested
+// before the checkpoint tiles, and the ring keys and corrections of the c
+// committed entries only (16 bytes per lane into LDS) right after them, once the
+// pointer word is in; the weights proceed while the checkpoint is in flight.  The 2T readouts S_0 x run on
 // the matrix cores from the state registers; the fold (when flushing) follows
 // from the same registers; the per-row solve runs one thread per row after that.
 template <int D, int N, int T, int LCAP>
@@ -106,14 +106,6 @@ __global__ __launch_bounds__(kBlock) void gdn_verify_kernel(GdnReplayParams p) {
     gd = p.g[((size_t)b * T + min(lane, T - 1)) * H + h];
     bt = p.beta[((size_t)b * T + min(lane, T - 1)) * H + h];
   }
-  uint4 kr[PASSES];  // ring key of slot ps*16 + wave*4 + lane/16, 8 columns per lane
-#pragma unroll
-  for (int ps = 0; ps < PASSES; ++ps)
-    kr[ps] = ld_u4(p.ring_k + (((size_t)b * G + g) * L + min(ps * 16 + wave * 4 + (lane >> 4), L - 1)) * N + sub * 8);
-  float4 uc[UP];  // ring corrections, 16 bytes per lane, slot-major as in memory
-#pragma unroll
-  for (int i = 0; i < UP; ++i)
-    uc[i] = ld_f4(p.ring_u + bh * L * D + min(tid + i * kBlock, L * D / 4 - 1) * 4);
 
   // ---- 2. the checkpoint, last (the scheduler may not hoist it above the rest)
   __builtin_amdgcn_sched_barrier(0);
@@ -133,11 +125,6 @@ __global__ __launch_bounds__(kBlock) void gdn_verify_kernel(GdnReplayParams p) {
     if (t < XC) *reinterpret_cast<uint4*>(&s_x[t * 8]) = xvc[i];
     else if (t < XC + VC) *reinterpret_cast<uint4*>(&s_vd[(t - XC) * 8]) = xvc[i];
   }
-#pragma unroll
-  for (int i = 0; i < UP; ++i) {
-    const int t = tid + i * kBlock;
-    if (t < L * D / 4) *reinterpret_cast<float4*>(&s_u[t * 4]) = uc[i];
-  }
   const RingPtr rp = unpack_ptr(word);
   int head = rp.head, cnt = rp.count;
   int bad = 0;
@@ -154,6 +141,25 @@ __global__ __launch_bounds__(kBlock) void gdn_verify_kernel(GdnReplayParams p) {
   const bool do_flush = (c + 2 * T > L);
   // logical entry held by physical slot sl (0 <= sl < L)
   auto logical = [&](int sl) { const int j = sl - head; return j < 0 ? j + L : j; };
+
+  // the committed entries' ring keys (slot ps*16 + wave*4 + lane/16, 8 columns per
+  // lane) and corrections (16 bytes per lane, by logical entry), now that the
+  // pointers are known: only the c entries in use, queued behind the checkpoint
+  uint4 kr[PASSES];
+#pragma unroll
+  for (int ps = 0; ps < PASSES; ++ps) {
+    const int sl = ps * 16 + wave * 4 + (lane >> 4);
+    kr[ps] = make_uint4(0, 0, 0, 0);
+    if (sl < L && logical(min(sl, L - 1)) < c)
+      kr[ps] = ld_u4(p.ring_k + (((size_t)b * G + g) * L + sl) * N + sub * 8);
+  }
+  float4 uc[UP];
+#pragma unroll
+  for (int i = 0; i < UP; ++i) {
+    const int t = tid + i * kBlock;
+    uc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (t < c * (D / 4)) uc[i] = ld_f4(p.ring_u + (bh * L + ring_slot(head, t / (D / 4), L)) * D + (t % (D / 4)) * 4);
+  }
 
   // ---- 4. wave 0: decay weights of the committed entries (lane l takes logical
   //      entry 63 - l, so products over later entries are prefix products), the
@@ -198,6 +204,13 @@ __global__ __launch_bounds__(kBlock) void gdn_verify_kernel(GdnReplayParams p) {
       *reinterpret_cast<uint4*>(p.ring_k + (((size_t)b * G + g) * L + ring_slot(head, c + sd, L)) * N + o) =
           *reinterpret_cast<const uint4*>(&s_x[sd * N + o]);
     }
+  }
+  // the committed corrections into their LDS slots (waits for them only here)
+#pragma unroll
+  for (int i = 0; i < UP; ++i) {
+    const int t = tid + i * kBlock;
+    if (t < c * (D / 4))
+      *reinterpret_cast<float4*>(&s_u[ring_slot(head, t / (D / 4), L) * D + (t % (D / 4)) * 4]) = uc[i];
   }
   __syncthreads();
 

@@ -49,18 +49,18 @@ __device__ __forceinline__ void load_tiles(float4 (&s)[RT][NCT], const float* S0
 //  VERIFY (T drafts): drafts are entries c .. c+T-1; draft s reads p_s = c+s+1
 //    entries; if c + 2T > L fold the c committed entries only.  pending <- T.
 //
-// Nothing waits for the checkpoint until it is needed.  This head's copy of the
-// pointer word, the queries and drafts, the step sizes and decays,
-// the group's ring keys and the head's ring values of all L physical slots are
-// requested first, the checkpoint tiles last.  Loads complete in issue order, so
-// the weights (wave 0) and the inner products k . q (all waves) go ahead while the
-// checkpoint is still streaming in; only the output combine and the fold wait for
-// it.  The new entries are cached in the ring by the last stores of the kernel.  Ring values arrive 16 bytes per lane
-// and are kept in LDS, where the new entries' values are written into their
-// slots, so the combine and the fold read every value from one array.  The ring
-// is read by physical slot; the pointers only decide which logical entry a slot
-// holds (j = slot - head mod L).  Weights are computed in logical order and
-// stored by physical slot.  LCAP (16 or 32) bounds L and sizes the arrays.
+// Issue order: this head's ring record (pointer word and step sizes), the
+// queries, drafts and new entries, then the checkpoint tiles, then -- once the
+// pointer word is in -- the ring keys and values of the c committed entries only
+// (on average half the ring).  Loads complete in issue order, so the weights
+// (wave 0) go ahead while the checkpoint streams in; the inner products k . q,
+// the output combine and the fold follow it.  Ring values arrive 16 bytes per
+// lane and are kept in LDS together with the new entries' values, so the
+// combine and the fold read every value from one array by physical slot; the
+// pointers decide which logical entry a slot holds (j = slot - head mod L).
+// Weights are computed in logical order and stored by physical slot.  The new
+// entries and the record are written by the last stores of the kernel.  LCAP
+// (16 or 32) bounds L and sizes the arrays.
 template <int D, int N, int T, bool APPEND, int LCAP>
 __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
   static_assert(N == 128, "key/query staging assumes n = 128 (16 lanes x 8 values)");
@@ -122,27 +122,13 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
     dt_bias = p.dt_bias[h];
     A_h = p.A[h];
   }
-  uint4 kr[PASSES];  // ring key of slot ps*16 + wave*4 + lane/16, 8 columns per lane
-#pragma unroll
-  for (int ps = 0; ps < PASSES; ++ps)
-    kr[ps] = ld_u4(p.ring_k + (((size_t)b * G + g) * L + min(ps * 16 + wave * 4 + (lane >> 4), L - 1)) * N + sub * 8);
-  uint4 rv[RVP];  // ring values, 16 bytes per lane, slot-major as in memory
-#pragma unroll
-  for (int i = 0; i < RVP; ++i)
-    rv[i] = ld_u4(p.ring_v + bh * L * D + min(tid + i * kBlock, L * D / 8 - 1) * 8);
 
-  // ---- 2. the checkpoint, last (the scheduler may not hoist it above the rest)
+  // ---- 2. the checkpoint (the scheduler may not hoist it above the rest)
   __builtin_amdgcn_sched_barrier(0);
   float4 st[RT][NCT];
   load_tiles<D, N, RT, NCT>(st, p.state0 + bh * D * N, wave, r, cq);
 
   // ---- 3. ring pointers (uniform per request), clamped into range
-#pragma unroll
-  for (int i = 0; i < RVP; ++i) {
-    const int t = tid + i * kBlock;
-    if (t < L * D / 8) *reinterpret_cast<uint4*>(&s_v[t * 8]) = rv[i];
-  }
-  __syncthreads();
   const RingPtr rp = unpack_ptr(word);
   int head = rp.head, cnt = rp.count;
   int bad = 0;
@@ -164,7 +150,27 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
   // logical entry held by physical slot sl (0 <= sl < L)
   auto logical = [&](int sl) { const int j = sl - head; return j < 0 ? j + L : j; };
 
-  // ---- 4. the new entries' values into their LDS slots (they are cached in the
+  // ---- 4. the committed entries' ring keys (slot ps*16 + wave*4 + lane/16, 8
+  //      columns per lane) and values (16 bytes per lane, by logical entry), now
+  //      that the pointers are known: only the c entries in use are fetched, and
+  //      they queue behind the checkpoint, which is needed first
+  uint4 kr[PASSES];
+#pragma unroll
+  for (int ps = 0; ps < PASSES; ++ps) {
+    const int sl = ps * 16 + wave * 4 + (lane >> 4);
+    kr[ps] = make_uint4(0, 0, 0, 0);
+    if (sl < L && logical(min(sl, L - 1)) < c)
+      kr[ps] = ld_u4(p.ring_k + (((size_t)b * G + g) * L + sl) * N + sub * 8);
+  }
+  uint4 rv[RVP];
+#pragma unroll
+  for (int i = 0; i < RVP; ++i) {
+    const int t = tid + i * kBlock;
+    rv[i] = make_uint4(0, 0, 0, 0);
+    if (t < c * (D / 8)) rv[i] = ld_u4(p.ring_v + (bh * L + ring_slot(head, t / (D / 8), L)) * D + (t % (D / 8)) * 8);
+  }
+
+  // ---- 5. the new entries' values into their LDS slots (they are cached in the
   //      ring at the end)
 #pragma unroll
   for (int i = 0; i < NCP; ++i) {
@@ -175,7 +181,7 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
     }
   }
 
-  // ---- 5. wave 0: decay weights, stored by physical slot.  Lane l takes logical
+  // ---- 6. wave 0: decay weights, stored by physical slot.  Lane l takes logical
   //      entry j = 63 - l, so products over the entries after j are prefix
   //      products over the lanes before l.
   if (wave == 0) {
@@ -211,7 +217,7 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
     }
   }
 
-  // ---- 6. all waves: k . q_s for every physical slot (16 lanes per slot); keys
+  // ---- 7. all waves: k . q_s for every physical slot (16 lanes per slot); keys
   //      to fold staged by slot (zero rows for slots not folded)
 #pragma unroll
   for (int ps = 0; ps < PASSES; ++ps) {
@@ -229,9 +235,16 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
       if (sub == 0) s_M[sd][sl] = dv;
     }
   }
+  // the committed values into their LDS slots (waits for them only here)
+#pragma unroll
+  for (int i = 0; i < RVP; ++i) {
+    const int t = tid + i * kBlock;
+    if (t < c * (D / 8))
+      *reinterpret_cast<uint4*>(&s_v[ring_slot(head, t / (D / 8), L) * D + (t % (D / 8)) * 8]) = rv[i];
+  }
   __syncthreads();
 
-  // ---- 7. output-only route, fold when flushing (the checkpoint is needed here)
+  // ---- 8. output-only route, fold when flushing (the checkpoint is needed here)
   float vj[RT][VJ];  // value of slot cq + 4m at this lane's rows, zero if not read
 #pragma unroll
   for (int m = 0; m < VJ; ++m) {
@@ -269,7 +282,7 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
   if (F > 0)
     fold_and_store<D, N, RT, NCT, VJ>(p.state0 + bh * D * N, st, s_fabar, s_k, s_fw, vj, L, wave, r, cq);
 
-  // ---- 8. the new entries cached in the ring unless this call empties it: v of
+  // ---- 9. the new entries cached in the ring unless this call empties it: v of
   //      this head, k by the group's first head.  Stores are issued last
   //      (measured slightly faster than in the middle phase).
   if (write_new) {
@@ -288,7 +301,7 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
     }
   }
 
-  // ---- 9. this head's record rewritten as whole lines by wave 0: the new
+  // ---- 10. this head's record rewritten as whole lines by wave 0: the new
   //      pointer word, A, and the step sizes with the new entries' in their slots
   if (wave == 0) {
     if (lane == 0 && h == 0) {
