@@ -284,10 +284,83 @@ def _row_sweep(torch, np, rd, synth, traffic, dev, stream, capacities=(4, 8, 16,
     return res
 
 
+def _row_flush(torch, np, rd, synth, traffic, dev, stream, reps=8):
+    """Explicit flush of full rings: Mamba-2 at the Nemotron-H shape after L - 1
+    appends, GDN at its verify shape after three fully accepted verify rounds
+    (c = 3T); each flush launch timed with HIP events."""
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+    out = {}
+    # Mamba-2
+    wl = synth.WORKLOADS[1]
+    sh, seed = wl.shape, wl.cfg_seed
+    B, H, D, N, G, L = sh.batch, sh.nheads, sh.head_dim, sh.state_dim, sh.ngroups, sh.capacity
+    dims = rd.Dims(B, H, D, N, G, L)
+    S0 = torch.randn((B, H, D, N), device=dev) * math.sqrt(0.1)
+    ring = rd.Ring(dims, device=dev)
+    A, bias = synth.mamba2_head_params(sh, seed, 1)
+    A, bias = torch.from_numpy(A).to(dev), torch.from_numpy(bias).to(dev)
+    st = synth.mamba2_step_inputs(sh, seed, 1, 0)
+    ip = {"v": bf(st["v"]), "k": bf(st["k"]), "q": bf(st["q"]), "dt": torch.from_numpy(st["dt"]).to(dev)}
+    y = torch.empty((B, H, D), device=dev)
+    app = rd.prepare_replay_append_decode(dims, S0, ring, ip["v"], ip["k"], ip["q"], ip["dt"], bias, A, y,
+                                          stream=stream)
+    ev = _events(torch, reps)
+    for i in range(reps + 1):
+        for _ in range(L - 1):
+            app()
+        if i > 0:
+            ev[i - 1][0].record(stream)
+        rd.replay_flush(dims, S0, ring, stream=stream)
+        if i > 0:
+            ev[i - 1][1].record(stream)
+    torch.cuda.synchronize()
+    us = float(np.mean([1e3 * a_.elapsed_time(b_) for a_, b_ in ev]))
+    byts = traffic.replay_flush(B, H, D, N, G, L - 1)
+    out["mamba2"] = {"workload": f"replay_flush of {L - 1} entries, batch {B}, {H} heads, head dim {D}, "
+                                 f"state {N}, {G} groups", "us": round(us, 3),
+                     "achieved_GBs": round(byts / (us * 1e-6) / 1e9, 1), "alg_bytes": byts}
+    del S0, ring
+    # GDN
+    wl = synth.WORKLOADS[4]
+    sh, seed = wl.shape, wl.cfg_seed
+    B, H, D, N, G, L, T = sh.batch, sh.nheads, sh.head_dim, sh.state_dim, sh.ngroups, sh.capacity, sh.T
+    dims = rd.Dims(B, H, D, N, G, L)
+    S0 = torch.randn((B, H, D, N), device=dev) * math.sqrt(0.1)
+    ring = rd.Ring(dims, gdn=True, device=dev)
+    st = synth.gdn_round_inputs(sh, seed, 4, 0)
+    ip = {"v": bf(st["v"]), "k": bf(st["k"]), "q": bf(st["q"]), "g": torch.from_numpy(st["g"]).to(dev),
+          "beta": torch.from_numpy(st["beta"]).to(dev)}
+    y = torch.empty((B, T, H, D), device=dev)
+    acc_all = torch.full((B,), T, dtype=torch.int32, device=dev)
+    rounds = (L - T) // T           # c = rounds * T committed, no early flush on the way
+    ev = _events(torch, reps)
+    for i in range(reps + 1):
+        for _ in range(rounds):
+            rd.gdn_replay_verify_T(dims, T, S0, ring, ip["v"], ip["k"], ip["q"], ip["g"], ip["beta"], y,
+                                   stream=stream)
+            rd.replay_rollback(dims, ring, acc_all, stream=stream)
+        if i > 0:
+            ev[i - 1][0].record(stream)
+        rd.gdn_replay_flush(dims, S0, ring, stream=stream)
+        if i > 0:
+            ev[i - 1][1].record(stream)
+    torch.cuda.synchronize()
+    if int(ring.err.item()) != 0:
+        raise RuntimeError("ring anomaly bits set in the flush row")
+    us = float(np.mean([1e3 * a_.elapsed_time(b_) for a_, b_ in ev]))
+    byts = traffic.gdn_flush(B, H, D, N, G, rounds * T)
+    out["gdn"] = {"workload": f"gdn_replay_flush of {rounds * T} entries, batch {B}, {H} heads, head dim {D}, "
+                              f"state {N}, {G} groups", "us": round(us, 3),
+                  "achieved_GBs": round(byts / (us * 1e-6) / 1e9, 1), "alg_bytes": byts}
+    return out
+
+
 def _rows(torch, np, rd, synth, traffic, dev, stream):
     return {"speculative_verify": _row_verify(torch, np, rd, synth, traffic, dev, stream, 2, False),
             "gdn_speculative_verify": _row_verify(torch, np, rd, synth, traffic, dev, stream, 4, True),
-            "capacity_sweep": _row_sweep(torch, np, rd, synth, traffic, dev, stream)}
+            "capacity_sweep": _row_sweep(torch, np, rd, synth, traffic, dev, stream),
+            "explicit_flush": _row_flush(torch, np, rd, synth, traffic, dev, stream)}
 
 
 def main(argv=None) -> int:

@@ -23,8 +23,8 @@ def standard_step(B, H, d, n, G) -> int:
 
 def replay_slot(H, d, n, G) -> int:
     """Bytes of one cached entry of one request: v (bf16, all heads), k (bf16, per
-    group), step size and decay (fp32 per head)."""
-    return BF16 * H * d + BF16 * G * n + 2 * F32 * H
+    group), step size (fp32 per head; the decay exp(A Delta) is recomputed)."""
+    return BF16 * H * d + BF16 * G * n + F32 * H
 
 
 def replay_append(B, H, d, n, G, h, flush: bool) -> int:
@@ -48,6 +48,16 @@ def replay_verify(B, H, d, n, G, T, c, flush: bool) -> int:
     if flush:
         per_req += F32 * H * d * n
     return B * per_req + 2 * F32 * H
+
+
+def replay_flush(B, H, d, n, G, c) -> int:
+    """Explicit flush of c committed entries: checkpoint read and write, the c
+    cached entries, the heads' A, the pointer word read and written."""
+    return B * (2 * F32 * H * d * n + c * replay_slot(H, d, n, G) + F32 * H + 2 * PTR)
+
+
+def gdn_flush(B, H, d, n, G, c) -> int:
+    return B * (2 * F32 * H * d * n + c * gdn_slot(H, d, n, G) + 2 * PTR)
 
 
 def gdn_slot(H, d, n, G) -> int:
