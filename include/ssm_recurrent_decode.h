@@ -155,7 +155,8 @@ int ssm_decode_step(const rssm_dims* dims, float* state, const uint16_t* v, cons
  * The flush decision is per request, read from count at run time.
  *   state0  fp32 [B, H, d, n] checkpoint, read (written on flush steps)
  *   ring    Mamba-2 ring; requires pending == 0 and count < L on entry
- *   v, k, q, dt, dt_bias, A, y  as ssm_decode_step
+ *   v, k, q, dt, dt_bias, A, y  as ssm_decode_step; A must be the same in every
+ *           call while entries are cached (the cached decays are exp(A Delta))
  *   flushed int32 [B] out (1 = this request flushed), may be NULL
  */
 int replay_append_decode(const rssm_dims* dims, float* state0, rssm_ring* ring,
@@ -187,6 +188,7 @@ int replay_flush(const rssm_dims* dims, float* state0, rssm_ring* ring, const in
  *   v bf16 [B, T, H, d];  k, q bf16 [B, T, G, n];  dt fp32 [B, T, H] raw
  *   y fp32 [B, T, H, d] out (every draft position, rejected ones included)
  *   flushed int32 [B] out, may be NULL
+ *   dt_bias, A as replay_append_decode (A the same while entries are cached)
  * Requires 1 <= T, 2T <= L; on entry pending == 0 and count + T <= L.
  */
 int replay_verify_T(const rssm_dims* dims, int32_t T, float* state0, rssm_ring* ring,

@@ -92,7 +92,7 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
   const int r = lane & 15, cq = lane >> 4, sub = lane & 15;
   const size_t bh = (size_t)b * H + h;
 
-  // ---- 1. this head's copy of the pointer word and every small operand
+  // ---- 1. this head's ring record (pointer word, step sizes) and every small operand
   const int MS = meta_words(L);
   float* rec = p.meta + bh * MS;  // this head's ring record
   const unsigned long long word = *reinterpret_cast<const unsigned long long*>(rec + kMetaPtr);
