@@ -97,6 +97,33 @@ def test_replay_append_decode_small(d, G, L, ring_dominant):
     assert torch.all(ring.count == 0)
 
 
+def test_ring_record_contents():
+    """The per-head ring record after a few appends: every head's pointer word
+    equal, word 2 the head's A, word 3 + slot the step size of the entry cached in
+    that slot (against the oracle's softplus, at fp32 rounding)."""
+    base = synth.WORKLOADS[0]
+    sh = base.shape.with_(capacity=8)
+    A, dt_bias, S0, seq = _mamba2_case(sh, base.cfg_seed, 0, 13, False)
+    dims = _dims(sh)
+    ring = rd.Ring(dims)
+    state0 = dev_f32(S0)
+    y = torch.empty(sh.batch, sh.nheads, sh.head_dim, device="cuda")
+    for st in seq:                       # 13 appends at L = 8: one flush, 5 cached
+        rd.replay_append_decode(dims, state0, ring, dev_bf16(st["v"]), dev_bf16(st["k"]),
+                                dev_bf16(st["q"]), dev_f32(st["dt"]), dev_f32(dt_bias), dev_f32(A), y)
+    torch.cuda.synchronize()
+    meta = ring.meta.cpu().numpy()
+    assert ring.copies_agree()
+    head, count = int(ring.head[0].item()), int(ring.count[0].item())
+    assert (head, count) == (0, 5)
+    assert np.array_equal(meta[:, :, 2], np.broadcast_to(A.astype(np.float32), meta[:, :, 2].shape))
+    for j in range(count):               # logical entry j is the append of step 8 + j
+        delta, _ = o_m2.step_size_and_decay(seq[8 + j]["dt"], dt_bias, A)
+        got = meta[:, :, 3 + (head + j) % sh.capacity].astype(np.float64)
+        assert np.max(np.abs(got - delta) / np.abs(delta)) <= 2e-6, j
+    assert int(ring.err.item()) == 0
+
+
 def test_replay_append_decode_is_deterministic():
     base = synth.WORKLOADS[0]
     sh = base.shape
