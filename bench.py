@@ -187,18 +187,43 @@ def _row_verify(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, rounds=
     fl = np.array([counts[r] + 2 * T > L for r in range(warm, R)])
     round_s = (sum(v_us) + sum(r_us)) * 1e-6
     gbs = sum(byts) / (sum(v_us) * 1e-6) / 1e9
-    return {"workload": ("Gated DeltaNet" if gdn else "Mamba-2") +
-                        f" speculative verify, batch {B}, {H} heads, head dim {D}, state {N}, "
-                        f"{G} group(s), ring capacity {L}, T={T}; two layer instances rotated",
-            "kernel": "gdn_replay_verify_T" if gdn else "replay_verify_T",
-            "rounds_timed": rounds, "verify_us": round(sum(v_us) / rounds, 3),
-            "rollback_us": round(sum(r_us) / rounds, 3),
-            "verified_positions_per_s": round(B * T * rounds / round_s, 1),
-            "accepted_tokens_per_s": round(float(acc[warm:].sum()) / round_s, 1),
-            "achieved_GBs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
-            "alg_bytes_per_round": round(sum(byts) / rounds),
-            "flush_rate": round(float(fl.mean()), 4),
-            "mean_committed_before": round(float(np.mean([counts[r] for r in range(warm, R)])), 3)}
+    base = None
+    if gdn:
+        # the baseline that rewrites the state every token, at the same shape
+        st1 = synth.gdn_round_inputs(sh.with_(T=1), seed, cfg_id, 0)
+        one = {k_: (bf(v_[:, 0]) if v_.dtype == np.uint16 else torch.from_numpy(np.ascontiguousarray(v_[:, 0])).to(dev))
+               for k_, v_ in st1.items()}
+        y1 = torch.empty((B, H, D), device=dev)
+        for _ in range(4):
+            rd.gdn_decode_step(dims, layers[0]["S0"], one["v"], one["k"], one["q"], one["g"], one["beta"], y1,
+                               stream=stream)
+        ev1 = _events(torch, 16)
+        torch.cuda.synchronize()
+        for i in range(16):
+            ev1[i][0].record(stream)
+            rd.gdn_decode_step(dims, layers[i % NLr]["S0"], one["v"], one["k"], one["q"], one["g"],
+                               one["beta"], y1, stream=stream)
+            ev1[i][1].record(stream)
+        torch.cuda.synchronize()
+        su = float(np.mean([1e3 * a_.elapsed_time(b_) for a_, b_ in ev1]))
+        sb = traffic.gdn_standard_step(B, H, D, N, G)
+        base = {"kernel": "gdn_decode_step", "us": round(su, 3), "GBs": round(sb / (su * 1e-6) / 1e9, 1),
+                "tokens_per_s": round(B / (su * 1e-6), 1)}
+    res = {"workload": ("Gated DeltaNet" if gdn else "Mamba-2") +
+                       f" speculative verify, batch {B}, {H} heads, head dim {D}, state {N}, "
+                       f"{G} group(s), ring capacity {L}, T={T}; two layer instances rotated",
+           "kernel": "gdn_replay_verify_T" if gdn else "replay_verify_T",
+           "rounds_timed": rounds, "verify_us": round(sum(v_us) / rounds, 3),
+           "rollback_us": round(sum(r_us) / rounds, 3),
+           "verified_positions_per_s": round(B * T * rounds / round_s, 1),
+           "accepted_tokens_per_s": round(float(acc[warm:].sum()) / round_s, 1),
+           "achieved_GBs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+           "alg_bytes_per_round": round(sum(byts) / rounds),
+           "flush_rate": round(float(fl.mean()), 4),
+           "mean_committed_before": round(float(np.mean([counts[r] for r in range(warm, R)])), 3)}
+    if base is not None:
+        res["standard_step"] = base
+    return res
 
 
 def _row_sweep(torch, np, rd, synth, traffic, dev, stream, capacities=(4, 8, 16, 32)):
@@ -468,6 +493,14 @@ def main(argv=None) -> int:
     end.record(stream)
     end.synchronize()
     kern_avg_ms = start.elapsed_time(end) / K
+    # the conv1d update alone, back to back (the other kernel of the step)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(K):
+        step_calls(t_kern + i)[0]()
+    end.record(stream)
+    end.synchronize()
+    conv_avg_ms = start.elapsed_time(end) / K
     total_ms = eager_ms
     graph_info = None
     if not a.no_graph:
@@ -526,6 +559,9 @@ def main(argv=None) -> int:
                      "traffic_note": traffic_note,
                      "kernel_avg_us": round(1e3 * kern_avg_ms, 3),
                      "alg_bytes_per_launch": round(alg_bytes / K)},
+        "conv1d": {"kernel": "causal_conv1d_update", "us": round(1e3 * conv_avg_ms, 3),
+                   "achieved_GBs": round(traffic.conv1d(B, C, W) / (conv_avg_ms * 1e-3) / 1e9, 1),
+                   "alg_bytes": traffic.conv1d(B, C, W)},
         "timing": {"step": "hip graph replay" if graph_info else "eager launches",
                    "eager_ms_per_step": round(eager_ms / K, 5), "graph": graph_info,
                    "kernel": "HIP events around K back-to-back replay_append_decode launches on "
