@@ -109,13 +109,23 @@ def _verify_bytes(traffic, gdn, H, D, N, G, T, L, counts):
     return tot
 
 
-def _row_verify(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, rounds=64, warm=16):
+def _draft_inputs(synth, sh, seed, cfg_id, r, gdn):
+    """One verify round of seeded draft inputs with the draft axis kept at T = 1."""
+    if gdn:
+        return synth.gdn_round_inputs(sh, seed, cfg_id, r)
+    st = synth.mamba2_step_inputs(sh, seed, cfg_id, r)
+    return {k_: v_[:, None] for k_, v_ in st.items()} if sh.T == 1 else st
+
+
+def _row_verify(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, rounds=64, warm=16, T=None,
+                with_standard=True):
     """Speculative verify rounds (verify kernel + device-side rollback) on two
     rotated layer instances.  A first pass records the committed count every
     request had before each round; the rings are reset and the same sequence is
-    replayed with HIP events around every launch."""
+    replayed with HIP events around every launch.  T overrides the workload's
+    draft window."""
     wl = synth.WORKLOADS[cfg_id]
-    sh, seed = wl.shape, wl.cfg_seed
+    sh, seed = (wl.shape if T is None else wl.shape.with_(T=T)), wl.cfg_seed
     B, H, D, N, G, L, T = sh.batch, sh.nheads, sh.head_dim, sh.state_dim, sh.ngroups, sh.capacity, sh.T
     NLr, P, R = 2, 8, warm + rounds
     dims = rd.Dims(B, H, D, N, G, L)
@@ -135,14 +145,9 @@ def _row_verify(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, rounds=
         layers.append(Ly)
     pool = []
     for p in range(P):
-        if gdn:
-            st = synth.gdn_round_inputs(sh, seed, cfg_id, p)
-            pool.append({"v": bf(st["v"]), "k": bf(st["k"]), "q": bf(st["q"]),
-                         "g": torch.from_numpy(st["g"]).to(dev), "beta": torch.from_numpy(st["beta"]).to(dev)})
-        else:
-            st = synth.mamba2_step_inputs(sh, seed, cfg_id, p)
-            pool.append({"v": bf(st["v"]), "k": bf(st["k"]), "q": bf(st["q"]),
-                         "dt": torch.from_numpy(st["dt"]).to(dev)})
+        st = _draft_inputs(synth, sh, seed, cfg_id, p, gdn)
+        pool.append({k_: (bf(v_) if v_.dtype == np.uint16 else torch.from_numpy(np.ascontiguousarray(v_)).to(dev))
+                     for k_, v_ in st.items()})
     acc = synth.accept_draws(seed, cfg_id, R, B, T)
     dacc = [torch.from_numpy(acc[r]).to(dev) for r in range(R)]
     y = torch.empty((B, T, H, D), device=dev)
@@ -188,27 +193,10 @@ def _row_verify(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, rounds=
     round_s = (sum(v_us) + sum(r_us)) * 1e-6
     gbs = sum(byts) / (sum(v_us) * 1e-6) / 1e9
     base = None
-    if gdn:
+    if gdn and with_standard:
         # the baseline that rewrites the state every token, at the same shape
-        st1 = synth.gdn_round_inputs(sh.with_(T=1), seed, cfg_id, 0)
-        one = {k_: (bf(v_[:, 0]) if v_.dtype == np.uint16 else torch.from_numpy(np.ascontiguousarray(v_[:, 0])).to(dev))
-               for k_, v_ in st1.items()}
-        y1 = torch.empty((B, H, D), device=dev)
-        for _ in range(4):
-            rd.gdn_decode_step(dims, layers[0]["S0"], one["v"], one["k"], one["q"], one["g"], one["beta"], y1,
-                               stream=stream)
-        ev1 = _events(torch, 16)
-        torch.cuda.synchronize()
-        for i in range(16):
-            ev1[i][0].record(stream)
-            rd.gdn_decode_step(dims, layers[i % NLr]["S0"], one["v"], one["k"], one["q"], one["g"],
-                               one["beta"], y1, stream=stream)
-            ev1[i][1].record(stream)
-        torch.cuda.synchronize()
-        su = float(np.mean([1e3 * a_.elapsed_time(b_) for a_, b_ in ev1]))
-        sb = traffic.gdn_standard_step(B, H, D, N, G)
-        base = {"kernel": "gdn_decode_step", "us": round(su, 3), "GBs": round(sb / (su * 1e-6) / 1e9, 1),
-                "tokens_per_s": round(B / (su * 1e-6), 1)}
+        base = _standard_step_row(torch, np, rd, synth, traffic, dev, stream, cfg_id, True,
+                                  [Ly["S0"] for Ly in layers])
     res = {"workload": ("Gated DeltaNet" if gdn else "Mamba-2") +
                        f" speculative verify, batch {B}, {H} heads, head dim {D}, state {N}, "
                        f"{G} group(s), ring capacity {L}, T={T}; two layer instances rotated",
@@ -224,6 +212,140 @@ def _row_verify(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, rounds=
     if base is not None:
         res["standard_step"] = base
     return res
+
+
+def _standard_step_row(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, states, reps=16):
+    """One-token standard decode (state read and rewritten) at a workload's shape,
+    rotated over the given state tensors; mean of per-launch HIP-event times."""
+    wl = synth.WORKLOADS[cfg_id]
+    sh, seed = wl.shape.with_(T=1), wl.cfg_seed
+    B, H, D, N, G = sh.batch, sh.nheads, sh.head_dim, sh.state_dim, sh.ngroups
+    dims = rd.Dims(B, H, D, N, G, sh.capacity)
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    y1 = torch.empty((B, H, D), device=dev)
+    if gdn:
+        st = synth.gdn_round_inputs(sh, seed, cfg_id, 0)
+        one = {k_: (bf(v_[:, 0]) if v_.dtype == np.uint16 else torch.from_numpy(np.ascontiguousarray(v_[:, 0])).to(dev))
+               for k_, v_ in st.items()}
+
+        def call(i):
+            rd.gdn_decode_step(dims, states[i % len(states)], one["v"], one["k"], one["q"], one["g"],
+                               one["beta"], y1, stream=stream)
+        name, byts = "gdn_decode_step", traffic.gdn_standard_step(B, H, D, N, G)
+    else:
+        st = synth.mamba2_step_inputs(sh, seed, cfg_id, 0)
+        A, bias = synth.mamba2_head_params(sh, seed, cfg_id)
+        one = {k_: (bf(v_) if v_.dtype == np.uint16 else torch.from_numpy(v_).to(dev)) for k_, v_ in st.items()}
+        A, bias = torch.from_numpy(A).to(dev), torch.from_numpy(bias).to(dev)
+
+        def call(i):
+            rd.ssm_decode_step(dims, states[i % len(states)], one["v"], one["k"], one["q"], one["dt"], bias, A,
+                               y1, stream=stream)
+        name, byts = "ssm_decode_step", traffic.standard_step(B, H, D, N, G)
+    for i in range(4):
+        call(i)
+    ev = _events(torch, reps)
+    torch.cuda.synchronize()
+    for i in range(reps):
+        ev[i][0].record(stream)
+        call(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    su = float(np.mean([1e3 * a_.elapsed_time(b_) for a_, b_ in ev]))
+    return {"kernel": name, "us": round(su, 3), "GBs": round(byts / (su * 1e-6) / 1e9, 1),
+            "tokens_per_s": round(B / (su * 1e-6), 1)}
+
+
+def _snapshot_rounds(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, T, rounds, warm):
+    """The per-draft snapshot route (verify + device-side commit) at a workload's
+    shape with window T, on two rotated layer instances of T + 1 state slots per
+    request; per-launch HIP-event times."""
+    wl = synth.WORKLOADS[cfg_id]
+    sh, seed = wl.shape.with_(T=T), wl.cfg_seed
+    B, H, D, N, G = sh.batch, sh.nheads, sh.head_dim, sh.state_dim, sh.ngroups
+    NLr, P, R, nslots = 2, 8, warm + rounds, T + 1
+    dims = rd.Dims(B, H, D, N, G, sh.capacity)
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    gen = torch.Generator(device=dev)
+    layers = []
+    for l in range(NLr):
+        gen.manual_seed(seed * 100 + l)
+        pool_l = torch.empty((B, nslots, H, D, N), device=dev)
+        pool_l[:, 0] = torch.randn((B, H, D, N), generator=gen, device=dev) * math.sqrt(0.1)
+        layers.append({"pool": pool_l, "slot": torch.zeros((B,), dtype=torch.int32, device=dev)})
+        if not gdn:
+            A, bias = synth.mamba2_head_params(sh, seed, cfg_id, layer=l)
+            layers[-1]["A"], layers[-1]["bias"] = torch.from_numpy(A).to(dev), torch.from_numpy(bias).to(dev)
+    ins = []
+    for p in range(P):
+        st = _draft_inputs(synth, sh, seed, cfg_id, p, gdn)
+        ins.append({k_: (bf(v_) if v_.dtype == np.uint16 else torch.from_numpy(np.ascontiguousarray(v_)).to(dev))
+                    for k_, v_ in st.items()})
+    acc = synth.accept_draws(seed, cfg_id, R, B, T)
+    dacc = [torch.from_numpy(acc[r]).to(dev) for r in range(R)]
+    y = torch.empty((B, T, H, D), device=dev)
+    err = torch.zeros((1,), dtype=torch.int32, device=dev)
+    ev_v, ev_c = _events(torch, R), _events(torch, R)
+    torch.cuda.synchronize()
+    for r in range(R):
+        Ly, ip = layers[r % NLr], ins[r % P]
+        ev_v[r][0].record(stream)
+        if gdn:
+            rd.gdn_snapshot_verify_T(dims, T, Ly["pool"], Ly["slot"], ip["v"], ip["k"], ip["q"], ip["g"],
+                                     ip["beta"], y, err, stream=stream)
+        else:
+            rd.ssm_snapshot_verify_T(dims, T, Ly["pool"], Ly["slot"], ip["v"], ip["k"], ip["q"], ip["dt"],
+                                     Ly["bias"], Ly["A"], y, err, stream=stream)
+        ev_v[r][1].record(stream)
+        rd.snapshot_commit(T, nslots, Ly["slot"], dacc[r], err, stream=stream)
+        ev_c[r][1].record(stream)
+    torch.cuda.synchronize()
+    if int(err.item()) != 0:
+        raise RuntimeError("snapshot route anomaly bits set")
+    v_us = [1e3 * ev_v[r][0].elapsed_time(ev_v[r][1]) for r in range(warm, R)]
+    c_us = [1e3 * ev_v[r][1].elapsed_time(ev_c[r][1]) for r in range(warm, R)]
+    byts = traffic.snapshot_verify(B, H, D, N, G, T, gdn)
+    us = sum(v_us) / rounds
+    return {"kernel": "gdn_snapshot_verify_T" if gdn else "ssm_snapshot_verify_T", "verify_us": round(us, 3),
+            "commit_us": round(sum(c_us) / rounds, 3), "achieved_GBs": round(byts / (us * 1e-6) / 1e9, 1),
+            "alg_bytes_per_round": byts}
+
+
+def _row_window(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, Ts=(1, 2, 3, 4, 5, 6), rounds=24,
+                warm=8):
+    """Kernel cost against the draft window: ReplaySSM verify and the per-draft
+    snapshot route for T = 1..6 at one workload's shape, each as a multiple of
+    the one-token standard decode step at that shape."""
+    wl = synth.WORKLOADS[cfg_id]
+    sh = wl.shape
+    B, H, D, N, G = sh.batch, sh.nheads, sh.head_dim, sh.state_dim, sh.ngroups
+    states = [torch.randn((B, H, D, N), device=dev) for _ in range(2)]
+    std = _standard_step_row(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, states)
+    del states
+    out = {"workload": ("Gated DeltaNet" if gdn else "Mamba-2") +
+                       f" verify against the draft window, batch {B}, {H} heads, head dim {D}, state {N}, "
+                       f"{G} group(s), ring capacity {sh.capacity}; two layer instances rotated; "
+                       f"acceptance uniform on 0..T",
+           "standard_step": std, "T": []}
+    for T in Ts:
+        rv = _row_verify(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, rounds=rounds, warm=warm, T=T,
+                         with_standard=False)
+        sn = _snapshot_rounds(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, T, rounds, warm)
+        out["T"].append({
+            "T": T, "replay_verify_us": rv["verify_us"], "replay_rollback_us": rv["rollback_us"],
+            "replay_GBs": rv["achieved_GBs"], "replay_flush_rate": rv["flush_rate"],
+            "snapshot_verify_us": sn["verify_us"], "snapshot_commit_us": sn["commit_us"],
+            "snapshot_GBs": sn["achieved_GBs"],
+            "replay_x_standard": round(rv["verify_us"] / std["us"], 3),
+            "snapshot_x_standard": round(sn["verify_us"] / std["us"], 3),
+            "speedup": round(sn["verify_us"] / rv["verify_us"], 3)})
+    return out
 
 
 def _row_sweep(torch, np, rd, synth, traffic, dev, stream, capacities=(4, 8, 16, 32)):
@@ -385,7 +507,9 @@ def _rows(torch, np, rd, synth, traffic, dev, stream):
     return {"speculative_verify": _row_verify(torch, np, rd, synth, traffic, dev, stream, 2, False),
             "gdn_speculative_verify": _row_verify(torch, np, rd, synth, traffic, dev, stream, 4, True),
             "capacity_sweep": _row_sweep(torch, np, rd, synth, traffic, dev, stream),
-            "explicit_flush": _row_flush(torch, np, rd, synth, traffic, dev, stream)}
+            "explicit_flush": _row_flush(torch, np, rd, synth, traffic, dev, stream),
+            "window_sweep": {"mamba2": _row_window(torch, np, rd, synth, traffic, dev, stream, 2, False),
+                             "gdn": _row_window(torch, np, rd, synth, traffic, dev, stream, 4, True)}}
 
 
 def main(argv=None) -> int:

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define RSSM_ABI_VERSION 3
+#define RSSM_ABI_VERSION 4
 
 #define RSSM_OK 0
 #define RSSM_EINVAL (-22)
@@ -248,6 +248,47 @@ int gdn_replay_verify_T(const rssm_dims* dims, int32_t T, float* state0, rssm_ri
  */
 int gdn_replay_flush(const rssm_dims* dims, float* state0, rssm_ring* ring, const int32_t* mask,
                      void* stream);
+
+/* ---------------------------------------------------------- speculative baseline */
+
+/*
+ * The speculative-decoding route that ReplaySSM replaces (background, "the cost
+ * of summarising": one full state snapshot kept per draft and restored on
+ * rejection; algorithms, "speculative decoding", baseline bullet: serial state
+ * update per draft position).  Every request owns nslots = P >= T + 1 state
+ * slots and slot[b] names the committed one.  The T drafts run serially from it
+ * and the state after draft s is stored, whole, into slot (slot[b] + 1 + s) mod P;
+ *     y_s = S_s q_s,  S_s the state after drafts 0..s.
+ * Restoring the snapshot of the last accepted draft is snapshot_commit's move of
+ * slot[b].  Per head and round: 4dn bytes read, T * 4dn bytes written.
+ *   pool  fp32 [B, P, H, d, n]: slot[b] read, the T slots after it overwritten
+ *   slot  int32 [B] (device), read only here; outside [0, P) it is reduced mod P
+ *         and RSSM_ERR_POINTERS is OR-ed into *err (err may be NULL)
+ *   Mamba-2: v bf16 [B, T, H, d]; k, q bf16 [B, T, G, n]; dt fp32 [B, T, H] raw;
+ *            dt_bias, A fp32 [H] (as ssm_decode_step)
+ *   GDN:     v, k, q as above; g, beta fp32 [B, T, H] (as gdn_decode_step)
+ *   y fp32 [B, T, H, d] out
+ * dims->capacity is not used.  Requires 1 <= T <= 8 and nslots >= T + 1.
+ */
+int ssm_snapshot_verify_T(const rssm_dims* dims, int32_t T, int32_t nslots, float* pool,
+                          const int32_t* slot, const uint16_t* v, const uint16_t* k,
+                          const uint16_t* q, const float* dt, const float* dt_bias, const float* A,
+                          float* y, int32_t* err, void* stream);
+int gdn_snapshot_verify_T(const rssm_dims* dims, int32_t T, int32_t nslots, float* pool,
+                          const int32_t* slot, const uint16_t* v, const uint16_t* k,
+                          const uint16_t* q, const float* g, const float* beta, float* y,
+                          int32_t* err, void* stream);
+
+/*
+ * Commit of the snapshot route, on the device: for every request
+ *     slot[b] <- (slot[b] + clamp(accepted[b], 0, T)) mod nslots,
+ * so the snapshot after the last accepted draft becomes the committed state
+ * (accepted 0 keeps the old one).  Out-of-range accepted or slot values are
+ * clamped / reduced and flagged (RSSM_ERR_ACCEPTED, RSSM_ERR_POINTERS) in *err.
+ *   slot int32 [B] in/out;  accepted int32 [B];  err int32 [1], may be NULL
+ */
+int snapshot_commit(int32_t batch, int32_t T, int32_t nslots, int32_t* slot,
+                    const int32_t* accepted, int32_t* err, void* stream);
 
 /* ---------------------------------------------------------- causal conv1d */
 

@@ -19,7 +19,7 @@ RSSM_ELAUNCH = -5
 RSSM_ERR_POINTERS = 1
 RSSM_ERR_ACCEPTED = 2
 RSSM_ERR_PENDING = 4
-ABI_VERSION = 3  # RSSM_ABI_VERSION of the header this binding follows
+ABI_VERSION = 4  # RSSM_ABI_VERSION of the header this binding follows
 
 
 class rssm_dims(ctypes.Structure):
@@ -49,6 +49,9 @@ SIGNATURES = {
     "gdn_decode_step": (c_int, [_D, _P, _P, _P, _P, _P, _P, _P, _P]),
     "gdn_replay_verify_T": (c_int, [_D, c_int32, _P, _R, _P, _P, _P, _P, _P, _P, _P, _P]),
     "gdn_replay_flush": (c_int, [_D, _P, _R, _P, _P]),
+    "ssm_snapshot_verify_T": (c_int, [_D, c_int32, c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "gdn_snapshot_verify_T": (c_int, [_D, c_int32, c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "snapshot_commit": (c_int, [c_int32, c_int32, c_int32, _P, _P, _P, _P]),
     "causal_conv1d_update": (c_int, [c_int32, c_int32, c_int32, _P, _P, _P, _P, _P]),
     "rssm_probe_copy": (c_int, [_P, _P, c_size_t, _P]),
     "rssm_probe_read": (c_int, [_P, c_size_t, _P, _P]),

@@ -235,6 +235,43 @@ def gdn_replay_flush(dims: Dims, state0, ring: Ring, mask=None, stream=None):
         _p(mask, "mask", _I32, (B,), allow_none=True), _stream(stream)), "gdn_replay_flush")
 
 
+# ------------------------------------------------------------------ snapshot baseline
+def _snapshot_args(dims: Dims, T: int, pool, slot, v, k, q, err):
+    B, H, D, N, G = dims.batch, dims.nheads, dims.head_dim, dims.state_dim, dims.ngroups
+    if not isinstance(pool, torch.Tensor) or pool.dim() != 5:
+        raise ValueError("pool must be a [B, P, H, d, n] tensor")
+    P = int(pool.shape[1])
+    return P, (_p(pool, "pool", _F32, (B, P, H, D, N)), _p(slot, "slot", _I32, (B,)),
+               _p(v, "v", _BF16, (B, T, H, D)), _p(k, "k", _BF16, (B, T, G, N)),
+               _p(q, "q", _BF16, (B, T, G, N)))
+
+
+def ssm_snapshot_verify_T(dims: Dims, T: int, pool, slot, v, k, q, dt, dt_bias, A, y, err=None,
+                          stream=None):
+    B, H, D = dims.batch, dims.nheads, dims.head_dim
+    P, args = _snapshot_args(dims, T, pool, slot, v, k, q, err)
+    rest = (_p(dt, "dt", _F32, (B, T, H)), _p(dt_bias, "dt_bias", _F32, (H,)), _p(A, "A", _F32, (H,)),
+            _p(y, "y", _F32, (B, T, H, D)), _p(err, "err", _I32, (1,), allow_none=True))
+    _lib.check(_lib.load().ssm_snapshot_verify_T(ctypes.byref(dims.c()), int(T), P, *args, *rest,
+                                                 _stream(stream)), "ssm_snapshot_verify_T")
+
+
+def gdn_snapshot_verify_T(dims: Dims, T: int, pool, slot, v, k, q, g, beta, y, err=None, stream=None):
+    B, H, D = dims.batch, dims.nheads, dims.head_dim
+    P, args = _snapshot_args(dims, T, pool, slot, v, k, q, err)
+    rest = (_p(g, "g", _F32, (B, T, H)), _p(beta, "beta", _F32, (B, T, H)),
+            _p(y, "y", _F32, (B, T, H, D)), _p(err, "err", _I32, (1,), allow_none=True))
+    _lib.check(_lib.load().gdn_snapshot_verify_T(ctypes.byref(dims.c()), int(T), P, *args, *rest,
+                                                 _stream(stream)), "gdn_snapshot_verify_T")
+
+
+def snapshot_commit(T: int, nslots: int, slot, accepted, err=None, stream=None):
+    B = int(slot.shape[0])
+    _lib.check(_lib.load().snapshot_commit(
+        B, int(T), int(nslots), _p(slot, "slot", _I32, (B,)), _p(accepted, "accepted", _I32, (B,)),
+        _p(err, "err", _I32, (1,), allow_none=True), _stream(stream)), "snapshot_commit")
+
+
 # ------------------------------------------------------------------ conv1d
 def causal_conv1d_update(conv_state, x, weight, out, stream=None):
     if conv_state.dim() != 3:

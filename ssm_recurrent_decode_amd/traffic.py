@@ -78,6 +78,16 @@ def gdn_standard_step(B, H, d, n, G) -> int:
     return B * (2 * F32 * H * d * n + BF16 * H * d + 2 * BF16 * G * n + 2 * F32 * H + F32 * H * d)
 
 
+def snapshot_verify(B, H, d, n, G, T, gdn: bool = False) -> int:
+    """ssm_snapshot_verify_T / gdn_snapshot_verify_T: the committed state read once,
+    T full snapshots written, T drafts in (Mamba-2: dt; GDN: g and beta), T outputs,
+    the slot index read; per-head A and dt_bias for Mamba-2."""
+    scal = (2 if gdn else 1) * F32 * H
+    per_req = (F32 * H * d * n + T * F32 * H * d * n
+               + T * (BF16 * H * d + 2 * BF16 * G * n + scal) + T * F32 * H * d + 4)
+    return B * per_req + (0 if gdn else 2 * F32 * H)
+
+
 def conv1d(B, C, W) -> int:
     """conv state read + write (bf16), x in (bf16), out (fp32), taps (bf16, shared)."""
     return B * C * (2 * BF16 * (W - 1) + BF16 + F32) + C * W * BF16

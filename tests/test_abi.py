@@ -32,7 +32,7 @@ def test_every_declared_function_is_exported_and_prototyped():
 
 def test_abi_version_and_strerror():
     lib = _lib.load()
-    assert lib.rssm_abi_version() == _lib.ABI_VERSION == 3
+    assert lib.rssm_abi_version() == _lib.ABI_VERSION == 4
     assert "invalid" in _lib.strerror(_lib.RSSM_EINVAL)
     assert "not supported" in _lib.strerror(_lib.RSSM_ENOTSUP)
 
@@ -104,6 +104,19 @@ def test_host_validation_codes():
     r_odd.meta = FAKE.value + 64
     assert lib.replay_rollback(ctypes.byref(d), ctypes.byref(r_odd), P, None) == EINVAL
     assert lib.rssm_ring_reset(ctypes.byref(d), ctypes.byref(r_odd), None, None) == EINVAL
+
+    # snapshot route: T in [1, 8], nslots >= T + 1, slot and pool present
+    for T, nslots, code in ((0, 4, EINVAL), (4, 4, EINVAL), (9, 10, ENOTSUP), (4, 5, ENOTSUP)):
+        dd = _dims(d=96) if code == ENOTSUP and T == 4 else d
+        assert lib.ssm_snapshot_verify_T(ctypes.byref(dd), T, nslots, P, P, P, P, P, P, P, P, P,
+                                         None, None) == code
+        assert lib.gdn_snapshot_verify_T(ctypes.byref(dd), T, nslots, P, P, P, P, P, P, P, P,
+                                         None, None) == code
+    assert lib.ssm_snapshot_verify_T(ctypes.byref(d), 2, 3, P, None, P, P, P, P, P, P, P,
+                                     None, None) == EINVAL
+    assert lib.snapshot_commit(4, 2, 2, P, P, None, None) == EINVAL
+    assert lib.snapshot_commit(4, 2, 3, P, None, None, None) == EINVAL
+    assert lib.snapshot_commit(0, 2, 3, P, P, None, None) == EINVAL
 
     # probes
     assert lib.rssm_probe_copy(P, P, 15, None) == EINVAL

@@ -263,3 +263,62 @@ def test_config4_gdn_verify_full():
         S, y_ref = o_gdn.householder_step(S, sub["v"], sub["k"], sub["q"], sub["g"], sub["beta"], 1)
         assert rel_err(yd[tb, th].cpu().numpy(), y_ref[:, 0]) <= Y_TOL, t
     assert rel_err(state0[tb, th].cpu().numpy(), S[:, 0]) <= S_TOL
+
+
+@pytest.mark.parametrize("gdn", [False, True])
+def test_snapshot_route_full(gdn):
+    """The per-draft snapshot route at the speculative workloads' full sizes
+    (Mamba-2 B=512, H=32, d=64, G=1; GDN B=256, H=32, d=128, G=32; T=4, T + 1
+    slots per request), 32 rounds with seeded acceptance and the device-side
+    commit: sampled y every round, the committed snapshot of the sampled pairs
+    every 8 rounds, every request's slot index every round."""
+    cid = 4 if gdn else 2
+    wl = synth.WORKLOADS[cid]
+    sh = wl.shape
+    B, H, D, N, G, T = sh.batch, sh.nheads, sh.head_dim, sh.state_dim, sh.ngroups, sh.T
+    P, R = T + 1, 32
+    S0 = synth.state0(sh, wl.cfg_seed, cid)
+    acc = synth.accept_draws(wl.cfg_seed, cid, R, B, T)
+    pairs = sample_pairs(B, H, NPAIRS, seed=55 + cid)
+    bi, hi, gi = _pairs_arrays(pairs, H, G)
+    tb, th = pair_index(pairs)
+    dims = rd.Dims(B, H, D, N, G, sh.capacity)
+    pool_d = torch.empty(B, P, H, D, N, device="cuda")
+    pool_d[:, 0] = dev_f32(S0)
+    del S0
+    slot = torch.zeros(B, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    y = torch.empty(B, T, H, D, device="cuda")
+    S = pool_d[tb, 0, th].cpu().numpy().astype(np.float64)[:, None]
+    if not gdn:
+        A, bias = synth.mamba2_head_params(sh, wl.cfg_seed, cid)
+        Ab, biasb = dev_f32(A), dev_f32(bias)
+        A_sub, bias_sub = A[hi].astype(np.float64)[:, None], bias[hi].astype(np.float64)[:, None]
+    cur = np.zeros(B, np.int64)
+    for r in range(R):
+        if gdn:
+            st = synth.gdn_round_inputs(sh, wl.cfg_seed, cid, r % 8)
+            ip = _dev_step(st)
+            rd.gdn_snapshot_verify_T(dims, T, pool_d, slot, ip["v"], ip["k"], ip["q"], ip["g"], ip["beta"], y, err)
+            sub = {"v": _f64(st["v"][bi, :, hi])[:, :, None], "k": _f64(st["k"][bi, :, gi])[:, :, None],
+                   "q": _f64(st["q"][bi, :, gi])[:, :, None],
+                   "g": st["g"][bi, :, hi].astype(np.float64)[:, :, None],
+                   "beta": st["beta"][bi, :, hi].astype(np.float64)[:, :, None]}
+            y_ref, S = o_gdn.spec_round_snapshot(S, sub, 1, acc[r, bi])
+        else:
+            st = synth.mamba2_step_inputs(sh, wl.cfg_seed, cid, r % 8)
+            ip = _dev_step(st)
+            rd.ssm_snapshot_verify_T(dims, T, pool_d, slot, ip["v"], ip["k"], ip["q"], ip["dt"], biasb, Ab, y,
+                                     err)
+            y_ref, S = o_m2.spec_round_snapshot(S, _sub_step(st, bi, hi, gi, True), bias_sub, A_sub, 1,
+                                                acc[r, bi])
+        e = rel_err(y[tb, :, th].cpu().numpy(), y_ref[:, :, 0])
+        assert e <= Y_TOL, (r, e)
+        rd.snapshot_commit(T, P, slot, dev_i32(acc[r]), err)
+        cur = (cur + acc[r]) % P
+        assert np.array_equal(slot.cpu().numpy(), cur), r
+        if r % 8 == 7:
+            got = pool_d[tb, slot[tb].long(), th].cpu().numpy()
+            es = rel_err(got, S[:, 0])
+            assert es <= S_TOL, (r, es)
+    assert int(err.item()) == 0
