@@ -12,6 +12,12 @@
 namespace rssm {
 
 // ======================================================= ReplaySSM
+// Draft windows from this size up combine on the matrix cores.  The MFMA chain
+// costs as many cycles as the vector dot products at T = 4 (measured: no gain
+// for T <= 4), but it needs far fewer registers: at T = 5 and 6 it keeps one
+// more wave per SIMD resident (T = 5: 187 -> 167 us per round at B = 512).
+constexpr int kMfmaCombineMinT = 5;
+
 struct ReplayParams {
   float* state0;
   uint16_t* ring_v;
@@ -253,30 +259,71 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const int row = (wave * RT + rt) * 16 + r;
-      vj[rt][m] = used ? bf16_to_f32(s_v[min(sl, LCAP - 1) * D + row]) : 0.f;
+      const float x = bf16_to_f32(s_v[min(sl, LCAP - 1) * D + row]);  // read unconditionally
+      vj[rt][m] = used ? x : 0.f;
     }
   }
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int row = (wave * RT + rt) * 16 + r;
-    float dots[T];
-#pragma unroll
-    for (int sd = 0; sd < T; ++sd) dots[sd] = 0.f;
+  if constexpr (T >= kMfmaCombineMinT) {
+    // All drafts at once on the matrix cores, output tile = [16 state rows] x
+    // [16 drafts] (drafts >= T are zero columns).  S_0 Q: the state tile in
+    // registers is the A operand as it stands (K index cq <-> column
+    // 16 ct + 4 cq + e for the e-th MFMA of a column tile); B is the query of
+    // draft r at the same columns.  Then the ring part V (W o M) accumulates on
+    // top: A = the values vj, B = w_{j,r} M_{j,r} for slot j = cq + 4m.  Lane
+    // (cq, r) ends with y_r at rows 4cq .. 4cq + 3 of the tile.
+    const bool draft = r < T;
+    const int rd = min(r, T - 1);
+    uint2 qb[NCT];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
+      qb[ct] = draft ? *reinterpret_cast<const uint2*>(&s_q[rd * N + ct * 16 + cq * 4]) : make_uint2(0, 0);
+    float wm[VJ];
 #pragma unroll
-      for (int sd = 0; sd < T; ++sd)
-        dots[sd] += dot4_bf16(st[rt][ct], *reinterpret_cast<const uint2*>(&s_q[sd * N + ct * 16 + cq * 4]));
+    for (int m = 0; m < VJ; ++m) wm[m] = draft ? s_w[rd][cq + 4 * m] * s_M[rd][cq + 4 * m] : 0.f;
+    const float ab = draft ? s_abar[rd] : 0.f;
 #pragma unroll
-    for (int sd = 0; sd < T; ++sd) {
-      float part = s_abar[sd] * dots[sd];
+    for (int rt = 0; rt < RT; ++rt) {
+      v4f z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        z = mfma4(st[rt][ct].x, bf16_lo(qb[ct].x), z);
+        z = mfma4(st[rt][ct].y, bf16_hi(qb[ct].x), z);
+        z = mfma4(st[rt][ct].z, bf16_lo(qb[ct].y), z);
+        z = mfma4(st[rt][ct].w, bf16_hi(qb[ct].y), z);
+      }
+      z *= ab;
 #pragma unroll
       for (int m = 0; m < VJ; ++m) {
-        const int sl = cq + 4 * m;
-        part += s_w[sd][sl] * s_M[sd][sl] * vj[rt][m];  // zero for slots not read
+        if (4 * m >= L) break;  // physical slots; uniform across the work-group
+        z = mfma4(vj[rt][m], wm[m], z);
       }
-      part = reduce_row4(part);
-      if ((sd & 3) == cq) p.y[(((size_t)b * T + sd) * H + h) * D + row] = part;
+      if (draft)
+        st_f4(p.y + (((size_t)b * T + rd) * H + h) * D + (wave * RT + rt) * 16 + cq * 4,
+              make_float4(z[0], z[1], z[2], z[3]));
+    }
+  } else {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int row = (wave * RT + rt) * 16 + r;
+      float dots[T];
+#pragma unroll
+      for (int sd = 0; sd < T; ++sd) dots[sd] = 0.f;
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int sd = 0; sd < T; ++sd)
+          dots[sd] += dot4_bf16(st[rt][ct], *reinterpret_cast<const uint2*>(&s_q[sd * N + ct * 16 + cq * 4]));
+#pragma unroll
+      for (int sd = 0; sd < T; ++sd) {
+        float part = s_abar[sd] * dots[sd];
+#pragma unroll
+        for (int m = 0; m < VJ; ++m) {
+          const int sl = cq + 4 * m;
+          part += s_w[sd][sl] * s_M[sd][sl] * vj[rt][m];  // zero for slots not read
+        }
+        part = reduce_row4(part);
+        if ((sd & 3) == cq) p.y[(((size_t)b * T + sd) * H + h) * D + row] = part;
+      }
     }
   }
   if (F > 0)
