@@ -431,6 +431,66 @@ def _row_sweep(torch, np, rd, synth, traffic, dev, stream, capacities=(4, 8, 16,
     return res
 
 
+def _row_gdn_append(torch, np, rd, synth, traffic, dev, stream):
+    """GDN standard decode through the ring (gdn_replay_append_decode) at the GDN
+    workload's shape, flush and non-flush steps reported separately, against the
+    standard GDN step; two layer instances rotated."""
+    wl = synth.WORKLOADS[4]
+    sh, seed = wl.shape.with_(T=1), wl.cfg_seed
+    B, H, D, N, G, L = sh.batch, sh.nheads, sh.head_dim, sh.state_dim, sh.ngroups, sh.capacity
+    NLs, P = 2, 4
+    dims = rd.Dims(B, H, D, N, G, L)
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    gen = torch.Generator(device=dev)
+    S0s = []
+    for l in range(NLs):
+        gen.manual_seed(seed * 100 + l)
+        S0s.append(torch.randn((B, H, D, N), generator=gen, device=dev) * math.sqrt(0.1))
+    ins = []
+    for p_ in range(P):
+        st = synth.gdn_round_inputs(sh, seed, 4, p_)
+        ins.append({k_: (bf(v_[:, 0]) if v_.dtype == np.uint16 else torch.from_numpy(np.ascontiguousarray(v_[:, 0])).to(dev))
+                    for k_, v_ in st.items()})
+    rings = [rd.Ring(dims, gdn=True, device=dev) for _ in range(NLs)]
+    y = torch.empty((B, H, D), device=dev)
+
+    def call(t):
+        ip = ins[(t // NLs) % P]
+        rd.gdn_replay_append_decode(dims, S0s[t % NLs], rings[t % NLs], ip["v"], ip["k"], ip["q"], ip["g"],
+                                    ip["beta"], y, stream=stream)
+    warm, K = NLs * L, NLs * L * 4
+    for t in range(warm):
+        call(t)
+    ev = _events(torch, K)
+    torch.cuda.synchronize()
+    for i in range(K):
+        ev[i][0].record(stream)
+        call(warm + i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    if any(int(r_.err.item()) for r_ in rings):
+        raise RuntimeError("ring anomaly bits set in the GDN append row")
+    us = np.array([1e3 * a_.elapsed_time(b_) for a_, b_ in ev])
+    h = np.array([((warm + i) // NLs) % L for i in range(K)])
+    fl = h == L - 1
+    byts = np.array([traffic.gdn_append(B, H, D, N, G, int(x), bool(x == L - 1)) for x in h])
+    std = _standard_step_row(torch, np, rd, synth, traffic, dev, stream, 4, True, S0s)
+    return {"workload": f"Gated DeltaNet append-decode (flush when full), batch {B}, {H} heads, head dim {D}, "
+                        f"state {N}, {G} groups, ring capacity {L}; two layer instances rotated",
+            "kernel": "gdn_replay_append_decode", "steps_timed": K,
+            "nonflush_us": round(float(us[~fl].mean()), 3),
+            "nonflush_GBs": round(float(byts[~fl].sum() / (us[~fl].sum() * 1e-6) / 1e9), 1),
+            "flush_us": round(float(us[fl].mean()), 3),
+            "flush_GBs": round(float(byts[fl].sum() / (us[fl].sum() * 1e-6) / 1e9), 1),
+            "avg_us": round(float(us.mean()), 3),
+            "avg_GBs": round(float(byts.sum() / (us.sum() * 1e-6) / 1e9), 1),
+            "tokens_per_s": round(float(B / (us.mean() * 1e-6)), 1),
+            "standard_step": std, "speedup": round(std["us"] / float(us.mean()), 3)}
+
+
 def _row_flush(torch, np, rd, synth, traffic, dev, stream, reps=8):
     """Explicit flush of full rings: Mamba-2 at the Nemotron-H shape after L - 1
     appends, GDN at its verify shape after three fully accepted verify rounds
@@ -508,6 +568,7 @@ def _rows(torch, np, rd, synth, traffic, dev, stream):
             "gdn_speculative_verify": _row_verify(torch, np, rd, synth, traffic, dev, stream, 4, True),
             "capacity_sweep": _row_sweep(torch, np, rd, synth, traffic, dev, stream),
             "explicit_flush": _row_flush(torch, np, rd, synth, traffic, dev, stream),
+            "gdn_append_decode": _row_gdn_append(torch, np, rd, synth, traffic, dev, stream),
             "window_sweep": {"mamba2": _row_window(torch, np, rd, synth, traffic, dev, stream, 2, False),
                              "gdn": _row_window(torch, np, rd, synth, traffic, dev, stream, 4, True)}}
 

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define RSSM_ABI_VERSION 4
+#define RSSM_ABI_VERSION 5
 
 #define RSSM_OK 0
 #define RSSM_EINVAL (-22)
@@ -239,6 +239,24 @@ int gdn_decode_step(const rssm_dims* dims, float* state, const uint16_t* v, cons
 int gdn_replay_verify_T(const rssm_dims* dims, int32_t T, float* state0, rssm_ring* ring,
                         const uint16_t* v, const uint16_t* k, const uint16_t* q, const float* g,
                         const float* beta, float* y, int32_t* flushed, void* stream);
+
+/*
+ * ReplaySSM GDN standard decode, one token per request (appendix, "GDN standard
+ * decode"; method, "core idea": flush when the ring is full).  With the c
+ * entries since the checkpoint, S_c = abar S_0 + sum_j w_j u_j k_j^T read only
+ * through S_c k and S_c q:
+ *     u = beta (v - alpha S_c k),  y = alpha S_c q + (k . q) u,  alpha = e^g;
+ * (u, k, alpha) is cached as entry c and committed in the same call (count + 1).
+ * When this append fills the ring (c + 1 == L) the same call folds all L entries:
+ * S_0 <- prod alpha S_0 + sum_j w_j u_j k_j^T, count = 0.
+ *   state0 fp32 [B, H, d, n];  ring GDN ring, pending == 0 and count < L on entry
+ *   v bf16 [B, H, d];  k, q bf16 [B, G, n];  g, beta fp32 [B, H] (as gdn_decode_step)
+ *   y fp32 [B, H, d] out;  flushed int32 [B] out, may be NULL
+ */
+int gdn_replay_append_decode(const rssm_dims* dims, float* state0, rssm_ring* ring,
+                             const uint16_t* v, const uint16_t* k, const uint16_t* q,
+                             const float* g, const float* beta, float* y, int32_t* flushed,
+                             void* stream);
 
 /*
  * Explicit GDN flush (appendix, state-and-output route): for requests with

@@ -19,7 +19,7 @@ RSSM_ELAUNCH = -5
 RSSM_ERR_POINTERS = 1
 RSSM_ERR_ACCEPTED = 2
 RSSM_ERR_PENDING = 4
-ABI_VERSION = 4  # RSSM_ABI_VERSION of the header this binding follows
+ABI_VERSION = 5  # RSSM_ABI_VERSION of the header this binding follows
 
 
 class rssm_dims(ctypes.Structure):
@@ -48,6 +48,7 @@ SIGNATURES = {
     "replay_rollback": (c_int, [_D, _R, _P, _P]),
     "gdn_decode_step": (c_int, [_D, _P, _P, _P, _P, _P, _P, _P, _P]),
     "gdn_replay_verify_T": (c_int, [_D, c_int32, _P, _R, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "gdn_replay_append_decode": (c_int, [_D, _P, _R, _P, _P, _P, _P, _P, _P, _P, _P]),
     "gdn_replay_flush": (c_int, [_D, _P, _R, _P, _P]),
     "ssm_snapshot_verify_T": (c_int, [_D, c_int32, c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "gdn_snapshot_verify_T": (c_int, [_D, c_int32, c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),

@@ -227,6 +227,18 @@ def gdn_replay_verify_T(dims: Dims, T: int, state0, ring: Ring, v, k, q, g, beta
                "gdn_replay_verify_T")
 
 
+def gdn_replay_append_decode(dims: Dims, state0, ring: Ring, v, k, q, g, beta, y, flushed=None,
+                             stream=None):
+    B, H, D, N, G = dims.batch, dims.nheads, dims.head_dim, dims.state_dim, dims.ngroups
+    d, rc = dims.c(), _ring_args(dims, ring, True)
+    args = (_p(state0, "state0", _F32, (B, H, D, N)), ctypes.byref(rc),
+            _p(v, "v", _BF16, (B, H, D)), _p(k, "k", _BF16, (B, G, N)), _p(q, "q", _BF16, (B, G, N)),
+            _p(g, "g", _F32, (B, H)), _p(beta, "beta", _F32, (B, H)), _p(y, "y", _F32, (B, H, D)),
+            _p(flushed, "flushed", _I32, (B,), allow_none=True))
+    _lib.check(_lib.load().gdn_replay_append_decode(ctypes.byref(d), *args, _stream(stream)),
+               "gdn_replay_append_decode")
+
+
 def gdn_replay_flush(dims: Dims, state0, ring: Ring, mask=None, stream=None):
     B, H, D, N = dims.batch, dims.nheads, dims.head_dim, dims.state_dim
     d, rc = dims.c(), _ring_args(dims, ring, True)

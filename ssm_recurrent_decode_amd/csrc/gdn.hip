@@ -213,6 +213,27 @@ extern "C" int gdn_replay_verify_T(const rssm_dims* dims, int32_t T, float* stat
   return rssm_host::launch_gdn_verify_hi(T, dims->head_dim, p, dims->batch, stream);
 }
 
+extern "C" int gdn_replay_append_decode(const rssm_dims* dims, float* state0, rssm_ring* ring,
+                                        const uint16_t* v, const uint16_t* k, const uint16_t* q,
+                                        const float* g, const float* beta, float* y, int32_t* flushed,
+                                        void* stream) {
+  if (!rssm_host::dims_ok(dims) || !rssm_host::ring_ok(ring) || !state0 || !v || !k || !q ||
+      !g || !beta || !y)
+    return RSSM_EINVAL;
+  if (dims->capacity < 1) return RSSM_EINVAL;
+  if (!rssm_host::ring_shape_supported(dims)) return RSSM_ENOTSUP;
+  GdnReplayParams p = make_gdn_params(dims, state0, ring);
+  p.v = v;
+  p.k = k;
+  p.q = q;
+  p.g = g;
+  p.beta = beta;
+  p.y = y;
+  p.flushed = flushed;
+  if (dims->head_dim == 64) return rssm_host::launch_gdn_window<64, 1, true>(p, dims->batch, stream);
+  return rssm_host::launch_gdn_window<128, 1, true>(p, dims->batch, stream);
+}
+
 extern "C" int gdn_replay_flush(const rssm_dims* dims, float* state0, rssm_ring* ring,
                                 const int32_t* mask, void* stream) {
   if (!rssm_host::dims_ok(dims) || !rssm_host::ring_ok(ring) || !state0) return RSSM_EINVAL;

@@ -30,6 +30,10 @@ struct GdnReplayParams {
 
 // One verify round of T drafts, one work-group of four waves per (request, head).
 // Entries in logical order: the c committed ones (ring), then the T drafts.
+// APPEND (T == 1, standard decode): the token is committed in the same call
+// (count <- c + 1, pending stays 0) and the ring is flushed when the append
+// fills it, the new entry included (S_0 <- prod alpha S_0 + sum_j w_j u_j k_j^T
+// over all L entries, after the new correction is known).
 //   committed-state readouts  S_c x = abar S_0 x + sum_{j<c} w_j u_j (k_j . x),
 //     abar = prod_{i<c} alpha_i,  w_j = prod_{j<i<c} alpha_i,  x in {k_s, q_s};
 //   R_s = beta_s (v_s - gamma_s S_c k_s),  gamma_s = prod_{s'<=s} alpha'_s';
@@ -47,9 +51,10 @@ struct GdnReplayParams {
 // pointer word is in; the weights proceed while the checkpoint is in flight.  The 2T readouts S_0 x run on
 // the matrix cores from the state registers; the fold (when flushing) follows
 // from the same registers; the per-row solve runs one thread per row after that.
-template <int D, int N, int T, int LCAP>
+template <int D, int N, int T, int LCAP, bool APPEND = false>
 __global__ __launch_bounds__(kBlock) void gdn_verify_kernel(GdnReplayParams p) {
   static_assert(N == 128, "key staging assumes n = 128");
+  static_assert(!APPEND || T == 1, "append-decode is one token");
   static_assert(2 * T <= 16, "readout vectors must fit one MFMA M axis");
   static_assert(D <= kBlock, "one thread per state row in the solve");
   static_assert(LCAP == 16 || LCAP == 32, "ring capacity bound");
@@ -67,6 +72,8 @@ __global__ __launch_bounds__(kBlock) void gdn_verify_kernel(GdnReplayParams p) {
   __shared__ float s_M[NV][LCAP];         // k_slot . x_v by physical slot
   __shared__ float s_w[LCAP];             // w_j by physical slot, zero if not committed
   __shared__ float s_abar;
+  __shared__ float s_fw[APPEND ? LCAP : 1];  // append flush: weights over all E entries
+  __shared__ float s_fabar;
   __shared__ float s_alpha_d[T];          // draft decays alpha'_s
   __shared__ float s_beta[T];
   __shared__ __attribute__((aligned(16))) uint16_t s_x[NV * N];     // readout vectors
@@ -132,13 +139,18 @@ __global__ __launch_bounds__(kBlock) void gdn_verify_kernel(GdnReplayParams p) {
     head %= L;
     bad |= RSSM_ERR_POINTERS;
   }
-  if (cnt > L - T) {
-    cnt = L - T;
+  const int cmax = APPEND ? L - 1 : L - T;
+  if (cnt > cmax) {
+    cnt = cmax;
     bad |= RSSM_ERR_POINTERS;
   }
   if (rp.pending != 0) bad |= RSSM_ERR_PENDING;
   const int c = cnt;
-  const bool do_flush = (c + 2 * T > L);
+  const int E = c + T;
+  // verify: early flush of the c committed entries; append: flush when full
+  const bool do_flush = APPEND ? (E == L) : (c + 2 * T > L);
+  const int F = do_flush ? (APPEND ? E : c) : 0;  // entries folded
+  const bool write_new = !(APPEND && do_flush);
   // logical entry held by physical slot sl (0 <= sl < L)
   auto logical = [&](int sl) { const int j = sl - head; return j < 0 ? j + L : j; };
 
@@ -172,6 +184,13 @@ __global__ __launch_bounds__(kBlock) void gdn_verify_kernel(GdnReplayParams p) {
     const float ex = prefix_product_excl(j < c ? al : 1.f, &all);
     if (j < LCAP) s_w[(j < L) ? sj : j] = (j < c) ? ex : 0.f;
     if (lane == 0) s_abar = all;
+    if constexpr (APPEND) {  // fold weights over the c committed entries and the new one
+      const float af = (j < c) ? al : expf(gd);
+      float allf;
+      const float exf = prefix_product_excl(j < F ? af : 1.f, &allf);
+      if (j < LCAP) s_fw[(j < L) ? sj : j] = (j < F) ? exf : 0.f;
+      if (lane == 0) s_fabar = allf;
+    }
     if (lane < T) {
       s_alpha_d[lane] = expf(gd);
       s_beta[lane] = bt;
@@ -191,14 +210,14 @@ __global__ __launch_bounds__(kBlock) void gdn_verify_kernel(GdnReplayParams p) {
     if (in_ring && sd >= 0 && sd < T) kv = *reinterpret_cast<const uint4*>(&s_x[sd * N + sub * 8]);
     if (in_ring)
       *reinterpret_cast<uint4*>(&s_k[sl * N + sub * 8]) =
-          (do_flush && j < c) ? kv : make_uint4(0, 0, 0, 0);
+          (j < F) ? kv : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
       const float d = reduce_quarter(dot8_bf16(kv, *reinterpret_cast<const uint4*>(&s_x[v * N + sub * 8])));
       if (sub == 0) s_M[v][sl] = d;
     }
   }
-  if (h % hpg == 0) {
+  if (write_new && h % hpg == 0) {
     for (int t = tid; t < T * (N / 8); t += kBlock) {
       const int sd = t / (N / 8), o = (t % (N / 8)) * 8;
       *reinterpret_cast<uint4*>(p.ring_k + (((size_t)b * G + g) * L + ring_slot(head, c + sd, L)) * N + o) =
@@ -235,7 +254,7 @@ __global__ __launch_bounds__(kBlock) void gdn_verify_kernel(GdnReplayParams p) {
   }
 
   // ---- 7. early flush of the committed entries (from the same registers)
-  if (do_flush) {
+  if (!APPEND && do_flush) {
     float uf[RT][VJ];  // correction of slot cq + 4m at this lane's rows, zero if not folded
 #pragma unroll
     for (int m = 0; m < VJ; ++m) {
@@ -300,7 +319,27 @@ __global__ __launch_bounds__(kBlock) void gdn_verify_kernel(GdnReplayParams p) {
         acc += ratio * s_M[T + sd][dslot[sp]] * u[sp];
       }
       p.y[(((size_t)b * T + sd) * H + h) * D + rho] = acc;
-      p.ring_u[(bh * L + dslot[sd]) * D + rho] = u[sd];
+      if (write_new) p.ring_u[(bh * L + dslot[sd]) * D + rho] = u[sd];
+      else s_u[dslot[sd] * D + rho] = u[sd];  // append filling the ring: folded below
+    }
+  }
+
+  // ---- 8b. append that fills the ring: fold all E entries, the new one included
+  if constexpr (APPEND) {
+    if (do_flush) {
+      __syncthreads();
+      float uf[RT][VJ];
+#pragma unroll
+      for (int m = 0; m < VJ; ++m) {
+        const int sl = cq + 4 * m;
+        const bool used = sl < L;  // every slot holds one of the E = L entries
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const float x = s_u[min(sl, LCAP - 1) * D + (wave * RT + rt) * 16 + r];
+          uf[rt][m] = used ? x : 0.f;
+        }
+      }
+      fold_and_store<D, N, RT, NCT, VJ>(S0, st, s_fabar, s_k, s_fw, uf, L, wave, r, cq);
     }
   }
 
@@ -311,13 +350,15 @@ __global__ __launch_bounds__(kBlock) void gdn_verify_kernel(GdnReplayParams p) {
       flag_error(p.err, bad);
       if (p.flushed != nullptr) p.flushed[b] = do_flush ? 1 : 0;
     }
-    const unsigned long long nw = pack_ptr(do_flush ? (head + c) % L : head, do_flush ? 0 : c, T);
+    const unsigned long long nw =
+        APPEND ? pack_ptr(do_flush ? (head + E) % L : head, do_flush ? 0 : E, 0)
+               : pack_ptr(do_flush ? (head + c) % L : head, do_flush ? 0 : c, T);
     const int sl = lane - kMetaSlot;
     const int sd = (sl >= 0 && sl < L) ? logical(sl) - c : -1;
     float x = rec_l;
     if (lane == kMetaPtr) x = __uint_as_float(uint32_t(nw));
     if (lane == kMetaPtr + 1) x = __uint_as_float(uint32_t(nw >> 32));
-    if (sd >= 0 && sd < T) x = s_alpha_d[min(max(sd, 0), T - 1)];
+    if (write_new && sd >= 0 && sd < T) x = s_alpha_d[min(max(sd, 0), T - 1)];
     if (lane < MS) rec[lane] = x;
   }
 }
@@ -328,11 +369,11 @@ namespace rssm_host {
 
 using rssm::GdnReplayParams;
 
-template <int D, int T>
+template <int D, int T, bool APPEND = false>
 int launch_gdn_window(const GdnReplayParams& p, int B, void* stream) {
   const dim3 grid(B * p.H), block(rssm::kBlock);
-  if (p.L <= 16) return launch(rssm::gdn_verify_kernel<D, 128, T, 16>, grid, block, stream, p);
-  return launch(rssm::gdn_verify_kernel<D, 128, T, 32>, grid, block, stream, p);
+  if (p.L <= 16) return launch(rssm::gdn_verify_kernel<D, 128, T, 16, APPEND>, grid, block, stream, p);
+  return launch(rssm::gdn_verify_kernel<D, 128, T, 32, APPEND>, grid, block, stream, p);
 }
 
 // Verify launchers for T = 1..4 and T = 5..8 live in their own translation units.

@@ -74,6 +74,16 @@ def gdn_verify(B, H, d, n, G, T, c, flush: bool) -> int:
     return B * per_req
 
 
+def gdn_append(B, H, d, n, G, h, flush: bool) -> int:
+    """gdn_replay_append_decode with h entries cached before the call: checkpoint
+    read, the h cached (u, k, alpha) entries, the token's inputs, y, the pointer
+    word; the new entry cached, or the checkpoint written back on a flush step."""
+    per_req = (F32 * H * d * n + h * gdn_slot(H, d, n, G)
+               + BF16 * H * d + 2 * BF16 * G * n + 2 * F32 * H + F32 * H * d + 2 * PTR)
+    per_req += F32 * H * d * n if flush else gdn_slot(H, d, n, G)
+    return B * per_req
+
+
 def gdn_standard_step(B, H, d, n, G) -> int:
     return B * (2 * F32 * H * d * n + BF16 * H * d + 2 * BF16 * G * n + 2 * F32 * H + F32 * H * d)
 

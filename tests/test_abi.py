@@ -32,7 +32,7 @@ def test_every_declared_function_is_exported_and_prototyped():
 
 def test_abi_version_and_strerror():
     lib = _lib.load()
-    assert lib.rssm_abi_version() == _lib.ABI_VERSION == 4
+    assert lib.rssm_abi_version() == _lib.ABI_VERSION == 5
     assert "invalid" in _lib.strerror(_lib.RSSM_EINVAL)
     assert "not supported" in _lib.strerror(_lib.RSSM_ENOTSUP)
 
@@ -104,6 +104,15 @@ def test_host_validation_codes():
     r_odd.meta = FAKE.value + 64
     assert lib.replay_rollback(ctypes.byref(d), ctypes.byref(r_odd), P, None) == EINVAL
     assert lib.rssm_ring_reset(ctypes.byref(d), ctypes.byref(r_odd), None, None) == EINVAL
+
+    # GDN append-decode: ring required, L in [1, 32], supported (d, n)
+    assert lib.gdn_replay_append_decode(ctypes.byref(d), P, None, P, P, P, P, P, P, None, None) == EINVAL
+    assert lib.gdn_replay_append_decode(ctypes.byref(_dims(L=0)), P, ctypes.byref(r), P, P, P, P, P, P,
+                                        None, None) == EINVAL
+    assert lib.gdn_replay_append_decode(ctypes.byref(_dims(L=33)), P, ctypes.byref(r), P, P, P, P, P, P,
+                                        None, None) == ENOTSUP
+    assert lib.gdn_replay_append_decode(ctypes.byref(_dims(d=96)), P, ctypes.byref(r), P, P, P, P, P, P,
+                                        None, None) == ENOTSUP
 
     # snapshot route: T in [1, 8], nslots >= T + 1, slot and pool present
     for T, nslots, code in ((0, 4, EINVAL), (4, 4, EINVAL), (9, 10, ENOTSUP), (4, 5, ENOTSUP)):

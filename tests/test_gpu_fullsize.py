@@ -322,3 +322,44 @@ def test_snapshot_route_full(gdn):
             es = rel_err(got, S[:, 0])
             assert es <= S_TOL, (r, es)
     assert int(err.item()) == 0
+
+
+def test_gdn_append_decode_full():
+    """GDN standard decode through the ring at the GDN workload's size (B=256,
+    H=32, d=128, G=32, L=16), 64 steps (4 flush cycles): sampled y every step and
+    the sampled checkpoint at every flush against the recurrence; flush flags and
+    pointers of every request every step."""
+    wl = synth.WORKLOADS[4]
+    sh = wl.shape.with_(T=1)
+    B, H, D, N, G, L = sh.batch, sh.nheads, sh.head_dim, sh.state_dim, sh.ngroups, sh.capacity
+    S0 = synth.state0(sh, wl.cfg_seed, 4)
+    pool = [synth.gdn_round_inputs(sh, wl.cfg_seed, 4, p) for p in range(16)]
+    pool = [{k: np.ascontiguousarray(v[:, 0]) for k, v in st.items()} for st in pool]
+    pairs = sample_pairs(B, H, NPAIRS, seed=66)
+    bi, hi, gi = _pairs_arrays(pairs, H, G)
+    tb, th = pair_index(pairs)
+    dims = rd.Dims(B, H, D, N, G, L)
+    ring = rd.Ring(dims, gdn=True)
+    state0 = dev_f32(S0)
+    y = torch.empty(B, H, D, device="cuda")
+    flushed = torch.zeros(B, dtype=torch.int32, device="cuda")
+    dpool = [_dev_step(st) for st in pool]
+    S = S0[bi, hi].astype(np.float64)[:, None]
+    del S0
+    for t in range(64):
+        st, ip = pool[t % 16], dpool[t % 16]
+        rd.gdn_replay_append_decode(dims, state0, ring, ip["v"], ip["k"], ip["q"], ip["g"], ip["beta"], y, flushed)
+        sub = {"v": _f64(st["v"][bi, hi])[:, None], "k": _f64(st["k"][bi, gi])[:, None],
+               "q": _f64(st["q"][bi, gi])[:, None], "g": st["g"][bi, hi].astype(np.float64)[:, None],
+               "beta": st["beta"][bi, hi].astype(np.float64)[:, None]}
+        S, y_ref = o_gdn.householder_step(S, sub["v"], sub["k"], sub["q"], sub["g"], sub["beta"], 1)
+        e = rel_err(y[tb, th].cpu().numpy(), y_ref[:, 0])
+        assert e <= Y_TOL, (t, e)
+        fl = (t + 1) % L == 0
+        assert bool(torch.all(flushed == int(fl))), t
+        assert bool(torch.all(ring.count == (t + 1) % L)) and bool(torch.all(ring.head == 0)), t
+        if fl:
+            es = rel_err(state0[tb, th].cpu().numpy(), S[:, 0])
+            assert es <= S_TOL, (t, es)
+    assert ring.copies_agree()
+    assert int(ring.err.item()) == 0

@@ -303,6 +303,48 @@ def test_gdn_replay_verify_small(d, G, L, T):
     assert es <= S_TOL, es
 
 
+@pytest.mark.parametrize("d,G,L", [(128, 32, 16), (64, 8, 8), (128, 16, 5), (64, 4, 32)])
+def test_gdn_replay_append_decode_small(d, G, L):
+    """GDN standard decode through the ring: y every step, flush flags, pointers
+    and the checkpoint at every flush against the oracle's flush-when-full
+    request model; the committed corrections in the ring against it too."""
+    base = synth.WORKLOADS[4]
+    sh = base.shape.with_(batch=3, head_dim=d, ngroups=G, capacity=L, T=1)
+    seed, steps = base.cfg_seed, 2 * L + 5
+    S0 = synth.state0(sh, seed, 4)
+    dims = _dims(sh)
+    ring = rd.Ring(dims, gdn=True)
+    state0 = dev_f32(S0)
+    y = torch.empty(sh.batch, sh.nheads, sh.head_dim, device="cuda")
+    flushed = torch.zeros(sh.batch, dtype=torch.int32, device="cuda")
+    S = S0.astype(np.float64)
+    reqs = [o_gdn.GDNReplayRequest(S0[b].astype(np.float64), L, G) for b in range(sh.batch)]
+    for t in range(steps):
+        st = synth.gdn_round_inputs(sh, seed, 4, t)
+        sq = {k_: np.ascontiguousarray(v_[:, 0]) for k_, v_ in st.items()}
+        s64 = gdn_step_f64(sq)
+        rd.gdn_replay_append_decode(dims, state0, ring, dev_bf16(sq["v"]), dev_bf16(sq["k"]), dev_bf16(sq["q"]),
+                                    dev_f32(sq["g"]), dev_f32(sq["beta"]), y, flushed)
+        S, y_rec = o_gdn.householder_step(S, s64["v"], s64["k"], s64["q"], s64["g"], s64["beta"], G)
+        assert rel_err(y.cpu().numpy(), y_rec) <= Y_TOL, t
+        for b in range(sh.batch):
+            yb, fb = reqs[b].decode_step(s64["v"][b], s64["k"][b], s64["q"][b], s64["g"][b], s64["beta"][b])
+            assert bool(flushed[b].item()) == fb, (t, b)
+            assert (ring.head[b].item(), ring.count[b].item(), ring.pending[b].item()) == \
+                (reqs[b].head, reqs[b].count, 0), (t, b)
+            if fb:
+                assert rel_err(state0[b].cpu().numpy(), reqs[b].S0) <= S_TOL, (t, b)
+        assert ring.copies_agree(), t
+    ring_u = ring.vu.cpu().numpy()
+    for b in range(sh.batch):
+        for j in range(reqs[b].count):
+            sl = (reqs[b].head + j) % L
+            assert rel_err(ring_u[b][:, sl], reqs[b].ring[sl].u) <= Y_TOL, (b, j)
+    assert int(ring.err.item()) == 0
+    rd.gdn_replay_flush(dims, state0, ring)
+    assert rel_err(state0.cpu().numpy(), S) <= S_TOL
+
+
 def test_causal_conv1d_update_config1_size():
     wl = synth.WORKLOADS[1]
     B, C = wl.shape.batch, wl.conv_channels
