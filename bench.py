@@ -491,6 +491,89 @@ def _row_gdn_append(torch, np, rd, synth, traffic, dev, stream):
             "standard_step": std, "speedup": round(std["us"] / float(us.mean()), 3)}
 
 
+def _row_pooled(torch, np, rd, synth, traffic, dev, stream):
+    """Append-decode at the Nemotron-H-like shape with the checkpoints and rings in
+    a pool of 2B request rows, each call's batch entries scattered over the pool
+    by a seeded permutation (serving layout), against the same launches with row
+    = batch entry; two layer instances rotated, per-launch HIP-event times."""
+    wl = synth.WORKLOADS[1]
+    sh, seed = wl.shape, wl.cfg_seed
+    B, H, D, N, G, L = sh.batch, sh.nheads, sh.head_dim, sh.state_dim, sh.ngroups, sh.capacity
+    rows, NLs, K = 2 * B, 2, 8 * L
+    dims = rd.Dims(B, H, D, N, G, L)
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    st = synth.mamba2_step_inputs(sh, seed, 1, 0)
+    ip = {k_: (bf(v_) if v_.dtype == np.uint16 else torch.from_numpy(v_).to(dev)) for k_, v_ in st.items()}
+    A, bias = synth.mamba2_head_params(sh, seed, 1)
+    A, bias = torch.from_numpy(A).to(dev), torch.from_numpy(bias).to(dev)
+    y = torch.empty((B, H, D), device=dev)
+    perm = np.random.default_rng(seed).permutation(rows)[:B].astype(np.int32)
+    res = {"workload": f"Mamba-2 append-decode, batch {B} over a pool of {rows} rows, {H} heads, head dim {D}, "
+                       f"state {N}, {G} groups, ring capacity {L}; two layer instances rotated",
+           "kernel": "replay_append_decode", "steps_timed": K}
+    for name, pooled in (("batch_rows", False), ("pooled", True)):
+        layers = []
+        for l in range(NLs):
+            S0 = torch.randn((rows if pooled else B, H, D, N), device=dev) * math.sqrt(0.1)
+            ring = rd.Ring(dims, device=dev, rows=rows if pooled else None)
+            if pooled:
+                ring.use_slots(torch.from_numpy(perm).to(dev))
+            layers.append(rd.prepare_replay_append_decode(dims, S0, ring, ip["v"], ip["k"], ip["q"], ip["dt"],
+                                                          bias, A, y, stream=stream))
+            layers[-1].keep_alive = (S0, ring)
+        for t in range(NLs * L):
+            layers[t % NLs]()
+        ev = _events(torch, K)
+        torch.cuda.synchronize()
+        for i in range(K):
+            ev[i][0].record(stream)
+            layers[i % NLs]()
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        us = float(np.mean([1e3 * a_.elapsed_time(b_) for a_, b_ in ev]))
+        byts = float(np.mean([traffic.replay_append(B, H, D, N, G, h, h == L - 1) for h in range(L)]))
+        res[name] = {"avg_us": round(us, 3), "avg_GBs": round(byts / (us * 1e-6) / 1e9, 1)}
+        del layers
+    return res
+
+
+def _row_capacity(torch, np, rd, synth, dev, budget=288 * 10**9, B_check=64):
+    """Decode-state bytes per request and the largest batch one MI355X's HBM holds
+    for one SSM layer, per route (standard, per-draft snapshots, ReplaySSM), at
+    the two speculative workloads' shapes; the model is checked against the
+    device memory that the routes' buffers actually take for a batch of 64."""
+    from ssm_recurrent_decode_amd import capacity
+    out = {"budget_bytes": budget}
+    for name, cid, gdn in (("mamba2", 2, False), ("gdn", 4, True)):
+        sh = synth.WORKLOADS[cid].shape
+        H, D, N, G, L, T = sh.nheads, sh.head_dim, sh.state_dim, sh.ngroups, sh.capacity, sh.T
+        tab = capacity.concurrency_table(H, D, N, G, L, T, gdn, budget)
+        torch.cuda.synchronize()
+        m0 = torch.cuda.memory_allocated(dev)
+        pool = torch.empty((B_check, T + 1, H, D, N), device=dev)
+        slot = torch.zeros((B_check,), dtype=torch.int32, device=dev)
+        m1 = torch.cuda.memory_allocated(dev)
+        del pool, slot
+        torch.cuda.synchronize()
+        m1b = torch.cuda.memory_allocated(dev)
+        S0 = torch.empty((B_check, H, D, N), device=dev)
+        ring = rd.Ring(rd.Dims(B_check, H, D, N, G, L), gdn=gdn, device=dev)
+        m2 = torch.cuda.memory_allocated(dev)
+        del S0, ring
+        tab["allocated_check"] = {
+            "batch": B_check,
+            "snapshot_bytes": m1 - m0,
+            "snapshot_model": B_check * capacity.bytes_per_request("snapshot", H, D, N, G, L, T, gdn),
+            "replay_bytes": m2 - m1b,
+            "replay_model": B_check * capacity.bytes_per_request("replay", H, D, N, G, L, T, gdn) + 4}
+        tab["shape"] = f"{H} heads, head dim {D}, state {N}, {G} group(s), ring capacity {L}, T={T}"
+        out[name] = tab
+    return out
+
+
 def _row_flush(torch, np, rd, synth, traffic, dev, stream, reps=8):
     """Explicit flush of full rings: Mamba-2 at the Nemotron-H shape after L - 1
     appends, GDN at its verify shape after three fully accepted verify rounds
@@ -569,6 +652,8 @@ def _rows(torch, np, rd, synth, traffic, dev, stream):
             "capacity_sweep": _row_sweep(torch, np, rd, synth, traffic, dev, stream),
             "explicit_flush": _row_flush(torch, np, rd, synth, traffic, dev, stream),
             "gdn_append_decode": _row_gdn_append(torch, np, rd, synth, traffic, dev, stream),
+            "max_concurrency": _row_capacity(torch, np, rd, synth, dev),
+            "pooled_append_decode": _row_pooled(torch, np, rd, synth, traffic, dev, stream),
             "window_sweep": {"mamba2": _row_window(torch, np, rd, synth, traffic, dev, stream, 2, False),
                              "gdn": _row_window(torch, np, rd, synth, traffic, dev, stream, 4, True)}}
 

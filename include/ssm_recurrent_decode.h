@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define RSSM_ABI_VERSION 5
+#define RSSM_ABI_VERSION 6
 
 #define RSSM_OK 0
 #define RSSM_EINVAL (-22)
@@ -55,6 +55,7 @@ extern "C" {
 #define RSSM_ERR_POINTERS 1  /* head/count/pending out of range on entry (clamped)       */
 #define RSSM_ERR_ACCEPTED 2  /* accepted[b] outside [0, pending[b]] (clamped)            */
 #define RSSM_ERR_PENDING 4   /* decode/verify called with uncommitted drafts (dropped)   */
+#define RSSM_ERR_SLOT 8      /* slots[b] >= rows: batch entry b skipped                   */
 
 typedef struct rssm_dims {
   int32_t batch;      /* B */
@@ -94,6 +95,16 @@ typedef struct rssm_dims {
  * (rssm_ring_reset re-zeroes the pointer words of a subset of requests).
  * Unsigned fields: a head >= L or a count above the largest legal value is
  * clamped and flagged (RSSM_ERR_POINTERS).  Bits 48-63 of the word are zero.
+ *
+ * Pooled rings (serving layout).  With slots == NULL, batch entry b owns row b
+ * of state0 and of the ring arrays.  With slots != NULL, state0, vu, k and meta
+ * hold `rows` request rows -- a block pool in which one block is one request's
+ * whole decode state -- and batch entry b of a call works on row slots[b]; the
+ * call's own inputs and outputs (v, k, q, dt, g, beta, y, flushed, accepted,
+ * mask) stay indexed by b.  A negative slot marks a padding entry (a batch
+ * padded up to a captured size): it is skipped, nothing of it read or written.
+ * slots[b] >= rows: skipped, RSSM_ERR_SLOT flagged.  Two entries of one call
+ * must not name the same row.  Sizes: rssm_ring_sizes with dims->batch = rows.
  */
 #define RSSM_META_WORDS(L) ((L) + 3 <= 32 ? 32 : 64)
 #define RSSM_PTR_HEAD(w) ((uint32_t)((w) & 0xFFFFu))
@@ -109,6 +120,8 @@ typedef struct rssm_ring {
   float* meta;       /* [B, H, RSSM_META_WORDS(L)] records: pointer word, A, Delta or
                         alpha per slot (see above)                                   */
   int32_t* err;      /* [1] anomaly bits (RSSM_ERR_*), may be NULL                  */
+  const int32_t* slots;  /* [B] pool row of each batch entry, or NULL (row = b)     */
+  int32_t rows;      /* pool rows when slots != NULL (>= 1); ignored otherwise       */
 } rssm_ring;
 
 int rssm_abi_version(void);

@@ -19,7 +19,8 @@ RSSM_ELAUNCH = -5
 RSSM_ERR_POINTERS = 1
 RSSM_ERR_ACCEPTED = 2
 RSSM_ERR_PENDING = 4
-ABI_VERSION = 5  # RSSM_ABI_VERSION of the header this binding follows
+RSSM_ERR_SLOT = 8
+ABI_VERSION = 6  # RSSM_ABI_VERSION of the header this binding follows
 
 
 class rssm_dims(ctypes.Structure):
@@ -28,7 +29,8 @@ class rssm_dims(ctypes.Structure):
 
 
 class rssm_ring(ctypes.Structure):
-    _fields_ = [("vu", c_void_p), ("k", c_void_p), ("meta", c_void_p), ("err", c_void_p)]
+    _fields_ = [("vu", c_void_p), ("k", c_void_p), ("meta", c_void_p), ("err", c_void_p),
+                ("slots", c_void_p), ("rows", c_int32)]
 
 
 _D = POINTER(rssm_dims)

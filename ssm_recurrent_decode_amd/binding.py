@@ -9,6 +9,7 @@ bit patterns.  PyTorch is used for device memory and streams only.
 from __future__ import annotations
 
 import ctypes
+import dataclasses
 from dataclasses import dataclass
 
 import torch
@@ -76,12 +77,18 @@ class Ring:
     pending 32-47) in words 0-1, then A and the per-slot step sizes (Mamba-2) or
     decays (GDN).  ``head``, ``count`` and ``pending`` are int32 views decoded
     from head 0's record, and ``copies_agree`` checks that every head's pointer
-    word is the same."""
+    word is the same.
 
-    def __init__(self, dims: Dims, gdn: bool = False, device="cuda"):
-        B, H, G, L = dims.batch, dims.nheads, dims.ngroups, dims.capacity
+    Pooled rings: ``rows`` request rows are allocated (default: the batch), and
+    ``use_slots(slots)`` makes every call map batch entry b to row slots[b]
+    (negative = padding entry, skipped); the checkpoint passed with it then has
+    ``rows`` rows too."""
+
+    def __init__(self, dims: Dims, gdn: bool = False, device="cuda", rows=None):
+        B = dims.batch if rows is None else int(rows)
+        H, G, L = dims.nheads, dims.ngroups, dims.capacity
         D, N = dims.head_dim, dims.state_dim
-        self.dims, self.gdn = dims, gdn
+        self.dims, self.gdn, self.rows, self.slots = dims, gdn, B, None
         z = dict(device=device)
         self.vu = torch.zeros((B, H, L, D), dtype=torch.float32 if gdn else torch.bfloat16, **z)
         self.k = torch.zeros((B, G, L, N), dtype=torch.bfloat16, **z)
@@ -122,9 +129,17 @@ class Ring:
         col = torch.tensor(words, dtype=torch.int64).to(self.meta.device)
         self.meta.view(torch.int64)[:, :, 0] = col[:, None]
 
+    def use_slots(self, slots):
+        """Map the batch entries of the following calls to pool rows (int32 device
+        tensor [B]); None returns to row = batch entry."""
+        if slots is not None:
+            _p(slots, "slots", _I32, (int(slots.shape[0]),))
+        self.slots = slots
+
     def c(self) -> _lib.rssm_ring:
+        sp = self.slots.data_ptr() if self.slots is not None else None
         return _lib.rssm_ring(self.vu.data_ptr(), self.k.data_ptr(), self.meta.data_ptr(),
-                              self.err.data_ptr())
+                              self.err.data_ptr(), sp, self.rows)
 
     def tensors(self):
         return {k: getattr(self, k) for k in ("vu", "k", "meta", "err")}
@@ -138,7 +153,7 @@ def ring_sizes(dims: Dims, gdn: bool = False):
 
 
 def rssm_ring_reset(dims: Dims, ring: Ring, mask=None, stream=None):
-    d, rc = dims.c(), ring.c()
+    d, rc = dims.c(), _ring_args(dims, ring, ring.gdn)
     m = _p(mask, "mask", _I32, (dims.batch,), allow_none=True)
     _lib.check(_lib.load().rssm_ring_reset(ctypes.byref(d), ctypes.byref(rc), m, _stream(stream)),
                "rssm_ring_reset")
@@ -158,8 +173,12 @@ def ssm_decode_step(dims: Dims, state, v, k, q, dt, dt_bias, A, y, stream=None):
 def _ring_args(dims: Dims, ring: Ring, gdn: bool):
     if ring.gdn != gdn:
         raise ValueError("ring kind does not match the call (Mamba-2 vs GDN)")
-    if ring.dims != dims:
+    if dataclasses.replace(ring.dims, batch=dims.batch) != dims:
         raise ValueError("ring was allocated for different dims")
+    if ring.slots is None and dims.batch != ring.rows:
+        raise ValueError("batch differs from the ring's rows and no slot map is set")
+    if ring.slots is not None and tuple(ring.slots.shape) != (dims.batch,):
+        raise ValueError("slot map length differs from the batch")
     return ring.c()
 
 
@@ -167,7 +186,7 @@ def replay_append_decode(dims: Dims, state0, ring: Ring, v, k, q, dt, dt_bias, A
                          flushed=None, stream=None):
     B, H, D, N, G = dims.batch, dims.nheads, dims.head_dim, dims.state_dim, dims.ngroups
     d, rc = dims.c(), _ring_args(dims, ring, False)
-    args = (_p(state0, "state0", _F32, (B, H, D, N)), ctypes.byref(rc),
+    args = (_p(state0, "state0", _F32, (ring.rows, H, D, N)), ctypes.byref(rc),
             _p(v, "v", _BF16, (B, H, D)), _p(k, "k", _BF16, (B, G, N)),
             _p(q, "q", _BF16, (B, G, N)), _p(dt, "dt", _F32, (B, H)),
             _p(dt_bias, "dt_bias", _F32, (H,)), _p(A, "A", _F32, (H,)),
@@ -180,7 +199,7 @@ def replay_flush(dims: Dims, state0, ring: Ring, mask=None, stream=None):
     B, H, D, N = dims.batch, dims.nheads, dims.head_dim, dims.state_dim
     d, rc = dims.c(), _ring_args(dims, ring, False)
     _lib.check(_lib.load().replay_flush(
-        ctypes.byref(d), _p(state0, "state0", _F32, (B, H, D, N)), ctypes.byref(rc),
+        ctypes.byref(d), _p(state0, "state0", _F32, (ring.rows, H, D, N)), ctypes.byref(rc),
         _p(mask, "mask", _I32, (B,), allow_none=True), _stream(stream)), "replay_flush")
 
 
@@ -188,7 +207,7 @@ def replay_verify_T(dims: Dims, T: int, state0, ring: Ring, v, k, q, dt, dt_bias
                     flushed=None, stream=None):
     B, H, D, N, G = dims.batch, dims.nheads, dims.head_dim, dims.state_dim, dims.ngroups
     d, rc = dims.c(), _ring_args(dims, ring, False)
-    args = (_p(state0, "state0", _F32, (B, H, D, N)), ctypes.byref(rc),
+    args = (_p(state0, "state0", _F32, (ring.rows, H, D, N)), ctypes.byref(rc),
             _p(v, "v", _BF16, (B, T, H, D)), _p(k, "k", _BF16, (B, T, G, N)),
             _p(q, "q", _BF16, (B, T, G, N)), _p(dt, "dt", _F32, (B, T, H)),
             _p(dt_bias, "dt_bias", _F32, (H,)), _p(A, "A", _F32, (H,)),
@@ -198,7 +217,7 @@ def replay_verify_T(dims: Dims, T: int, state0, ring: Ring, v, k, q, dt, dt_bias
 
 
 def replay_rollback(dims: Dims, ring: Ring, accepted, stream=None):
-    d, rc = dims.c(), ring.c()
+    d, rc = dims.c(), _ring_args(dims, ring, ring.gdn)
     _lib.check(_lib.load().replay_rollback(
         ctypes.byref(d), ctypes.byref(rc), _p(accepted, "accepted", _I32, (dims.batch,)),
         _stream(stream)), "replay_rollback")
@@ -218,7 +237,7 @@ def gdn_replay_verify_T(dims: Dims, T: int, state0, ring: Ring, v, k, q, g, beta
                         flushed=None, stream=None):
     B, H, D, N, G = dims.batch, dims.nheads, dims.head_dim, dims.state_dim, dims.ngroups
     d, rc = dims.c(), _ring_args(dims, ring, True)
-    args = (_p(state0, "state0", _F32, (B, H, D, N)), ctypes.byref(rc),
+    args = (_p(state0, "state0", _F32, (ring.rows, H, D, N)), ctypes.byref(rc),
             _p(v, "v", _BF16, (B, T, H, D)), _p(k, "k", _BF16, (B, T, G, N)),
             _p(q, "q", _BF16, (B, T, G, N)), _p(g, "g", _F32, (B, T, H)),
             _p(beta, "beta", _F32, (B, T, H)), _p(y, "y", _F32, (B, T, H, D)),
@@ -231,7 +250,7 @@ def gdn_replay_append_decode(dims: Dims, state0, ring: Ring, v, k, q, g, beta, y
                              stream=None):
     B, H, D, N, G = dims.batch, dims.nheads, dims.head_dim, dims.state_dim, dims.ngroups
     d, rc = dims.c(), _ring_args(dims, ring, True)
-    args = (_p(state0, "state0", _F32, (B, H, D, N)), ctypes.byref(rc),
+    args = (_p(state0, "state0", _F32, (ring.rows, H, D, N)), ctypes.byref(rc),
             _p(v, "v", _BF16, (B, H, D)), _p(k, "k", _BF16, (B, G, N)), _p(q, "q", _BF16, (B, G, N)),
             _p(g, "g", _F32, (B, H)), _p(beta, "beta", _F32, (B, H)), _p(y, "y", _F32, (B, H, D)),
             _p(flushed, "flushed", _I32, (B,), allow_none=True))
@@ -243,7 +262,7 @@ def gdn_replay_flush(dims: Dims, state0, ring: Ring, mask=None, stream=None):
     B, H, D, N = dims.batch, dims.nheads, dims.head_dim, dims.state_dim
     d, rc = dims.c(), _ring_args(dims, ring, True)
     _lib.check(_lib.load().gdn_replay_flush(
-        ctypes.byref(d), _p(state0, "state0", _F32, (B, H, D, N)), ctypes.byref(rc),
+        ctypes.byref(d), _p(state0, "state0", _F32, (ring.rows, H, D, N)), ctypes.byref(rc),
         _p(mask, "mask", _I32, (B,), allow_none=True), _stream(stream)), "gdn_replay_flush")
 
 
@@ -338,7 +357,7 @@ def prepare_replay_append_decode(dims: Dims, state0, ring: Ring, v, k, q, dt, dt
                                  flushed=None, stream=None) -> Prepared:
     B, H, D, N, G = dims.batch, dims.nheads, dims.head_dim, dims.state_dim, dims.ngroups
     d, rc = dims.c(), _ring_args(dims, ring, False)
-    args = (ctypes.byref(d), _p(state0, "state0", _F32, (B, H, D, N)), ctypes.byref(rc),
+    args = (ctypes.byref(d), _p(state0, "state0", _F32, (ring.rows, H, D, N)), ctypes.byref(rc),
             _p(v, "v", _BF16, (B, H, D)), _p(k, "k", _BF16, (B, G, N)),
             _p(q, "q", _BF16, (B, G, N)), _p(dt, "dt", _F32, (B, H)),
             _p(dt_bias, "dt_bias", _F32, (H,)), _p(A, "A", _F32, (H,)),

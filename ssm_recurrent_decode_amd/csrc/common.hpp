@@ -150,6 +150,20 @@ __device__ __forceinline__ void flag_error(int32_t* err, int bits) {
   if (err != nullptr && bits != 0) atomicOr(err, bits);
 }
 
+// Pool row of batch entry b: b itself without a slot map, else slots[b]; -1
+// when the entry is skipped (a negative slot marks padding; a slot past the
+// pool is also flagged).  Uniform per request.
+__device__ __forceinline__ int pool_row(const int32_t* slots, int rows, int b, int32_t* err,
+                                        bool report) {
+  if (slots == nullptr) return b;
+  const int s = slots[b];
+  if (s >= rows) {
+    if (report) flag_error(err, RSSM_ERR_SLOT);
+    return -1;
+  }
+  return s < 0 ? -1 : s;
+}
+
 // One fp32 MFMA step of the transposed tile product: acc[m][nn] += sum_k a[m][k] b[k][nn]
 // with lane l supplying a[l & 15][l >> 4] and b[l >> 4][l & 15].
 __device__ __forceinline__ v4f mfma4(float a, float b, v4f acc) {
@@ -225,7 +239,8 @@ inline bool ring_shape_supported(const rssm_dims* d) {
 }
 
 inline bool meta_ok(const rssm_ring* r) {
-  return r != nullptr && r->meta != nullptr && reinterpret_cast<uintptr_t>(r->meta) % 128 == 0;
+  return r != nullptr && r->meta != nullptr && reinterpret_cast<uintptr_t>(r->meta) % 128 == 0 &&
+         (r->slots == nullptr || r->rows >= 1);
 }
 
 inline bool ring_ok(const rssm_ring* r) {

@@ -98,7 +98,9 @@ __global__ __launch_bounds__(kBlock) void gdn_flush_kernel(GdnReplayParams p) {
   const int r = lane & 15, cq = lane >> 4;
 
   if (p.mask != nullptr && p.mask[b] == 0) return;
-  const size_t bh = (size_t)b * H + h;
+  const int rb = pool_row(p.slots, p.rows, b, p.err, tid == 0 && h == 0);
+  if (rb < 0) return;
+  const size_t bh = (size_t)rb * H + h;
   float* rec = p.meta + bh * meta_words(L);  // this head's ring record
   const RingPtr rp = unpack_ptr(*reinterpret_cast<const unsigned long long*>(rec + kMetaPtr));
   int head = rp.head, cnt = rp.count;
@@ -148,7 +150,7 @@ __global__ __launch_bounds__(kBlock) void gdn_flush_kernel(GdnReplayParams p) {
   for (int t = tid; t < F * (N / 8); t += kBlock) {
     const int j = t / (N / 8), o = (t % (N / 8)) * 8;
     *reinterpret_cast<uint4*>(&s_k[j * N + o]) =
-        ld_u4(p.ring_k + (((size_t)b * G + g) * L + (head + j) % L) * N + o);
+        ld_u4(p.ring_k + (((size_t)rb * G + g) * L + (head + j) % L) * N + o);
   }
   __syncthreads();
   if (F > 0) fold_and_store<D, N, RT, NCT, kVJ>(S0, s, s_abar, s_k, s_w, uf, F, wave, r, cq);
@@ -173,6 +175,8 @@ GdnReplayParams make_gdn_params(const rssm_dims* d, float* state0, rssm_ring* ri
   p.ring_k = ring->k;
   p.meta = ring->meta;
   p.err = ring->err;
+  p.slots = ring->slots;
+  p.rows = ring->rows;
   p.H = d->nheads;
   p.G = d->ngroups;
   p.L = d->capacity;

@@ -25,6 +25,8 @@ struct GdnReplayParams {
   float* y;            // [B, T, H, D]
   int32_t* flushed;
   const int32_t* mask;
+  const int32_t* slots;  // pool row per batch entry, or null
+  int rows;
   int H, G, L;
 };
 
@@ -86,7 +88,9 @@ __global__ __launch_bounds__(kBlock) void gdn_verify_kernel(GdnReplayParams p) {
   const int b = wg / H, h = wg - b * H, hpg = H / G, g = h / hpg;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, cq = lane >> 4, sub = lane & 15;
-  const size_t bh = (size_t)b * H + h;
+  const int rb = pool_row(p.slots, p.rows, b, p.err, tid == 0 && h == 0);  // request's row
+  if (rb < 0) return;                 // padding or outside the pool: whole work-group
+  const size_t bh = (size_t)rb * H + h;  // per-(row, head) checkpoint, ring and record
 
   // ---- 1. this head's copy of the pointer word and every small operand
   const int MS = meta_words(L);
@@ -163,7 +167,7 @@ __global__ __launch_bounds__(kBlock) void gdn_verify_kernel(GdnReplayParams p) {
     const int sl = ps * 16 + wave * 4 + (lane >> 4);
     kr[ps] = make_uint4(0, 0, 0, 0);
     if (sl < L && logical(min(sl, L - 1)) < c)
-      kr[ps] = ld_u4(p.ring_k + (((size_t)b * G + g) * L + sl) * N + sub * 8);
+      kr[ps] = ld_u4(p.ring_k + (((size_t)rb * G + g) * L + sl) * N + sub * 8);
   }
   float4 uc[UP];
 #pragma unroll
@@ -220,7 +224,7 @@ __global__ __launch_bounds__(kBlock) void gdn_verify_kernel(GdnReplayParams p) {
   if (write_new && h % hpg == 0) {
     for (int t = tid; t < T * (N / 8); t += kBlock) {
       const int sd = t / (N / 8), o = (t % (N / 8)) * 8;
-      *reinterpret_cast<uint4*>(p.ring_k + (((size_t)b * G + g) * L + ring_slot(head, c + sd, L)) * N + o) =
+      *reinterpret_cast<uint4*>(p.ring_k + (((size_t)rb * G + g) * L + ring_slot(head, c + sd, L)) * N + o) =
           *reinterpret_cast<const uint4*>(&s_x[sd * N + o]);
     }
   }

@@ -97,7 +97,9 @@ __global__ __launch_bounds__(kBlock) void replay_flush_kernel(ReplayParams p) {
   const int r = lane & 15, cq = lane >> 4;
 
   if (p.mask != nullptr && p.mask[b] == 0) return;
-  const size_t bh = (size_t)b * H + h;
+  const int rb = pool_row(p.slots, p.rows, b, p.err, tid == 0 && h == 0);
+  if (rb < 0) return;
+  const size_t bh = (size_t)rb * H + h;
   float* rec = p.meta + bh * meta_words(L);  // this head's ring record
   const RingPtr rp = unpack_ptr(*reinterpret_cast<const unsigned long long*>(rec + kMetaPtr));
   int head = rp.head, cnt = rp.count;
@@ -151,7 +153,7 @@ __global__ __launch_bounds__(kBlock) void replay_flush_kernel(ReplayParams p) {
   for (int t = tid; t < F * (N / 8); t += kBlock) {
     const int j = t / (N / 8), o = (t % (N / 8)) * 8;
     *reinterpret_cast<uint4*>(&s_k[j * N + o]) =
-        ld_u4(p.ring_k + (((size_t)b * G + g) * L + (head + j) % L) * N + o);
+        ld_u4(p.ring_k + (((size_t)rb * G + g) * L + (head + j) % L) * N + o);
   }
   __syncthreads();
   if (F > 0) fold_and_store<D, N, RT, NCT, kVJ>(S0, s, s_fabar, s_k, s_fw, vj, F, wave, r, cq);
@@ -167,6 +169,8 @@ struct PtrParams {
   int32_t* err;
   const int32_t* accepted;
   const int32_t* mask;
+  const int32_t* slots;
+  int rows;
   int B, H, L;
 };
 
@@ -179,9 +183,12 @@ __device__ __forceinline__ unsigned long long* ptr_word(const PtrParams& p, int 
 __global__ __launch_bounds__(kBlock) void rollback_kernel(PtrParams p) {
   const int i = blockIdx.x * kBlock + threadIdx.x;
   if (i >= p.B * p.H) return;
-  unsigned long long* w = ptr_word(p, i);
+  const int b = i / p.H, h = i - b * p.H;
+  const int rb = pool_row(p.slots, p.rows, b, p.err, h == 0);
+  if (rb < 0) return;
+  unsigned long long* w = ptr_word(p, rb * p.H + h);
   const RingPtr rp = unpack_ptr(*w);
-  int head = rp.head, cnt = rp.count, pend = rp.pending, acc = p.accepted[i / p.H];
+  int head = rp.head, cnt = rp.count, pend = rp.pending, acc = p.accepted[b];
   int bad = 0;
   if (head >= p.L) {
     head %= p.L;
@@ -207,7 +214,10 @@ __global__ __launch_bounds__(kBlock) void ring_reset_kernel(PtrParams p) {
   const int i = blockIdx.x * kBlock + threadIdx.x;
   if (i == 0 && p.err != nullptr) *p.err = 0;
   if (i >= p.B * p.H) return;
-  if (p.mask == nullptr || p.mask[i / p.H] != 0) *ptr_word(p, i) = 0ull;
+  const int b = i / p.H, h = i - b * p.H;
+  if (p.mask != nullptr && p.mask[b] == 0) return;
+  const int rb = pool_row(p.slots, p.rows, b, nullptr, false);
+  if (rb >= 0) *ptr_word(p, rb * p.H + h) = 0ull;
 }
 
 }  // namespace rssm
@@ -225,6 +235,8 @@ ReplayParams make_replay_params(const rssm_dims* d, float* state0, rssm_ring* ri
   p.ring_k = ring->k;
   p.meta = ring->meta;
   p.err = ring->err;
+  p.slots = ring->slots;
+  p.rows = ring->rows;
   p.H = d->nheads;
   p.G = d->ngroups;
   p.L = d->capacity;
@@ -307,7 +319,8 @@ extern "C" int replay_rollback(const rssm_dims* dims, rssm_ring* ring, const int
   if (!rssm_host::dims_ok(dims) || !rssm_host::meta_ok(ring) || !accepted) return RSSM_EINVAL;
   if (dims->capacity < 1) return RSSM_EINVAL;
   if (dims->capacity > kMaxL) return RSSM_ENOTSUP;
-  PtrParams p{ring->meta, ring->err, accepted, nullptr, dims->batch, dims->nheads, dims->capacity};
+  PtrParams p{ring->meta, ring->err, accepted, nullptr, ring->slots, ring->rows,
+              dims->batch, dims->nheads, dims->capacity};
   const dim3 grid((dims->batch * dims->nheads + kBlock - 1) / kBlock);
   return launch(rollback_kernel, grid, dim3(kBlock), stream, p);
 }
@@ -317,7 +330,8 @@ extern "C" int rssm_ring_reset(const rssm_dims* dims, rssm_ring* ring, const int
   if (!rssm_host::dims_ok(dims) || !rssm_host::meta_ok(ring)) return RSSM_EINVAL;
   if (dims->capacity < 1) return RSSM_EINVAL;
   if (dims->capacity > kMaxL) return RSSM_ENOTSUP;
-  PtrParams p{ring->meta, ring->err, nullptr, mask, dims->batch, dims->nheads, dims->capacity};
+  PtrParams p{ring->meta, ring->err, nullptr, mask, ring->slots, ring->rows,
+              dims->batch, dims->nheads, dims->capacity};
   const dim3 grid((dims->batch * dims->nheads + kBlock - 1) / kBlock);
   return launch(ring_reset_kernel, grid, dim3(kBlock), stream, p);
 }

@@ -33,6 +33,8 @@ struct ReplayParams {
   float* y;            // [B, T, H, D]
   int32_t* flushed;
   const int32_t* mask;  // explicit flush only
+  const int32_t* slots;  // pool row per batch entry, or null
+  int rows;
   int H, G, L;
 };
 
@@ -96,7 +98,9 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
   const int b = wg / H, h = wg - b * H, hpg = H / G, g = h / hpg;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, cq = lane >> 4, sub = lane & 15;
-  const size_t bh = (size_t)b * H + h;
+  const int rb = pool_row(p.slots, p.rows, b, p.err, tid == 0 && h == 0);  // request's row
+  if (rb < 0) return;                 // padding or outside the pool: whole work-group
+  const size_t bh = (size_t)rb * H + h;  // per-(row, head) checkpoint, ring and record
 
   // ---- 1. this head's ring record (pointer word, step sizes) and every small operand
   const int MS = meta_words(L);
@@ -166,7 +170,7 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
     const int sl = ps * 16 + wave * 4 + (lane >> 4);
     kr[ps] = make_uint4(0, 0, 0, 0);
     if (sl < L && logical(min(sl, L - 1)) < c)
-      kr[ps] = ld_u4(p.ring_k + (((size_t)b * G + g) * L + sl) * N + sub * 8);
+      kr[ps] = ld_u4(p.ring_k + (((size_t)rb * G + g) * L + sl) * N + sub * 8);
   }
   uint4 rv[RVP];
 #pragma unroll
@@ -343,7 +347,7 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
       } else if (k_owner && t < NCH) {
         const int tk = t - NEWV;
         const int sd = tk / (N / 8), o = (tk % (N / 8)) * 8;
-        *reinterpret_cast<uint4*>(p.ring_k + (((size_t)b * G + g) * L + ring_slot(head, c + sd, L)) * N + o) = newc[i];
+        *reinterpret_cast<uint4*>(p.ring_k + (((size_t)rb * G + g) * L + ring_slot(head, c + sd, L)) * N + o) = newc[i];
       }
     }
   }

@@ -32,7 +32,7 @@ def test_every_declared_function_is_exported_and_prototyped():
 
 def test_abi_version_and_strerror():
     lib = _lib.load()
-    assert lib.rssm_abi_version() == _lib.ABI_VERSION == 5
+    assert lib.rssm_abi_version() == _lib.ABI_VERSION == 6
     assert "invalid" in _lib.strerror(_lib.RSSM_EINVAL)
     assert "not supported" in _lib.strerror(_lib.RSSM_ENOTSUP)
 
@@ -42,7 +42,7 @@ def _dims(B=4, H=8, d=64, n=128, G=1, L=8):
 
 
 def _ring():
-    return _lib.rssm_ring(*([FAKE.value] * 4))
+    return _lib.rssm_ring(*([FAKE.value] * 4), None, 0)
 
 
 def test_ring_sizes():
@@ -104,6 +104,16 @@ def test_host_validation_codes():
     r_odd.meta = FAKE.value + 64
     assert lib.replay_rollback(ctypes.byref(d), ctypes.byref(r_odd), P, None) == EINVAL
     assert lib.rssm_ring_reset(ctypes.byref(d), ctypes.byref(r_odd), None, None) == EINVAL
+
+    # a pooled ring needs at least one row
+    r_pool = _ring()
+    r_pool.slots, r_pool.rows = FAKE.value, 0
+    assert lib.replay_append_decode(ctypes.byref(d), P, ctypes.byref(r_pool), P, P, P, P, P, P, P,
+                                    None, None) == EINVAL
+    assert lib.replay_rollback(ctypes.byref(d), ctypes.byref(r_pool), P, None) == EINVAL
+    r_pool.rows = 3
+    assert lib.replay_append_decode(ctypes.byref(_dims(d=96)), P, ctypes.byref(r_pool), P, P, P, P, P,
+                                    P, P, None, None) == ENOTSUP
 
     # GDN append-decode: ring required, L in [1, 32], supported (d, n)
     assert lib.gdn_replay_append_decode(ctypes.byref(d), P, None, P, P, P, P, P, P, None, None) == EINVAL
