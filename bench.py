@@ -491,6 +491,67 @@ def _row_gdn_append(torch, np, rd, synth, traffic, dev, stream):
             "standard_step": std, "speedup": round(std["us"] / float(us.mean()), 3)}
 
 
+def _row_fused_conv(torch, np, rd, synth, traffic, dev, stream):
+    """The layer's front-end fused into the append: conv1d + SiLU over the xBC
+    channels (C = H d + 2 G n = 4096 at the Nemotron-H-like shape) producing v, k, q
+    in the same launch, against the conv kernel followed by the append kernel (its
+    v, k, q already in bf16: the cast between them is not counted); two layer
+    instances rotated, per-step HIP-event times."""
+    wl = synth.WORKLOADS[1]
+    sh, seed = wl.shape, wl.cfg_seed
+    B, H, D, N, G, L = sh.batch, sh.nheads, sh.head_dim, sh.state_dim, sh.ngroups, sh.capacity
+    C, NLs, K = H * D + 2 * G * N, 2, 8 * L
+    dims = rd.Dims(B, H, D, N, G, L)
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    st = synth.mamba2_step_inputs(sh, seed, 1, 0)
+    ip = {k_: (bf(v_) if v_.dtype == np.uint16 else torch.from_numpy(v_).to(dev)) for k_, v_ in st.items()}
+    A, bias = synth.mamba2_head_params(sh, seed, 1)
+    A, bias = torch.from_numpy(A).to(dev), torch.from_numpy(bias).to(dev)
+    cs_bits, w_bits = synth.conv_layer(B, C, 4, seed, 1)
+    w = bf(w_bits)
+    x = bf(synth.conv_step_input(B, C, seed, 1, 0))
+    y = torch.empty((B, H, D), device=dev)
+    conv_out = torch.empty((B, C), device=dev)
+    layers = [{"S0": torch.randn((B, H, D, N), device=dev) * math.sqrt(0.1), "ring": rd.Ring(dims, device=dev),
+               "cs": [bf(cs_bits), bf(cs_bits)]} for _ in range(NLs)]
+
+    def fused(t):
+        Ly = layers[t % NLs]
+        rd.replay_append_decode_conv(dims, Ly["S0"], Ly["ring"], Ly["cs"][(t // NLs) % 2], Ly["cs"][(t // NLs + 1) % 2],
+                                     x, w, ip["dt"], bias, A, y, stream=stream)
+
+    def unfused(t):
+        Ly = layers[t % NLs]
+        rd.causal_conv1d_update(Ly["cs"][0], x, w, conv_out, stream=stream)
+        rd.replay_append_decode(dims, Ly["S0"], Ly["ring"], ip["v"], ip["k"], ip["q"], ip["dt"], bias, A, y,
+                                stream=stream)
+    res = {"workload": f"Mamba-2 layer step, batch {B}, {H} heads, head dim {D}, state {N}, {G} groups, "
+                       f"ring capacity {L}, conv over C = {C} xBC channels (width 4); two layer instances rotated",
+           "kernel": "replay_append_decode_conv", "steps_timed": K}
+    byts = float(np.mean([traffic.replay_append_conv(B, H, D, N, G, h, h == L - 1) for h in range(L)]))
+    for name, fn in (("unfused_conv_then_append", unfused), ("fused", fused)):
+        for Ly in layers:
+            rd.rssm_ring_reset(dims, Ly["ring"], stream=stream)
+        for t in range(NLs * L):
+            fn(t)
+        ev = _events(torch, K)
+        torch.cuda.synchronize()
+        for i in range(K):
+            ev[i][0].record(stream)
+            fn(i)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        us = float(np.mean([1e3 * a_.elapsed_time(b_) for a_, b_ in ev]))
+        res[name] = {"us_per_step": round(us, 3), "GBs": round(byts / (us * 1e-6) / 1e9, 1),
+                     "tokens_per_s": round(B / (us * 1e-6), 1)}
+    res["alg_bytes_per_step"] = round(byts)
+    res["speedup"] = round(res["unfused_conv_then_append"]["us_per_step"] / res["fused"]["us_per_step"], 3)
+    return res
+
+
 def _row_pooled(torch, np, rd, synth, traffic, dev, stream):
     """Append-decode at the Nemotron-H-like shape with the checkpoints and rings in
     a pool of 2B request rows, each call's batch entries scattered over the pool
@@ -654,6 +715,7 @@ def _rows(torch, np, rd, synth, traffic, dev, stream):
             "gdn_append_decode": _row_gdn_append(torch, np, rd, synth, traffic, dev, stream),
             "max_concurrency": _row_capacity(torch, np, rd, synth, dev),
             "pooled_append_decode": _row_pooled(torch, np, rd, synth, traffic, dev, stream),
+            "fused_front_end": _row_fused_conv(torch, np, rd, synth, traffic, dev, stream),
             "window_sweep": {"mamba2": _row_window(torch, np, rd, synth, traffic, dev, stream, 2, False),
                              "gdn": _row_window(torch, np, rd, synth, traffic, dev, stream, 4, True)}}
 

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define RSSM_ABI_VERSION 6
+#define RSSM_ABI_VERSION 7
 
 #define RSSM_OK 0
 #define RSSM_EINVAL (-22)
@@ -176,6 +176,30 @@ int replay_append_decode(const rssm_dims* dims, float* state0, rssm_ring* ring,
                          const uint16_t* v, const uint16_t* k, const uint16_t* q,
                          const float* dt, const float* dt_bias, const float* A, float* y,
                          int32_t* flushed, void* stream);
+
+/*
+ * replay_append_decode with the layer's front-end fused in: the token's v, k, q
+ * are produced in the same launch by the causal depthwise conv1d (width 4) with
+ * SiLU over the layer's xBC channels, the step before the mixer (vLLM hybrid
+ * page: conv state (dim, state_len), "DS" layout), instead of being read as
+ * inputs.  Channel order of xBC (C = H d + 2 G n channels): x of head h at
+ * h d .. h d + d - 1 (-> v), B of group g at H d + g n .. (-> k), C of group g at
+ * H d + G n + g n .. (-> q).  Per channel, window = [state[0..2], xbc]:
+ *     out = SiLU(sum_w conv_w[c, w] window[w]),  new state = window[1..3];
+ * v, k, q = out rounded to bf16 (nearest even), then the ReplaySSM step exactly
+ * as replay_append_decode.
+ *   conv_state_in  bf16 [B, C, 3] (pooled: [rows, C, 3]) read
+ *   conv_state_out bf16 [B, C, 3] written; must not be conv_state_in (the heads
+ *                  of a group read B and C states while one of them writes them):
+ *                  swap the two buffers every step
+ *   xbc bf16 [B, C];  conv_w bf16 [C, 4] (no bias);  other arguments as
+ *   replay_append_decode.
+ */
+int replay_append_decode_conv(const rssm_dims* dims, float* state0, rssm_ring* ring,
+                              const uint16_t* conv_state_in, uint16_t* conv_state_out,
+                              const uint16_t* xbc, const uint16_t* conv_w, const float* dt,
+                              const float* dt_bias, const float* A, float* y, int32_t* flushed,
+                              void* stream);
 
 /*
  * Explicit flush of the committed entries (method, "core idea": summarise the

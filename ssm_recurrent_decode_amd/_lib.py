@@ -20,7 +20,7 @@ RSSM_ERR_POINTERS = 1
 RSSM_ERR_ACCEPTED = 2
 RSSM_ERR_PENDING = 4
 RSSM_ERR_SLOT = 8
-ABI_VERSION = 6  # RSSM_ABI_VERSION of the header this binding follows
+ABI_VERSION = 7  # RSSM_ABI_VERSION of the header this binding follows
 
 
 class rssm_dims(ctypes.Structure):
@@ -45,6 +45,7 @@ SIGNATURES = {
     "rssm_ring_reset": (c_int, [_D, _R, _P, _P]),
     "ssm_decode_step": (c_int, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "replay_append_decode": (c_int, [_D, _P, _R, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "replay_append_decode_conv": (c_int, [_D, _P, _R, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "replay_flush": (c_int, [_D, _P, _R, _P, _P]),
     "replay_verify_T": (c_int, [_D, c_int32, _P, _R, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "replay_rollback": (c_int, [_D, _R, _P, _P]),

@@ -195,6 +195,21 @@ def replay_append_decode(dims: Dims, state0, ring: Ring, v, k, q, dt, dt_bias, A
                "replay_append_decode")
 
 
+def replay_append_decode_conv(dims: Dims, state0, ring: Ring, conv_state_in, conv_state_out, xbc, conv_w,
+                              dt, dt_bias, A, y, flushed=None, stream=None):
+    B, H, D, N, G = dims.batch, dims.nheads, dims.head_dim, dims.state_dim, dims.ngroups
+    C = H * D + 2 * G * N
+    d, rc = dims.c(), _ring_args(dims, ring, False)
+    args = (_p(state0, "state0", _F32, (ring.rows, H, D, N)), ctypes.byref(rc),
+            _p(conv_state_in, "conv_state_in", _BF16, (ring.rows, C, 3)),
+            _p(conv_state_out, "conv_state_out", _BF16, (ring.rows, C, 3)),
+            _p(xbc, "xbc", _BF16, (B, C)), _p(conv_w, "conv_w", _BF16, (C, 4)),
+            _p(dt, "dt", _F32, (B, H)), _p(dt_bias, "dt_bias", _F32, (H,)), _p(A, "A", _F32, (H,)),
+            _p(y, "y", _F32, (B, H, D)), _p(flushed, "flushed", _I32, (B,), allow_none=True))
+    _lib.check(_lib.load().replay_append_decode_conv(ctypes.byref(d), *args, _stream(stream)),
+               "replay_append_decode_conv")
+
+
 def replay_flush(dims: Dims, state0, ring: Ring, mask=None, stream=None):
     B, H, D, N = dims.batch, dims.nheads, dims.head_dim, dims.state_dim
     d, rc = dims.c(), _ring_args(dims, ring, False)

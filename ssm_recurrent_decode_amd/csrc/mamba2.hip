@@ -279,6 +279,30 @@ extern "C" int replay_append_decode(const rssm_dims* dims, float* state0, rssm_r
   return rssm_host::launch_window<128, 1, true>(p, dims->batch, stream);
 }
 
+extern "C" int replay_append_decode_conv(const rssm_dims* dims, float* state0, rssm_ring* ring,
+                                         const uint16_t* conv_state_in, uint16_t* conv_state_out,
+                                         const uint16_t* xbc, const uint16_t* conv_w, const float* dt,
+                                         const float* dt_bias, const float* A, float* y,
+                                         int32_t* flushed, void* stream) {
+  if (!rssm_host::dims_ok(dims) || !rssm_host::ring_ok(ring) || !state0 || !conv_state_in ||
+      !conv_state_out || !xbc || !conv_w || !dt || !dt_bias || !A || !y)
+    return RSSM_EINVAL;
+  if (conv_state_in == conv_state_out || dims->capacity < 1) return RSSM_EINVAL;
+  if (!rssm_host::ring_shape_supported(dims)) return RSSM_ENOTSUP;
+  ReplayParams p = make_replay_params(dims, state0, ring);
+  p.conv_in = conv_state_in;
+  p.conv_out = conv_state_out;
+  p.xbc = xbc;
+  p.conv_w = conv_w;
+  p.dt = dt;
+  p.dt_bias = dt_bias;
+  p.A = A;
+  p.y = y;
+  p.flushed = flushed;
+  if (dims->head_dim == 64) return rssm_host::launch_window<64, 1, true, true>(p, dims->batch, stream);
+  return rssm_host::launch_window<128, 1, true, true>(p, dims->batch, stream);
+}
+
 extern "C" int replay_flush(const rssm_dims* dims, float* state0, rssm_ring* ring,
                             const int32_t* mask, void* stream) {
   if (!rssm_host::dims_ok(dims) || !rssm_host::ring_ok(ring) || !state0) return RSSM_EINVAL;

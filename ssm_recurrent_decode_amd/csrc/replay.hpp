@@ -35,8 +35,24 @@ struct ReplayParams {
   const int32_t* mask;  // explicit flush only
   const int32_t* slots;  // pool row per batch entry, or null
   int rows;
+  // fused front-end (append only): depthwise causal conv1d (width 4) + SiLU over
+  // the layer's xBC channels [x (H*D) | B (G*N) | C (G*N)] produce v, k, q
+  const uint16_t* conv_in;   // bf16 [rows, C, 3] conv state read
+  uint16_t* conv_out;        // bf16 [rows, C, 3] conv state written (not conv_in)
+  const uint16_t* xbc;       // bf16 [B, C] conv inputs of this token
+  const uint16_t* conv_w;    // bf16 [C, 4] taps (the last multiplies the token)
   int H, G, L;
 };
+
+// fp64 -> bf16 bits, round to nearest even, in one rounding: the value is first
+// cut to fp32 toward zero with a sticky last bit (round to odd, 16 spare bits),
+// then rounded to bf16 -- the same as rounding the fp64 value directly.
+__device__ __forceinline__ uint32_t f64_to_bf16_rne(double x) {
+  const float t = __double2float_rz(x);
+  uint32_t u = __float_as_uint(t);
+  if ((double)t != x) u |= 1u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
 
 // Load the checkpoint tiles of one head (tile layout) into registers.
 template <int D, int N, int RT, int NCT>
@@ -69,10 +85,19 @@ __device__ __forceinline__ void load_tiles(float4 (&s)[RT][NCT], const float* S0
 // Weights are computed in logical order and stored by physical slot.  The new
 // entries and the record are written by the last stores of the kernel.  LCAP
 // (16 or 32) bounds L and sizes the arrays.
-template <int D, int N, int T, bool APPEND, int LCAP>
+//  CONV (APPEND only): v, k, q are not inputs but the SiLU outputs of the causal
+//    conv1d over this head's x channels and its group's B and C channels,
+//    rounded to bf16 (the precision of the ring); the conv states of the x
+//    channels are written by their head, those of B and C by the group's first
+//    head, into a second buffer (the group's other heads still read the first).
+template <int D, int N, int T, bool APPEND, int LCAP, bool CONV = false>
 __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
   static_assert(N == 128, "key/query staging assumes n = 128 (16 lanes x 8 values)");
   static_assert(LCAP == 16 || LCAP == 32, "ring capacity bound");
+  static_assert(!CONV || (APPEND && T == 1), "the fused front-end is one token");
+  constexpr int NCONV = D + 2 * N;  // channels of one head: its x, the group's B and C
+  constexpr int NCQ = NCONV / 4;     // threads of the conv, four channels each
+  static_assert(NCQ <= kBlock, "one pass of the conv");
   constexpr int NCT = N / 16;
   constexpr int RT = D / (16 * kWavesPerBlock);
   constexpr int VJ = LCAP / 4;         // physical slots per lane in the combine and fold
@@ -92,6 +117,7 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t s_q[T * N];
   __shared__ __attribute__((aligned(16))) uint16_t s_k[LCAP * N];  // keys to fold by slot
   __shared__ __attribute__((aligned(16))) uint16_t s_v[LCAP * D];  // values by slot
+  __shared__ __attribute__((aligned(16))) uint16_t s_conv[CONV ? NCONV : 8];  // v | k | q
 
   const int H = p.H, G = p.G, L = p.L;
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
@@ -107,23 +133,42 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
   float* rec = p.meta + bh * MS;  // this head's ring record
   const unsigned long long word = *reinterpret_cast<const unsigned long long*>(rec + kMetaPtr);
   uint4 qm[T], kin[T];
-#pragma unroll
-  for (int sd = 0; sd < T; ++sd) {
-    qm[sd] = ld_u4(p.q + (((size_t)b * T + sd) * G + g) * N + sub * 8);
-    kin[sd] = ld_u4(p.k + (((size_t)b * T + sd) * G + g) * N + sub * 8);
-  }
   uint4 newc[NCP];  // chunks of the new entries: the head's v, then the group's k
+  // conv operands of the four channels this thread computes (CONV only): state
+  // 4 x 3 bf16 (three 8-byte words), the token 4 bf16, the taps 4 x 4 bf16
+  int cch = 0;
+  uint2 cst[3], cxv;
+  uint4 cwv[2];
+  if constexpr (!CONV) {
 #pragma unroll
-  for (int i = 0; i < NCP; ++i) {
-    const int t = min(tid + i * kBlock, NCH - 1);
-    const uint16_t* src;
-    if (t < NEWV) {
-      src = p.v + (((size_t)b * T + t / (D / 8)) * H + h) * D + (t % (D / 8)) * 8;
-    } else {
-      const int tk = t - NEWV;
-      src = p.k + (((size_t)b * T + tk / (N / 8)) * G + g) * N + (tk % (N / 8)) * 8;
+    for (int sd = 0; sd < T; ++sd) {
+      qm[sd] = ld_u4(p.q + (((size_t)b * T + sd) * G + g) * N + sub * 8);
+      kin[sd] = ld_u4(p.k + (((size_t)b * T + sd) * G + g) * N + sub * 8);
     }
-    newc[i] = ld_u4(src);
+#pragma unroll
+    for (int i = 0; i < NCP; ++i) {
+      const int t = min(tid + i * kBlock, NCH - 1);
+      const uint16_t* src;
+      if (t < NEWV) {
+        src = p.v + (((size_t)b * T + t / (D / 8)) * H + h) * D + (t % (D / 8)) * 8;
+      } else {
+        const int tk = t - NEWV;
+        src = p.k + (((size_t)b * T + tk / (N / 8)) * G + g) * N + (tk % (N / 8)) * 8;
+      }
+      newc[i] = ld_u4(src);
+    }
+  } else {
+    if (tid < NCQ) {
+      const int C = H * D + 2 * G * N;
+      const int lc = 4 * tid;  // first local channel: x | B | C (segments of 4k channels)
+      cch = lc < D ? h * D + lc : (lc < D + N ? H * D + g * N + (lc - D) : H * D + G * N + g * N + (lc - D - N));
+      const uint16_t* sp = p.conv_in + ((size_t)rb * C + cch) * 3;
+#pragma unroll
+      for (int w = 0; w < 3; ++w) cst[w] = *reinterpret_cast<const uint2*>(sp + 4 * w);
+      cxv = *reinterpret_cast<const uint2*>(p.xbc + (size_t)b * C + cch);
+      cwv[0] = *reinterpret_cast<const uint4*>(p.conv_w + (size_t)cch * 4);
+      cwv[1] = *reinterpret_cast<const uint4*>(p.conv_w + (size_t)cch * 4 + 8);
+    }
   }
   float rec_l = 0.f, dt_draft = 0.f, dt_bias = 0.f, A_h = 0.f;
   if (wave == 0) {  // the whole record (step sizes of every slot), the drafts' raw dt
@@ -137,6 +182,69 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
   __builtin_amdgcn_sched_barrier(0);
   float4 st[RT][NCT];
   load_tiles<D, N, RT, NCT>(st, p.state0 + bh * D * N, wave, r, cq);
+
+  if constexpr (CONV) {
+    // ---- 2b. the token's v, k, q from the conv (its operands arrive ahead of
+    //      the checkpoint): window [s0, s1, s2, x], SiLU, bf16; shifted states out
+    const int C = H * D + 2 * G * N;
+    const bool owner = (h % hpg) == 0;
+    if (tid < NCQ) {
+      const int lc = 4 * tid;
+      // the 12 state values (channel m owns 3m .. 3m + 2, oldest first), 4 tokens, 16 taps
+      uint32_t sv[12], xv[4], wv[16];
+#pragma unroll
+      for (int w = 0; w < 3; ++w) {
+        sv[4 * w] = cst[w].x & 0xffffu;
+        sv[4 * w + 1] = cst[w].x >> 16;
+        sv[4 * w + 2] = cst[w].y & 0xffffu;
+        sv[4 * w + 3] = cst[w].y >> 16;
+      }
+      xv[0] = cxv.x & 0xffffu;
+      xv[1] = cxv.x >> 16;
+      xv[2] = cxv.y & 0xffffu;
+      xv[3] = cxv.y >> 16;
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const uint32_t q4[4] = {cwv[w].x, cwv[w].y, cwv[w].z, cwv[w].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          wv[8 * w + 2 * e] = q4[e] & 0xffffu;
+          wv[8 * w + 2 * e + 1] = q4[e] >> 16;
+        }
+      }
+      uint32_t o[4], ns[12];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t win[4] = {sv[3 * m], sv[3 * m + 1], sv[3 * m + 2], xv[m]};
+        // fp64 (as fast as fp32 on this part): the products of bf16 values are
+        // exact and the sum runs oldest tap first, so the value whose rounding to
+        // bf16 is decided here does not depend on contraction or library rounding
+        double z = (double)bf16_to_f32(wv[4 * m]) * (double)bf16_to_f32(win[0]);
+#pragma unroll
+        for (int k = 1; k < 4; ++k) z = z + (double)bf16_to_f32(wv[4 * m + k]) * (double)bf16_to_f32(win[k]);
+        o[m] = f64_to_bf16_rne(z / (1.0 + exp(-z)));
+        ns[3 * m] = win[1];
+        ns[3 * m + 1] = win[2];
+        ns[3 * m + 2] = win[3];
+      }
+      *reinterpret_cast<uint2*>(&s_conv[lc]) = make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16));
+      if (lc < D || owner) {
+        uint16_t* dp = p.conv_out + ((size_t)rb * C + cch) * 3;
+#pragma unroll
+        for (int w = 0; w < 3; ++w)
+          *reinterpret_cast<uint2*>(dp + 4 * w) = make_uint2(ns[4 * w] | (ns[4 * w + 1] << 16),
+                                                             ns[4 * w + 2] | (ns[4 * w + 3] << 16));
+      }
+    }
+    __syncthreads();
+    qm[0] = *reinterpret_cast<const uint4*>(&s_conv[D + N + sub * 8]);
+    kin[0] = *reinterpret_cast<const uint4*>(&s_conv[D + sub * 8]);
+#pragma unroll
+    for (int i = 0; i < NCP; ++i) {
+      const int t = min(tid + i * kBlock, NCH - 1);
+      newc[i] = *reinterpret_cast<const uint4*>(&s_conv[t < NEWV ? t * 8 : D + (t - NEWV) * 8]);
+    }
+  }
 
   // ---- 3. ring pointers (uniform per request), clamped into range
   const RingPtr rp = unpack_ptr(word);
@@ -379,11 +487,11 @@ namespace rssm_host {
 
 using rssm::ReplayParams;
 
-template <int D, int T, bool APPEND>
+template <int D, int T, bool APPEND, bool CONV = false>
 int launch_window(const ReplayParams& p, int B, void* stream) {
   const dim3 grid(B * p.H), block(rssm::kBlock);
-  if (p.L <= 16) return launch(rssm::replay_window_kernel<D, 128, T, APPEND, 16>, grid, block, stream, p);
-  return launch(rssm::replay_window_kernel<D, 128, T, APPEND, 32>, grid, block, stream, p);
+  if (p.L <= 16) return launch(rssm::replay_window_kernel<D, 128, T, APPEND, 16, CONV>, grid, block, stream, p);
+  return launch(rssm::replay_window_kernel<D, 128, T, APPEND, 32, CONV>, grid, block, stream, p);
 }
 
 // Verify launchers for T = 1..4 and T = 5..8 live in their own translation units.

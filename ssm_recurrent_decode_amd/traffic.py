@@ -39,6 +39,15 @@ def replay_append(B, H, d, n, G, h, flush: bool) -> int:
     return B * per_req + 2 * F32 * H
 
 
+def replay_append_conv(B, H, d, n, G, h, flush: bool, W: int = 4) -> int:
+    """replay_append_decode_conv: as replay_append, with the conv state of the
+    C = H d + 2 G n xBC channels read and written (bf16, W - 1 per channel) and
+    the taps read once; the token's xBC (2C bytes) replaces the v, k, q inputs,
+    which are the same bytes."""
+    C = H * d + 2 * G * n
+    return replay_append(B, H, d, n, G, h, flush) + B * C * 2 * BF16 * (W - 1) + C * W * BF16
+
+
 def replay_verify(B, H, d, n, G, T, c, flush: bool) -> int:
     """replay_verify_T with c committed entries: checkpoint read, c cached entries,
     T drafts in, T outputs, T new entries cached, checkpoint write on a flush."""

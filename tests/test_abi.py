@@ -32,7 +32,7 @@ def test_every_declared_function_is_exported_and_prototyped():
 
 def test_abi_version_and_strerror():
     lib = _lib.load()
-    assert lib.rssm_abi_version() == _lib.ABI_VERSION == 6
+    assert lib.rssm_abi_version() == _lib.ABI_VERSION == 7
     assert "invalid" in _lib.strerror(_lib.RSSM_EINVAL)
     assert "not supported" in _lib.strerror(_lib.RSSM_ENOTSUP)
 
@@ -104,6 +104,15 @@ def test_host_validation_codes():
     r_odd.meta = FAKE.value + 64
     assert lib.replay_rollback(ctypes.byref(d), ctypes.byref(r_odd), P, None) == EINVAL
     assert lib.rssm_ring_reset(ctypes.byref(d), ctypes.byref(r_odd), None, None) == EINVAL
+
+    # fused front-end: both conv buffers present and distinct
+    assert lib.replay_append_decode_conv(ctypes.byref(d), P, ctypes.byref(r), P, P, P, P, P, P, P, P,
+                                         None, None) == EINVAL
+    Q = ctypes.c_void_p(0x2000)
+    assert lib.replay_append_decode_conv(ctypes.byref(d), P, ctypes.byref(r), None, Q, P, P, P, P, P, P,
+                                         None, None) == EINVAL
+    assert lib.replay_append_decode_conv(ctypes.byref(_dims(d=96)), P, ctypes.byref(r), P, Q, P, P, P, P,
+                                         P, P, None, None) == ENOTSUP
 
     # a pooled ring needs at least one row
     r_pool = _ring()

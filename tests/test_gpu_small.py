@@ -345,6 +345,52 @@ def test_gdn_replay_append_decode_small(d, G, L):
     assert rel_err(state0.cpu().numpy(), S) <= S_TOL
 
 
+@pytest.mark.parametrize("d,G,L", [(64, 1, 8), (64, 2, 5), (128, 4, 16)])
+def test_replay_append_decode_conv_small(d, G, L):
+    """Fused front-end: conv1d + SiLU over the xBC channels gives v, k, q (bf16),
+    then the ReplaySSM step.  y every step against the oracle conv -> bf16 ->
+    recurrence; the written conv state bit-exact every step (buffers swapped);
+    the checkpoint at every flush."""
+    base = synth.WORKLOADS[0]
+    sh = base.shape.with_(head_dim=d, ngroups=G, capacity=L)
+    B, H, N = sh.batch, sh.nheads, sh.state_dim
+    C = H * d + 2 * G * N
+    seed, steps = base.cfg_seed, 2 * L + 3
+    A, dt_bias = synth.mamba2_head_params(sh, seed, 0)
+    S0 = synth.state0(sh, seed, 0)
+    cs_bits, w_bits = synth.conv_layer(B, C, 4, seed, 0)
+    dims = _dims(sh)
+    ring = rd.Ring(dims)
+    state0 = dev_f32(S0)
+    cs = [dev_bf16(cs_bits), dev_bf16(cs_bits)]
+    w = dev_bf16(w_bits)
+    y = torch.empty(B, H, d, device="cuda")
+    flushed = torch.zeros(B, dtype=torch.int32, device="cuda")
+    S = S0.astype(np.float64)
+    cs64 = synth.bf16_bits_to_f64(cs_bits)
+    W64 = synth.bf16_bits_to_f64(w_bits)
+    for t in range(steps):
+        x_bits = synth.conv_step_input(B, C, seed, 0, t)
+        dt = synth.mamba2_step_inputs(sh, seed, 0, t)["dt"]
+        cin, cout = cs[t % 2], cs[(t + 1) % 2]
+        rd.replay_append_decode_conv(dims, state0, ring, cin, cout, dev_bf16(x_bits), w, dev_f32(dt),
+                                     dev_f32(dt_bias), dev_f32(A), y, flushed)
+        out, cs64 = o_conv.update(cs64, synth.bf16_bits_to_f64(x_bits), W64)
+        v, k, q = o_conv.split_xbc(o_conv.round_bf16(out), H, d, G, N)
+        delta, a = o_m2.step_size_and_decay(dt.astype(np.float64), dt_bias.astype(np.float64),
+                                            A.astype(np.float64))
+        S, y_ref = o_m2.standard_step(S, v, k, q, delta, a, G)
+        e = rel_err(y.cpu().numpy(), y_ref)
+        assert e <= Y_TOL, (t, e)
+        got = synth.bf16_bits_to_f64(cout.view(torch.int16).cpu().numpy().view(np.uint16))
+        assert np.array_equal(got, cs64), t
+        fl = (t + 1) % L == 0
+        assert bool(torch.all(flushed == int(fl))), t
+        if fl:
+            assert rel_err(state0.cpu().numpy(), S) <= S_TOL, t
+    assert int(ring.err.item()) == 0
+
+
 def test_causal_conv1d_update_config1_size():
     wl = synth.WORKLOADS[1]
     B, C = wl.shape.batch, wl.conv_channels
