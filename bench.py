@@ -68,6 +68,42 @@ def _calibrate_copy():
                       "bytes_written_per_launch": n, "launches": 8}))
 
 
+def _ceiling_probes(torch, rd, dev, stream, launch_bytes):
+    """This part's streaming ceilings, measured in the same process: the read probe
+    over one launch's checkpoint bytes (four buffers rotated, so nothing stays in
+    the 256 MB Infinity Cache) and over 1 GiB, and the 1 GiB copy probe (read +
+    write); mean of 16 back-to-back launches timed with HIP events."""
+    res = {}
+    for name, nbytes, nbuf, copy in (("read_one_launch", launch_bytes, 4, False),
+                                     ("read_1GiB", 1 << 30, 1, False), ("copy_1GiB", 1 << 30, 1, True)):
+        nbytes -= nbytes % 16
+        bufs = [torch.empty(nbytes // 4, device=dev) for _ in range(nbuf)]
+        for b_ in bufs:
+            b_.zero_()
+        dst = torch.empty_like(bufs[0]) if copy else None
+        sink = torch.empty(rd.probe_read_sink_floats(nbytes), device=dev)
+
+        def run(i):
+            if copy:
+                rd.rssm_probe_copy(dst, bufs[i % nbuf], stream=stream)
+            else:
+                rd.rssm_probe_read(bufs[i % nbuf], sink, stream=stream)
+        for i in range(4):
+            run(i)
+        ev = _events(torch, 16)
+        torch.cuda.synchronize()
+        for i in range(16):
+            ev[i][0].record(stream)
+            run(i)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        us = sum(1e3 * a_.elapsed_time(b_) for a_, b_ in ev) / 16
+        moved = nbytes * (2 if copy else 1)
+        res[name] = {"bytes": moved, "us": round(us, 2), "GBs": round(moved / (us * 1e-6) / 1e9, 1)}
+        del bufs, dst, sink
+    return res
+
+
 def _cpu_baseline(steps: int):
     """The CPU oracle (ReplaySSM standard mode, float64) on the full batch of the
     same workload for `steps` decode steps; single-threaded numpy elementwise code."""
@@ -873,6 +909,7 @@ def main(argv=None) -> int:
     ms_per_step = total_ms / K
     value = B * K / (total_ms / 1e3)
     traffic_bytes, traffic_note = profiling.stored_traffic("replay_append_decode")
+    ceiling = _ceiling_probes(torch, rd, dev, stream, B * H * D * N * 4)
 
     out = {
         "metric": "SSM decode tokens/s at batch 256 (Mamba-2 shape); achieved HBM GB/s vs peak",
@@ -890,7 +927,9 @@ def main(argv=None) -> int:
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_bytes,
                      "traffic_note": traffic_note,
                      "kernel_avg_us": round(1e3 * kern_avg_ms, 3),
-                     "alg_bytes_per_launch": round(alg_bytes / K)},
+                     "alg_bytes_per_launch": round(alg_bytes / K),
+                     "frac_of_read_probe": round(achieved / ceiling["read_one_launch"]["GBs"], 4)},
+        "ceiling_probes": ceiling,
         "conv1d": {"kernel": "causal_conv1d_update", "us": round(1e3 * conv_avg_ms, 3),
                    "achieved_GBs": round(traffic.conv1d(B, C, W) / (conv_avg_ms * 1e-3) / 1e9, 1),
                    "alg_bytes": traffic.conv1d(B, C, W)},

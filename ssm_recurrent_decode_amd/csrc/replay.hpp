@@ -114,6 +114,7 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
   __shared__ float s_fw[LCAP];         // fold weights by physical slot
   __shared__ float s_fabar;
   __shared__ float s_dtn[T];  // the new entries' step sizes
+  __shared__ __attribute__((aligned(16))) float s_y[T * D];  // outputs, stored whole lines at the end
   __shared__ __attribute__((aligned(16))) uint16_t s_q[T * N];
   __shared__ __attribute__((aligned(16))) uint16_t s_k[LCAP * N];  // keys to fold by slot
   __shared__ __attribute__((aligned(16))) uint16_t s_v[LCAP * D];  // values by slot
@@ -410,8 +411,8 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
         z = mfma4(vj[rt][m], wm[m], z);
       }
       if (draft)
-        st_f4(p.y + (((size_t)b * T + rd) * H + h) * D + (wave * RT + rt) * 16 + cq * 4,
-              make_float4(z[0], z[1], z[2], z[3]));
+        *reinterpret_cast<float4*>(&s_y[rd * D + (wave * RT + rt) * 16 + cq * 4]) =
+            make_float4(z[0], z[1], z[2], z[3]);
     }
   } else {
 #pragma unroll
@@ -434,12 +435,20 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
           part += s_w[sd][sl] * s_M[sd][sl] * vj[rt][m];  // zero for slots not read
         }
         part = reduce_row4(part);
-        if ((sd & 3) == cq) p.y[(((size_t)b * T + sd) * H + h) * D + row] = part;
+        if ((sd & 3) == cq) s_y[sd * D + row] = part;
       }
     }
   }
   if (F > 0)
     fold_and_store<D, N, RT, NCT, VJ>(p.state0 + bh * D * N, st, s_fabar, s_k, s_fw, vj, L, wave, r, cq);
+
+  // ---- 8b. the outputs, each draft's D values as whole lines (the waves hold 16
+  //      rows each: staged through LDS, a quarter-line store per wave cost more)
+  __syncthreads();
+  for (int i = tid; i < T * D / 4; i += kBlock) {
+    const int sd = i / (D / 4), o = (i % (D / 4)) * 4;
+    st_f4(p.y + (((size_t)b * T + sd) * H + h) * D + o, *reinterpret_cast<const float4*>(&s_y[sd * D + o]));
+  }
 
   // ---- 9. the new entries cached in the ring unless this call empties it: v of
   //      this head, k by the group's first head.  Stores are issued last

@@ -363,3 +363,67 @@ def test_gdn_append_decode_full():
             assert es <= S_TOL, (t, es)
     assert ring.copies_agree()
     assert int(ring.err.item()) == 0
+
+
+def test_fused_front_end_full():
+    """replay_append_decode_conv at the Nemotron-H-like size (B=256, H=32, d=64,
+    G=8, L=16, C = H d + 2 G n = 4096 xBC channels), 48 steps (3 flushes): sampled
+    y every step and the sampled checkpoint at every flush against the oracle's
+    conv -> bf16 -> recurrence on those (request, head) pairs' channels; the whole
+    written conv state bit-exact every 8 steps."""
+    wl = synth.WORKLOADS[1]
+    sh = wl.shape
+    B, H, D, N, G, L = sh.batch, sh.nheads, sh.head_dim, sh.state_dim, sh.ngroups, sh.capacity
+    C, seed = H * D + 2 * G * N, wl.cfg_seed
+    A, bias = synth.mamba2_head_params(sh, seed, 1)
+    S0 = synth.state0(sh, seed, 1)
+    cs_bits, w_bits = synth.conv_layer(B, C, 4, seed, 1, layer=1)
+    pairs = sample_pairs(B, H, NPAIRS, seed=77)
+    bi, hi, gi = _pairs_arrays(pairs, H, G)
+    tb, th = pair_index(pairs)
+    # the channels each pair's oracle follows: its head's x, its group's B and C
+    chans = np.stack([np.concatenate([h * D + np.arange(D), H * D + g * N + np.arange(N),
+                                      H * D + G * N + g * N + np.arange(N)]) for h, g in zip(hi, gi)])
+    dims = rd.Dims(B, H, D, N, G, L)
+    ring = rd.Ring(dims)
+    state0 = dev_f32(S0)
+    cs = [dev_bf16(cs_bits), dev_bf16(cs_bits)]
+    w = dev_bf16(w_bits)
+    y = torch.empty(B, H, D, device="cuda")
+    S = S0[bi, hi].astype(np.float64)[:, None]
+    del S0
+    cs64_all = _f64(cs_bits)
+    W64 = _f64(w_bits)
+    sub_state = np.stack([cs64_all[b][ch] for b, ch in zip(bi, chans)])       # [P, 320, 3]
+    sub_w = np.stack([W64[ch] for ch in chans])                               # [P, 320, 4]
+    Ab, biasb = dev_f32(A), dev_f32(bias)
+    for t in range(48):
+        x_bits = synth.conv_step_input(B, C, seed, 1, t, layer=1)
+        dt = synth.mamba2_step_inputs(sh, seed, 1, t)["dt"]
+        cin, cout = cs[t % 2], cs[(t + 1) % 2]
+        rd.replay_append_decode_conv(dims, state0, ring, cin, cout, dev_bf16(x_bits), w, dev_f32(dt), biasb, Ab,
+                                     y)
+        x64 = _f64(x_bits)
+        xs = np.stack([x64[b][ch] for b, ch in zip(bi, chans)])              # [P, 320]
+        # per pair: the oracle conv over its own channels (each pair has its taps)
+        outs, states = [], []
+        for p_ in range(len(pairs)):
+            o_, s_ = o_conv.update(sub_state[p_:p_ + 1], xs[p_:p_ + 1], sub_w[p_])
+            outs.append(o_[0])
+            states.append(s_[0])
+        out = o_conv.round_bf16(np.stack(outs))
+        sub_state = np.stack(states)
+        v, k, q = out[:, None, :D], out[:, None, D:D + N], out[:, None, D + N:]
+        delta, a = o_m2.step_size_and_decay(dt[bi, hi].astype(np.float64)[:, None],
+                                            bias[hi].astype(np.float64)[:, None], A[hi].astype(np.float64)[:, None])
+        S, y_ref = o_m2.standard_step(S, v, k, q, delta, a, 1)
+        e = rel_err(y[tb, th].cpu().numpy(), y_ref[:, 0])
+        assert e <= Y_TOL, (t, e)
+        cs64_all = np.concatenate([cs64_all[:, :, 1:], x64[:, :, None]], axis=-1)   # the state shift
+        if t % 8 == 7:
+            got = _f64(cout.view(torch.int16).cpu().numpy().view(np.uint16))
+            assert np.array_equal(got, cs64_all), t
+        if (t + 1) % L == 0:
+            es = rel_err(state0[tb, th].cpu().numpy(), S[:, 0])
+            assert es <= S_TOL, (t, es)
+    assert int(ring.err.item()) == 0
