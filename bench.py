@@ -134,14 +134,17 @@ def _events(torch, n):
             for _ in range(n)]
 
 
-def _verify_bytes(traffic, gdn, H, D, N, G, T, L, counts):
+def _verify_bytes(traffic, gdn, H, D, N, G, T, L, counts, flags=0):
     """Algorithmic bytes of one verify launch from the committed counts the
-    kernel saw (one per request)."""
-    fn = traffic.gdn_verify if gdn else traffic.replay_verify
+    kernel saw (one per request); flags select bf16 y / bf16 GDN corrections."""
+    yb = 2 if flags & 1 else 4
     tot = 0
     for c in set(int(x) for x in counts):
         nb = int((counts == c).sum())
-        tot += fn(nb, H, D, N, G, T, c, c + 2 * T > L)
+        if gdn:
+            tot += traffic.gdn_verify(nb, H, D, N, G, T, c, c + 2 * T > L, yb, 2 if flags & 2 else 4)
+        else:
+            tot += traffic.replay_verify(nb, H, D, N, G, T, c, c + 2 * T > L, yb)
     return tot
 
 
@@ -154,7 +157,7 @@ def _draft_inputs(synth, sh, seed, cfg_id, r, gdn):
 
 
 def _row_verify(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, rounds=64, warm=16, T=None,
-                with_standard=True):
+                with_standard=True, flags=0):
     """Speculative verify rounds (verify kernel + device-side rollback) on two
     rotated layer instances.  A first pass records the committed count every
     request had before each round; the rings are reset and the same sequence is
@@ -164,7 +167,7 @@ def _row_verify(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, rounds=
     sh, seed = (wl.shape if T is None else wl.shape.with_(T=T)), wl.cfg_seed
     B, H, D, N, G, L, T = sh.batch, sh.nheads, sh.head_dim, sh.state_dim, sh.ngroups, sh.capacity, sh.T
     NLr, P, R = 2, 8, warm + rounds
-    dims = rd.Dims(B, H, D, N, G, L)
+    dims = rd.Dims(B, H, D, N, G, L, flags=flags)
 
     def bf(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -186,7 +189,7 @@ def _row_verify(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, rounds=
                      for k_, v_ in st.items()})
     acc = synth.accept_draws(seed, cfg_id, R, B, T)
     dacc = [torch.from_numpy(acc[r]).to(dev) for r in range(R)]
-    y = torch.empty((B, T, H, D), device=dev)
+    y = torch.empty((B, T, H, D), dtype=torch.bfloat16 if flags & 1 else torch.float32, device=dev)
     flushed = torch.zeros((B,), dtype=torch.int32, device=dev)
 
     def verify(r):
@@ -224,7 +227,7 @@ def _row_verify(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, rounds=
         raise RuntimeError(f"ring anomaly bits set: {errs}")
     v_us = [1e3 * ev_v[r][0].elapsed_time(ev_v[r][1]) for r in range(warm, R)]
     r_us = [1e3 * ev_v[r][1].elapsed_time(ev_r[r][1]) for r in range(warm, R)]
-    byts = [_verify_bytes(traffic, gdn, H, D, N, G, T, L, counts[r]) for r in range(warm, R)]
+    byts = [_verify_bytes(traffic, gdn, H, D, N, G, T, L, counts[r], flags) for r in range(warm, R)]
     fl = np.array([counts[r] + 2 * T > L for r in range(warm, R)])
     round_s = (sum(v_us) + sum(r_us)) * 1e-6
     gbs = sum(byts) / (sum(v_us) * 1e-6) / 1e9
@@ -351,6 +354,24 @@ def _snapshot_rounds(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, T,
     return {"kernel": "gdn_snapshot_verify_T" if gdn else "ssm_snapshot_verify_T", "verify_us": round(us, 3),
             "commit_us": round(sum(c_us) / rounds, 3), "achieved_GBs": round(byts / (us * 1e-6) / 1e9, 1),
             "alg_bytes_per_round": byts}
+
+
+def _row_precision(torch, np, rd, synth, traffic, dev, stream):
+    """The speculative verify rows again with the storage-precision options of the
+    method page's serving setup: bf16 outputs (Mamba-2), bf16 outputs and bf16
+    cached corrections (GDN); per round, against the default fp32 storage."""
+    out = {}
+    for name, cid, gdn, flags in (("mamba2_y_bf16", 2, False, 1), ("gdn_y_u_bf16", 4, True, 3)):
+        base = _row_verify(torch, np, rd, synth, traffic, dev, stream, cid, gdn, rounds=32, warm=8,
+                           with_standard=False)
+        var = _row_verify(torch, np, rd, synth, traffic, dev, stream, cid, gdn, rounds=32, warm=8,
+                          with_standard=False, flags=flags)
+        out[name] = {"workload": var["workload"], "flags": flags,
+                     "default_verify_us": base["verify_us"], "verify_us": var["verify_us"],
+                     "speedup": round(base["verify_us"] / var["verify_us"], 3),
+                     "alg_bytes_per_round": var["alg_bytes_per_round"], "achieved_GBs": var["achieved_GBs"],
+                     "verified_positions_per_s": var["verified_positions_per_s"]}
+    return out
 
 
 def _row_window(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, Ts=(1, 2, 3, 4, 5, 6), rounds=24,
@@ -752,6 +773,7 @@ def _rows(torch, np, rd, synth, traffic, dev, stream):
             "max_concurrency": _row_capacity(torch, np, rd, synth, dev),
             "pooled_append_decode": _row_pooled(torch, np, rd, synth, traffic, dev, stream),
             "fused_front_end": _row_fused_conv(torch, np, rd, synth, traffic, dev, stream),
+            "storage_precision": _row_precision(torch, np, rd, synth, traffic, dev, stream),
             "window_sweep": {"mamba2": _row_window(torch, np, rd, synth, traffic, dev, stream, 2, False),
                              "gdn": _row_window(torch, np, rd, synth, traffic, dev, stream, 4, True)}}
 

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define RSSM_ABI_VERSION 7
+#define RSSM_ABI_VERSION 8
 
 #define RSSM_OK 0
 #define RSSM_EINVAL (-22)
@@ -64,7 +64,25 @@ typedef struct rssm_dims {
   int32_t state_dim;  /* n: key / query length, columns of the per-head state  */
   int32_t ngroups;    /* G: k and q are shared by the H/G heads of a group     */
   int32_t capacity;   /* L: ring capacity (ignored by the standard-step calls) */
+  int32_t flags;      /* RSSM_F_* storage-precision options; 0 = fp32 y and GDN u   */
 } rssm_dims;
+
+/*
+ * Storage-precision options (the precision the method page's serving setup keeps
+ * decode vectors in: bf16; the default here is fp32 for y and for the GDN
+ * corrections, see each entry point).  Unknown bits: RSSM_EINVAL.
+ *   RSSM_F_Y_BF16  outputs y stored as bf16 (round to nearest even) instead of
+ *                  fp32, same shape; honoured by replay_append_decode(_conv),
+ *                  replay_verify_T, gdn_replay_verify_T, gdn_replay_append_decode;
+ *                  the standard-step and snapshot calls return RSSM_ENOTSUP.
+ *   RSSM_F_U_BF16  GDN rings cache the corrections u as bf16 [B, H, L, d] (a
+ *                  property of the ring: every call on it must carry the flag, and
+ *                  rssm_ring_sizes sizes vu by it).  The outputs of the call that
+ *                  computes u use it unrounded; later calls (and a fold) read the
+ *                  rounded value.  Mamba-2 calls ignore it.
+ */
+#define RSSM_F_Y_BF16 1
+#define RSSM_F_U_BF16 2
 
 /*
  * Per-request ReplaySSM decode memory besides the checkpoint state S_0.

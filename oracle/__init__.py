@@ -21,9 +21,11 @@ replay   ReplaySSM bookkeeping written out on its own: a ring of recent inputs, 
 gdn      Gated DeltaNet: the Householder-form recurrence, its snapshot semantics,
          the ReplaySSM route that caches the corrections u, and the chunk-wise
          lower-triangular solve for a draft window.
-conv1d   the causal depthwise conv1d state update with SiLU.
+conv1d   the causal depthwise conv1d state update with SiLU, and the split of a
+         Mamba-2 layer's xBC channels into v, k, q.
+rounding rounding to the bf16 grid, where a vector is handed on in bf16.
 
-Every function's docstring names the passage it follows.  Readings of passages the
-page leaves open are listed in DESIGN.md.  Nothing here is "parity unpinned": each
+Every function's docstring names the passage it follows, and states the reading
+taken where the page leaves a step open.  Nothing here is "parity unpinned": each
 function has at least one pin that does not reuse its own formula.
 """

@@ -18,6 +18,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from .rounding import round_bf16  # noqa: F401  (the fused front-end's output rounding)
+
 
 def silu(x):
     return x / (1.0 + np.exp(-x))
@@ -32,15 +34,6 @@ def update(state, x, weight):
     for w in range(1, window.shape[-1]):                            # oldest tap first
         pre = pre + prods[:, :, w]
     return silu(pre), window[:, :, 1:]
-
-
-def round_bf16(x):
-    """Nearest bf16 value of each float64 (8 significand bits, ties to even),
-    returned as float64; finite inputs within the bf16 range."""
-    x = np.asarray(x, np.float64)
-    m, e = np.frexp(x)                    # x = m * 2^e, 0.5 <= |m| < 1
-    scaled = m * 256.0                    # 8 significand bits above the point
-    return np.ldexp(np.round(scaled), e - 8)   # numpy rounds halves to even
 
 
 def split_xbc(out, H, d, G, n):

@@ -29,6 +29,7 @@ from __future__ import annotations
 import numpy as np
 
 from .mamba2 import group_of_head
+from .rounding import round_bf16
 
 
 def householder_step(S, v, k, q, g, beta, G):
@@ -77,7 +78,11 @@ class GDNReplayRequest:
     """ReplaySSM memory of one GDN request: checkpoint S_0 [H,d,n], ring of
     (u, k, alpha) with capacity L, head, count (committed), pending (drafts)."""
 
-    def __init__(self, S0, L: int, G: int):
+    def __init__(self, S0, L: int, G: int, u_bf16: bool = False):
+        """u_bf16: the ring keeps the corrections in bf16 -- each u is rounded
+        when it is cached; the outputs of the step that computes it use it
+        unrounded."""
+        self.u_bf16 = u_bf16
         self.S0 = np.array(S0, dtype=np.float64)
         self.H, self.d, self.n = self.S0.shape
         self.L, self.G = L, G
@@ -119,7 +124,7 @@ class GDNReplayRequest:
         kh, qh = k[self.grp], q[self.grp]
         u = beta[:, None] * (v - alpha[:, None] * np.sum(S_h * kh[:, None, :], axis=-1))
         y = alpha[:, None] * np.sum(S_h * qh[:, None, :], axis=-1) + u * np.sum(kh * qh, axis=-1)[:, None]
-        self.ring[(self.head + self.count) % self.L] = _Entry(u, k, alpha)
+        self.ring[(self.head + self.count) % self.L] = _Entry(self._cached(u), k, alpha)
         self.count += 1
         flushed = False
         if self.count == self.L:
@@ -150,7 +155,7 @@ class GDNReplayRequest:
             S = alpha[:, None, None] * S + u[:, :, None] * kh[:, None, :]
             ys.append(np.sum(S * qh[:, None, :], axis=-1))
             us.append(u)
-            self.ring[(self.head + c + s) % self.L] = _Entry(u, k[s], alpha)
+            self.ring[(self.head + c + s) % self.L] = _Entry(self._cached(u), k[s], alpha)
         self.pending = T
         flushed = False
         if c + 2 * T > self.L:
@@ -159,6 +164,9 @@ class GDNReplayRequest:
             self.count = 0
             flushed = True
         return np.stack(ys), np.stack(us), flushed
+
+    def _cached(self, u):
+        return round_bf16(u) if self.u_bf16 else u
 
     def flush(self):
         if self.count == 0:

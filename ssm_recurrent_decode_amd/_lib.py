@@ -20,12 +20,14 @@ RSSM_ERR_POINTERS = 1
 RSSM_ERR_ACCEPTED = 2
 RSSM_ERR_PENDING = 4
 RSSM_ERR_SLOT = 8
-ABI_VERSION = 7  # RSSM_ABI_VERSION of the header this binding follows
+RSSM_F_Y_BF16 = 1
+RSSM_F_U_BF16 = 2
+ABI_VERSION = 8  # RSSM_ABI_VERSION of the header this binding follows
 
 
 class rssm_dims(ctypes.Structure):
     _fields_ = [("batch", c_int32), ("nheads", c_int32), ("head_dim", c_int32),
-                ("state_dim", c_int32), ("ngroups", c_int32), ("capacity", c_int32)]
+                ("state_dim", c_int32), ("ngroups", c_int32), ("capacity", c_int32), ("flags", c_int32)]
 
 
 class rssm_ring(ctypes.Structure):

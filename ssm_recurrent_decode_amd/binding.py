@@ -29,10 +29,16 @@ class Dims:
     state_dim: int
     ngroups: int
     capacity: int = 1
+    flags: int = 0   # RSSM_F_Y_BF16 | RSSM_F_U_BF16
 
     def c(self) -> _lib.rssm_dims:
         return _lib.rssm_dims(self.batch, self.nheads, self.head_dim, self.state_dim,
-                              self.ngroups, self.capacity)
+                              self.ngroups, self.capacity, self.flags)
+
+    @property
+    def y_dtypes(self):
+        """Accepted dtypes of the outputs y under these flags."""
+        return _BF16 if self.flags & _lib.RSSM_F_Y_BF16 else _F32
 
 
 def _stream(stream) -> int:
@@ -90,7 +96,8 @@ class Ring:
         D, N = dims.head_dim, dims.state_dim
         self.dims, self.gdn, self.rows, self.slots = dims, gdn, B, None
         z = dict(device=device)
-        self.vu = torch.zeros((B, H, L, D), dtype=torch.float32 if gdn else torch.bfloat16, **z)
+        u32 = gdn and not (dims.flags & _lib.RSSM_F_U_BF16)
+        self.vu = torch.zeros((B, H, L, D), dtype=torch.float32 if u32 else torch.bfloat16, **z)
         self.k = torch.zeros((B, G, L, N), dtype=torch.bfloat16, **z)
         self.meta = torch.zeros((B, H, meta_words(L)), dtype=torch.float32, **z)
         self.err = torch.zeros((1,), dtype=torch.int32, **z)
@@ -190,7 +197,7 @@ def replay_append_decode(dims: Dims, state0, ring: Ring, v, k, q, dt, dt_bias, A
             _p(v, "v", _BF16, (B, H, D)), _p(k, "k", _BF16, (B, G, N)),
             _p(q, "q", _BF16, (B, G, N)), _p(dt, "dt", _F32, (B, H)),
             _p(dt_bias, "dt_bias", _F32, (H,)), _p(A, "A", _F32, (H,)),
-            _p(y, "y", _F32, (B, H, D)), _p(flushed, "flushed", _I32, (B,), allow_none=True))
+            _p(y, "y", dims.y_dtypes, (B, H, D)), _p(flushed, "flushed", _I32, (B,), allow_none=True))
     _lib.check(_lib.load().replay_append_decode(ctypes.byref(d), *args, _stream(stream)),
                "replay_append_decode")
 
@@ -205,7 +212,7 @@ def replay_append_decode_conv(dims: Dims, state0, ring: Ring, conv_state_in, con
             _p(conv_state_out, "conv_state_out", _BF16, (ring.rows, C, 3)),
             _p(xbc, "xbc", _BF16, (B, C)), _p(conv_w, "conv_w", _BF16, (C, 4)),
             _p(dt, "dt", _F32, (B, H)), _p(dt_bias, "dt_bias", _F32, (H,)), _p(A, "A", _F32, (H,)),
-            _p(y, "y", _F32, (B, H, D)), _p(flushed, "flushed", _I32, (B,), allow_none=True))
+            _p(y, "y", dims.y_dtypes, (B, H, D)), _p(flushed, "flushed", _I32, (B,), allow_none=True))
     _lib.check(_lib.load().replay_append_decode_conv(ctypes.byref(d), *args, _stream(stream)),
                "replay_append_decode_conv")
 
@@ -226,7 +233,7 @@ def replay_verify_T(dims: Dims, T: int, state0, ring: Ring, v, k, q, dt, dt_bias
             _p(v, "v", _BF16, (B, T, H, D)), _p(k, "k", _BF16, (B, T, G, N)),
             _p(q, "q", _BF16, (B, T, G, N)), _p(dt, "dt", _F32, (B, T, H)),
             _p(dt_bias, "dt_bias", _F32, (H,)), _p(A, "A", _F32, (H,)),
-            _p(y, "y", _F32, (B, T, H, D)), _p(flushed, "flushed", _I32, (B,), allow_none=True))
+            _p(y, "y", dims.y_dtypes, (B, T, H, D)), _p(flushed, "flushed", _I32, (B,), allow_none=True))
     _lib.check(_lib.load().replay_verify_T(ctypes.byref(d), int(T), *args, _stream(stream)),
                "replay_verify_T")
 
@@ -255,7 +262,7 @@ def gdn_replay_verify_T(dims: Dims, T: int, state0, ring: Ring, v, k, q, g, beta
     args = (_p(state0, "state0", _F32, (ring.rows, H, D, N)), ctypes.byref(rc),
             _p(v, "v", _BF16, (B, T, H, D)), _p(k, "k", _BF16, (B, T, G, N)),
             _p(q, "q", _BF16, (B, T, G, N)), _p(g, "g", _F32, (B, T, H)),
-            _p(beta, "beta", _F32, (B, T, H)), _p(y, "y", _F32, (B, T, H, D)),
+            _p(beta, "beta", _F32, (B, T, H)), _p(y, "y", dims.y_dtypes, (B, T, H, D)),
             _p(flushed, "flushed", _I32, (B,), allow_none=True))
     _lib.check(_lib.load().gdn_replay_verify_T(ctypes.byref(d), int(T), *args, _stream(stream)),
                "gdn_replay_verify_T")
@@ -267,7 +274,7 @@ def gdn_replay_append_decode(dims: Dims, state0, ring: Ring, v, k, q, g, beta, y
     d, rc = dims.c(), _ring_args(dims, ring, True)
     args = (_p(state0, "state0", _F32, (ring.rows, H, D, N)), ctypes.byref(rc),
             _p(v, "v", _BF16, (B, H, D)), _p(k, "k", _BF16, (B, G, N)), _p(q, "q", _BF16, (B, G, N)),
-            _p(g, "g", _F32, (B, H)), _p(beta, "beta", _F32, (B, H)), _p(y, "y", _F32, (B, H, D)),
+            _p(g, "g", _F32, (B, H)), _p(beta, "beta", _F32, (B, H)), _p(y, "y", dims.y_dtypes, (B, H, D)),
             _p(flushed, "flushed", _I32, (B,), allow_none=True))
     _lib.check(_lib.load().gdn_replay_append_decode(ctypes.byref(d), *args, _stream(stream)),
                "gdn_replay_append_decode")
@@ -376,7 +383,7 @@ def prepare_replay_append_decode(dims: Dims, state0, ring: Ring, v, k, q, dt, dt
             _p(v, "v", _BF16, (B, H, D)), _p(k, "k", _BF16, (B, G, N)),
             _p(q, "q", _BF16, (B, G, N)), _p(dt, "dt", _F32, (B, H)),
             _p(dt_bias, "dt_bias", _F32, (H,)), _p(A, "A", _F32, (H,)),
-            _p(y, "y", _F32, (B, H, D)), _p(flushed, "flushed", _I32, (B,), allow_none=True),
+            _p(y, "y", dims.y_dtypes, (B, H, D)), _p(flushed, "flushed", _I32, (B,), allow_none=True),
             _stream(stream))
     return Prepared(_lib.load().replay_append_decode, *args, keep=(d, rc))
 

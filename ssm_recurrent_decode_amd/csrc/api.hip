@@ -59,7 +59,7 @@ extern "C" int rssm_ring_sizes(const rssm_dims* d, int is_gdn, size_t out[4]) {
   if (d->capacity > rssm::kMaxL) return RSSM_ENOTSUP;
   const size_t B = d->batch, H = d->nheads, G = d->ngroups, L = d->capacity;
   const size_t D = d->head_dim, N = d->state_dim;
-  out[0] = B * H * L * D * (is_gdn ? 4 : 2);
+  out[0] = B * H * L * D * ((is_gdn && !(d->flags & RSSM_F_U_BF16)) ? 4 : 2);
   out[1] = B * G * L * N * 2;
   out[2] = B * H * (size_t)rssm::meta_words((int)L) * 4;
   out[3] = 4;

@@ -112,6 +112,12 @@ __device__ __forceinline__ float reduce_quarter(float v) {
 }
 
 __device__ __forceinline__ float4 ld_f4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+
+// fp32 -> bf16 bits, round to nearest even (finite values).
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
 __device__ __forceinline__ void st_f4(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
 __device__ __forceinline__ uint2 ld_u2(const uint16_t* p) { return *reinterpret_cast<const uint2*>(p); }
 __device__ __forceinline__ uint4 ld_u4(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -226,6 +232,7 @@ inline bool dims_ok(const rssm_dims* d) {
   if (d->batch < 1 || d->nheads < 1 || d->ngroups < 1 || d->head_dim < 1 || d->state_dim < 1)
     return false;
   if (d->nheads % d->ngroups != 0) return false;
+  if (d->flags & ~(RSSM_F_Y_BF16 | RSSM_F_U_BF16)) return false;
   if ((long long)d->batch * d->nheads > (1LL << 30)) return false;
   return true;
 }

@@ -132,7 +132,9 @@ __global__ __launch_bounds__(kBlock) void gdn_flush_kernel(GdnReplayParams p) {
 #pragma unroll
     for (int m = 0; m < kVJ; ++m) {
       const int j = cq + 4 * m;
-      uf[rt][m] = (j < F) ? p.ring_u[(bh * L + (head + j) % L) * D + row] : 0.f;
+      const size_t ua = (bh * L + (head + j) % L) * D + row;
+      uf[rt][m] = (j < F) ? (p.u_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(p.ring_u)[ua]) : p.ring_u[ua])
+                          : 0.f;
     }
   }
   if (wave == 0) {
@@ -177,6 +179,8 @@ GdnReplayParams make_gdn_params(const rssm_dims* d, float* state0, rssm_ring* ri
   p.err = ring->err;
   p.slots = ring->slots;
   p.rows = ring->rows;
+  p.y_bf16 = (d->flags & RSSM_F_Y_BF16) != 0;
+  p.u_bf16 = (d->flags & RSSM_F_U_BF16) != 0;
   p.H = d->nheads;
   p.G = d->ngroups;
   p.L = d->capacity;
@@ -189,7 +193,7 @@ extern "C" int gdn_decode_step(const rssm_dims* dims, float* state, const uint16
                                const uint16_t* k, const uint16_t* q, const float* g,
                                const float* beta, float* y, void* stream) {
   if (!rssm_host::dims_ok(dims) || !state || !v || !k || !q || !g || !beta || !y) return RSSM_EINVAL;
-  if (!rssm_host::shape_supported(dims)) return RSSM_ENOTSUP;
+  if (!rssm_host::shape_supported(dims) || (dims->flags & RSSM_F_Y_BF16)) return RSSM_ENOTSUP;
   GdnStdParams p{state, v, k, q, g, beta, y, dims->nheads, dims->ngroups};
   const dim3 grid(dims->batch * dims->nheads);
   if (dims->head_dim == 64) return launch(gdn_step_kernel<64, 128>, grid, dim3(kBlock), stream, p);

@@ -27,6 +27,8 @@ struct GdnReplayParams {
   const int32_t* mask;
   const int32_t* slots;  // pool row per batch entry, or null
   int rows;
+  int y_bf16;          // outputs stored as bf16
+  int u_bf16;          // ring corrections cached as bf16 [B, H, L, D]
   int H, G, L;
 };
 
@@ -169,12 +171,17 @@ __global__ __launch_bounds__(kBlock) void gdn_verify_kernel(GdnReplayParams p) {
     if (sl < L && logical(min(sl, L - 1)) < c)
       kr[ps] = ld_u4(p.ring_k + (((size_t)rb * G + g) * L + sl) * N + sub * 8);
   }
-  float4 uc[UP];
+  const int cpe = p.u_bf16 ? D / 8 : D / 4;  // 16-byte chunks per cached correction
+  uint4 uc[UP];
 #pragma unroll
   for (int i = 0; i < UP; ++i) {
     const int t = tid + i * kBlock;
-    uc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (t < c * (D / 4)) uc[i] = ld_f4(p.ring_u + (bh * L + ring_slot(head, t / (D / 4), L)) * D + (t % (D / 4)) * 4);
+    uc[i] = make_uint4(0, 0, 0, 0);
+    if (t < c * cpe) {
+      const size_t e = (bh * L + ring_slot(head, t / cpe, L)) * D;
+      uc[i] = p.u_bf16 ? ld_u4(reinterpret_cast<const uint16_t*>(p.ring_u) + e + (t % cpe) * 8)
+                       : *reinterpret_cast<const uint4*>(p.ring_u + e + (t % cpe) * 4);
+    }
   }
 
   // ---- 4. wave 0: decay weights of the committed entries (lane l takes logical
@@ -232,8 +239,18 @@ __global__ __launch_bounds__(kBlock) void gdn_verify_kernel(GdnReplayParams p) {
 #pragma unroll
   for (int i = 0; i < UP; ++i) {
     const int t = tid + i * kBlock;
-    if (t < c * (D / 4))
-      *reinterpret_cast<float4*>(&s_u[ring_slot(head, t / (D / 4), L) * D + (t % (D / 4)) * 4]) = uc[i];
+    if (t < c * cpe) {
+      float* dst = &s_u[ring_slot(head, t / cpe, L) * D];
+      if (p.u_bf16) {
+        const int o = (t % cpe) * 8;
+        *reinterpret_cast<float4*>(dst + o) =
+            make_float4(bf16_lo(uc[i].x), bf16_hi(uc[i].x), bf16_lo(uc[i].y), bf16_hi(uc[i].y));
+        *reinterpret_cast<float4*>(dst + o + 4) =
+            make_float4(bf16_lo(uc[i].z), bf16_hi(uc[i].z), bf16_lo(uc[i].w), bf16_hi(uc[i].w));
+      } else {
+        *reinterpret_cast<uint4*>(dst + (t % cpe) * 4) = uc[i];
+      }
+    }
   }
   __syncthreads();
 
@@ -322,9 +339,19 @@ __global__ __launch_bounds__(kBlock) void gdn_verify_kernel(GdnReplayParams p) {
         if (sp < sd) ratio *= s_alpha_d[sp + 1];
         acc += ratio * s_M[T + sd][dslot[sp]] * u[sp];
       }
-      p.y[(((size_t)b * T + sd) * H + h) * D + rho] = acc;
-      if (write_new) p.ring_u[(bh * L + dslot[sd]) * D + rho] = u[sd];
-      else s_u[dslot[sd] * D + rho] = u[sd];  // append filling the ring: folded below
+      const size_t at = (((size_t)b * T + sd) * H + h) * D + rho;
+      if (p.y_bf16) reinterpret_cast<uint16_t*>(p.y)[at] = (uint16_t)bf16_rne(acc);
+      else p.y[at] = acc;
+      // the correction as cached (rounded when the ring holds bf16); this call's
+      // outputs above used it unrounded
+      const uint32_t ub = bf16_rne(u[sd]);
+      const size_t ua = (bh * L + dslot[sd]) * D + rho;
+      if (write_new) {
+        if (p.u_bf16) reinterpret_cast<uint16_t*>(p.ring_u)[ua] = (uint16_t)ub;
+        else p.ring_u[ua] = u[sd];
+      } else {
+        s_u[dslot[sd] * D + rho] = p.u_bf16 ? bf16_to_f32(ub) : u[sd];  // append filling the ring: folded below
+      }
     }
   }
 

@@ -237,6 +237,7 @@ ReplayParams make_replay_params(const rssm_dims* d, float* state0, rssm_ring* ri
   p.err = ring->err;
   p.slots = ring->slots;
   p.rows = ring->rows;
+  p.y_bf16 = (d->flags & RSSM_F_Y_BF16) != 0;
   p.H = d->nheads;
   p.G = d->ngroups;
   p.L = d->capacity;
@@ -250,7 +251,7 @@ extern "C" int ssm_decode_step(const rssm_dims* dims, float* state, const uint16
                                const float* dt_bias, const float* A, float* y, void* stream) {
   if (!rssm_host::dims_ok(dims) || !state || !v || !k || !q || !dt || !dt_bias || !A || !y)
     return RSSM_EINVAL;
-  if (!rssm_host::shape_supported(dims)) return RSSM_ENOTSUP;
+  if (!rssm_host::shape_supported(dims) || (dims->flags & RSSM_F_Y_BF16)) return RSSM_ENOTSUP;
   StdParams p{state, v, k, q, dt, dt_bias, A, y, dims->nheads, dims->ngroups};
   const dim3 grid(dims->batch * dims->nheads);
   if (dims->head_dim == 64) return launch(ssm_step_kernel<64, 128>, grid, dim3(kBlock), stream, p);

@@ -41,6 +41,7 @@ struct ReplayParams {
   uint16_t* conv_out;        // bf16 [rows, C, 3] conv state written (not conv_in)
   const uint16_t* xbc;       // bf16 [B, C] conv inputs of this token
   const uint16_t* conv_w;    // bf16 [C, 4] taps (the last multiplies the token)
+  int y_bf16;                // outputs stored as bf16
   int H, G, L;
 };
 
@@ -447,7 +448,13 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
   __syncthreads();
   for (int i = tid; i < T * D / 4; i += kBlock) {
     const int sd = i / (D / 4), o = (i % (D / 4)) * 4;
-    st_f4(p.y + (((size_t)b * T + sd) * H + h) * D + o, *reinterpret_cast<const float4*>(&s_y[sd * D + o]));
+    const float4 f = *reinterpret_cast<const float4*>(&s_y[sd * D + o]);
+    const size_t at = (((size_t)b * T + sd) * H + h) * D + o;
+    if (p.y_bf16)
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.y) + at) =
+          make_uint2(bf16_rne(f.x) | (bf16_rne(f.y) << 16), bf16_rne(f.z) | (bf16_rne(f.w) << 16));
+    else
+      st_f4(p.y + at, f);
   }
 
   // ---- 9. the new entries cached in the ring unless this call empties it: v of

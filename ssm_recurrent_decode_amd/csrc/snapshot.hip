@@ -189,7 +189,7 @@ int snapshot_common(const rssm_dims* dims, int32_t T, int32_t nslots, float* poo
                     SnapParams& p) {
   if (!rssm_host::dims_ok(dims) || !pool || !slot || !v || !k || !q) return RSSM_EINVAL;
   if (T < 1 || nslots < T + 1) return RSSM_EINVAL;
-  if (!rssm_host::shape_supported(dims) || T > kMaxT) return RSSM_ENOTSUP;
+  if (!rssm_host::shape_supported(dims) || T > kMaxT || (dims->flags & RSSM_F_Y_BF16)) return RSSM_ENOTSUP;
   p.pool = pool;
   p.slot = slot;
   p.v = v;

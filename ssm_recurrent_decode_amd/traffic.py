@@ -48,12 +48,13 @@ def replay_append_conv(B, H, d, n, G, h, flush: bool, W: int = 4) -> int:
     return replay_append(B, H, d, n, G, h, flush) + B * C * 2 * BF16 * (W - 1) + C * W * BF16
 
 
-def replay_verify(B, H, d, n, G, T, c, flush: bool) -> int:
+def replay_verify(B, H, d, n, G, T, c, flush: bool, y_bytes: int = F32) -> int:
     """replay_verify_T with c committed entries: checkpoint read, c cached entries,
-    T drafts in, T outputs, T new entries cached, checkpoint write on a flush."""
+    T drafts in, T outputs (fp32, or bf16 with y_bytes = 2), T new entries
+    cached, checkpoint write on a flush."""
     per_req = (F32 * H * d * n + c * replay_slot(H, d, n, G)
                + T * (BF16 * H * d + 2 * BF16 * G * n + F32 * H)
-               + T * F32 * H * d + T * replay_slot(H, d, n, G) + 2 * PTR)
+               + T * y_bytes * H * d + T * replay_slot(H, d, n, G) + 2 * PTR)
     if flush:
         per_req += F32 * H * d * n
     return B * per_req + 2 * F32 * H
@@ -69,15 +70,16 @@ def gdn_flush(B, H, d, n, G, c) -> int:
     return B * (2 * F32 * H * d * n + c * gdn_slot(H, d, n, G) + 2 * PTR)
 
 
-def gdn_slot(H, d, n, G) -> int:
-    """One cached GDN entry: u (fp32), k (bf16 per group), alpha (fp32)."""
-    return F32 * H * d + BF16 * G * n + F32 * H
+def gdn_slot(H, d, n, G, u_bytes: int = F32) -> int:
+    """One cached GDN entry: u (fp32, or bf16 with u_bytes = 2), k (bf16 per
+    group), alpha (fp32)."""
+    return u_bytes * H * d + BF16 * G * n + F32 * H
 
 
-def gdn_verify(B, H, d, n, G, T, c, flush: bool) -> int:
-    per_req = (F32 * H * d * n + c * gdn_slot(H, d, n, G)
+def gdn_verify(B, H, d, n, G, T, c, flush: bool, y_bytes: int = F32, u_bytes: int = F32) -> int:
+    per_req = (F32 * H * d * n + c * gdn_slot(H, d, n, G, u_bytes)
                + T * (BF16 * H * d + 2 * BF16 * G * n + 2 * F32 * H)
-               + T * F32 * H * d + T * gdn_slot(H, d, n, G) + 2 * PTR)
+               + T * y_bytes * H * d + T * gdn_slot(H, d, n, G, u_bytes) + 2 * PTR)
     if flush:
         per_req += F32 * H * d * n
     return B * per_req

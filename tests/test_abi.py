@@ -32,7 +32,7 @@ def test_every_declared_function_is_exported_and_prototyped():
 
 def test_abi_version_and_strerror():
     lib = _lib.load()
-    assert lib.rssm_abi_version() == _lib.ABI_VERSION == 7
+    assert lib.rssm_abi_version() == _lib.ABI_VERSION == 8
     assert "invalid" in _lib.strerror(_lib.RSSM_EINVAL)
     assert "not supported" in _lib.strerror(_lib.RSSM_ENOTSUP)
 
@@ -123,6 +123,20 @@ def test_host_validation_codes():
     r_pool.rows = 3
     assert lib.replay_append_decode(ctypes.byref(_dims(d=96)), P, ctypes.byref(r_pool), P, P, P, P, P,
                                     P, P, None, None) == ENOTSUP
+
+    # storage-precision flags: unknown bits rejected; bf16 y only where honoured
+    bad_flags = _dims()
+    bad_flags.flags = 4
+    assert lib.ssm_decode_step(ctypes.byref(bad_flags), P, P, P, P, P, P, P, P, None) == EINVAL
+    ybf = _dims()
+    ybf.flags = _lib.RSSM_F_Y_BF16
+    assert lib.ssm_decode_step(ctypes.byref(ybf), P, P, P, P, P, P, P, P, None) == ENOTSUP
+    assert lib.gdn_decode_step(ctypes.byref(ybf), P, P, P, P, P, P, P, None) == ENOTSUP
+    assert lib.ssm_snapshot_verify_T(ctypes.byref(ybf), 2, 3, P, P, P, P, P, P, P, P, P, None, None) == ENOTSUP
+    out = (ctypes.c_size_t * 4)()
+    ubf = _dims(B=2, H=4, d=64, L=8)
+    ubf.flags = _lib.RSSM_F_U_BF16
+    assert lib.rssm_ring_sizes(ctypes.byref(ubf), 1, out) == 0 and out[0] == 2 * 4 * 8 * 64 * 2
 
     # GDN append-decode: ring required, L in [1, 32], supported (d, n)
     assert lib.gdn_replay_append_decode(ctypes.byref(d), P, None, P, P, P, P, P, P, None, None) == EINVAL

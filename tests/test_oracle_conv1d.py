@@ -4,7 +4,7 @@ shift is exact."""
 import numpy as np
 import scipy.special
 
-from oracle import conv1d
+from oracle import conv1d, rounding
 
 
 def test_conv_update_equals_full_causal_convolution():
@@ -39,12 +39,12 @@ def test_silu_special_values():
 
 def test_round_bf16_ties_and_carry():
     one = 1.0
-    assert conv1d.round_bf16(one + 2.0**-8) == one                   # tie -> even (1.0)
-    assert conv1d.round_bf16(one + 3 * 2.0**-8) == one + 2.0**-6     # tie -> even mantissa
-    assert conv1d.round_bf16(one + 2.0**-8 + 2.0**-20) == one + 2.0**-7
-    assert conv1d.round_bf16(2.0 - 2.0**-9) == 2.0                   # carry into the exponent
-    assert conv1d.round_bf16(-(one + 2.0**-7)) == -(one + 2.0**-7)   # representable stays
-    assert conv1d.round_bf16(0.0) == 0.0
+    assert rounding.round_bf16(one + 2.0**-8) == one                   # tie -> even (1.0)
+    assert rounding.round_bf16(one + 3 * 2.0**-8) == one + 2.0**-6     # tie -> even mantissa
+    assert rounding.round_bf16(one + 2.0**-8 + 2.0**-20) == one + 2.0**-7
+    assert rounding.round_bf16(2.0 - 2.0**-9) == 2.0                   # carry into the exponent
+    assert rounding.round_bf16(-(one + 2.0**-7)) == -(one + 2.0**-7)   # representable stays
+    assert rounding.round_bf16(0.0) == 0.0
 
 
 def test_round_bf16_matches_library_conversion():
@@ -52,11 +52,11 @@ def test_round_bf16_matches_library_conversion():
     rng = np.random.default_rng(5)
     x = (rng.standard_normal(20000) * np.exp(rng.uniform(-20, 20, 20000))).astype(np.float32)
     ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
-    got = conv1d.round_bf16(x.astype(np.float64))
+    got = rounding.round_bf16(x.astype(np.float64))
     assert np.array_equal(got, ref)
     # within half an ulp (at most 2^-8 of |x|: 8 significand bits) and idempotent
     assert np.all(np.abs(got - x) <= np.abs(x) * 2.0**-8)
-    assert np.array_equal(conv1d.round_bf16(got), got)
+    assert np.array_equal(rounding.round_bf16(got), got)
 
 
 def test_split_xbc_channel_order():

@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 import scipy.linalg
 
-from oracle import gdn
+from oracle import gdn, rounding
 from tests.util import tiny_gdn
 
 
@@ -150,3 +150,31 @@ def test_chunkwise_solve_matches_serial_and_textbook(T):
         S = al * S + np.outer(u, k[s])
         assert np.allclose(U[s], u, rtol=0, atol=1e-12)
         assert np.allclose(Y[s], S @ q[s], rtol=0, atol=1e-12)
+
+
+def test_bf16_corrections_follow_the_rounded_recurrence():
+    """With the ring in bf16, a step's outputs use its correction unrounded and
+    every later step sees the state built from rounded corrections:
+        u_t = beta (v - alpha S k),  y_t = alpha S q + u_t (k . q),
+        S <- alpha S + bf16(u_t) k^T,
+    written out per head (the rounding itself is pinned in test_oracle_conv1d)."""
+    rng = np.random.default_rng(12)
+    B, H, d, n, G, L, steps = 2, 2, 4, 6, 1, 3, 11
+    S0, seq = tiny_gdn(rng, B, H, d, n, G, steps)
+    reqs = [gdn.GDNReplayRequest(S0[b], L, G, u_bf16=True) for b in range(B)]
+    S = np.array(S0, dtype=np.float64)
+    for t, st in enumerate(seq):
+        for b in range(B):
+            y, f = reqs[b].decode_step(st["v"][b], st["k"][b], st["q"][b], st["g"][b], st["beta"][b])
+            for h in range(H):
+                k, q = st["k"][b, 0], st["q"][b, 0]
+                a = np.exp(st["g"][b, h])
+                u = st["beta"][b, h] * (st["v"][b, h] - a * (S[b, h] @ k))
+                assert np.allclose(y[h], a * (S[b, h] @ q) + u * (k @ q), rtol=0, atol=1e-12)
+                S[b, h] = a * S[b, h] + np.outer(rounding.round_bf16(u), k)
+            if f:
+                assert np.allclose(reqs[b].S0, S[b], rtol=0, atol=1e-12)
+    for b in range(B):
+        for e in reqs[b].ring:
+            if e is not None:
+                assert np.array_equal(rounding.round_bf16(e.u), e.u)
