@@ -391,6 +391,7 @@ def _row_window(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, Ts=(1, 
                        f"acceptance uniform on 0..T",
            "standard_step": std, "T": []}
     for T in Ts:
+        print(f"[bench]   window {'gdn' if gdn else 'mamba2'} T={T}", file=sys.stderr, flush=True)
         rv = _row_verify(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, rounds=rounds, warm=warm, T=T,
                          with_standard=False)
         sn = _snapshot_rounds(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, T, rounds, warm)
@@ -765,17 +766,26 @@ def _row_flush(torch, np, rd, synth, traffic, dev, stream, reps=8):
 
 
 def _rows(torch, np, rd, synth, traffic, dev, stream):
-    return {"speculative_verify": _row_verify(torch, np, rd, synth, traffic, dev, stream, 2, False),
-            "gdn_speculative_verify": _row_verify(torch, np, rd, synth, traffic, dev, stream, 4, True),
-            "capacity_sweep": _row_sweep(torch, np, rd, synth, traffic, dev, stream),
-            "explicit_flush": _row_flush(torch, np, rd, synth, traffic, dev, stream),
-            "gdn_append_decode": _row_gdn_append(torch, np, rd, synth, traffic, dev, stream),
-            "max_concurrency": _row_capacity(torch, np, rd, synth, dev),
-            "pooled_append_decode": _row_pooled(torch, np, rd, synth, traffic, dev, stream),
-            "fused_front_end": _row_fused_conv(torch, np, rd, synth, traffic, dev, stream),
-            "storage_precision": _row_precision(torch, np, rd, synth, traffic, dev, stream),
-            "window_sweep": {"mamba2": _row_window(torch, np, rd, synth, traffic, dev, stream, 2, False),
-                             "gdn": _row_window(torch, np, rd, synth, traffic, dev, stream, 4, True)}}
+    """Every measured row; a progress line per row goes to stderr (stdout keeps
+    the one JSON line)."""
+    rows = [
+        ("speculative_verify", lambda: _row_verify(torch, np, rd, synth, traffic, dev, stream, 2, False)),
+        ("gdn_speculative_verify", lambda: _row_verify(torch, np, rd, synth, traffic, dev, stream, 4, True)),
+        ("capacity_sweep", lambda: _row_sweep(torch, np, rd, synth, traffic, dev, stream)),
+        ("explicit_flush", lambda: _row_flush(torch, np, rd, synth, traffic, dev, stream)),
+        ("gdn_append_decode", lambda: _row_gdn_append(torch, np, rd, synth, traffic, dev, stream)),
+        ("max_concurrency", lambda: _row_capacity(torch, np, rd, synth, dev)),
+        ("pooled_append_decode", lambda: _row_pooled(torch, np, rd, synth, traffic, dev, stream)),
+        ("fused_front_end", lambda: _row_fused_conv(torch, np, rd, synth, traffic, dev, stream)),
+        ("storage_precision", lambda: _row_precision(torch, np, rd, synth, traffic, dev, stream)),
+        ("window_sweep", lambda: {"mamba2": _row_window(torch, np, rd, synth, traffic, dev, stream, 2, False),
+                                  "gdn": _row_window(torch, np, rd, synth, traffic, dev, stream, 4, True)}),
+    ]
+    out = {}
+    for name, fn in rows:
+        print(f"[bench] row {name}", file=sys.stderr, flush=True)
+        out[name] = fn()
+    return out
 
 
 def main(argv=None) -> int:

@@ -197,6 +197,7 @@ def main(argv=None) -> int:
     s.add_argument("--calib-fetch", required=True)
     s.add_argument("--calib-write", required=True)
     s.add_argument("--command", required=True)
+    s.add_argument("--out", default=None, help="output json (default profiles/<kernel>_traffic.json)")
     m = sub.add_parser("mfma")
     m.add_argument("--csv", required=True)
     m.add_argument("--out", required=True)
@@ -216,14 +217,17 @@ def main(argv=None) -> int:
         print(open(a.out).read())
         return 0
     if a.cmd == "mfma":
-        kernels = [("replay_append_decode", "replay_window_kernel<64, 128, 1, true"),
+        kernels = [("replay_append_decode", "replay_window_kernel<64, 128, 1, true, 16, false"),
+                   ("replay_append_decode_conv", "replay_window_kernel<64, 128, 1, true, 16, true"),
                    ("replay_verify_T (T=4)", "replay_window_kernel<64, 128, 4, false"),
-                   ("gdn_replay_verify_T (T=4)", "gdn_verify_kernel<128, 128, 4"),
+                   ("replay_verify_T (T=6, combine on MFMA)", "replay_window_kernel<64, 128, 6, false"),
+                   ("gdn_replay_verify_T (T=4)", "gdn_verify_kernel<128, 128, 4, 16, false"),
+                   ("gdn_replay_append_decode", "gdn_verify_kernel<128, 128, 1, 16, true"),
                    ("ssm_decode_step", "ssm_step_kernel")]
         mfma_summary(a.csv, kernels, a.command, a.out)
         print(open(a.out).read())
         return 0
-    res = summarize(a.kernel, a.match, a.fetch, a.write, a.calib_fetch, a.calib_write, a.command)
+    res = summarize(a.kernel, a.match, a.fetch, a.write, a.calib_fetch, a.calib_write, a.command, a.out)
     print(json.dumps(res, indent=1))
     return 0
 
