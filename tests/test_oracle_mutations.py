@@ -4,7 +4,7 @@ swapped operand, a wrong group mapping."""
 import numpy as np
 import pytest
 
-from oracle import conv1d, gdn, mamba2, replay
+from oracle import conv1d, gdn, mamba2, replay, rounding
 from tests import test_oracle_conv1d as t_conv
 from tests import test_oracle_gdn as t_gdn
 from tests import test_oracle_mamba2 as t_m2
@@ -181,3 +181,40 @@ def test_conv_reversed_taps_are_caught(monkeypatch):
     orig = conv1d.update
     monkeypatch.setattr(conv1d, "update", lambda s, x, w: orig(s, x, w[:, ::-1]))
     _fails(t_conv.test_conv_update_equals_full_causal_convolution)
+
+
+def test_bf16_rounding_ties_away_is_caught(monkeypatch):
+    def bad(x):
+        x = np.asarray(x, np.float64)
+        m, e = np.frexp(x)
+        return np.ldexp(np.trunc(m * 256.0 + np.copysign(0.5, m)), e - 8)   # halves away from zero
+    monkeypatch.setattr(rounding, "round_bf16", bad)
+    _fails(t_conv.test_round_bf16_ties_and_carry)
+
+
+def test_swapped_key_and_query_channels_are_caught(monkeypatch):
+    def bad(out, H, d, G, n):
+        Bt = out.shape[0]
+        v = out[:, :H * d].reshape(Bt, H, d)
+        q = out[:, H * d:H * d + G * n].reshape(Bt, G, n)
+        k = out[:, H * d + G * n:].reshape(Bt, G, n)
+        return v, k, q
+    monkeypatch.setattr(conv1d, "split_xbc", bad)
+    _fails(t_conv.test_split_xbc_channel_order)
+
+
+def test_bf16_correction_rounded_for_its_own_output_is_caught(monkeypatch):
+    orig_decode = gdn.GDNReplayRequest.decode_step
+
+    def bad(self, v, k, q, g, beta):
+        # outputs computed as if the step's own correction were already rounded
+        S_h = self.rebuilt_state_closed(self._logical(self.count))
+        alpha = np.exp(g)
+        kh, qh = k[self.grp], q[self.grp]
+        u = beta[:, None] * (v - alpha[:, None] * np.sum(S_h * kh[:, None, :], axis=-1))
+        y_bad = alpha[:, None] * np.sum(S_h * qh[:, None, :], axis=-1) + \
+            self._cached(u) * np.sum(kh * qh, axis=-1)[:, None]
+        _, flushed = orig_decode(self, v, k, q, g, beta)
+        return y_bad, flushed
+    monkeypatch.setattr(gdn.GDNReplayRequest, "decode_step", bad)
+    _fails(t_gdn.test_bf16_corrections_follow_the_rounded_recurrence)
