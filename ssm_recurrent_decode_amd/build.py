@@ -85,9 +85,29 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB_PATH)
+    _build_c_example(verbose)
     if verbose:
         print(f"built {LIB_PATH}")
     return LIB_PATH
+
+
+C_EXAMPLE = os.path.join(ROOT, "tests", "c_abi", "abi_roundtrip.cpp")
+
+
+def _build_c_example(verbose: bool) -> None:
+    """The C++ program that drives the C ABI without Python (a GPU test runs it),
+    linked against the in-tree library through an rpath relative to itself."""
+    if not os.path.exists(C_EXAMPLE):
+        return
+    exe = os.path.splitext(C_EXAMPLE)[0]
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-O2", "-std=c++17",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-I", INCLUDE, C_EXAMPLE, "-o", exe + ".tmp", "-L", PKG, "-lssm_recurrent_decode",
+           "-Wl,-rpath,$ORIGIN/../../ssm_recurrent_decode_amd"]
+    _run(cmd, "hipcc (abi_roundtrip)")
+    os.replace(exe + ".tmp", exe)
+    if verbose:
+        print(f"built {exe}")
 
 
 def main(argv=None) -> int:
