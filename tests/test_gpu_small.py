@@ -57,7 +57,8 @@ def test_ssm_decode_step_small(d, G):
 
 @pytest.mark.parametrize("d,G,L,ring_dominant", [(64, 1, 8, False), (128, 2, 8, False),
                                                  (64, 2, 5, False), (64, 1, 8, True),
-                                                 (128, 4, 32, True)])
+                                                 (128, 4, 32, True),
+                                                 (64, 8, 1, False), (64, 1, 2, False)])  # every step / every other folds
 def test_replay_append_decode_small(d, G, L, ring_dominant):
     """Config-0 workload (and variants): y every step, S_0 at every flush, pointers
     and flush flags every step, against the oracle."""
@@ -172,11 +173,15 @@ def test_replay_flush_masked():
 
 
 def _spec_inputs(sh, seed, cfg_id, rounds):
-    return [synth.mamba2_step_inputs(sh, seed, cfg_id, r) for r in range(rounds)]
+    out = [synth.mamba2_step_inputs(sh, seed, cfg_id, r) for r in range(rounds)]
+    if sh.T == 1:   # the generator drops the draft axis at T = 1
+        out = [{k_: v_[:, None] for k_, v_ in st.items()} for st in out]
+    return out
 
 
 @pytest.mark.parametrize("d,G,L,T", [(64, 1, 16, 4), (64, 2, 8, 2), (128, 4, 16, 3), (64, 1, 8, 4),
-                                     (64, 2, 32, 8), (128, 1, 20, 5), (64, 4, 12, 6)])
+                                     (64, 2, 32, 8), (128, 1, 20, 5), (64, 4, 12, 6),
+                                     (64, 1, 2, 1)])  # L = 2T: every round with committed entries folds
 def test_replay_verify_rollback_small(d, G, L, T):
     """Speculative rounds: every draft's y (rejected included) against the
     per-draft snapshot semantics; pointers and early-flush flags bit-exact; the
@@ -303,7 +308,7 @@ def test_gdn_replay_verify_small(d, G, L, T):
     assert es <= S_TOL, es
 
 
-@pytest.mark.parametrize("d,G,L", [(128, 32, 16), (64, 8, 8), (128, 16, 5), (64, 4, 32)])
+@pytest.mark.parametrize("d,G,L", [(128, 32, 16), (64, 8, 8), (128, 16, 5), (64, 4, 32), (64, 8, 1), (128, 32, 2)])
 def test_gdn_replay_append_decode_small(d, G, L):
     """GDN standard decode through the ring: y every step, flush flags, pointers
     and the checkpoint at every flush against the oracle's flush-when-full
@@ -388,6 +393,42 @@ def test_replay_append_decode_conv_small(d, G, L):
         assert bool(torch.all(flushed == int(fl))), t
         if fl:
             assert rel_err(state0.cpu().numpy(), S) <= S_TOL, t
+    assert int(ring.err.item()) == 0
+
+
+def test_single_request_single_head():
+    """The smallest batch: one request, one head, one group; append-decode over
+    three ring cycles, then verify rounds with rollback, against the oracle."""
+    base = synth.WORKLOADS[0]
+    sh = base.shape.with_(batch=1, nheads=1, ngroups=1, capacity=4)
+    seed, steps = base.cfg_seed, 13
+    A, dt_bias, S0, seq = _mamba2_case(sh, seed, 0, steps)
+    dims = _dims(sh)
+    ring = rd.Ring(dims)
+    state0 = dev_f32(S0)
+    y = torch.empty(1, 1, sh.head_dim, device="cuda")
+    ys_ref, Ss_ref = o_m2.run_standard(S0.astype(np.float64), [mamba2_step_f64(st) for st in seq],
+                                       dt_bias.astype(np.float64), A.astype(np.float64), 1)
+    for t, st in enumerate(seq):
+        rd.replay_append_decode(dims, state0, ring, dev_bf16(st["v"]), dev_bf16(st["k"]), dev_bf16(st["q"]),
+                                dev_f32(st["dt"]), dev_f32(dt_bias), dev_f32(A), y)
+        assert rel_err(y.cpu().numpy(), ys_ref[t]) <= Y_TOL, t
+    assert ring.count.cpu().tolist() == [steps % 4]
+    S = Ss_ref[-1]
+    T = 2
+    shv = sh.with_(T=T)
+    acc = np.array([[2], [0], [1], [2], [1]], dtype=np.int32)
+    y2 = torch.empty(1, T, 1, sh.head_dim, device="cuda")
+    for r in range(len(acc)):
+        st = synth.mamba2_step_inputs(shv, seed, 0, 100 + r)
+        rd.replay_verify_T(dims, T, state0, ring, dev_bf16(st["v"]), dev_bf16(st["k"]), dev_bf16(st["q"]),
+                           dev_f32(st["dt"]), dev_f32(dt_bias), dev_f32(A), y2)
+        y_ref, S = o_m2.spec_round_snapshot(S, mamba2_step_f64(st), dt_bias.astype(np.float64),
+                                            A.astype(np.float64), 1, acc[r])
+        assert rel_err(y2.cpu().numpy(), y_ref) <= Y_TOL, r
+        rd.replay_rollback(dims, ring, dev_i32(acc[r]))
+    rd.replay_flush(dims, state0, ring)
+    assert rel_err(state0.cpu().numpy(), S) <= S_TOL
     assert int(ring.err.item()) == 0
 
 
