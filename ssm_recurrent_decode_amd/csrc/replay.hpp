@@ -12,11 +12,29 @@
 namespace rssm {
 
 // ======================================================= ReplaySSM
-// Draft windows from this size up combine on the matrix cores.  The MFMA chain
-// costs as many cycles as the vector dot products at T = 4 (measured: no gain
-// for T <= 4), but it needs far fewer registers: at T = 5 and 6 it keeps one
-// more wave per SIMD resident (T = 5: 187 -> 167 us per round at B = 512).
-constexpr int kMfmaCombineMinT = 5;
+// Draft windows from this size up combine on the matrix cores (measured against
+// the vector-ALU dot products, interleaved on the same buffers at B = 512:
+// T = 2 equal, T = 3 -0.8 %, T = 4 -2.2 %, and at T = 5, 6 the vector path
+// also costs a wave per SIMD in registers).
+constexpr int kMfmaCombineMinT = 3;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Two bf16 MFMA operands whose sum is the fp32 vector x: hi = the upper halves
+// (truncation), lo = the remainders x - hi (exact in fp32) cut to bf16.  hi + lo
+// is within 2^-14 of x relative; products with bf16 values are exact in the fp32
+// accumulator.
+__device__ __forceinline__ void split_bf16x8(const float (&x)[8], u32x4_t& hi, u32x4_t& lo) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t ua = __float_as_uint(x[2 * e]), ub = __float_as_uint(x[2 * e + 1]);
+    hi[e] = __builtin_amdgcn_perm(ub, ua, 0x07060302u);  // [ua.hi16 | ub.hi16 << 16]
+    const float la = x[2 * e] - __uint_as_float(ua & 0xFFFF0000u);
+    const float lb = x[2 * e + 1] - __uint_as_float(ub & 0xFFFF0000u);
+    lo[e] = __builtin_amdgcn_perm(__float_as_uint(lb), __float_as_uint(la), 0x07060302u);
+  }
+}
 
 struct ReplayParams {
   float* state0;
@@ -379,12 +397,14 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
   }
   if constexpr (T >= kMfmaCombineMinT) {
     // All drafts at once on the matrix cores, output tile = [16 state rows] x
-    // [16 drafts] (drafts >= T are zero columns).  S_0 Q: the state tile in
-    // registers is the A operand as it stands (K index cq <-> column
-    // 16 ct + 4 cq + e for the e-th MFMA of a column tile); B is the query of
-    // draft r at the same columns.  Then the ring part V (W o M) accumulates on
-    // top: A = the values vj, B = w_{j,r} M_{j,r} for slot j = cq + 4m.  Lane
-    // (cq, r) ends with y_r at rows 4cq .. 4cq + 3 of the tile.
+    // [16 drafts] (drafts >= T are zero columns).  S_0 Q on v_mfma_f32_16x16x32_bf16
+    // (lane l: A[l%16][8(l/16)..+7], B[8(l/16)..+7][l%16]): the state tile in
+    // registers is the A operand as it stands, split into bf16 hi + lo (two MFMAs
+    // per pair of column tiles), K index 8cq + e <-> column 32jj + 4cq + e and
+    // 8cq + 4 + e <-> column 32jj + 16 + 4cq + e; B is the query of draft r at the
+    // same columns, bf16 as stored.  Then the ring part V (W o M) accumulates on
+    // top in fp32 (16x16x4): A = the values vj, B = w_{j,r} M_{j,r} for slot
+    // j = cq + 4m.  Lane (cq, r) ends with y_r at rows 4cq .. 4cq + 3 of the tile.
     const bool draft = r < T;
     const int rd = min(r, T - 1);
     uint2 qb[NCT];
@@ -399,11 +419,15 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
     for (int rt = 0; rt < RT; ++rt) {
       v4f z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        z = mfma4(st[rt][ct].x, bf16_lo(qb[ct].x), z);
-        z = mfma4(st[rt][ct].y, bf16_hi(qb[ct].x), z);
-        z = mfma4(st[rt][ct].z, bf16_lo(qb[ct].y), z);
-        z = mfma4(st[rt][ct].w, bf16_hi(qb[ct].y), z);
+      for (int jj = 0; jj < NCT / 2; ++jj) {
+        const float4 s0 = st[rt][2 * jj], s1 = st[rt][2 * jj + 1];
+        const float xs[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+        u32x4_t hi, lo;
+        split_bf16x8(xs, hi, lo);
+        const u32x4_t qv = {qb[2 * jj].x, qb[2 * jj].y, qb[2 * jj + 1].x, qb[2 * jj + 1].y};
+        const bf16x8_t qbf = __builtin_bit_cast(bf16x8_t, qv);
+        z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, hi), qbf, z, 0, 0, 0);
+        z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, lo), qbf, z, 0, 0, 0);
       }
       z *= ab;
 #pragma unroll
