@@ -176,6 +176,24 @@ __device__ __forceinline__ v4f mfma4(float a, float b, v4f acc) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
 }
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Two bf16 MFMA operands whose sum is the fp32 vector x: hi = the upper halves
+// (truncation), lo = the remainders x - hi (exact in fp32) cut to bf16.  hi + lo
+// is within 2^-14 of x relative; products with bf16 values are exact in the fp32
+// accumulator.
+__device__ __forceinline__ void split_bf16x8(const float (&x)[8], u32x4_t& hi, u32x4_t& lo) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t ua = __float_as_uint(x[2 * e]), ub = __float_as_uint(x[2 * e + 1]);
+    hi[e] = __builtin_amdgcn_perm(ub, ua, 0x07060302u);  // [ua.hi16 | ub.hi16 << 16]
+    const float la = x[2 * e] - __uint_as_float(ua & 0xFFFF0000u);
+    const float lb = x[2 * e + 1] - __uint_as_float(ub & 0xFFFF0000u);
+    lo[e] = __builtin_amdgcn_perm(__float_as_uint(lb), __float_as_uint(la), 0x07060302u);
+  }
+}
+
 // Per-lane slice of the entries used in the output combine and the fold: lane
 // (r, cq) handles entries j = cq + 4m, m < kMaxL / 4.
 constexpr int kVJ = kMaxL / 4;

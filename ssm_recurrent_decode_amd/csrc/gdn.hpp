@@ -254,19 +254,28 @@ __global__ __launch_bounds__(kBlock) void gdn_verify_kernel(GdnReplayParams p) {
   }
   __syncthreads();
 
-  // ---- 6. readouts Z = S_0 [K|Q] on the matrix cores: A[m][k] = x_m[col], B[k][nn]
-  //      = S_0[row nn][col]; lane (r, cq) ends with Z[4cq+i][row r of the tile]
+  // ---- 6. readouts Z = S_0 [K|Q] on the matrix cores (v_mfma_f32_16x16x32_bf16):
+  //      A[m][k] = x_m[col] (bf16 as stored), B[k][nn] = S_0[row nn][col] split into
+  //      bf16 hi + lo (two MFMAs per pair of column tiles; K index 8cq + e <->
+  //      column 32jj + 4cq + e, 8cq + 4 + e <-> 32jj + 16 + 4cq + e); lane (r, cq)
+  //      ends with Z[4cq+i][row r of the tile]
+  uint2 xq[NCT];  // this lane's readout vector x_r at the columns of each tile
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct)
+    xq[ct] = (r < NV) ? *reinterpret_cast<const uint2*>(&s_x[r * N + ct * 16 + cq * 4]) : make_uint2(0, 0);
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const uint2 xv = (r < NV) ? *reinterpret_cast<const uint2*>(&s_x[r * N + ct * 16 + cq * 4])
-                                : make_uint2(0, 0);
-      acc = mfma4(bf16_lo(xv.x), st[rt][ct].x, acc);
-      acc = mfma4(bf16_hi(xv.x), st[rt][ct].y, acc);
-      acc = mfma4(bf16_lo(xv.y), st[rt][ct].z, acc);
-      acc = mfma4(bf16_hi(xv.y), st[rt][ct].w, acc);
+    for (int jj = 0; jj < NCT / 2; ++jj) {
+      const float4 s0 = st[rt][2 * jj], s1 = st[rt][2 * jj + 1];
+      const float xs[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+      u32x4_t hi, lo;
+      split_bf16x8(xs, hi, lo);
+      const u32x4_t xv = {xq[2 * jj].x, xq[2 * jj].y, xq[2 * jj + 1].x, xq[2 * jj + 1].y};
+      const bf16x8_t xbf = __builtin_bit_cast(bf16x8_t, xv);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xbf, __builtin_bit_cast(bf16x8_t, hi), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xbf, __builtin_bit_cast(bf16x8_t, lo), acc, 0, 0, 0);
     }
     const int row = (wave * RT + rt) * 16 + r;
 #pragma unroll
