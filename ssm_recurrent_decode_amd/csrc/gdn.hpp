@@ -56,7 +56,7 @@ struct GdnReplayParams {
 // the matrix cores from the state registers; the fold (when flushing) follows
 // from the same registers; the per-row solve runs one thread per row after that.
 template <int D, int N, int T, int LCAP, bool APPEND = false>
-__global__ __launch_bounds__(kBlock) void gdn_verify_kernel(GdnReplayParams p) {
+__global__ __launch_bounds__(kBlock, 4) void gdn_verify_kernel(GdnReplayParams p) {
   static_assert(N == 128, "key staging assumes n = 128");
   static_assert(!APPEND || T == 1, "append-decode is one token");
   static_assert(2 * T <= 16, "readout vectors must fit one MFMA M axis");
