@@ -37,14 +37,20 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float softplus_f32(float x) { return x > 20.f ? x : log1pf(expf(x)); }
 
 // Work-groups are dispatched round-robin over the XCDs (block i -> XCD i % 8).
-// Renumber so that each XCD receives a contiguous range of logical work-groups:
-// neighbouring heads of one request (which share k/q and the group's ring keys)
-// then meet in the same L2.  Blocks past the largest multiple of 8 keep their id.
+// Renumber so that each XCD receives chunks of kXcdChunk consecutive logical
+// work-groups, the chunks dealt round-robin: neighbouring heads (a group's k/q and
+// ring keys) meet in one L2, while all eight XCDs stream from the same region of
+// the state at any time.  Measured against one contiguous eighth per XCD and
+// against the plain dispatch order, interleaved launch by launch on the same
+// buffers: chunks of 4 were fastest for the append (-6 %), GDN verify (-3.8 %)
+// and standard step (-2.5 %); the Mamba-2 verify was 1 % faster still with the
+// plain order.  Blocks past the largest multiple of 8 * kXcdChunk keep their id.
+constexpr int kXcdChunk = 4;
 __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
-  const int per = nblocks / kNumXcd;
-  const int full = per * kNumXcd;
+  const int full = (nblocks / (kNumXcd * kXcdChunk)) * (kNumXcd * kXcdChunk);
   if (bid >= full) return bid;
-  return (bid % kNumXcd) * per + bid / kNumXcd;
+  const int x = bid % kNumXcd, i = bid / kNumXcd;  // XCD, and dispatch order within it
+  return ((i / kXcdChunk) * kNumXcd + x) * kXcdChunk + i % kXcdChunk;
 }
 
 // Physical slot of logical ring entry j (0 <= j < L) when the oldest entry sits in
