@@ -90,6 +90,7 @@ def summarize(kernel, match, fetch, write, calib_fetch, calib_write, command, ou
 
 
 MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_VALU_MFMA_BUSY_CYCLES")
+BF16_COUNTER = "SQ_INSTS_VALU_MFMA_MOPS_BF16"
 NUM_SIMDS = 256 * 4
 CLOCK_HZ = 2.4e9
 FP32_MFMA_PEAK = 157.3e12
@@ -110,38 +111,43 @@ def per_dispatch_counters(path: str):
 
 def mfma_summary(path: str, kernels, command: str, out_md: str):
     """Per kernel (substring match) and grid size, split into dispatches with and
-    without MFMA work: MFMA flops per dispatch (SQ_INSTS_VALU_MFMA_MOPS_F32 x 512),
+    without MFMA work: MFMA flops per dispatch (SQ_INSTS_VALU_MFMA_MOPS_F32 x 512,
+    plus SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 when the run collected it),
     duration (dispatch timestamps of the counter run), achieved MFMA FLOP/s
     against the fp32 dense peak, and the MFMA busy fraction of all SIMD cycles
     (SQ_VALU_MFMA_BUSY_CYCLES summed over SIMDs / (duration x 2.4 GHz x 1024))."""
     disp = per_dispatch_counters(path)
     lines = ["# MFMA use of the decode kernels (rocprofv3 counters)", "",
              "Command (repository root on one MI355X; `<repo>` is its path):", "", "```", command, "```", "",
-             "Per dispatch: fp32 MFMA flops = `SQ_INSTS_VALU_MFMA_MOPS_F32` x 512; duration from the "
-             "dispatch timestamps of the same run; MFMA busy = `SQ_VALU_MFMA_BUSY_CYCLES` (summed over "
-             "SIMDs) / (duration x 2.4 GHz x 1024 SIMDs).  Peak: 157.3 TFLOP/s dense fp32.  The "
-             "kernels are HBM-bound; these figures show that the matrix-core work (the fold of a "
-             "flush, the GDN readouts) stays far from being a bottleneck.", "",
-             "| kernel | work-items (threads) | dispatches | MFMA GFLOP / dispatch | us | MFMA TFLOP/s | of fp32 peak | MFMA busy |",
+             "Per dispatch: MFMA flops = (`SQ_INSTS_VALU_MFMA_MOPS_F32` + `SQ_INSTS_VALU_MFMA_MOPS_BF16`) "
+             "x 512 (the bf16 ones are the hi/lo split products of the verify combine and the GDN "
+             "readouts); duration from the dispatch timestamps of the same run; MFMA busy = "
+             "`SQ_VALU_MFMA_BUSY_CYCLES` (summed over SIMDs) / (duration x 2.4 GHz x 1024 SIMDs).  "
+             "Peaks: 157.3 TFLOP/s dense fp32, 2.5 PFLOP/s dense bf16.  The kernels are HBM-bound; "
+             "these figures show that the matrix-core work (the fold of a flush, the verify "
+             "combine, the GDN readouts) stays far from being a bottleneck.", "",
+             "| kernel | work-items (threads) | dispatches | fp32 MFMA GFLOP / dispatch | bf16 MFMA GFLOP / dispatch | us | MFMA TFLOP/s | MFMA busy |",
              "|---|---|---|---|---|---|---|---|"]
     res = {}
     for label, match in kernels:
         groups = {}
         for d in disp.values():
             if match in d["name"] and all(c in d for c in MFMA_COUNTERS):
-                kind = "with MFMA work" if d["SQ_INSTS_VALU_MFMA_MOPS_F32"] > 0 else "without"
+                work = d["SQ_INSTS_VALU_MFMA_MOPS_F32"] + d.get(BF16_COUNTER, 0.0)
+                kind = "with MFMA work" if work > 0 else "without"
                 groups.setdefault((d["grid"], kind), []).append(d)
         for (grid, kind), ds in sorted(groups.items()):
             n = len(ds)
-            flops = sum(d["SQ_INSTS_VALU_MFMA_MOPS_F32"] for d in ds) * 512 / n
+            f32 = sum(d["SQ_INSTS_VALU_MFMA_MOPS_F32"] for d in ds) * 512 / n
+            b16 = sum(d.get(BF16_COUNTER, 0.0) for d in ds) * 512 / n
             t = sum(d["dur_s"] for d in ds) / n
             busy = sum(d["SQ_VALU_MFMA_BUSY_CYCLES"] for d in ds) / n
-            rate = flops / t if t > 0 else 0.0
+            rate = (f32 + b16) / t if t > 0 else 0.0
             frac_busy = busy / (t * CLOCK_HZ * NUM_SIMDS) if t > 0 else 0.0
-            res[(label, grid, kind)] = {"dispatches": n, "flops": flops, "us": t * 1e6, "rate": rate,
-                                        "busy": frac_busy}
-            lines.append(f"| {label} ({kind}) | {grid} | {n} | {flops / 1e9:.3f} | {t * 1e6:.1f} | "
-                         f"{rate / 1e12:.2f} | {rate / FP32_MFMA_PEAK:.4f} | {frac_busy:.4f} |")
+            res[(label, grid, kind)] = {"dispatches": n, "flops_f32": f32, "flops_bf16": b16, "us": t * 1e6,
+                                        "rate": rate, "busy": frac_busy}
+            lines.append(f"| {label} ({kind}) | {grid} | {n} | {f32 / 1e9:.3f} | {b16 / 1e9:.3f} | {t * 1e6:.1f} | "
+                         f"{rate / 1e12:.2f} | {frac_busy:.4f} |")
     with open(out_md, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     return res
