@@ -43,7 +43,8 @@ def _args(argv=None):
     ap.add_argument("--pool", type=int, default=32, help="distinct pre-generated step inputs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-standard", action="store_true", help="skip the standard-step comparator")
-    ap.add_argument("--cpu-steps", type=int, default=32)
+    ap.add_argument("--cpu-steps", type=int, default=96,
+                    help="decode steps of the CPU oracle sample (96: about 10 s on one core)")
     ap.add_argument("--no-graph", action="store_true", help="time the step eagerly only")
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the other measured rows (verify, GDN verify, capacity sweep)")
@@ -104,28 +105,70 @@ def _ceiling_probes(torch, rd, dev, stream, launch_bytes):
     return res
 
 
-def _cpu_baseline(steps: int):
-    """The CPU oracle (ReplaySSM standard mode, float64) on the full batch of the
-    same workload for `steps` decode steps; single-threaded numpy elementwise code."""
+def _cpu_inputs(steps: int, lo: int, hi: int):
+    """Requests lo..hi-1 of the headline workload as float64: checkpoint, head
+    parameters and `steps` decode steps (the values the GPU receives)."""
     import numpy as np
 
-    from oracle import replay as o_rep
     from ssm_recurrent_decode_amd import synth
     wl = synth.WORKLOADS[1]
     sh, seed = wl.shape, wl.cfg_seed
     A, bias = synth.mamba2_head_params(sh, seed, 1)
-    S0 = synth.state0(sh, seed, 1).astype(np.float64)
+    S0 = synth.state0(sh, seed, 1)[lo:hi].astype(np.float64)
     seq = []
     for t in range(steps):
         st = synth.mamba2_step_inputs(sh, seed, 1, t)
-        seq.append({"v": synth.bf16_bits_to_f64(st["v"]), "k": synth.bf16_bits_to_f64(st["k"]),
-                    "q": synth.bf16_bits_to_f64(st["q"]), "dt": st["dt"].astype(np.float64)})
+        seq.append({"v": synth.bf16_bits_to_f64(st["v"][lo:hi]), "k": synth.bf16_bits_to_f64(st["k"][lo:hi]),
+                    "q": synth.bf16_bits_to_f64(st["q"][lo:hi]), "dt": st["dt"][lo:hi].astype(np.float64)})
+    return sh, S0, seq, bias.astype(np.float64), A.astype(np.float64)
+
+
+def _cpu_worker(job):
+    """One process of the all-cores leg: the oracle over its slice of requests,
+    started together with the others at a shared barrier; returns its wall-clock
+    interval (CLOCK_MONOTONIC is system-wide)."""
+    steps, lo, hi, barrier = job
+    from oracle import replay as o_rep
+    sh, S0, seq, bias, A = _cpu_inputs(steps, lo, hi)
+    barrier.wait()
+    t0 = time.monotonic()
+    o_rep.run_standard(S0, seq, bias, A, sh.capacity, sh.ngroups)
+    return t0, time.monotonic()
+
+
+def _cpu_baseline(steps: int):
+    """The CPU oracle (ReplaySSM standard mode, float64) on the full batch of the
+    same workload for `steps` decode steps; single-threaded numpy elementwise code."""
+    from oracle import replay as o_rep
+    sh, S0, seq, bias, A = _cpu_inputs(steps, 0, None)
     t0 = time.perf_counter()
-    o_rep.run_standard(S0, seq, bias.astype(np.float64), A.astype(np.float64), sh.capacity, sh.ngroups)
+    o_rep.run_standard(S0, seq, bias, A, sh.capacity, sh.ngroups)
     dt = time.perf_counter() - t0
     return {"value": sh.batch * steps / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"ReplaySSM standard-mode oracle, full batch {sh.batch}, {steps} decode steps "
                       f"({steps // sh.capacity} flushes), float64 numpy, {dt:.1f} s"}
+
+
+def _cpu_baseline_all_cores(steps: int, max_workers: int = 16):
+    """The same oracle on every host core this process may use (at most
+    `max_workers`): requests are independent, so the batch is split into equal
+    slices, one fresh (spawned) process per slice, all released at once; the rate
+    is the whole batch over the span from the first start to the last finish."""
+    import multiprocessing as mp
+
+    from ssm_recurrent_decode_amd import synth
+    B = synth.WORKLOADS[1].shape.batch
+    W = max(1, min(len(os.sched_getaffinity(0)), max_workers, B))
+    cuts = [B * i // W for i in range(W + 1)]
+    ctx = mp.get_context("spawn")
+    with ctx.Manager() as mgr:
+        barrier = mgr.Barrier(W)
+        with ctx.Pool(W) as pool:
+            spans = pool.map(_cpu_worker, [(steps, cuts[i], cuts[i + 1], barrier) for i in range(W)])
+    dt = max(e for _, e in spans) - min(s for s, _ in spans)
+    return {"value": B * steps / dt, "unit": "tokens/s", "cores": W, "kind": "oracle",
+            "sample": f"the same oracle, full batch {B} split over {W} processes, {steps} decode steps, "
+                      f"{dt:.1f} s wall"}
 
 
 # ------------------------------------------------------------------ other rows
@@ -1004,6 +1047,7 @@ def main(argv=None) -> int:
 
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = _cpu_baseline(a.cpu_steps)
+        out["cpu_baseline_all_cores"] = _cpu_baseline_all_cores(a.cpu_steps)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -1,0 +1,35 @@
+"""Host-side parts of bench.py that run without a GPU: the one-GPU guard and the
+two CPU-oracle legs (single process, and the batch split over spawned processes).
+The rates themselves are not checked, only that each leg runs the oracle over the
+stated sample and reports what it used."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_cpu_baseline_single_core():
+    res = bench._cpu_baseline(1)
+    assert res["kind"] == "oracle" and res["cores"] == 1 and res["unit"] == "tokens/s"
+    assert res["value"] > 0 and "256" in res["sample"]
+
+
+@pytest.mark.timeout(300)
+def test_cpu_baseline_all_cores_splits_the_batch():
+    res = bench._cpu_baseline_all_cores(1, max_workers=2)
+    assert res["kind"] == "oracle" and res["unit"] == "tokens/s"
+    assert res["cores"] == min(2, len(os.sched_getaffinity(0)))
+    assert res["value"] > 0 and f"over {res['cores']} processes" in res["sample"]
