@@ -52,6 +52,12 @@ def sample_pairs(B: int, H: int, n: int, seed: int):
     return pairs[:n]
 
 
+def every_request_pairs(B: int, H: int, per: int = 2):
+    """``per`` heads of every request, rotating so that the heads taken over all
+    requests cover every head: (b, (b + j H / per) mod H) for j < per."""
+    return [(b, (b + j * (H // per)) % H) for b in range(B) for j in range(per)]
+
+
 def sub_mamba2(pairs, H, G, st: dict, spec: bool = False) -> dict:
     """Slice one step's (or round's) float64 inputs to pseudo-requests (b, h):
     one head and one group each."""

@@ -2,8 +2,11 @@
 times, over the full step/round counts.
 
 The oracle follows sampled (request, head) pairs, each as its own pseudo-request
-(heads and requests are independent, so this is an exact check of those outputs);
-ring pointers and flush flags are compared for every request at every step.  Step
+(heads and requests are independent, so this is an exact check of those outputs),
+over the whole run; over the first 2L steps (8 verify rounds) it also follows two
+heads of every request, the heads rotating so that every head is covered, which
+includes every request's first flush; ring pointers and flush flags are compared
+for every request at every step.  Step
 inputs cycle through a pool of seeded synthetic steps (the work does not depend on
 the values).  Bars: y 1e-3 and fp32 state 1e-4 (tests/util.rel_err); integers
 bit-exact.
@@ -18,7 +21,7 @@ from oracle import gdn as o_gdn
 from oracle import mamba2 as o_m2
 from oracle import replay as o_rep
 from ssm_recurrent_decode_amd import synth
-from tests.gpu_util import dev_bf16, dev_f32, dev_i32, pair_index, sample_pairs
+from tests.gpu_util import dev_bf16, dev_f32, dev_i32, every_request_pairs, pair_index, sample_pairs
 from tests.util import rel_err
 
 pytestmark = pytest.mark.gpu
@@ -49,6 +52,57 @@ def _sub_step(st, bi, hi, gi, spec):
 
 def _dev_step(st):
     return {k: (dev_bf16(v) if v.dtype == np.uint16 else dev_f32(v)) for k, v in st.items()}
+
+
+class _EveryRequest:
+    """The early-window check: the oracle over two heads of every request."""
+
+    def __init__(self, B, H, G, S0, pool, window, spec, gdn=False, A=None, bias=None):
+        self.pairs = every_request_pairs(B, H)
+        self.bi, self.hi, self.gi = _pairs_arrays(self.pairs, H, G)
+        self.tb, self.th = pair_index(self.pairs)
+        self.window, self.spec, self.gdn, self.P = window, spec, gdn, len(pool)
+        bi, hi, gi = self.bi, self.hi, self.gi
+        pool = pool[:min(window, len(pool))]  # step t uses pool[t % P], as on the device
+        if gdn:
+            self.sub = [{"v": _f64(st["v"][bi, :, hi])[:, :, None], "k": _f64(st["k"][bi, :, gi])[:, :, None],
+                         "q": _f64(st["q"][bi, :, gi])[:, :, None],
+                         "g": st["g"][bi, :, hi].astype(np.float64)[:, :, None],
+                         "beta": st["beta"][bi, :, hi].astype(np.float64)[:, :, None]} for st in pool]
+        else:
+            self.sub = [_sub_step(st, bi, hi, gi, spec) for st in pool]
+            self.A = A[hi].astype(np.float64)[:, None]
+            self.bias = bias[hi].astype(np.float64)[:, None]
+        self.S = S0[bi, hi].astype(np.float64)[:, None]
+
+    def step(self, t, y, state0, flushed):
+        """Standard decode step t (< window): y every step, S_0 on a flush step."""
+        st = self.sub[t % self.P]
+        delta, a = o_m2.step_size_and_decay(st["dt"], self.bias, self.A)
+        self.S, y_ref = o_m2.standard_step(self.S, st["v"], st["k"], st["q"], delta, a, 1)
+        e = rel_err(y[self.tb, self.th].cpu().numpy(), y_ref[:, 0])
+        assert e <= Y_TOL, ("every request", t, e)
+        fl = flushed.cpu().numpy()[self.bi].astype(bool)
+        if fl.any():
+            e = rel_err(state0[self.tb, self.th].cpu().numpy()[fl], self.S[fl, 0])
+            assert e <= S_TOL, ("every request", t, e)
+
+    def round(self, r, acc, y, state0, flushed):
+        """Verify round r (< window): every draft's y; for the requests that flushed
+        this round, S_0 equals the committed state at the round's start."""
+        before = self.S
+        if self.gdn:
+            y_ref, self.S = o_gdn.spec_round_snapshot(self.S, self.sub[r % self.P], 1, acc[r, self.bi])
+        else:
+            y_ref, self.S = o_m2.spec_round_snapshot(self.S, self.sub[r % self.P], self.bias, self.A, 1,
+                                                     acc[r, self.bi])
+        e = rel_err(y[self.tb, :, self.th].cpu().numpy(), y_ref[:, :, 0])
+        assert e <= Y_TOL, ("every request", r, e)
+        fl = flushed.cpu().numpy()[self.bi].astype(bool)
+        if fl.any():
+            got = state0[self.tb, self.th].cpu().numpy()[fl]
+            e = rel_err(got, before[fl, 0])
+            assert e <= S_TOL, ("every request", r, e)
 
 
 def _mamba2_setup(wl, shape, pool_size, spec=False):
@@ -83,6 +137,7 @@ def test_config1_standard_and_replay_full():
     S = S0[bi, hi].astype(np.float64)[:, None]
     A_sub, bias_sub = A[hi].astype(np.float64)[:, None], bias[hi].astype(np.float64)[:, None]
     sched = o_rep.pointer_schedule_standard(L, wl.steps)
+    early = _EveryRequest(B, H, G, S0, pool, 2 * L, False, A=A, bias=bias)
     # conv1d state update at the same size
     C = wl.conv_channels
     cst, cw = synth.conv_layer(B, C, 4, wl.cfg_seed, 1)
@@ -105,6 +160,8 @@ def test_config1_standard_and_replay_full():
         es = rel_err(y_s[tb, th].cpu().numpy(), y_ref[:, 0])
         assert er <= Y_TOL and es <= Y_TOL, (t, er, es)
         worst[0] = max(worst[0], er, es)
+        if t < early.window:
+            early.step(t, y_r, state_r, flushed)
         head, count, fl = sched[t]
         assert bool(torch.all(ring.head == head)) and bool(torch.all(ring.count == count)), t
         assert ring.copies_agree(), t
@@ -147,6 +204,7 @@ def test_config2_speculative_verify_full():
     scheds = [o_rep.pointer_schedule_spec(L, T, acc[:, b]) for b in range(B)]
     sched_arr = np.array(scheds)            # [B, R, 5]
     dacc = [dev_i32(acc[r]) for r in range(wl.steps)]
+    early = _EveryRequest(B, H, G, S0, pool, 8, True, A=A, bias=bias)
     for r in range(wl.steps):
         ip = dpool[r % 32]
         rd.replay_verify_T(dims, T, state0, ring, ip["v"], ip["k"], ip["q"], ip["dt"], biasb, Ab, y,
@@ -154,6 +212,8 @@ def test_config2_speculative_verify_full():
         y_ref, S = o_m2.spec_round_snapshot(S, subpool[r % 32], bias_sub, A_sub, 1, acc[r, bi])
         e = rel_err(y[tb, :, th].cpu().numpy(), y_ref[:, :, 0])
         assert e <= Y_TOL, (r, e)
+        if r < early.window:
+            early.round(r, acc, y, state0, flushed)
         assert np.array_equal(flushed.cpu().numpy(), sched_arr[:, r, 1].astype(np.int32)), r
         assert np.array_equal(ring.head.cpu().numpy(), sched_arr[:, r, 2]), r
         assert np.array_equal(ring.count.cpu().numpy(), sched_arr[:, r, 3]), r
@@ -187,6 +247,7 @@ def test_config3_capacity_sweep_full(L):
     S = S0[bi, hi].astype(np.float64)[:, None]
     A_sub, bias_sub = A[hi].astype(np.float64)[:, None], bias[hi].astype(np.float64)[:, None]
     sched = o_rep.pointer_schedule_standard(L, wl.steps)
+    early = _EveryRequest(B, H, G, S0, pool, 2 * L, False, A=A, bias=bias)
     for t in range(wl.steps):
         ip = dpool[t % 32]
         rd.replay_append_decode(dims, state0, ring, ip["v"], ip["k"], ip["q"], ip["dt"], biasb, Ab, y,
@@ -196,6 +257,8 @@ def test_config3_capacity_sweep_full(L):
         S, y_ref = o_m2.standard_step(S, st["v"], st["k"], st["q"], delta, a, 1)
         e = rel_err(y[tb, th].cpu().numpy(), y_ref[:, 0])
         assert e <= Y_TOL, (t, e)
+        if t < early.window:
+            early.step(t, y, state0, flushed)
         head, count, fl = sched[t]
         if t % 64 == 0 or fl:
             assert bool(torch.all(ring.head == head)) and bool(torch.all(ring.count == count)), t
@@ -236,6 +299,7 @@ def test_config4_gdn_verify_full():
     S = S0[bi, hi].astype(np.float64)[:, None]
     scheds = np.array([o_rep.pointer_schedule_spec(L, T, acc[:, b]) for b in range(B)])
     dacc = [dev_i32(acc[r]) for r in range(wl.steps)]
+    early = _EveryRequest(B, H, G, S0, pool, 8, True, gdn=True)
     for r in range(wl.steps):
         ip = dpool[r % 32]
         rd.gdn_replay_verify_T(dims, T, state0, ring, ip["v"], ip["k"], ip["q"], ip["g"], ip["beta"], y,
@@ -243,6 +307,8 @@ def test_config4_gdn_verify_full():
         y_ref, S = o_gdn.spec_round_snapshot(S, subpool[r % 32], 1, acc[r, bi])
         e = rel_err(y[tb, :, th].cpu().numpy(), y_ref[:, :, 0])
         assert e <= Y_TOL, (r, e)
+        if r < early.window:
+            early.round(r, acc, y, state0, flushed)
         assert np.array_equal(flushed.cpu().numpy(), scheds[:, r, 1].astype(np.int32)), r
         assert np.array_equal(ring.count.cpu().numpy(), scheds[:, r, 3]), r
         assert ring.copies_agree(), r
