@@ -48,6 +48,8 @@ def _args(argv=None):
     ap.add_argument("--no-graph", action="store_true", help="time the step eagerly only")
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the other measured rows (verify, GDN verify, capacity sweep)")
+    ap.add_argument("--rows", default=None,
+                    help="comma-separated subset of the rows to run (default: all)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run the 1 GiB copy probe (for scaling traffic counters) and exit")
     return ap.parse_args(argv)
@@ -289,6 +291,11 @@ def _row_verify(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, rounds=
            "accepted_tokens_per_s": round(float(acc[warm:].sum()) / round_s, 1),
            "achieved_GBs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
            "alg_bytes_per_round": round(sum(byts) / rounds),
+           # over every launch of the kernel (both passes replay rounds 0..R-1): the
+           # figure hardware traffic counters over the whole run compare with
+           "alg_bytes_avg_all_launches": round(float(np.mean(
+               [_verify_bytes(traffic, gdn, H, D, N, G, T, L, counts[r], flags) for r in range(R)]))),
+           "launches": 2 * R,
            "flush_rate": round(float(fl.mean()), 4),
            "mean_committed_before": round(float(np.mean([counts[r] for r in range(warm, R)])), 3)}
     if base is not None:
@@ -338,7 +345,7 @@ def _standard_step_row(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, 
     torch.cuda.synchronize()
     su = float(np.mean([1e3 * a_.elapsed_time(b_) for a_, b_ in ev]))
     return {"kernel": name, "us": round(su, 3), "GBs": round(byts / (su * 1e-6) / 1e9, 1),
-            "tokens_per_s": round(B / (su * 1e-6), 1)}
+            "tokens_per_s": round(B / (su * 1e-6), 1), "alg_bytes": byts, "launches": 4 + reps}
 
 
 def _snapshot_rounds(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, T, rounds, warm):
@@ -396,7 +403,7 @@ def _snapshot_rounds(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, T,
     us = sum(v_us) / rounds
     return {"kernel": "gdn_snapshot_verify_T" if gdn else "ssm_snapshot_verify_T", "verify_us": round(us, 3),
             "commit_us": round(sum(c_us) / rounds, 3), "achieved_GBs": round(byts / (us * 1e-6) / 1e9, 1),
-            "alg_bytes_per_round": byts}
+            "alg_bytes_per_round": byts, "launches": R}
 
 
 def _row_precision(torch, np, rd, synth, traffic, dev, stream):
@@ -443,6 +450,9 @@ def _row_window(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, Ts=(1, 
             "replay_GBs": rv["achieved_GBs"], "replay_flush_rate": rv["flush_rate"],
             "snapshot_verify_us": sn["verify_us"], "snapshot_commit_us": sn["commit_us"],
             "snapshot_GBs": sn["achieved_GBs"],
+            "replay_alg_bytes_avg_all_launches": rv["alg_bytes_avg_all_launches"],
+            "replay_launches": rv["launches"],
+            "snapshot_alg_bytes": sn["alg_bytes_per_round"], "snapshot_launches": sn["launches"],
             "replay_x_standard": round(rv["verify_us"] / std["us"], 3),
             "snapshot_x_standard": round(sn["verify_us"] / std["us"], 3),
             "speedup": round(sn["verify_us"] / rv["verify_us"], 3)})
@@ -578,6 +588,7 @@ def _row_gdn_append(torch, np, rd, synth, traffic, dev, stream):
     h = np.array([((warm + i) // NLs) % L for i in range(K)])
     fl = h == L - 1
     byts = np.array([traffic.gdn_append(B, H, D, N, G, int(x), bool(x == L - 1)) for x in h])
+    every = [traffic.gdn_append(B, H, D, N, G, (t // NLs) % L, (t // NLs) % L == L - 1) for t in range(warm + K)]
     std = _standard_step_row(torch, np, rd, synth, traffic, dev, stream, 4, True, S0s)
     return {"workload": f"Gated DeltaNet append-decode (flush when full), batch {B}, {H} heads, head dim {D}, "
                         f"state {N}, {G} groups, ring capacity {L}; two layer instances rotated",
@@ -589,6 +600,7 @@ def _row_gdn_append(torch, np, rd, synth, traffic, dev, stream):
             "avg_us": round(float(us.mean()), 3),
             "avg_GBs": round(float(byts.sum() / (us.sum() * 1e-6) / 1e9), 1),
             "tokens_per_s": round(float(B / (us.mean() * 1e-6)), 1),
+            "alg_bytes_avg_all_launches": round(float(np.mean(every))), "launches": warm + K,
             "standard_step": std, "speedup": round(std["us"] / float(us.mean()), 3)}
 
 
@@ -771,7 +783,8 @@ def _row_flush(torch, np, rd, synth, traffic, dev, stream, reps=8):
     byts = traffic.replay_flush(B, H, D, N, G, L - 1)
     out["mamba2"] = {"workload": f"replay_flush of {L - 1} entries, batch {B}, {H} heads, head dim {D}, "
                                  f"state {N}, {G} groups", "us": round(us, 3),
-                     "achieved_GBs": round(byts / (us * 1e-6) / 1e9, 1), "alg_bytes": byts}
+                     "achieved_GBs": round(byts / (us * 1e-6) / 1e9, 1), "alg_bytes": byts,
+                     "launches": reps + 1}
     del S0, ring
     # GDN
     wl = synth.WORKLOADS[4]
@@ -802,15 +815,20 @@ def _row_flush(torch, np, rd, synth, traffic, dev, stream, reps=8):
         raise RuntimeError("ring anomaly bits set in the flush row")
     us = float(np.mean([1e3 * a_.elapsed_time(b_) for a_, b_ in ev]))
     byts = traffic.gdn_flush(B, H, D, N, G, rounds * T)
+    # the verify rounds that fill the rings (committed count r T before round r)
+    buildup = (reps + 1) * sum(_verify_bytes(traffic, True, H, D, N, G, T, L, np.full(B, r * T))
+                               for r in range(rounds))
     out["gdn"] = {"workload": f"gdn_replay_flush of {rounds * T} entries, batch {B}, {H} heads, head dim {D}, "
                               f"state {N}, {G} groups", "us": round(us, 3),
-                  "achieved_GBs": round(byts / (us * 1e-6) / 1e9, 1), "alg_bytes": byts}
+                  "achieved_GBs": round(byts / (us * 1e-6) / 1e9, 1), "alg_bytes": byts,
+                  "launches": reps + 1, "buildup_verify_launches": (reps + 1) * rounds,
+                  "buildup_verify_alg_bytes_total": int(buildup)}
     return out
 
 
-def _rows(torch, np, rd, synth, traffic, dev, stream):
-    """Every measured row; a progress line per row goes to stderr (stdout keeps
-    the one JSON line)."""
+def _rows(torch, np, rd, synth, traffic, dev, stream, only=None):
+    """Every measured row (or the named subset); a progress line per row goes to
+    stderr (stdout keeps the one JSON line)."""
     rows = [
         ("speculative_verify", lambda: _row_verify(torch, np, rd, synth, traffic, dev, stream, 2, False)),
         ("gdn_speculative_verify", lambda: _row_verify(torch, np, rd, synth, traffic, dev, stream, 4, True)),
@@ -824,6 +842,11 @@ def _rows(torch, np, rd, synth, traffic, dev, stream):
         ("window_sweep", lambda: {"mamba2": _row_window(torch, np, rd, synth, traffic, dev, stream, 2, False),
                                   "gdn": _row_window(torch, np, rd, synth, traffic, dev, stream, 4, True)}),
     ]
+    if only is not None:
+        unknown = set(only) - {name for name, _ in rows}
+        if unknown:
+            raise SystemExit(f"unknown rows: {sorted(unknown)}")
+        rows = [(name, fn) for name, fn in rows if name in only]
     out = {}
     for name, fn in rows:
         print(f"[bench] row {name}", file=sys.stderr, flush=True)
@@ -1043,7 +1066,8 @@ def main(argv=None) -> int:
     if not a.no_rows:
         del calls, layers
         torch.cuda.empty_cache()
-        out["rows"] = _rows(torch, np, rd, synth, traffic, dev, stream)
+        out["rows"] = _rows(torch, np, rd, synth, traffic, dev, stream,
+                            None if a.rows is None else [x for x in a.rows.split(",") if x])
 
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = _cpu_baseline(a.cpu_steps)

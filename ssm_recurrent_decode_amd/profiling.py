@@ -89,6 +89,113 @@ def summarize(kernel, match, fetch, write, calib_fetch, calib_write, command, ou
     return res
 
 
+def _calibration(calib_fetch: str, calib_write: str):
+    """Bytes per FETCH_SIZE and per WRITE_SIZE unit, from the copy probe's runs
+    (median over its launches after the first, which also maps the pages)."""
+    cf = per_dispatch(calib_fetch, "probe_copy", "FETCH_SIZE")
+    cw = per_dispatch(calib_write, "probe_copy", "WRITE_SIZE")
+    if not (cf and cw):
+        raise RuntimeError("missing copy-probe dispatches in the calibration files")
+    cfv = sorted(cf[1:] or cf)[len(cf[1:] or cf) // 2]
+    cwv = sorted(cw[1:] or cw)[len(cw[1:] or cw) // 2]
+    return CALIB_BYTES / cfv, CALIB_BYTES / cwv
+
+
+def _row_kernels(bench: dict):
+    """(label, kernel-name substring, work-items, algorithmic bytes per launch
+    averaged over every launch of that kernel in the run) for the rows present
+    in one bench JSON line.  Rows that launch the same kernel at the same grid
+    (the T = 4 verify of the verify row and of the window sweep; the GDN verify
+    rounds that fill the rings before an explicit flush) are merged, weighted by
+    their launch counts."""
+    parts = []  # (label, match, grid, launches, total algorithmic bytes)
+
+    def add(label, match, grid, n, avg):
+        parts.append((label, match, grid, n, n * avg))
+
+    rows = bench.get("rows", {})
+    std = bench.get("standard_step")
+    if std and "alg_bytes" in std:
+        c = bench["config"]
+        add("ssm_decode_step (standard Mamba-2 step, headline shape)", "ssm_step_kernel<64, 128>",
+            c["batch"] * c["nheads"] * 256, 1, std["alg_bytes"])
+    m2v, gv = "replay_window_kernel<64, 128, {T}, false, 16, false>", "gdn_verify_kernel<128, 128, {T}, 16, false>"
+    g_m2, g_gdn = 512 * 32 * 256, 256 * 32 * 256
+    sv = rows.get("speculative_verify")
+    if sv:
+        add("replay_verify_T, T = 4", m2v.format(T=4), g_m2, sv["launches"], sv["alg_bytes_avg_all_launches"])
+    gs = rows.get("gdn_speculative_verify")
+    if gs:
+        add("gdn_replay_verify_T, T = 4", gv.format(T=4), g_gdn, gs["launches"], gs["alg_bytes_avg_all_launches"])
+        st = gs["standard_step"]
+        add("gdn_decode_step (standard GDN step)", "gdn_step_kernel<128, 128>", g_gdn, st["launches"], st["alg_bytes"])
+    ga = rows.get("gdn_append_decode")
+    if ga:
+        add("gdn_replay_append_decode", "gdn_verify_kernel<128, 128, 1, 16, true>", g_gdn, ga["launches"],
+            ga["alg_bytes_avg_all_launches"])
+        st = ga["standard_step"]
+        add("gdn_decode_step (standard GDN step)", "gdn_step_kernel<128, 128>", g_gdn, st["launches"], st["alg_bytes"])
+    fl = rows.get("explicit_flush")
+    if fl:
+        add("replay_flush (15 entries)", "replay_flush_kernel<64, 128>", 256 * 32 * 256, fl["mamba2"]["launches"],
+            fl["mamba2"]["alg_bytes"])
+        g = fl["gdn"]
+        add("gdn_replay_flush (12 entries)", "gdn_flush_kernel<128, 128>", g_gdn, g["launches"], g["alg_bytes"])
+        n = g["buildup_verify_launches"]
+        add("gdn_replay_verify_T, T = 4", gv.format(T=4), g_gdn, n, g["buildup_verify_alg_bytes_total"] / n)
+    ws = rows.get("window_sweep")
+    if ws:
+        for fam, d, grid, gdn in (("mamba2", 64, g_m2, False), ("gdn", 128, g_gdn, True)):
+            w = ws[fam]
+            st = w["standard_step"]
+            add("gdn_decode_step (standard GDN step)" if gdn else "ssm_decode_step (standard Mamba-2 step, B = 512)",
+                f"{'gdn_step_kernel' if gdn else 'ssm_step_kernel'}<{d}, 128>", grid, st["launches"], st["alg_bytes"])
+            for t in w["T"]:
+                T = t["T"]
+                add(f"{'gdn_replay_verify_T' if gdn else 'replay_verify_T'}, T = {T}",
+                    (gv if gdn else m2v).format(T=T), grid, t["replay_launches"],
+                    t["replay_alg_bytes_avg_all_launches"])
+                add(f"{'gdn_snapshot_verify_T' if gdn else 'ssm_snapshot_verify_T'}, T = {T}",
+                    f"snapshot_verify_kernel<{d}, 128, {T}, {'true' if gdn else 'false'}>", grid,
+                    t["snapshot_launches"], t["snapshot_alg_bytes"])
+    merged = {}
+    for label, match, grid, n, tot in parts:
+        m = merged.setdefault((match, grid), [label, 0, 0.0])
+        m[1] += n
+        m[2] += tot
+    return [(label, match, grid, tot / n) for (match, grid), (label, n, tot) in merged.items()]
+
+
+def rows_traffic(fetch, write, calib_fetch, calib_write, bench_log, command, title, out_md):
+    """Measured HBM bytes (calibrated FETCH_SIZE + WRITE_SIZE, mean per dispatch)
+    against the algorithmic bytes of every row kernel the bench run launched."""
+    with open(bench_log) as fh:
+        bench = json.loads([ln for ln in fh.read().splitlines() if ln.startswith("{")][-1])
+    rs, ws = _calibration(calib_fetch, calib_write)
+    f, w = per_dispatch_counters(fetch), per_dispatch_counters(write)
+    lines = [f"# {title}", "", "Commands (repository root on one MI355X; `<repo>` is its path):", "", "```",
+             command, "```", "",
+             f"Measured = mean per dispatch of FETCH_SIZE x {rs:.1f} B plus WRITE_SIZE x {ws:.1f} B (the "
+             "units of the 1 GiB copy probe, read and written once per launch); algorithmic = the "
+             "traffic model's bytes, averaged over the same dispatches (every launch of the kernel in the "
+             "run, warm-up and untimed passes included).  Kernels are told apart by name and grid.", "",
+             "| kernel | work-items | dispatches | read MB | written MB | measured MB | algorithmic MB | measured / algorithmic |",
+             "|---|---|---|---|---|---|---|---|"]
+    res = []
+    for label, match, grid, alg in _row_kernels(bench):
+        fv = [d["FETCH_SIZE"] for d in f.values() if match in d["name"] and d["grid"] == grid and "FETCH_SIZE" in d]
+        wv = [d["WRITE_SIZE"] for d in w.values() if match in d["name"] and d["grid"] == grid and "WRITE_SIZE" in d]
+        if not fv or not wv:
+            continue
+        rb, wb = sum(fv) / len(fv) * rs, sum(wv) / len(wv) * ws
+        res.append((label, rb + wb, alg))
+        lines.append(f"| {label} | {grid} | {len(fv)} | {rb / 1e6:.1f} | {wb / 1e6:.1f} | {(rb + wb) / 1e6:.1f} | "
+                     f"{alg / 1e6:.1f} | {(rb + wb) / alg:.3f} |")
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    return res
+
+
 MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_VALU_MFMA_BUSY_CYCLES")
 BF16_COUNTER = "SQ_INSTS_VALU_MFMA_MOPS_BF16"
 NUM_SIMDS = 256 * 4
@@ -213,10 +320,23 @@ def main(argv=None) -> int:
     t.add_argument("--out", required=True)
     t.add_argument("--title", required=True)
     t.add_argument("--command", required=True)
+    rt = sub.add_parser("rows-traffic")
+    rt.add_argument("--fetch", required=True)
+    rt.add_argument("--write", required=True)
+    rt.add_argument("--calib-fetch", required=True)
+    rt.add_argument("--calib-write", required=True)
+    rt.add_argument("--bench-log", required=True, help="the stdout of one of the two counter runs")
+    rt.add_argument("--title", required=True)
+    rt.add_argument("--command", required=True)
+    rt.add_argument("--out", required=True)
     sub.add_parser("hash")
     a = ap.parse_args(argv)
     if a.cmd == "hash":
         print(kernel_source_hash())
+        return 0
+    if a.cmd == "rows-traffic":
+        rows_traffic(a.fetch, a.write, a.calib_fetch, a.calib_write, a.bench_log, a.command, a.title, a.out)
+        print(open(a.out).read())
         return 0
     if a.cmd == "trace":
         trace_summary(a.csv, a.command, a.out, a.title)
