@@ -257,7 +257,9 @@ inline bool dims_ok(const rssm_dims* d) {
     return false;
   if (d->nheads % d->ngroups != 0) return false;
   if (d->flags & ~(RSSM_F_Y_BF16 | RSSM_F_U_BF16)) return false;
-  if ((long long)d->batch * d->nheads > (1LL << 30)) return false;
+  // one work-group of kBlock threads per (request, head): the grid's work-item
+  // count has to fit 32 bits
+  if ((long long)d->batch * d->nheads > 0xFFFFFFFFLL / rssm::kBlock) return false;
   return true;
 }
 

@@ -128,6 +128,11 @@ def test_host_validation_codes():
     bad_flags = _dims()
     bad_flags.flags = 4
     assert lib.ssm_decode_step(ctypes.byref(bad_flags), P, P, P, P, P, P, P, P, None) == EINVAL
+    # one 256-thread work-group per (request, head): B * H beyond 2^24 - 1 is refused
+    huge = _lib.rssm_dims(1 << 23, 2, 64, 128, 1, 8, 0)
+    assert lib.ssm_decode_step(ctypes.byref(huge), P, P, P, P, P, P, P, P, None) == EINVAL
+    assert lib.replay_append_decode(ctypes.byref(huge), P, ctypes.byref(r), P, P, P, P, P, P, P, None,
+                                    None) == EINVAL
     ybf = _dims()
     ybf.flags = _lib.RSSM_F_Y_BF16
     assert lib.ssm_decode_step(ctypes.byref(ybf), P, P, P, P, P, P, P, P, None) == ENOTSUP
