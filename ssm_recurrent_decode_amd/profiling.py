@@ -178,7 +178,9 @@ def rows_traffic(fetch, write, calib_fetch, calib_write, bench_log, command, tit
              f"Measured = mean per dispatch of FETCH_SIZE x {rs:.1f} B plus WRITE_SIZE x {ws:.1f} B (the "
              "units of the 1 GiB copy probe, read and written once per launch); algorithmic = the "
              "traffic model's bytes, averaged over the same dispatches (every launch of the kernel in the "
-             "run, warm-up and untimed passes included).  Kernels are told apart by name and grid.", "",
+             "run, warm-up and untimed passes included).  Kernels are told apart by name and grid.  "
+             f"Kernel sources at the time of the runs: hash `{kernel_source_hash()}` "
+             "(`python -m ssm_recurrent_decode_amd.profiling hash`).", "",
              "| kernel | work-items | dispatches | read MB | written MB | measured MB | algorithmic MB | measured / algorithmic |",
              "|---|---|---|---|---|---|---|---|"]
     res = []
