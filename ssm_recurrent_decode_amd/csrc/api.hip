@@ -10,11 +10,21 @@ struct CopyParams {
   size_t n16;
 };
 
+// Loads in flight per thread per pass of the probes (issued before any use).
+constexpr int kProbeUnroll = 4;
+
 // Grid-stride float4 copy: one read and one write of every byte.
 __global__ __launch_bounds__(kBlock) void probe_copy_kernel(CopyParams p) {
-  const size_t stride = (size_t)gridDim.x * kBlock;
-  for (size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x; i < p.n16; i += stride)
-    p.dst[i] = p.src[i];
+  const size_t stride = (size_t)gridDim.x * kBlock * kProbeUnroll;
+  for (size_t i = (size_t)blockIdx.x * kBlock * kProbeUnroll + threadIdx.x; i < p.n16; i += stride) {
+    float4 v[kProbeUnroll];
+#pragma unroll
+    for (int u = 0; u < kProbeUnroll; ++u)
+      if (i + (size_t)u * kBlock < p.n16) v[u] = p.src[i + (size_t)u * kBlock];
+#pragma unroll
+    for (int u = 0; u < kProbeUnroll; ++u)
+      if (i + (size_t)u * kBlock < p.n16) p.dst[i + (size_t)u * kBlock] = v[u];
+  }
 }
 
 struct ReadParams {
@@ -28,11 +38,15 @@ constexpr int kProbeBlocks = 4096;
 // Grid-stride float4 read; one checksum per work-group keeps the loads live.
 __global__ __launch_bounds__(kBlock) void probe_read_kernel(ReadParams p) {
   __shared__ float red[kBlock / kWave];
-  const size_t stride = (size_t)gridDim.x * kBlock;
+  const size_t stride = (size_t)gridDim.x * kBlock * kProbeUnroll;
   float acc = 0.f;
-  for (size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x; i < p.n16; i += stride) {
-    const float4 v = p.src[i];
-    acc += (v.x + v.y) + (v.z + v.w);
+  for (size_t i = (size_t)blockIdx.x * kBlock * kProbeUnroll + threadIdx.x; i < p.n16; i += stride) {
+    float4 v[kProbeUnroll];
+#pragma unroll
+    for (int u = 0; u < kProbeUnroll; ++u)
+      v[u] = (i + (size_t)u * kBlock < p.n16) ? p.src[i + (size_t)u * kBlock] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < kProbeUnroll; ++u) acc += (v[u].x + v[u].y) + (v[u].z + v[u].w);
   }
   for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, kWave);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
@@ -69,13 +83,15 @@ extern "C" int rssm_ring_sizes(const rssm_dims* d, int is_gdn, size_t out[4]) {
 extern "C" int rssm_probe_copy(void* dst, const void* src, size_t bytes, void* stream) {
   if (!dst || !src || bytes == 0 || bytes % 16 != 0) return RSSM_EINVAL;
   rssm::CopyParams p{static_cast<float4*>(dst), static_cast<const float4*>(src), bytes / 16};
-  const size_t want = (p.n16 + rssm::kBlock - 1) / rssm::kBlock;
+  const size_t per_block = (size_t)rssm::kBlock * rssm::kProbeUnroll;
+  const size_t want = (p.n16 + per_block - 1) / per_block;
   const dim3 grid((unsigned)(want < rssm::kProbeBlocks ? want : rssm::kProbeBlocks));
   return rssm_host::launch(rssm::probe_copy_kernel, grid, dim3(rssm::kBlock), stream, p);
 }
 
 extern "C" size_t rssm_probe_read_sink_floats(size_t bytes) {
-  const size_t want = (bytes / 16 + rssm::kBlock - 1) / rssm::kBlock;
+  const size_t per_block = (size_t)rssm::kBlock * rssm::kProbeUnroll;
+  const size_t want = (bytes / 16 + per_block - 1) / per_block;
   return want < (size_t)rssm::kProbeBlocks ? (want ? want : 1) : (size_t)rssm::kProbeBlocks;
 }
 
