@@ -34,7 +34,7 @@ def test_abi_version_and_strerror():
     lib = _lib.load()
     assert lib.rssm_abi_version() == _lib.ABI_VERSION == 8
     assert "invalid" in _lib.strerror(_lib.RSSM_EINVAL)
-    assert "not supported" in _lib.strerror(_lib.RSSM_ENOTSUP)
+    assert "not compiled" in _lib.strerror(_lib.RSSM_ENOTSUP)
 
 
 def _dims(B=4, H=8, d=64, n=128, G=1, L=8):
