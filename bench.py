@@ -665,6 +665,60 @@ def _row_fused_conv(torch, np, rd, synth, traffic, dev, stream):
     return res
 
 
+def _row_staggered(torch, np, rd, synth, traffic, dev, stream):
+    """The headline append-decode with the requests' ring fill levels staggered
+    (request b starts with b mod L entries cached, as under continuous batching),
+    so that every launch folds about B / L requests instead of every L-th launch
+    folding all of them; against the same launches with synchronised rings.  Four
+    layer instances rotated, the same algorithmic bytes per launch on average in
+    both (every fill level equally often), back-to-back launches timed as one."""
+    wl = synth.WORKLOADS[1]
+    sh, seed = wl.shape, wl.cfg_seed
+    B, H, D, N, G, L = sh.batch, sh.nheads, sh.head_dim, sh.state_dim, sh.ngroups, sh.capacity
+    NLs, K = 4, 4 * 4 * L
+    dims = rd.Dims(B, H, D, N, G, L)
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    st = synth.mamba2_step_inputs(sh, seed, 1, 0)
+    ip = {k_: (bf(v_) if v_.dtype == np.uint16 else torch.from_numpy(v_).to(dev)) for k_, v_ in st.items()}
+    A, bias = synth.mamba2_head_params(sh, seed, 1)
+    A, bias = torch.from_numpy(A).to(dev), torch.from_numpy(bias).to(dev)
+    y = torch.empty((B, H, D), device=dev)
+    byts = sum(traffic.replay_append(B, H, D, N, G, h, h == L - 1) for h in range(L)) / L
+    res = {"workload": f"Mamba-2 append-decode, batch {B}, {H} heads, head dim {D}, state {N}, {G} groups, "
+                       f"ring capacity {L}; four layer instances rotated",
+           "kernel": "replay_append_decode", "steps_timed": K, "alg_bytes_per_step": round(byts)}
+    for name, stagger in (("synchronised", False), ("staggered", True)):
+        layers = []
+        for l in range(NLs):
+            S0 = torch.randn((B, H, D, N), device=dev) * math.sqrt(0.1)
+            ring = rd.Ring(dims, device=dev)
+            if stagger:
+                ring.set_pointers(head=[0] * B, count=[b % L for b in range(B)], pending=[0] * B)
+            layers.append(rd.prepare_replay_append_decode(dims, S0, ring, ip["v"], ip["k"], ip["q"], ip["dt"],
+                                                          bias, A, y, stream=stream))
+            layers[-1].keep_alive = (S0, ring)
+        for t in range(NLs * L):
+            layers[t % NLs]()
+        a_, b_ = _events(torch, 1)[0]
+        torch.cuda.synchronize()
+        a_.record(stream)
+        for i in range(K):
+            layers[i % NLs]()
+        b_.record(stream)
+        torch.cuda.synchronize()
+        if any(int(Ly.keep_alive[1].err.item()) for Ly in layers):
+            raise RuntimeError("ring anomaly bits set in the staggered row")
+        us = 1e3 * a_.elapsed_time(b_) / K
+        res[name] = {"avg_us": round(us, 3), "avg_GBs": round(byts / (us * 1e-6) / 1e9, 1),
+                     "frac_of_peak": round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "tokens_per_s": round(B / (us * 1e-6), 1)}
+        del layers
+    return res
+
+
 def _row_pooled(torch, np, rd, synth, traffic, dev, stream):
     """Append-decode at the Nemotron-H-like shape with the checkpoints and rings in
     a pool of 2B request rows, each call's batch entries scattered over the pool
@@ -837,6 +891,7 @@ def _rows(torch, np, rd, synth, traffic, dev, stream, only=None):
         ("gdn_append_decode", lambda: _row_gdn_append(torch, np, rd, synth, traffic, dev, stream)),
         ("max_concurrency", lambda: _row_capacity(torch, np, rd, synth, dev)),
         ("pooled_append_decode", lambda: _row_pooled(torch, np, rd, synth, traffic, dev, stream)),
+        ("staggered_append_decode", lambda: _row_staggered(torch, np, rd, synth, traffic, dev, stream)),
         ("fused_front_end", lambda: _row_fused_conv(torch, np, rd, synth, traffic, dev, stream)),
         ("storage_precision", lambda: _row_precision(torch, np, rd, synth, traffic, dev, stream)),
         ("window_sweep", lambda: {"mamba2": _row_window(torch, np, rd, synth, traffic, dev, stream, 2, False),
