@@ -700,7 +700,7 @@ def _row_staggered(torch, np, rd, synth, traffic, dev, stream):
             layers.append(rd.prepare_replay_append_decode(dims, S0, ring, ip["v"], ip["k"], ip["q"], ip["dt"],
                                                           bias, A, y, stream=stream))
             layers[-1].keep_alive = (S0, ring)
-        for t in range(NLs * L):
+        for t in range(4 * NLs * L):          # four ring cycles per layer before timing
             layers[t % NLs]()
         a_, b_ = _events(torch, 1)[0]
         torch.cuda.synchronize()
@@ -752,7 +752,7 @@ def _row_pooled(torch, np, rd, synth, traffic, dev, stream):
             layers.append(rd.prepare_replay_append_decode(dims, S0, ring, ip["v"], ip["k"], ip["q"], ip["dt"],
                                                           bias, A, y, stream=stream))
             layers[-1].keep_alive = (S0, ring)
-        for t in range(NLs * L):
+        for t in range(4 * NLs * L):
             layers[t % NLs]()
         ev = _events(torch, K)
         torch.cuda.synchronize()
