@@ -262,7 +262,8 @@ def mfma_summary(path: str, kernels, command: str, out_md: str):
     return res
 
 
-def trace_summary(trace_csv: str, command: str, out_md: str, title: str, match: str = "rssm"):
+def trace_summary(trace_csv: str, command: str, out_md: str, title: str, match: str = "rssm",
+                  segment: str = ""):
     """Kernel durations of a rocprofv3 --kernel-trace CSV grouped by kernel name and
     grid size (one template instance can serve several workload shapes)."""
     groups = {}
@@ -281,6 +282,23 @@ def trace_summary(trace_csv: str, command: str, out_md: str, title: str, match: 
         v = sorted(v)
         lines.append(f"| {name.replace('|', '/')} | {grid} | {len(v)} | {sum(v) / len(v):.2f} | "
                      f"{v[len(v) // 2]:.2f} | {v[0]:.2f} | {v[-1]:.2f} |")
+    if segment:
+        runs, cur = [], []
+        for row in sorted(_counter_rows(trace_csv), key=lambda r_: int(r_["Start_Timestamp"])):
+            if segment in row.get("Kernel_Name", ""):
+                cur.append((int(row["Start_Timestamp"]), int(row["End_Timestamp"])))
+            elif cur:
+                runs.append(cur)
+                cur = []
+        if cur:
+            runs.append(cur)
+        if runs:
+            run = max(runs, key=len)
+            dur = [(e - s_) * 1e-3 for s_, e in run]
+            gap = (run[-1][0] - run[0][0]) * 1e-3 / max(len(run) - 1, 1)
+            lines += ["", f"Longest run of consecutive `{segment}` dispatches (the bench's back-to-back "
+                          f"timed pass): {len(run)} launches, average duration {sum(dur) / len(dur):.2f} us, "
+                          f"average start-to-start spacing {gap:.2f} us."]
     with open(out_md, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     return groups
@@ -322,6 +340,8 @@ def main(argv=None) -> int:
     t.add_argument("--out", required=True)
     t.add_argument("--title", required=True)
     t.add_argument("--command", required=True)
+    t.add_argument("--segment", default="",
+                   help="also report the longest run of consecutive dispatches of this kernel")
     rt = sub.add_parser("rows-traffic")
     rt.add_argument("--fetch", required=True)
     rt.add_argument("--write", required=True)
@@ -341,7 +361,7 @@ def main(argv=None) -> int:
         print(open(a.out).read())
         return 0
     if a.cmd == "trace":
-        trace_summary(a.csv, a.command, a.out, a.title)
+        trace_summary(a.csv, a.command, a.out, a.title, segment=a.segment)
         print(open(a.out).read())
         return 0
     if a.cmd == "mfma":

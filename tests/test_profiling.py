@@ -114,3 +114,18 @@ def test_mfma_summary_counts_both_precisions(tmp_path):
     assert abs(w["busy"] - 0.5) < 1e-9 and abs(w["us"] - 100.0) < 1e-9
     assert res[("gdn verify", G_GDN, "without")]["dispatches"] == 1
     assert os.path.exists(tmp_path / "m.md")
+
+
+def test_trace_reports_the_longest_back_to_back_run(tmp_path):
+    tr = tmp_path / "trace.csv"
+    rows = [("conv", 0, 5), (APPEND, 10, 60), ("conv", 61, 66), (APPEND, 70, 120)]      # eager: interleaved
+    rows += [(APPEND, 200 + 55 * i, 250 + 55 * i) for i in range(4)]                   # timed pass
+    rows += [("other", 1000, 1001)]
+    with open(tr, "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(["Kernel_Name", "Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z", "Start_Timestamp", "End_Timestamp"])
+        w.writerows([(n, 1, 1, 1, s * 1000, e * 1000) for n, s, e in rows])
+    out = tmp_path / "t.md"
+    pf.trace_summary(str(tr), "cmd", str(out), "title", match="", segment="replay_window_kernel")
+    text = out.read_text()
+    assert "4 launches, average duration 50.00 us, average start-to-start spacing 55.00 us" in text
