@@ -283,13 +283,16 @@ def trace_summary(trace_csv: str, command: str, out_md: str, title: str, match: 
         lines.append(f"| {name.replace('|', '/')} | {grid} | {len(v)} | {sum(v) / len(v):.2f} | "
                      f"{v[len(v) // 2]:.2f} | {v[0]:.2f} | {v[-1]:.2f} |")
     if segment:
+        # a run ends at another kernel or at an idle gap over 20 us (the bench
+        # synchronises between its passes)
         runs, cur = [], []
         for row in sorted(_counter_rows(trace_csv), key=lambda r_: int(r_["Start_Timestamp"])):
-            if segment in row.get("Kernel_Name", ""):
-                cur.append((int(row["Start_Timestamp"]), int(row["End_Timestamp"])))
-            elif cur:
+            s_, e = int(row["Start_Timestamp"]), int(row["End_Timestamp"])
+            if cur and (segment not in row.get("Kernel_Name", "") or s_ - cur[-1][1] > 20_000):
                 runs.append(cur)
                 cur = []
+            if segment in row.get("Kernel_Name", ""):
+                cur.append((s_, e))
         if cur:
             runs.append(cur)
         if runs:
