@@ -138,6 +138,35 @@ __device__ __forceinline__ float dot8_bf16(uint4 a, uint4 b) {
          bf16_lo(a.w) * bf16_lo(b.w) + bf16_hi(a.w) * bf16_hi(b.w);
 }
 
+__device__ __forceinline__ float dot4_bf16x(uint2 a, uint2 b) {
+  return bf16_lo(a.x) * bf16_lo(b.x) + bf16_hi(a.x) * bf16_hi(b.x) + bf16_lo(a.y) * bf16_lo(b.y) +
+         bf16_hi(a.y) * bf16_hi(b.y);
+}
+
+template <typename V> __device__ __forceinline__ V zero_chunk();
+template <> __device__ __forceinline__ uint2 zero_chunk<uint2>() { return make_uint2(0, 0); }
+template <> __device__ __forceinline__ uint4 zero_chunk<uint4>() { return make_uint4(0, 0, 0, 0); }
+
+// A key or query vector of n bf16 values spread over 16 lanes: lane `sub` holds
+// columns sub * n / 16 .. +n/16 as C chunks of W values (n = 64: one 8-byte
+// chunk; 128: one 16-byte chunk; 256: two).
+template <int N> struct KeyLanes;
+template <> struct KeyLanes<64> {
+  using Chunk = uint2;
+  static constexpr int C = 1, W = 4;
+  __device__ static float dot(Chunk a, Chunk b) { return dot4_bf16x(a, b); }
+};
+template <> struct KeyLanes<128> {
+  using Chunk = uint4;
+  static constexpr int C = 1, W = 8;
+  __device__ static float dot(Chunk a, Chunk b) { return dot8_bf16(a, b); }
+};
+template <> struct KeyLanes<256> {
+  using Chunk = uint4;
+  static constexpr int C = 2, W = 8;
+  __device__ static float dot(Chunk a, Chunk b) { return dot8_bf16(a, b); }
+};
+
 // Per-(request, head) ring record: words 0-1 the pointer word (head in bits
 // 0-15, count 16-31, pending 32-47), word 2 the head's A (Mamba-2), word 3 + s
 // the step size (Mamba-2) or decay (GDN) of physical slot s.  Each head has its
@@ -261,6 +290,18 @@ inline bool dims_ok(const rssm_dims* d) {
   // count has to fit 32 bits
   if ((long long)d->batch * d->nheads > 0xFFFFFFFFLL / rssm::kBlock) return false;
   return true;
+}
+
+// Mamba-2 standard step, ReplaySSM append / verify / flush / rollback: state
+// sizes n in {64, 128, 256}.  The other calls (GDN, the snapshot route, the
+// fused front-end) are built for n = 128 only (shape_supported below).
+inline bool m2_shape_supported(const rssm_dims* d) {
+  return (d->head_dim == 64 || d->head_dim == 128) &&
+         (d->state_dim == 64 || d->state_dim == 128 || d->state_dim == 256);
+}
+
+inline bool m2_ring_shape_supported(const rssm_dims* d) {
+  return m2_shape_supported(d) && d->capacity <= rssm::kMaxL;
 }
 
 inline bool shape_supported(const rssm_dims* d) {

@@ -251,11 +251,18 @@ extern "C" int ssm_decode_step(const rssm_dims* dims, float* state, const uint16
                                const float* dt_bias, const float* A, float* y, void* stream) {
   if (!rssm_host::dims_ok(dims) || !state || !v || !k || !q || !dt || !dt_bias || !A || !y)
     return RSSM_EINVAL;
-  if (!rssm_host::shape_supported(dims) || (dims->flags & RSSM_F_Y_BF16)) return RSSM_ENOTSUP;
+  if (!rssm_host::m2_shape_supported(dims) || (dims->flags & RSSM_F_Y_BF16)) return RSSM_ENOTSUP;
   StdParams p{state, v, k, q, dt, dt_bias, A, y, dims->nheads, dims->ngroups};
   const dim3 grid(dims->batch * dims->nheads);
-  if (dims->head_dim == 64) return launch(ssm_step_kernel<64, 128>, grid, dim3(kBlock), stream, p);
-  return launch(ssm_step_kernel<128, 128>, grid, dim3(kBlock), stream, p);
+  const bool d64 = dims->head_dim == 64;
+  switch (dims->state_dim) {
+    case 64:
+      return launch(d64 ? ssm_step_kernel<64, 64> : ssm_step_kernel<128, 64>, grid, dim3(kBlock), stream, p);
+    case 256:
+      return launch(d64 ? ssm_step_kernel<64, 256> : ssm_step_kernel<128, 256>, grid, dim3(kBlock), stream, p);
+    default:
+      return launch(d64 ? ssm_step_kernel<64, 128> : ssm_step_kernel<128, 128>, grid, dim3(kBlock), stream, p);
+  }
 }
 
 extern "C" int replay_append_decode(const rssm_dims* dims, float* state0, rssm_ring* ring,
@@ -266,7 +273,7 @@ extern "C" int replay_append_decode(const rssm_dims* dims, float* state0, rssm_r
       !dt || !dt_bias || !A || !y)
     return RSSM_EINVAL;
   if (dims->capacity < 1) return RSSM_EINVAL;
-  if (!rssm_host::ring_shape_supported(dims)) return RSSM_ENOTSUP;
+  if (!rssm_host::m2_ring_shape_supported(dims)) return RSSM_ENOTSUP;
   ReplayParams p = make_replay_params(dims, state0, ring);
   p.v = v;
   p.k = k;
@@ -276,6 +283,8 @@ extern "C" int replay_append_decode(const rssm_dims* dims, float* state0, rssm_r
   p.A = A;
   p.y = y;
   p.flushed = flushed;
+  if (dims->state_dim == 64) return rssm_host::launch_replay_n64(0, dims->head_dim, p, dims->batch, stream);
+  if (dims->state_dim == 256) return rssm_host::launch_replay_n256(0, dims->head_dim, p, dims->batch, stream);
   if (dims->head_dim == 64) return rssm_host::launch_window<64, 1, true>(p, dims->batch, stream);
   return rssm_host::launch_window<128, 1, true>(p, dims->batch, stream);
 }
@@ -308,12 +317,21 @@ extern "C" int replay_flush(const rssm_dims* dims, float* state0, rssm_ring* rin
                             const int32_t* mask, void* stream) {
   if (!rssm_host::dims_ok(dims) || !rssm_host::ring_ok(ring) || !state0) return RSSM_EINVAL;
   if (dims->capacity < 1) return RSSM_EINVAL;
-  if (!rssm_host::ring_shape_supported(dims)) return RSSM_ENOTSUP;
+  if (!rssm_host::m2_ring_shape_supported(dims)) return RSSM_ENOTSUP;
   ReplayParams p = make_replay_params(dims, state0, ring);
   p.mask = mask;
   const dim3 grid(dims->batch * dims->nheads);
-  if (dims->head_dim == 64) return launch(replay_flush_kernel<64, 128>, grid, dim3(kBlock), stream, p);
-  return launch(replay_flush_kernel<128, 128>, grid, dim3(kBlock), stream, p);
+  const bool d64 = dims->head_dim == 64;
+  switch (dims->state_dim) {
+    case 64:
+      return launch(d64 ? replay_flush_kernel<64, 64> : replay_flush_kernel<128, 64>, grid, dim3(kBlock), stream, p);
+    case 256:
+      return launch(d64 ? replay_flush_kernel<64, 256> : replay_flush_kernel<128, 256>, grid, dim3(kBlock), stream,
+                    p);
+    default:
+      return launch(d64 ? replay_flush_kernel<64, 128> : replay_flush_kernel<128, 128>, grid, dim3(kBlock), stream,
+                    p);
+  }
 }
 
 extern "C" int replay_verify_T(const rssm_dims* dims, int32_t T, float* state0, rssm_ring* ring,
@@ -324,7 +342,7 @@ extern "C" int replay_verify_T(const rssm_dims* dims, int32_t T, float* state0, 
       !dt || !dt_bias || !A || !y)
     return RSSM_EINVAL;
   if (T < 1 || dims->capacity < 2 * T) return RSSM_EINVAL;
-  if (!rssm_host::ring_shape_supported(dims) || T > kMaxT) return RSSM_ENOTSUP;
+  if (!rssm_host::m2_ring_shape_supported(dims) || T > kMaxT) return RSSM_ENOTSUP;
   ReplayParams p = make_replay_params(dims, state0, ring);
   p.v = v;
   p.k = k;
@@ -335,6 +353,8 @@ extern "C" int replay_verify_T(const rssm_dims* dims, int32_t T, float* state0, 
   p.y = y;
   p.flushed = flushed;
   const int D = dims->head_dim;
+  if (dims->state_dim == 64) return rssm_host::launch_replay_n64(T, D, p, dims->batch, stream);
+  if (dims->state_dim == 256) return rssm_host::launch_replay_n256(T, D, p, dims->batch, stream);
   if (T <= 4) return rssm_host::launch_replay_verify_lo(T, D, p, dims->batch, stream);
   return rssm_host::launch_replay_verify_hi(T, D, p, dims->batch, stream);
 }

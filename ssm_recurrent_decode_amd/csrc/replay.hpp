@@ -93,7 +93,8 @@ __device__ __forceinline__ void load_tiles(float4 (&s)[RT][NCT], const float* S0
 //    head, into a second buffer (the group's other heads still read the first).
 template <int D, int N, int T, bool APPEND, int LCAP, bool CONV = false>
 __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
-  static_assert(N == 128, "key/query staging assumes n = 128 (16 lanes x 8 values)");
+  static_assert(N == 64 || N == 128 || N == 256, "keys and queries: 16 lanes of n / 16 values");
+  static_assert(!CONV || N == 128, "the fused front-end is built for n = 128");
   static_assert(LCAP == 16 || LCAP == 32, "ring capacity bound");
   static_assert(!CONV || (APPEND && T == 1), "the fused front-end is one token");
   constexpr int NCONV = D + 2 * N;  // channels of one head: its x, the group's B and C
@@ -109,6 +110,9 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
   constexpr int NCP = (NCH + kBlock - 1) / kBlock;
   constexpr int RVC = LCAP * D / 8;    // 16-byte chunks of the head's ring values
   constexpr int RVP = (RVC + kBlock - 1) / kBlock;
+  using KL = KeyLanes<N>;           // a key or query over 16 lanes, KQC chunks of KQW values each
+  using KC = typename KL::Chunk;
+  constexpr int KQC = KL::C, KQW = KL::W, KPL = N / 16;
   __shared__ float s_w[T][LCAP];       // w_{j,s} by physical slot, zero where not read
   __shared__ float s_M[T][LCAP];       // k . q_s by physical slot
   __shared__ float s_abar[T];
@@ -134,7 +138,7 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
   const int MS = meta_words(L);
   float* rec = p.meta + bh * MS;  // this head's ring record
   const unsigned long long word = *reinterpret_cast<const unsigned long long*>(rec + kMetaPtr);
-  uint4 qm[T], kin[T];
+  KC qm[T][KQC], kin[T][KQC];
   uint4 newc[NCP];  // chunks of the new entries: the head's v, then the group's k
   // conv operands of the four channels this thread computes (CONV only): state
   // 4 x 3 bf16 (three 8-byte words), the token 4 bf16, the taps 4 x 4 bf16
@@ -144,8 +148,11 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
   if constexpr (!CONV) {
 #pragma unroll
     for (int sd = 0; sd < T; ++sd) {
-      qm[sd] = ld_u4(p.q + (((size_t)b * T + sd) * G + g) * N + sub * 8);
-      kin[sd] = ld_u4(p.k + (((size_t)b * T + sd) * G + g) * N + sub * 8);
+#pragma unroll
+      for (int ch = 0; ch < KQC; ++ch) {
+        qm[sd][ch] = *reinterpret_cast<const KC*>(p.q + (((size_t)b * T + sd) * G + g) * N + sub * KPL + ch * KQW);
+        kin[sd][ch] = *reinterpret_cast<const KC*>(p.k + (((size_t)b * T + sd) * G + g) * N + sub * KPL + ch * KQW);
+      }
     }
 #pragma unroll
     for (int i = 0; i < NCP; ++i) {
@@ -239,8 +246,8 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
       }
     }
     __syncthreads();
-    qm[0] = *reinterpret_cast<const uint4*>(&s_conv[D + N + sub * 8]);
-    kin[0] = *reinterpret_cast<const uint4*>(&s_conv[D + sub * 8]);
+    qm[0][0] = *reinterpret_cast<const KC*>(&s_conv[D + N + sub * 8]);
+    kin[0][0] = *reinterpret_cast<const KC*>(&s_conv[D + sub * 8]);
 #pragma unroll
     for (int i = 0; i < NCP; ++i) {
       const int t = min(tid + i * kBlock, NCH - 1);
@@ -274,13 +281,18 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
   //      columns per lane) and values (16 bytes per lane, by logical entry), now
   //      that the pointers are known: only the c entries in use are fetched, and
   //      they queue behind the checkpoint, which is needed first
-  uint4 kr[PASSES];
+  KC kr[PASSES][KQC];
 #pragma unroll
   for (int ps = 0; ps < PASSES; ++ps) {
     const int sl = ps * 16 + wave * 4 + (lane >> 4);
-    kr[ps] = make_uint4(0, 0, 0, 0);
-    if (sl < L && logical(min(sl, L - 1)) < c)
-      kr[ps] = ld_u4(p.ring_k + (((size_t)rb * G + g) * L + sl) * N + sub * 8);
+#pragma unroll
+    for (int ch = 0; ch < KQC; ++ch) kr[ps][ch] = zero_chunk<KC>();
+    if (sl < L && logical(min(sl, L - 1)) < c) {
+#pragma unroll
+      for (int ch = 0; ch < KQC; ++ch)
+        kr[ps][ch] = *reinterpret_cast<const KC*>(p.ring_k + (((size_t)rb * G + g) * L + sl) * N + sub * KPL +
+                                                  ch * KQW);
+    }
   }
   uint4 rv[RVP];
 #pragma unroll
@@ -333,7 +345,9 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
     if (j >= c && j < E) s_dtn[j - c] = dl;  // the new entries' step sizes
     if (lane < 16) {
 #pragma unroll
-      for (int sd = 0; sd < T; ++sd) *reinterpret_cast<uint4*>(&s_q[sd * N + sub * 8]) = qm[sd];
+      for (int sd = 0; sd < T; ++sd)
+#pragma unroll
+        for (int ch = 0; ch < KQC; ++ch) *reinterpret_cast<KC*>(&s_q[sd * N + sub * KPL + ch * KQW]) = qm[sd][ch];
     }
   }
 
@@ -344,14 +358,24 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
     const int sl = ps * 16 + wave * 4 + (lane >> 4);
     const bool in_ring = sl < L;
     const int j = logical(min(sl, L - 1));
-    uint4 kv = (in_ring && j < c) ? kr[ps] : make_uint4(0, 0, 0, 0);
+    KC kv[KQC];
+#pragma unroll
+    for (int ch = 0; ch < KQC; ++ch) kv[ch] = (in_ring && j < c) ? kr[ps][ch] : zero_chunk<KC>();
 #pragma unroll
     for (int sd = 0; sd < T; ++sd)
-      if (in_ring && j == c + sd) kv = kin[sd];
-    if (in_ring) *reinterpret_cast<uint4*>(&s_k[sl * N + sub * 8]) = (j < F) ? kv : make_uint4(0, 0, 0, 0);
+      if (in_ring && j == c + sd)
+#pragma unroll
+        for (int ch = 0; ch < KQC; ++ch) kv[ch] = kin[sd][ch];
+    if (in_ring)
+#pragma unroll
+      for (int ch = 0; ch < KQC; ++ch)
+        *reinterpret_cast<KC*>(&s_k[sl * N + sub * KPL + ch * KQW]) = (j < F) ? kv[ch] : zero_chunk<KC>();
 #pragma unroll
     for (int sd = 0; sd < T; ++sd) {
-      const float dv = reduce_quarter(dot8_bf16(kv, qm[sd]));
+      float dd = KL::dot(kv[0], qm[sd][0]);
+#pragma unroll
+      for (int ch = 1; ch < KQC; ++ch) dd += KL::dot(kv[ch], qm[sd][ch]);
+      const float dv = reduce_quarter(dd);
       if (sub == 0) s_M[sd][sl] = dv;
     }
   }
@@ -509,15 +533,19 @@ namespace rssm_host {
 
 using rssm::ReplayParams;
 
-template <int D, int T, bool APPEND, bool CONV = false>
+template <int D, int T, bool APPEND, bool CONV = false, int N = 128>
 int launch_window(const ReplayParams& p, int B, void* stream) {
   const dim3 grid(B * p.H), block(rssm::kBlock);
-  if (p.L <= 16) return launch(rssm::replay_window_kernel<D, 128, T, APPEND, 16, CONV>, grid, block, stream, p);
-  return launch(rssm::replay_window_kernel<D, 128, T, APPEND, 32, CONV>, grid, block, stream, p);
+  if (p.L <= 16) return launch(rssm::replay_window_kernel<D, N, T, APPEND, 16, CONV>, grid, block, stream, p);
+  return launch(rssm::replay_window_kernel<D, N, T, APPEND, 32, CONV>, grid, block, stream, p);
 }
 
-// Verify launchers for T = 1..4 and T = 5..8 live in their own translation units.
+// Verify launchers for T = 1..4 and T = 5..8 (n = 128) live in their own
+// translation units, and so do the append and verify launchers of n = 64 and
+// n = 256 (T = 0 selects the append).
 __attribute__((visibility("hidden"))) int launch_replay_verify_lo(int T, int D, const ReplayParams& p, int B, void* stream);
 __attribute__((visibility("hidden"))) int launch_replay_verify_hi(int T, int D, const ReplayParams& p, int B, void* stream);
+__attribute__((visibility("hidden"))) int launch_replay_n64(int T, int D, const ReplayParams& p, int B, void* stream);
+__attribute__((visibility("hidden"))) int launch_replay_n256(int T, int D, const ReplayParams& p, int B, void* stream);
 
 }  // namespace rssm_host

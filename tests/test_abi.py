@@ -13,6 +13,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ssm_recurrent_decode.h")
 
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation returns first
+FAKE2 = ctypes.c_void_p(0x2000)  # a second distinct fake pointer (outputs that must not alias)
 
 
 def _declared():
@@ -73,11 +74,27 @@ def test_host_validation_codes():
     # H % G != 0
     bad = _dims(H=6, G=4)
     assert lib.ssm_decode_step(ctypes.byref(bad), P, P, P, P, P, P, P, P, None) == EINVAL
-    # unsupported head/state dims
-    for dd in (_dims(d=96), _dims(n=64), _dims(d=256)):
+    # unsupported head/state dims (Mamba-2 calls: d in {64, 128}, n in {64, 128, 256})
+    for dd in (_dims(d=96), _dims(n=96), _dims(n=32), _dims(n=512), _dims(d=256)):
         assert lib.ssm_decode_step(ctypes.byref(dd), P, P, P, P, P, P, P, P, None) == ENOTSUP
         assert lib.replay_append_decode(ctypes.byref(dd), P, ctypes.byref(r), P, P, P, P, P, P, P,
                                         None, None) == ENOTSUP
+        assert lib.replay_verify_T(ctypes.byref(dd), 2, P, ctypes.byref(r), P, P, P, P, P, P, P,
+                                   None, None) == ENOTSUP
+        assert lib.replay_flush(ctypes.byref(dd), P, ctypes.byref(r), None, None) == ENOTSUP
+    # GDN, the snapshot route and the fused front-end are built for n = 128 only
+    for n in (64, 256):
+        dd = _dims(n=n)
+        assert lib.gdn_decode_step(ctypes.byref(dd), P, P, P, P, P, P, P, None) == ENOTSUP
+        assert lib.gdn_replay_verify_T(ctypes.byref(dd), 2, P, ctypes.byref(r), P, P, P, P, P, P,
+                                       None, None) == ENOTSUP
+        assert lib.gdn_replay_flush(ctypes.byref(dd), P, ctypes.byref(r), None, None) == ENOTSUP
+        assert lib.gdn_replay_append_decode(ctypes.byref(dd), P, ctypes.byref(r), P, P, P, P, P, P,
+                                            None, None) == ENOTSUP
+        assert lib.ssm_snapshot_verify_T(ctypes.byref(dd), 2, 3, P, P, P, P, P, P, P, P, P, P,
+                                         None) == ENOTSUP
+        assert lib.replay_append_decode_conv(ctypes.byref(dd), P, ctypes.byref(r), P, FAKE2, P, P, P, P,
+                                             P, P, None, None) == ENOTSUP
     # capacity limits
     assert lib.replay_append_decode(ctypes.byref(_dims(L=0)), P, ctypes.byref(r), P, P, P, P, P, P,
                                     P, None, None) == EINVAL

@@ -1,7 +1,7 @@
 """Seeded random configurations through the C ABI, against the oracle.
 
 Each case draws its own combination of what the other GPU tests exercise one at
-a time: head dim, groups and heads per group, ring capacity, decode mode
+a time: head dim, state size (Mamba-2), groups and heads per group, ring capacity, decode mode
 (append-decode, or verify rounds with random acceptance and device-side
 rollback), a pooled ring whose slot map changes every call (padding entries
 included), explicit flushes of a random subset of requests between calls, and
@@ -48,8 +48,10 @@ def _case(i):
         flags |= _lib.RSSM_F_Y_BF16
     if gdn and rng.random() < 0.3:
         flags |= _lib.RSSM_F_U_BF16
-    return dict(gdn=gdn, d=d, G=G, H=G * hpg, L=L, verify=verify, T=T, B=B, pooled=pooled, rows=rows,
-                flags=flags, seed=int(rng.integers(1 << 30)))
+    seed = int(rng.integers(1 << 30))
+    n = 128 if gdn else (128, 64, 128, 256)[(i // 2) % 4]   # GDN is built for n = 128
+    return dict(gdn=gdn, d=d, n=n, G=G, H=G * hpg, L=L, verify=verify, T=T, B=B, pooled=pooled, rows=rows,
+                flags=flags, seed=seed)
 
 
 def _slot_map(rng, B, rows, pooled):
@@ -68,7 +70,8 @@ def test_random_configuration(i):
     verify, flags, seed = cf["verify"], cf["flags"], cf["seed"]
     ybf, ubf = bool(flags & _lib.RSSM_F_Y_BF16), bool(flags & _lib.RSSM_F_U_BF16)
     cid = 4 if gdn else 2
-    sh = synth.WORKLOADS[cid].shape.with_(batch=B, nheads=H, head_dim=d, ngroups=G, capacity=L, T=T)
+    sh = synth.WORKLOADS[cid].shape.with_(batch=B, nheads=H, head_dim=d, state_dim=cf["n"], ngroups=G, capacity=L,
+                                          T=T)
     y_tol = (1e-3 + 2.0**-7 if ubf else 1e-3) + (2.0**-8 if ybf else 0.0)
     s_tol = 1e-3 + 2.0**-7 if ubf else 1e-4
     rng = np.random.default_rng(seed)
