@@ -303,11 +303,12 @@ def _row_verify(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, rounds=
     return res
 
 
-def _standard_step_row(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, states, reps=16):
-    """One-token standard decode (state read and rewritten) at a workload's shape,
-    rotated over the given state tensors; mean of per-launch HIP-event times."""
+def _standard_step_row(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, states, reps=16, shape=None):
+    """One-token standard decode (state read and rewritten) at a workload's shape
+    (or the given one), rotated over the given state tensors; mean of per-launch
+    HIP-event times."""
     wl = synth.WORKLOADS[cfg_id]
-    sh, seed = wl.shape.with_(T=1), wl.cfg_seed
+    sh, seed = (wl.shape if shape is None else shape).with_(T=1), wl.cfg_seed
     B, H, D, N, G = sh.batch, sh.nheads, sh.head_dim, sh.state_dim, sh.ngroups
     dims = rd.Dims(B, H, D, N, G, sh.capacity)
 
@@ -719,6 +720,59 @@ def _row_staggered(torch, np, rd, synth, traffic, dev, stream):
     return res
 
 
+def _row_state_sizes(torch, np, rd, synth, traffic, dev, stream):
+    """Append-decode at the Nemotron-H-like shape with state size n = 64, 128 and
+    256 (everything else as the headline), and the standard step beside it; four
+    layer instances rotated, back-to-back launches timed as one, averaged over
+    whole ring cycles."""
+    wl = synth.WORKLOADS[1]
+    base, seed = wl.shape, wl.cfg_seed
+    NLs = 4
+    res = {"workload": f"Mamba-2 append-decode, batch {base.batch}, {base.nheads} heads, head dim "
+                       f"{base.head_dim}, {base.ngroups} groups, ring capacity {base.capacity}, state size "
+                       f"n in (64, 128, 256); four layer instances rotated", "kernel": "replay_append_decode"}
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    for n in (64, 128, 256):
+        sh = base.with_(state_dim=n)
+        B, H, D, G, L = sh.batch, sh.nheads, sh.head_dim, sh.ngroups, sh.capacity
+        dims = rd.Dims(B, H, D, n, G, L)
+        st = synth.mamba2_step_inputs(sh, seed, 1, 0)
+        ip = {k_: (bf(v_) if v_.dtype == np.uint16 else torch.from_numpy(v_).to(dev)) for k_, v_ in st.items()}
+        A, bias = synth.mamba2_head_params(sh, seed, 1)
+        A, bias = torch.from_numpy(A).to(dev), torch.from_numpy(bias).to(dev)
+        y = torch.empty((B, H, D), device=dev)
+        layers, stds = [], []
+        for l in range(NLs):
+            S0 = torch.randn((B, H, D, n), device=dev) * math.sqrt(0.1)
+            ring = rd.Ring(dims, device=dev)
+            layers.append(rd.prepare_replay_append_decode(dims, S0, ring, ip["v"], ip["k"], ip["q"], ip["dt"],
+                                                          bias, A, y, stream=stream))
+            layers[-1].keep_alive = (S0, ring)
+        K = 4 * NLs * L
+        for t in range(K):
+            layers[t % NLs]()
+        a_, b_ = _events(torch, 1)[0]
+        torch.cuda.synchronize()
+        a_.record(stream)
+        for i in range(K):
+            layers[i % NLs]()
+        b_.record(stream)
+        torch.cuda.synchronize()
+        us = 1e3 * a_.elapsed_time(b_) / K
+        byts = sum(traffic.replay_append(B, H, D, n, G, h, h == L - 1) for h in range(L)) / L
+        std = _standard_step_row(torch, np, rd, synth, traffic, dev, stream, 1, False,
+                                 [Ly.keep_alive[0] for Ly in layers], shape=sh)
+        res[f"n{n}"] = {"avg_us": round(us, 3), "avg_GBs": round(byts / (us * 1e-6) / 1e9, 1),
+                        "frac_of_peak": round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                        "tokens_per_s": round(B / (us * 1e-6), 1), "alg_bytes_per_step": round(byts),
+                        "standard_step": std, "speedup": round(std["us"] / us, 3)}
+        del layers
+    return res
+
+
 def _row_pooled(torch, np, rd, synth, traffic, dev, stream):
     """Append-decode at the Nemotron-H-like shape with the checkpoints and rings in
     a pool of 2B request rows, each call's batch entries scattered over the pool
@@ -892,6 +946,7 @@ def _rows(torch, np, rd, synth, traffic, dev, stream, only=None):
         ("max_concurrency", lambda: _row_capacity(torch, np, rd, synth, dev)),
         ("pooled_append_decode", lambda: _row_pooled(torch, np, rd, synth, traffic, dev, stream)),
         ("staggered_append_decode", lambda: _row_staggered(torch, np, rd, synth, traffic, dev, stream)),
+        ("state_sizes", lambda: _row_state_sizes(torch, np, rd, synth, traffic, dev, stream)),
         ("fused_front_end", lambda: _row_fused_conv(torch, np, rd, synth, traffic, dev, stream)),
         ("storage_precision", lambda: _row_precision(torch, np, rd, synth, traffic, dev, stream)),
         ("window_sweep", lambda: {"mamba2": _row_window(torch, np, rd, synth, traffic, dev, stream, 2, False),
