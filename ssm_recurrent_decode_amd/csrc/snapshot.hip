@@ -167,29 +167,31 @@ namespace {
 
 using namespace rssm;
 
-template <int D, bool GDN>
+template <int D, int N, bool GDN>
 int launch_snapshot(int T, const SnapParams& p, const dim3& grid, void* stream) {
   using rssm_host::launch;
   const dim3 blk(kBlock);
   switch (T) {
-    case 1: return launch(snapshot_verify_kernel<D, 128, 1, GDN>, grid, blk, stream, p);
-    case 2: return launch(snapshot_verify_kernel<D, 128, 2, GDN>, grid, blk, stream, p);
-    case 3: return launch(snapshot_verify_kernel<D, 128, 3, GDN>, grid, blk, stream, p);
-    case 4: return launch(snapshot_verify_kernel<D, 128, 4, GDN>, grid, blk, stream, p);
-    case 5: return launch(snapshot_verify_kernel<D, 128, 5, GDN>, grid, blk, stream, p);
-    case 6: return launch(snapshot_verify_kernel<D, 128, 6, GDN>, grid, blk, stream, p);
-    case 7: return launch(snapshot_verify_kernel<D, 128, 7, GDN>, grid, blk, stream, p);
-    case 8: return launch(snapshot_verify_kernel<D, 128, 8, GDN>, grid, blk, stream, p);
+    case 1: return launch(snapshot_verify_kernel<D, N, 1, GDN>, grid, blk, stream, p);
+    case 2: return launch(snapshot_verify_kernel<D, N, 2, GDN>, grid, blk, stream, p);
+    case 3: return launch(snapshot_verify_kernel<D, N, 3, GDN>, grid, blk, stream, p);
+    case 4: return launch(snapshot_verify_kernel<D, N, 4, GDN>, grid, blk, stream, p);
+    case 5: return launch(snapshot_verify_kernel<D, N, 5, GDN>, grid, blk, stream, p);
+    case 6: return launch(snapshot_verify_kernel<D, N, 6, GDN>, grid, blk, stream, p);
+    case 7: return launch(snapshot_verify_kernel<D, N, 7, GDN>, grid, blk, stream, p);
+    case 8: return launch(snapshot_verify_kernel<D, N, 8, GDN>, grid, blk, stream, p);
     default: return RSSM_ENOTSUP;
   }
 }
 
 int snapshot_common(const rssm_dims* dims, int32_t T, int32_t nslots, float* pool,
                     const int32_t* slot, const uint16_t* v, const uint16_t* k, const uint16_t* q,
-                    SnapParams& p) {
+                    bool gdn, SnapParams& p) {
   if (!rssm_host::dims_ok(dims) || !pool || !slot || !v || !k || !q) return RSSM_EINVAL;
   if (T < 1 || nslots < T + 1) return RSSM_EINVAL;
-  if (!rssm_host::shape_supported(dims) || T > kMaxT || (dims->flags & RSSM_F_Y_BF16)) return RSSM_ENOTSUP;
+  // Mamba-2: n in {64, 128, 256}; GDN: n = 128, as the other calls of each family
+  const bool shape = gdn ? rssm_host::shape_supported(dims) : rssm_host::m2_shape_supported(dims);
+  if (!shape || T > kMaxT || (dims->flags & RSSM_F_Y_BF16)) return RSSM_ENOTSUP;
   p.pool = pool;
   p.slot = slot;
   p.v = v;
@@ -208,7 +210,7 @@ extern "C" int ssm_snapshot_verify_T(const rssm_dims* dims, int32_t T, int32_t n
                                      const uint16_t* q, const float* dt, const float* dt_bias,
                                      const float* A, float* y, int32_t* err, void* stream) {
   SnapParams p{};
-  const int rc = snapshot_common(dims, T, nslots, pool, slot, v, k, q, p);
+  const int rc = snapshot_common(dims, T, nslots, pool, slot, v, k, q, false, p);
   if (rc != RSSM_OK) return rc;
   if (!dt || !dt_bias || !A || !y) return RSSM_EINVAL;
   p.gate = dt;
@@ -217,8 +219,12 @@ extern "C" int ssm_snapshot_verify_T(const rssm_dims* dims, int32_t T, int32_t n
   p.y = y;
   p.err = err;
   const dim3 grid(dims->batch * dims->nheads);
-  if (dims->head_dim == 64) return launch_snapshot<64, false>(T, p, grid, stream);
-  return launch_snapshot<128, false>(T, p, grid, stream);
+  const bool d64 = dims->head_dim == 64;
+  switch (dims->state_dim) {
+    case 64: return d64 ? launch_snapshot<64, 64, false>(T, p, grid, stream) : launch_snapshot<128, 64, false>(T, p, grid, stream);
+    case 256: return d64 ? launch_snapshot<64, 256, false>(T, p, grid, stream) : launch_snapshot<128, 256, false>(T, p, grid, stream);
+    default: return d64 ? launch_snapshot<64, 128, false>(T, p, grid, stream) : launch_snapshot<128, 128, false>(T, p, grid, stream);
+  }
 }
 
 extern "C" int gdn_snapshot_verify_T(const rssm_dims* dims, int32_t T, int32_t nslots, float* pool,
@@ -226,7 +232,7 @@ extern "C" int gdn_snapshot_verify_T(const rssm_dims* dims, int32_t T, int32_t n
                                      const uint16_t* q, const float* g, const float* beta, float* y,
                                      int32_t* err, void* stream) {
   SnapParams p{};
-  const int rc = snapshot_common(dims, T, nslots, pool, slot, v, k, q, p);
+  const int rc = snapshot_common(dims, T, nslots, pool, slot, v, k, q, true, p);
   if (rc != RSSM_OK) return rc;
   if (!g || !beta || !y) return RSSM_EINVAL;
   p.gate = g;
@@ -234,8 +240,8 @@ extern "C" int gdn_snapshot_verify_T(const rssm_dims* dims, int32_t T, int32_t n
   p.y = y;
   p.err = err;
   const dim3 grid(dims->batch * dims->nheads);
-  if (dims->head_dim == 64) return launch_snapshot<64, true>(T, p, grid, stream);
-  return launch_snapshot<128, true>(T, p, grid, stream);
+  if (dims->head_dim == 64) return launch_snapshot<64, 128, true>(T, p, grid, stream);
+  return launch_snapshot<128, 128, true>(T, p, grid, stream);
 }
 
 extern "C" int snapshot_commit(int32_t batch, int32_t T, int32_t nslots, int32_t* slot,

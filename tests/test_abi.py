@@ -82,7 +82,9 @@ def test_host_validation_codes():
         assert lib.replay_verify_T(ctypes.byref(dd), 2, P, ctypes.byref(r), P, P, P, P, P, P, P,
                                    None, None) == ENOTSUP
         assert lib.replay_flush(ctypes.byref(dd), P, ctypes.byref(r), None, None) == ENOTSUP
-    # GDN, the snapshot route and the fused front-end are built for n = 128 only
+        assert lib.ssm_snapshot_verify_T(ctypes.byref(dd), 2, 3, P, P, P, P, P, P, P, P, P, P,
+                                         None) == ENOTSUP
+    # GDN (its snapshot route included) and the fused front-end are built for n = 128 only
     for n in (64, 256):
         dd = _dims(n=n)
         assert lib.gdn_decode_step(ctypes.byref(dd), P, P, P, P, P, P, P, None) == ENOTSUP
@@ -91,7 +93,7 @@ def test_host_validation_codes():
         assert lib.gdn_replay_flush(ctypes.byref(dd), P, ctypes.byref(r), None, None) == ENOTSUP
         assert lib.gdn_replay_append_decode(ctypes.byref(dd), P, ctypes.byref(r), P, P, P, P, P, P,
                                             None, None) == ENOTSUP
-        assert lib.ssm_snapshot_verify_T(ctypes.byref(dd), 2, 3, P, P, P, P, P, P, P, P, P, P,
+        assert lib.gdn_snapshot_verify_T(ctypes.byref(dd), 2, 3, P, P, P, P, P, P, P, P, P,
                                          None) == ENOTSUP
         assert lib.replay_append_decode_conv(ctypes.byref(dd), P, ctypes.byref(r), P, FAKE2, P, P, P, P,
                                              P, P, None, None) == ENOTSUP

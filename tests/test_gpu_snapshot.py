@@ -92,6 +92,13 @@ def test_ssm_snapshot_verify_commit_small(d, G, T, extra):
     _run_rounds(sh, T, T + 1 + extra, 12, gdn=False, cfg_id=2)
 
 
+@pytest.mark.parametrize("d,n,G,T", [(64, 64, 1, 4), (128, 64, 2, 3), (64, 256, 2, 2), (128, 256, 1, 6)])
+def test_ssm_snapshot_state_sizes(d, n, G, T):
+    """Mamba-2 snapshot route at state sizes 64 and 256."""
+    sh = synth.WORKLOADS[2].shape.with_(batch=3, nheads=4, head_dim=d, state_dim=n, ngroups=G, T=T)
+    _run_rounds(sh, T, T + 2, 8, gdn=False, cfg_id=2)
+
+
 @pytest.mark.parametrize("d,G,T,extra", [(128, 32, 4, 0), (64, 8, 2, 1), (128, 16, 6, 0), (64, 4, 8, 0)])
 def test_gdn_snapshot_verify_commit_small(d, G, T, extra):
     sh = synth.WORKLOADS[4].shape.with_(batch=3, head_dim=d, ngroups=G, T=T)
