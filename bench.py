@@ -13,10 +13,14 @@ timed region; consecutive steps rotate over several independent layer instances
 Infinity Cache and the state is streamed from HBM.
 
 Prints ONE JSON line.  `value` is decode tokens/s of the layer (batch x steps /
-time).  `roofline` is for the dominant kernel, replay_append_decode: algorithmic
-bytes per launch / its average launch duration measured with HIP events on its
-stream, against the 8 TB/s HBM peak.  `cpu_baseline` is the CPU oracle (ReplaySSM
-bookkeeping in float64 numpy) timed on a bounded sample of the same workload.
+time), from the median of at least 20 timed replays of a HIP graph holding one
+ring cycle of every rotated layer (flush steps included).  `roofline` is for the
+dominant kernel, replay_append_decode: algorithmic bytes per launch averaged over
+whole ring cycles / its average launch duration over those launches, measured
+with HIP events on its stream, against the 8 TB/s HBM peak; flush and non-flush
+launches are also reported separately.  `cpu_baseline` is the CPU oracle
+(ReplaySSM bookkeeping in float64 numpy) timed on a bounded sample of the same
+workload, with the host's CPU model and core count.
 """
 from __future__ import annotations
 
@@ -138,6 +142,23 @@ def _cpu_worker(job):
     return t0, time.monotonic()
 
 
+def _cpu_model() -> str:
+    """The host CPU's model name (first processor entry of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _host():
+    return {"cpu_model": _cpu_model(), "cores_available": len(os.sched_getaffinity(0))}
+
+
 def _cpu_baseline(steps: int):
     """The CPU oracle (ReplaySSM standard mode, float64) on the full batch of the
     same workload for `steps` decode steps; single-threaded numpy elementwise code."""
@@ -148,19 +169,26 @@ def _cpu_baseline(steps: int):
     dt = time.perf_counter() - t0
     return {"value": sh.batch * steps / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"ReplaySSM standard-mode oracle, full batch {sh.batch}, {steps} decode steps "
-                      f"({steps // sh.capacity} flushes), float64 numpy, {dt:.1f} s"}
+                      f"({steps // sh.capacity} flushes), float64 numpy, {dt:.1f} s", **_host()}
 
 
-def _cpu_baseline_all_cores(steps: int, max_workers: int = 16):
-    """The same oracle on every host core this process may use (at most
-    `max_workers`): requests are independent, so the batch is split into equal
-    slices, one fresh (spawned) process per slice, all released at once; the rate
-    is the whole batch over the span from the first start to the last finish."""
+# Worker processes of the all-cores leg: the share of a multi-GPU host's cores
+# that one GPU's jobs may use.
+CPU_WORKERS_MAX = 16
+
+
+def _cpu_baseline_all_cores(steps: int, max_workers: int = CPU_WORKERS_MAX):
+    """The same oracle on the host cores this process may use, at most
+    `max_workers` of them: requests are independent, so the batch is split into
+    equal slices, one fresh (spawned) process per slice, all released at once;
+    the rate is the whole batch over the span from the first start to the last
+    finish."""
     import multiprocessing as mp
 
     from ssm_recurrent_decode_amd import synth
     B = synth.WORKLOADS[1].shape.batch
-    W = max(1, min(len(os.sched_getaffinity(0)), max_workers, B))
+    host = _host()
+    W = max(1, min(host["cores_available"], max_workers, B))
     cuts = [B * i // W for i in range(W + 1)]
     ctx = mp.get_context("spawn")
     with ctx.Manager() as mgr:
@@ -169,8 +197,49 @@ def _cpu_baseline_all_cores(steps: int, max_workers: int = 16):
             spans = pool.map(_cpu_worker, [(steps, cuts[i], cuts[i + 1], barrier) for i in range(W)])
     dt = max(e for _, e in spans) - min(s for s, _ in spans)
     return {"value": B * steps / dt, "unit": "tokens/s", "cores": W, "kind": "oracle",
-            "sample": f"the same oracle, full batch {B} split over {W} processes, {steps} decode steps, "
-                      f"{dt:.1f} s wall"}
+            "sample": f"the same oracle, full batch {B} split over {W} processes ({W} of the "
+                      f"{host['cores_available']} cores this process may use; at most {max_workers}), "
+                      f"{steps} decode steps, {dt:.1f} s wall", **host}
+
+
+def _cpu_spec_baseline(cfg_id: int, requests: int, rounds: int = 16):
+    """The speculative oracle (float64, one core) on a bounded sample of a verify
+    workload: the first `requests` requests of the batch over `rounds` verify
+    rounds with the workload's acceptance draws.  Mamba-2: ReplaySSM spec-mode
+    bookkeeping; GDN: the committed state rebuilt from the ring, T serial draft
+    steps.  Rates are per verified position and per accepted token."""
+    import numpy as np
+
+    from oracle import gdn as o_gdn
+    from oracle import replay as o_rep
+    from ssm_recurrent_decode_amd import synth
+    wl = synth.WORKLOADS[cfg_id]
+    sh, seed, gdn = wl.shape, wl.cfg_seed, cfg_id == 4
+    n, T = min(requests, sh.batch), sh.T
+    S0 = np.stack([synth.state0_request(sh, seed, cfg_id, b) for b in range(n)]).astype(np.float64)
+    acc = synth.accept_draws(seed, cfg_id, rounds, sh.batch, T)[:, :n]
+    seq = []
+    for r in range(rounds):
+        st = synth.gdn_round_inputs(sh, seed, cfg_id, r) if gdn else synth.mamba2_step_inputs(sh, seed, cfg_id, r)
+        seq.append({k: (synth.bf16_bits_to_f64(v[:n]) if v.dtype == np.uint16 else v[:n].astype(np.float64))
+                    for k, v in st.items()})
+    if gdn:
+        reqs = [o_gdn.GDNReplayRequest(S0[b], sh.capacity, sh.ngroups) for b in range(n)]
+        t0 = time.perf_counter()
+        for r, rd_ in enumerate(seq):
+            for b, q in enumerate(reqs):
+                q.verify_round(rd_["v"][b], rd_["k"][b], rd_["q"][b], rd_["g"][b], rd_["beta"][b])
+                q.commit(int(acc[r, b]))
+        dt = time.perf_counter() - t0
+    else:
+        A, bias = synth.mamba2_head_params(sh, seed, cfg_id)
+        t0 = time.perf_counter()
+        o_rep.run_spec(S0, seq, bias.astype(np.float64), A.astype(np.float64), sh.capacity, sh.ngroups, acc)
+        dt = time.perf_counter() - t0
+    return {"value": n * T * rounds / dt, "unit": "verified positions/s",
+            "accepted_tokens_per_s": float(acc.sum()) / dt, "cores": 1, "kind": "oracle",
+            "sample": f"{'GDN' if gdn else 'Mamba-2'} speculative oracle, requests 0..{n - 1} of {sh.batch}, "
+                      f"{rounds} verify rounds of T={T}, float64 numpy, {dt:.1f} s", **_host()}
 
 
 # ------------------------------------------------------------------ other rows
@@ -276,6 +345,7 @@ def _row_verify(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, rounds=
     fl = np.array([counts[r] + 2 * T > L for r in range(warm, R)])
     round_s = (sum(v_us) + sum(r_us)) * 1e-6
     gbs = sum(byts) / (sum(v_us) * 1e-6) / 1e9
+    fixed = _fixed_pointer_rounds(torch, np, rd, traffic, stream, layers, pool, verify, y, dims, gdn, flags)
     base = None
     if gdn and with_standard:
         # the baseline that rewrites the state every token, at the same shape
@@ -298,9 +368,50 @@ def _row_verify(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, rounds=
            "launches": 2 * R,
            "flush_rate": round(float(fl.mean()), 4),
            "mean_committed_before": round(float(np.mean([counts[r] for r in range(warm, R)])), 3)}
+    if fixed is not None:
+        res["fixed_pointer_rounds"] = fixed
     if base is not None:
         res["standard_step"] = base
     return res
+
+
+def _fixed_pointer_rounds(torch, np, rd, traffic, stream, layers, pool, verify, y, dims, gdn, flags,
+                          reps=24):
+    """The verify kernel with every request at the same committed count, so that
+    no request folds (c = L - 2T, the largest count that does not) or every one
+    does (c = L - T, the largest count a round can start from): the fold's cost
+    separated from the rest of a round.  Before each timed launch the pointer
+    words of every record are set on the stream (head 0, pending 0, the ring
+    slots still hold earlier rounds' entries); events bracket the verify launch
+    alone, which folds the c entries (or not) exactly as in a mixed round."""
+    B, H, D, N, G, L = dims.batch, dims.nheads, dims.head_dim, dims.state_dim, dims.ngroups, dims.capacity
+    T = int(y.shape[1])
+    if L < 2 * T or L - 2 * T == L - T:
+        return None
+    out = {}
+    for tag, c in (("no_fold", L - 2 * T), ("all_fold", L - T)):
+        word = c << 16                      # head 0, count c, pending 0
+        ev = _events(torch, reps)
+        torch.cuda.synchronize()
+        for i in range(reps):
+            Ly = layers[i % len(layers)]
+            with torch.cuda.stream(stream):
+                Ly["ring"].meta.view(torch.int64)[:, :, 0].fill_(word)
+            ev[i][0].record(stream)
+            verify(i)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        us = sorted(1e3 * a_.elapsed_time(b_) for a_, b_ in ev[4:])
+        med = us[len(us) // 2]
+        nbytes = _verify_bytes(traffic, gdn, H, D, N, G, T, L, np.full(B, c), flags)
+        out[tag] = {"committed_count": c, "folds": c + 2 * T > L, "median_us": round(med, 3),
+                    "min_us": round(us[0], 3), "alg_bytes": nbytes,
+                    "achieved_GBs": round(nbytes / (med * 1e-6) / 1e9, 1),
+                    "frac_of_peak": round(nbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    for Ly in layers:
+        rd.rssm_ring_reset(dims, Ly["ring"], stream=stream)
+    torch.cuda.synchronize()
+    return out
 
 
 def _standard_step_row(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, states, reps=16, shape=None):
@@ -1047,6 +1158,7 @@ def main(argv=None) -> int:
         return layer_step % L
 
     K = a.steps
+    cyc = NL * L                       # one ring cycle of every rotated layer
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     # eager pass: the step as launched (conv, then replay), timed as a whole
@@ -1059,63 +1171,104 @@ def main(argv=None) -> int:
     end.record(stream)
     end.synchronize()
     eager_ms = start.elapsed_time(end)
-    # the dominant kernel alone: the next K replay launches back to back on its
-    # stream, HIP events around the whole run (average launch duration)
-    t_kern = a.warmup + K
+    # the dominant kernel alone over whole ring cycles of every layer, whatever
+    # K is: K_kern launches back to back on its stream (a multiple of NL * L, so
+    # every layer folds its ring once per cycle and the bytes are the L-cycle
+    # average exactly), HIP events around the whole run
+    # (at least four cycles, after four untimed ones whatever --warmup was: the
+    # first cycles of back-to-back launches run 2-10 % slower on this part)
+    K_kern = cyc * max(4, math.ceil(K / cyc))
+    t_kern = a.warmup + K + 4 * cyc
+    for i in range(4 * cyc):
+        step_calls(a.warmup + K + i)[1]()
+    ev_cyc = _events(torch, K_kern // cyc)
     torch.cuda.synchronize()
     start.record(stream)
-    for i in range(K):
+    for i in range(K_kern):
+        if i % cyc == 0:
+            ev_cyc[i // cyc][0].record(stream)
         step_calls(t_kern + i)[1]()
+        if i % cyc == cyc - 1:
+            ev_cyc[i // cyc][1].record(stream)
     end.record(stream)
     end.synchronize()
-    kern_avg_ms = start.elapsed_time(end) / K
+    kern_avg_ms = start.elapsed_time(end) / K_kern
+    cycle_us = [round(1e3 * a_.elapsed_time(b_) / cyc, 3) for a_, b_ in ev_cyc]
+    # the same launches one cycle further on, each between its own events: the
+    # launches that fold the ring and those that do not, separately
+    t_cls = t_kern + K_kern
+    n_cls = 2 * cyc
+    ev_cls = _events(torch, n_cls)
+    torch.cuda.synchronize()
+    for i in range(n_cls):
+        ev_cls[i][0].record(stream)
+        step_calls(t_cls + i)[1]()
+        ev_cls[i][1].record(stream)
+    torch.cuda.synchronize()
+    cls_us = {False: [], True: []}
+    for i in range(n_cls):
+        cls_us[cached_before(t_cls + i) == L - 1].append(1e3 * ev_cls[i][0].elapsed_time(ev_cls[i][1]))
     # the conv1d update alone, back to back (the other kernel of the step)
     torch.cuda.synchronize()
     start.record(stream)
-    for i in range(K):
+    for i in range(K_kern):
         step_calls(t_kern + i)[0]()
     end.record(stream)
     end.synchronize()
-    conv_avg_ms = start.elapsed_time(end) / K
-    total_ms = eager_ms
+    conv_avg_ms = start.elapsed_time(end) / K_kern
     graph_info = None
     if not a.no_graph:
-        # the same step sequence captured once per ring cycle of every layer and
-        # replayed: no host launch cost between kernels
-        GS = NL * L
-        t0 = a.warmup + 2 * K
+        # the step sequence of one ring cycle of every layer (NL * L steps, each
+        # conv then append) captured once and replayed: no host launch cost
+        # between kernels.  5 untimed replays, then R >= 20 replays each between
+        # its own events; the value is taken from the median replay.
+        t0 = t_cls + n_cls
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=side):
-            for j in range(GS):
+            for j in range(cyc):
                 conv, app = step_calls(t0 + j)
                 conv()
                 app()
-        reps = max(1, K // GS)
+        R = max(20, math.ceil(K / cyc))
+        ev_g = _events(torch, R)
         with torch.cuda.stream(side):
-            g.replay()                              # warm replay
-            torch.cuda.synchronize()
-            start.record(side)
-            for _ in range(reps):
+            for _ in range(5):
                 g.replay()
-            end.record(side)
-        end.synchronize()
-        total_ms = start.elapsed_time(end) * K / (reps * GS)
-        graph_info = {"steps_per_graph": GS, "replays": reps,
-                      "ms_per_step": round(start.elapsed_time(end) / (reps * GS), 5)}
+            torch.cuda.synchronize()
+            for i in range(R):
+                ev_g[i][0].record(side)
+                g.replay()
+                ev_g[i][1].record(side)
+        torch.cuda.synchronize()
+        rep_ms = sorted(a_.elapsed_time(b_) for a_, b_ in ev_g)
+        med_ms = rep_ms[R // 2] if R % 2 else 0.5 * (rep_ms[R // 2 - 1] + rep_ms[R // 2])
+        step_ms = med_ms / cyc
+        graph_info = {"steps_per_replay": cyc, "replays_timed": R, "warmup_replays": 5,
+                      "median_ms_per_replay": round(med_ms, 5), "min_ms_per_replay": round(rep_ms[0], 5),
+                      "max_ms_per_replay": round(rep_ms[-1], 5),
+                      "ms_per_step_median": round(step_ms, 6), "ms_per_step_min": round(rep_ms[0] / cyc, 6),
+                      "tokens_per_s_min_replay": round(B * cyc / (rep_ms[0] / 1e3), 1),
+                      "steps_timed": R * cyc}
+    else:
+        step_ms = eager_ms / K
     errs = [int(Ly["ring"].err.item()) for Ly in layers]
     if any(errs):
         raise RuntimeError(f"ring anomaly bits set: {errs}")
 
     alg_bytes = 0
     nflush = 0
-    for i in range(K):
+    for i in range(K_kern):
         h = cached_before(t_kern + i)
         fl = (h == L - 1)
         nflush += fl
         alg_bytes += traffic.replay_append(B, H, D, N, G, h, fl)
-    achieved = alg_bytes / K / (kern_avg_ms * 1e-3) / 1e9
-    ms_per_step = total_ms / K
-    value = B * K / (total_ms / 1e3)
+    achieved = alg_bytes / K_kern / (kern_avg_ms * 1e-3) / 1e9
+    b_nf = sum(traffic.replay_append(B, H, D, N, G, h, False) for h in range(L - 1)) / (L - 1)
+    b_fl = traffic.replay_append(B, H, D, N, G, L - 1, True)
+    nf_us, fl_us = sorted(cls_us[False]), sorted(cls_us[True])
+    nf_med, fl_med = nf_us[len(nf_us) // 2], fl_us[len(fl_us) // 2]
+    ms_per_step = step_ms
+    value = B / (step_ms / 1e3)
     traffic_bytes, traffic_note = profiling.stored_traffic("replay_append_decode")
     ceiling = _ceiling_probes(torch, rd, dev, stream, B * H * D * N * 4)
 
@@ -1135,16 +1288,27 @@ def main(argv=None) -> int:
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_bytes,
                      "traffic_note": traffic_note,
                      "kernel_avg_us": round(1e3 * kern_avg_ms, 3),
-                     "alg_bytes_per_launch": round(alg_bytes / K),
+                     "launches_timed": K_kern, "flush_launches_timed": nflush,
+                     "cycle_avg_us": cycle_us,
+                     "alg_bytes_per_launch": round(alg_bytes / K_kern),
+                     "nonflush_launch": {"median_us": round(nf_med, 3), "min_us": round(nf_us[0], 3),
+                                         "alg_bytes_avg": round(b_nf),
+                                         "achieved_GBs": round(b_nf / (nf_med * 1e-6) / 1e9, 1),
+                                         "launches": len(nf_us)},
+                     "flush_launch": {"median_us": round(fl_med, 3), "min_us": round(fl_us[0], 3),
+                                      "alg_bytes": b_fl,
+                                      "achieved_GBs": round(b_fl / (fl_med * 1e-6) / 1e9, 1),
+                                      "launches": len(fl_us)},
                      "frac_of_read_probe": round(achieved / ceiling["read_one_launch"]["GBs"], 4)},
         "ceiling_probes": ceiling,
         "conv1d": {"kernel": "causal_conv1d_update", "us": round(1e3 * conv_avg_ms, 3),
                    "achieved_GBs": round(traffic.conv1d(B, C, W) / (conv_avg_ms * 1e-3) / 1e9, 1),
                    "alg_bytes": traffic.conv1d(B, C, W)},
-        "timing": {"step": "hip graph replay" if graph_info else "eager launches",
+        "timing": {"step": "median of the timed HIP graph replays" if graph_info else "eager launches",
                    "eager_ms_per_step": round(eager_ms / K, 5), "graph": graph_info,
-                   "kernel": "HIP events around K back-to-back replay_append_decode launches on "
-                             "their stream"},
+                   "kernel": "HIP events around the back-to-back replay_append_decode launches of "
+                             "whole ring cycles of every layer on their stream (launches_timed); "
+                             "flush and non-flush launches from a second pass, one event pair each"},
     }
 
     if not a.no_standard:
@@ -1159,7 +1323,7 @@ def main(argv=None) -> int:
             std_calls[t % NL][(t // NL) % P]()
         s_a = torch.cuda.Event(enable_timing=True)
         s_b = torch.cuda.Event(enable_timing=True)
-        Ks = min(K, 512)
+        Ks = max(cyc, min(K, 512))
         torch.cuda.synchronize()
         s_a.record(stream)
         for t in range(Ks):
@@ -1182,6 +1346,11 @@ def main(argv=None) -> int:
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = _cpu_baseline(a.cpu_steps)
         out["cpu_baseline_all_cores"] = _cpu_baseline_all_cores(a.cpu_steps)
+        rows = out.get("rows", {})
+        for name, cfg_id, nreq in (("speculative_verify", 2, 128), ("gdn_speculative_verify", 4, 32)):
+            if name in rows:
+                print(f"[bench] cpu oracle for {name}", file=sys.stderr, flush=True)
+                rows[name]["cpu_baseline"] = _cpu_spec_baseline(cfg_id, nreq)
     print(json.dumps(out), flush=True)
     return 0
 

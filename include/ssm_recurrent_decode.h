@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define RSSM_ABI_VERSION 8
+#define RSSM_ABI_VERSION 9
 
 #define RSSM_OK 0
 #define RSSM_EINVAL (-22)
@@ -60,6 +60,7 @@ extern "C" {
 #define RSSM_ERR_ACCEPTED 2  /* accepted[b] outside [0, pending[b]] (clamped)            */
 #define RSSM_ERR_PENDING 4   /* decode/verify called with uncommitted drafts (dropped)   */
 #define RSSM_ERR_SLOT 8      /* slots[b] >= rows: batch entry b skipped                   */
+#define RSSM_ERR_DIVERGED 16 /* the H records of one request hold different pointer words  */
 
 typedef struct rssm_dims {
   int32_t batch;      /* B */
@@ -96,21 +97,23 @@ typedef struct rssm_dims {
  * entry j (0 = oldest) of request b is (head + j) % L.
  *
  * Everything else a call needs about request b's ring as head h sees it sits in
- * one record of RSSM_META_WORDS(L) 32-bit words (one or two 128-byte lines),
- * meta[(b * H + h) * RSSM_META_WORDS(L) + ...]:
- *   words 0-1   the pointer word (uint64, RSSM_PTR_* below): head, count =
- *               committed entries since the checkpoint, pending = uncommitted
- *               drafts that follow them;
- *   word  2     Mamba-2: the head's A of the cached entries (so a flush needs no
+ * one record (rssm_ring_record below) of RSSM_META_WORDS(L) 32-bit words: one
+ * 128-byte line for L <= 29, two for larger L.  The records of a ring are
+ * meta[(b * H + h) * RSSM_RECORD_LINES(L) + ...], and each holds
+ *   ptr         the pointer word (RSSM_PTR_* below): head, count = committed
+ *               entries since the checkpoint, pending = uncommitted drafts that
+ *               follow them;
+ *   A           Mamba-2: the head's A of the cached entries (so a flush needs no
  *               parameters); GDN: unused;
- *   words 3..   per physical slot s < L, word 3 + s: Mamba-2 Delta (after
- *               softplus; the decay is a = exp(A Delta)); GDN alpha = exp(g);
- *   the rest    unused.
+ *   slot s      (RSSM_RECORD_SLOT(rec, s), s < L; for L > 29 the slots run on
+ *               into the record's second line) Mamba-2: Delta after softplus
+ *               (the decay is a = exp(A Delta)); GDN: alpha = exp(g).
  * A call writes each record it moves as whole lines, so the per-step bookkeeping
  * costs one full-line write per head instead of several partial ones.  Every
  * call moves all H records of a request the same way, so their pointer words
  * stay equal; the work of head h reads and writes only record h, so no two
- * work-groups share one and no atomics are needed.
+ * work-groups share one and no atomics are needed.  rssm_ring_pointers gives
+ * the per-request int32 view of the pointer words on the device.
  *
  * Caller allocates every array (meta 128-byte aligned) and zero-fills meta and
  * err once before the first call; afterwards only the library writes them
@@ -129,6 +132,7 @@ typedef struct rssm_dims {
  * must not name the same row.  Sizes: rssm_ring_sizes with dims->batch = rows.
  */
 #define RSSM_META_WORDS(L) ((L) + 3 <= 32 ? 32 : 64)
+#define RSSM_RECORD_LINES(L) (RSSM_META_WORDS(L) / 32)
 #define RSSM_PTR_HEAD(w) ((uint32_t)((w) & 0xFFFFu))
 #define RSSM_PTR_COUNT(w) ((uint32_t)(((w) >> 16) & 0xFFFFu))
 #define RSSM_PTR_PENDING(w) ((uint32_t)(((w) >> 32) & 0xFFFFu))
@@ -136,11 +140,20 @@ typedef struct rssm_dims {
   (((uint64_t)(head) & 0xFFFFu) | (((uint64_t)(count) & 0xFFFFu) << 16) | \
    (((uint64_t)(pending) & 0xFFFFu) << 32))
 
+/* One 128-byte line of a ring record (see above). */
+typedef struct rssm_ring_record {
+  uint64_t ptr;     /* pointer word (RSSM_PTR_*)                                  */
+  float A;          /* Mamba-2: A of the cached entries; GDN: unused              */
+  float slot[29];   /* per physical slot: Delta (Mamba-2) or alpha (GDN); slots
+                       29..L-1 of a two-line record continue in the next line    */
+} rssm_ring_record;
+/* Slot s of the record starting at rec (any s < L, either line). */
+#define RSSM_RECORD_SLOT(rec, s) (((float*)(rec))[3 + (s)])
+
 typedef struct rssm_ring {
   void* vu;          /* Mamba-2: v  bf16 [B, H, L, d];  GDN: u fp32 [B, H, L, d]     */
   uint16_t* k;       /* bf16 [B, G, L, n]                                           */
-  float* meta;       /* [B, H, RSSM_META_WORDS(L)] records: pointer word, A, Delta or
-                        alpha per slot (see above)                                   */
+  rssm_ring_record* meta;  /* [B, H, RSSM_RECORD_LINES(L)] records (see above)     */
   int32_t* err;      /* [1] anomaly bits (RSSM_ERR_*), may be NULL                  */
   const int32_t* slots;  /* [B] pool row of each batch entry, or NULL (row = b)     */
   int32_t rows;      /* pool rows when slots != NULL (>= 1); ignored otherwise       */
@@ -160,6 +173,23 @@ int rssm_ring_sizes(const rssm_dims* dims, int is_gdn, size_t out_bytes[4]);
  * replay_flush to recycle a request slot, or to start a new request from a
  * checkpoint state. */
 int rssm_ring_reset(const rssm_dims* dims, rssm_ring* ring, const int32_t* mask, void* stream);
+
+/*
+ * The ring pointers of every request as int32 arrays, written on the device
+ * (CUDA-Graph notes, "device-side commit and rollback": the pointers live on the
+ * GPU and are moved there by kernels, so a scheduler that needs them -- to size
+ * the next window, to spot requests about to flush -- reads them without a host
+ * synchronisation, and the call can sit inside a captured graph).
+ *   head[b], count[b], pending[b]  int32 [B] out, each may be NULL: the fields
+ *        of request b's pointer word (its row slots[b] in a pooled ring;
+ *        padding entries and rows outside the pool get -1 in every field)
+ * The call also compares the H records of each request and ORs
+ * RSSM_ERR_DIVERGED into *ring->err when their pointer words differ (only
+ * possible after a write outside the library); the fields then come from head
+ * 0's record.  Works on Mamba-2 and GDN rings alike; the ring is only read.
+ */
+int rssm_ring_pointers(const rssm_dims* dims, const rssm_ring* ring, int32_t* head, int32_t* count,
+                       int32_t* pending, void* stream);
 
 /* ---------------------------------------------------------------- Mamba-2 */
 

@@ -20,9 +20,10 @@ RSSM_ERR_POINTERS = 1
 RSSM_ERR_ACCEPTED = 2
 RSSM_ERR_PENDING = 4
 RSSM_ERR_SLOT = 8
+RSSM_ERR_DIVERGED = 16
 RSSM_F_Y_BF16 = 1
 RSSM_F_U_BF16 = 2
-ABI_VERSION = 8  # RSSM_ABI_VERSION of the header this binding follows
+ABI_VERSION = 9  # RSSM_ABI_VERSION of the header this binding follows
 
 
 class rssm_dims(ctypes.Structure):
@@ -45,6 +46,7 @@ SIGNATURES = {
     "rssm_strerror": (c_char_p, [c_int]),
     "rssm_ring_sizes": (c_int, [_D, c_int, POINTER(c_size_t)]),
     "rssm_ring_reset": (c_int, [_D, _R, _P, _P]),
+    "rssm_ring_pointers": (c_int, [_D, _R, _P, _P, _P, _P]),
     "ssm_decode_step": (c_int, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "replay_append_decode": (c_int, [_D, _P, _R, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "replay_append_decode_conv": (c_int, [_D, _P, _R, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),

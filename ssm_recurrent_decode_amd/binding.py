@@ -81,9 +81,9 @@ class Ring:
     corrections u instead of bf16 values v.  ``meta`` holds one record per
     (request, head): the packed pointer word (head in bits 0-15, count 16-31,
     pending 32-47) in words 0-1, then A and the per-slot step sizes (Mamba-2) or
-    decays (GDN).  ``head``, ``count`` and ``pending`` are int32 views decoded
-    from head 0's record, and ``copies_agree`` checks that every head's pointer
-    word is the same.
+    decays (GDN).  ``head``, ``count`` and ``pending`` are int32 [rows] tensors
+    written by the library's rssm_ring_pointers (one per pool row), and
+    ``copies_agree`` checks that every head's pointer word is the same.
 
     Pooled rings: ``rows`` request rows are allocated (default: the batch), and
     ``use_slots(slots)`` makes every call map batch entry b to row slots[b]
@@ -107,20 +107,25 @@ class Ring:
         """Pointer words [B, H] (int64 view into the records)."""
         return self.meta.view(torch.int64)[:, :, 0]
 
-    def _field(self, shift: int):
-        return ((self.ptr[:, 0] >> shift) & 0xFFFF).to(torch.int32)
+    def pointers(self, stream=None):
+        """(head, count, pending) of every pool row as int32 device tensors, from
+        rssm_ring_pointers on ``stream`` (the current stream by default)."""
+        out = [torch.empty((self.rows,), dtype=torch.int32, device=self.meta.device) for _ in range(3)]
+        rssm_ring_pointers(dataclasses.replace(self.dims, batch=self.rows), self, *out, rows_view=True,
+                           stream=stream)
+        return tuple(out)
 
     @property
     def head(self):
-        return self._field(0)
+        return self.pointers()[0]
 
     @property
     def count(self):
-        return self._field(16)
+        return self.pointers()[1]
 
     @property
     def pending(self):
-        return self._field(32)
+        return self.pointers()[2]
 
     def copies_agree(self) -> bool:
         w = self.ptr
@@ -157,6 +162,25 @@ def ring_sizes(dims: Dims, gdn: bool = False):
     d = dims.c()
     _lib.check(_lib.load().rssm_ring_sizes(ctypes.byref(d), int(gdn), out), "rssm_ring_sizes")
     return list(out)
+
+
+def rssm_ring_pointers(dims: Dims, ring: Ring, head=None, count=None, pending=None, rows_view=False,
+                       stream=None):
+    """Write the ring pointers of the call's batch entries (int32 [B] each, any
+    may be None) on the device; ``rows_view`` reads pool rows 0..B-1 directly,
+    ignoring the ring's slot map."""
+    d = dims.c()
+    if rows_view:
+        if dims.batch != ring.rows:
+            raise ValueError("rows_view needs batch == ring.rows")
+        rc = ring.c()
+        rc.slots = None
+    else:
+        rc = _ring_args(dims, ring, ring.gdn)
+    outs = [_p(t, name, _I32, (dims.batch,), allow_none=True)
+            for t, name in ((head, "head"), (count, "count"), (pending, "pending"))]
+    _lib.check(_lib.load().rssm_ring_pointers(ctypes.byref(d), ctypes.byref(rc), *outs, _stream(stream)),
+               "rssm_ring_pointers")
 
 
 def rssm_ring_reset(dims: Dims, ring: Ring, mask=None, stream=None):

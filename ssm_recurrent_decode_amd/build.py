@@ -13,6 +13,7 @@ import argparse
 import concurrent.futures as cf
 import glob
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -79,6 +80,7 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
         isa_check = None
     if isa_check is not None:
         isa_check.check(asms)
+    check_no_spills(asms)
     tmp = LIB_PATH + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -89,6 +91,38 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     if verbose:
         print(f"built {LIB_PATH}")
     return LIB_PATH
+
+
+_KERNEL_META = re.compile(r"^\s+\.name:\s+(\S+)\s*$|^\s+\.private_segment_fixed_size:\s+(\d+)\s*$",
+                          re.MULTILINE)
+
+
+def kernel_scratch(asm_text: str) -> dict:
+    """Per-kernel scratch bytes per work-item (.private_segment_fixed_size of the
+    code-object metadata) in one device assembly file.  Within a kernel's
+    metadata entry the fields are listed alphabetically, so .name precedes
+    .private_segment_fixed_size."""
+    out, name = {}, None
+    for m in _KERNEL_META.finditer(asm_text):
+        if m.group(1) is not None:
+            name = m.group(1)
+        elif name is not None:
+            out[name] = int(m.group(2))
+            name = None
+    return out
+
+
+def check_no_spills(asm_files) -> None:
+    """Every decode kernel streams HBM: registers spilled to scratch would add
+    per-lane memory traffic, so a kernel with any private segment fails the build."""
+    bad = []
+    for path in asm_files:
+        with open(path) as f:
+            for name, nbytes in kernel_scratch(f.read()).items():
+                if nbytes:
+                    bad.append(f"{os.path.basename(path)}: {name} spills {nbytes} B per work-item")
+    if bad:
+        raise RuntimeError("kernels spill registers to scratch:\n" + "\n".join(bad))
 
 
 C_EXAMPLE = os.path.join(ROOT, "tests", "c_abi", "abi_roundtrip.cpp")

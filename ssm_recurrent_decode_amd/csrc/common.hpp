@@ -14,6 +14,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include "ssm_recurrent_decode.h"
@@ -174,6 +175,11 @@ template <> struct KeyLanes<256> {
 // of head h reads and writes only record h.
 constexpr int kMetaPtr = 0, kMetaA = 2, kMetaSlot = 3;
 __host__ __device__ constexpr int meta_words(int L) { return L + kMetaSlot <= 32 ? 32 : 64; }
+static_assert(sizeof(rssm_ring_record) == 128 && offsetof(rssm_ring_record, A) == 4 * kMetaA &&
+                  offsetof(rssm_ring_record, slot) == 4 * kMetaSlot,
+              "record words as the kernels index them");
+static_assert(RSSM_META_WORDS(16) == meta_words(16) && RSSM_META_WORDS(32) == meta_words(32),
+              "record size as the header states it");
 struct RingPtr {
   int head, count, pending;
 };

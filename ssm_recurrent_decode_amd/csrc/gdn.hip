@@ -175,7 +175,7 @@ GdnReplayParams make_gdn_params(const rssm_dims* d, float* state0, rssm_ring* ri
   p.state0 = state0;
   p.ring_u = static_cast<float*>(ring->vu);
   p.ring_k = ring->k;
-  p.meta = ring->meta;
+  p.meta = reinterpret_cast<float*>(ring->meta);
   p.err = ring->err;
   p.slots = ring->slots;
   p.rows = ring->rows;

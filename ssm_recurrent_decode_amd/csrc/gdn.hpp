@@ -55,8 +55,20 @@ struct GdnReplayParams {
 // pointer word is in; the weights proceed while the checkpoint is in flight.  The 2T readouts S_0 x run on
 // the matrix cores from the state registers; the fold (when flushing) follows
 // from the same registers; the per-row solve runs one thread per row after that.
+// Waves per SIMD the register budget is sized for: four (128 registers) with a
+// ring of up to 16 slots; a 32-slot ring keeps twice the committed corrections
+// and fold operands live, so three (168) where that fits without spilling to
+// scratch, two (256) or one (512, accumulation registers included) for the
+// widest windows.  The build rejects any kernel that spills.
+template <int D, int T, int LCAP>
+constexpr int gdn_waves_per_simd() {
+  if (LCAP == 16) return 4;
+  if (D == 64) return T <= 6 ? 3 : 2;
+  return T <= 2 ? 3 : (T <= 6 ? 2 : 1);
+}
+
 template <int D, int N, int T, int LCAP, bool APPEND = false>
-__global__ __launch_bounds__(kBlock, 4) void gdn_verify_kernel(GdnReplayParams p) {
+__global__ __launch_bounds__(kBlock, (gdn_waves_per_simd<D, T, LCAP>())) void gdn_verify_kernel(GdnReplayParams p) {
   static_assert(N == 128, "key staging assumes n = 128");
   static_assert(!APPEND || T == 1, "append-decode is one token");
   static_assert(2 * T <= 16, "readout vectors must fit one MFMA M axis");

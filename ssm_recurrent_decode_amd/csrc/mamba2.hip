@@ -210,6 +210,42 @@ __global__ __launch_bounds__(kBlock) void rollback_kernel(PtrParams p) {
   flag_error(p.err, bad);
 }
 
+struct PtrViewParams {
+  const float* meta;
+  int32_t* err;
+  int32_t* head;
+  int32_t* count;
+  int32_t* pending;
+  const int32_t* slots;
+  int rows;
+  int B, H, L;
+};
+
+// One thread per request: the fields of head 0's pointer word as int32, and a
+// check that the request's other H - 1 records hold the same word.
+__global__ __launch_bounds__(kBlock) void ring_pointers_kernel(PtrViewParams p) {
+  const int b = blockIdx.x * kBlock + threadIdx.x;
+  if (b >= p.B) return;
+  const int rb = pool_row(p.slots, p.rows, b, p.err, true);
+  int hd = -1, ct = -1, pd = -1;
+  if (rb >= 0) {
+    const int MS = meta_words(p.L);
+    const float* rec = p.meta + (size_t)rb * p.H * MS;
+    const unsigned long long w0 = *reinterpret_cast<const unsigned long long*>(rec + kMetaPtr);
+    bool same = true;
+    for (int h = 1; h < p.H; ++h)
+      same &= *reinterpret_cast<const unsigned long long*>(rec + (size_t)h * MS + kMetaPtr) == w0;
+    if (!same) flag_error(p.err, RSSM_ERR_DIVERGED);
+    const RingPtr rp = unpack_ptr(w0);
+    hd = rp.head;
+    ct = rp.count;
+    pd = rp.pending;
+  }
+  if (p.head != nullptr) p.head[b] = hd;
+  if (p.count != nullptr) p.count[b] = ct;
+  if (p.pending != nullptr) p.pending[b] = pd;
+}
+
 __global__ __launch_bounds__(kBlock) void ring_reset_kernel(PtrParams p) {
   const int i = blockIdx.x * kBlock + threadIdx.x;
   if (i == 0 && p.err != nullptr) *p.err = 0;
@@ -233,7 +269,7 @@ ReplayParams make_replay_params(const rssm_dims* d, float* state0, rssm_ring* ri
   p.state0 = state0;
   p.ring_v = static_cast<uint16_t*>(ring->vu);
   p.ring_k = ring->k;
-  p.meta = ring->meta;
+  p.meta = reinterpret_cast<float*>(ring->meta);
   p.err = ring->err;
   p.slots = ring->slots;
   p.rows = ring->rows;
@@ -364,7 +400,7 @@ extern "C" int replay_rollback(const rssm_dims* dims, rssm_ring* ring, const int
   if (!rssm_host::dims_ok(dims) || !rssm_host::meta_ok(ring) || !accepted) return RSSM_EINVAL;
   if (dims->capacity < 1) return RSSM_EINVAL;
   if (dims->capacity > kMaxL) return RSSM_ENOTSUP;
-  PtrParams p{ring->meta, ring->err, accepted, nullptr, ring->slots, ring->rows,
+  PtrParams p{reinterpret_cast<float*>(ring->meta), ring->err, accepted, nullptr, ring->slots, ring->rows,
               dims->batch, dims->nheads, dims->capacity};
   const dim3 grid((dims->batch * dims->nheads + kBlock - 1) / kBlock);
   return launch(rollback_kernel, grid, dim3(kBlock), stream, p);
@@ -375,8 +411,19 @@ extern "C" int rssm_ring_reset(const rssm_dims* dims, rssm_ring* ring, const int
   if (!rssm_host::dims_ok(dims) || !rssm_host::meta_ok(ring)) return RSSM_EINVAL;
   if (dims->capacity < 1) return RSSM_EINVAL;
   if (dims->capacity > kMaxL) return RSSM_ENOTSUP;
-  PtrParams p{ring->meta, ring->err, nullptr, mask, ring->slots, ring->rows,
+  PtrParams p{reinterpret_cast<float*>(ring->meta), ring->err, nullptr, mask, ring->slots, ring->rows,
               dims->batch, dims->nheads, dims->capacity};
   const dim3 grid((dims->batch * dims->nheads + kBlock - 1) / kBlock);
   return launch(ring_reset_kernel, grid, dim3(kBlock), stream, p);
+}
+
+extern "C" int rssm_ring_pointers(const rssm_dims* dims, const rssm_ring* ring, int32_t* head,
+                                  int32_t* count, int32_t* pending, void* stream) {
+  if (!rssm_host::dims_ok(dims) || !rssm_host::meta_ok(ring)) return RSSM_EINVAL;
+  if (dims->capacity < 1) return RSSM_EINVAL;
+  if (dims->capacity > kMaxL) return RSSM_ENOTSUP;
+  PtrViewParams p{reinterpret_cast<const float*>(ring->meta), ring->err, head, count, pending, ring->slots,
+                  ring->rows, dims->batch, dims->nheads, dims->capacity};
+  const dim3 grid((dims->batch + kBlock - 1) / kBlock);
+  return launch(ring_pointers_kernel, grid, dim3(kBlock), stream, p);
 }

@@ -2,9 +2,12 @@
 // stream, the standard Mamba-2 step and ReplaySSM append-decode run side by side on
 // the same inputs for 2L + 3 steps (two flushes).  ReplaySSM computes the same
 // outputs as the recurrence it replaces, so the two y must agree (relative 1e-3 of
-// the largest output), and the pointer word must follow the flush-when-full
-// schedule (count = (t + 1) mod L after step t).  Exit status 0 and "ok" on
-// success.  Built next to the library by ssm_recurrent_decode_amd.build.
+// the largest output), and the ring pointers must follow the flush-when-full
+// schedule (count = (t + 1) mod L after step t, head advancing by L at a flush,
+// i.e. staying 0): read per request through rssm_ring_pointers into device int32
+// arrays, and cross-checked against the typed record of the last head of every
+// request.  Exit status 0 and "ok" on success.  Built next to the library by
+// ssm_recurrent_decode_amd.build.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -73,6 +76,7 @@ int main() {
 
   float *state, *state0, *dA, *dbias, *ddt, *ys, *yr;
   uint16_t *dv, *dk, *dq;
+  int32_t* dptr;  // [3][B]: head, count, pending
   void* ring_mem[4];
   CHECK_HIP(hipMalloc(&state, ns * 4));
   CHECK_HIP(hipMalloc(&state0, ns * 4));
@@ -84,6 +88,7 @@ int main() {
   CHECK_HIP(hipMalloc(&dv, (size_t)B * H * D * 2));
   CHECK_HIP(hipMalloc(&dk, (size_t)B * G * N * 2));
   CHECK_HIP(hipMalloc(&dq, (size_t)B * G * N * 2));
+  CHECK_HIP(hipMalloc(&dptr, 3 * B * 4));
   for (int i = 0; i < 4; ++i) {
     CHECK_HIP(hipMalloc(&ring_mem[i], rs[i]));
     CHECK_HIP(hipMemset(ring_mem[i], 0, rs[i]));
@@ -92,8 +97,9 @@ int main() {
   CHECK_HIP(hipMemcpy(state0, S.data(), ns * 4, hipMemcpyHostToDevice));
   CHECK_HIP(hipMemcpy(dA, A.data(), H * 4, hipMemcpyHostToDevice));
   CHECK_HIP(hipMemcpy(dbias, bias.data(), H * 4, hipMemcpyHostToDevice));
-  rssm_ring ring{ring_mem[0], static_cast<uint16_t*>(ring_mem[1]), static_cast<float*>(ring_mem[2]),
+  rssm_ring ring{ring_mem[0], static_cast<uint16_t*>(ring_mem[1]), static_cast<rssm_ring_record*>(ring_mem[2]),
                  static_cast<int32_t*>(ring_mem[3]), nullptr, 0};
+  const size_t lines = RSSM_RECORD_LINES(L);  // 128-byte lines per (request, head) record
   hipStream_t stream;
   CHECK_HIP(hipStreamCreate(&stream));
 
@@ -113,8 +119,13 @@ int main() {
     CHECK_RC(replay_append_decode(&dims, state0, &ring, dv, dk, dq, ddt, dbias, dA, yr, nullptr, stream));
     CHECK_HIP(hipMemcpyAsync(hs.data(), ys, hs.size() * 4, hipMemcpyDeviceToHost, stream));
     CHECK_HIP(hipMemcpyAsync(hr.data(), yr, hr.size() * 4, hipMemcpyDeviceToHost, stream));
-    uint64_t word = 0;
-    CHECK_HIP(hipMemcpyAsync(&word, ring.meta, 8, hipMemcpyDeviceToHost, stream));
+    CHECK_RC(rssm_ring_pointers(&dims, &ring, dptr, dptr + B, dptr + 2 * B, stream));
+    int32_t ptrs[3 * B];
+    CHECK_HIP(hipMemcpyAsync(ptrs, dptr, sizeof(ptrs), hipMemcpyDeviceToHost, stream));
+    std::vector<rssm_ring_record> last(B);  // record of head H - 1 of every request
+    for (int b = 0; b < B; ++b)
+      CHECK_HIP(hipMemcpyAsync(&last[b], ring.meta + ((size_t)b * H + H - 1) * lines, sizeof(rssm_ring_record),
+                               hipMemcpyDeviceToHost, stream));
     CHECK_HIP(hipStreamSynchronize(stream));
     double mx = 0.0, err = 0.0;
     for (size_t i = 0; i < hs.size(); ++i) {
@@ -125,9 +136,14 @@ int main() {
       std::printf("step %d: replay and standard outputs differ (max %g, largest |y| %g)\n", t, err, mx);
       return 1;
     }
-    if (RSSM_PTR_COUNT(word) != (uint32_t)((t + 1) % L) || RSSM_PTR_PENDING(word) != 0) {
-      std::printf("step %d: pointer word count %u pending %u\n", t, RSSM_PTR_COUNT(word), RSSM_PTR_PENDING(word));
-      return 1;
+    for (int b = 0; b < B; ++b) {
+      const uint64_t w = last[b].ptr;
+      if (ptrs[b] != 0 || ptrs[B + b] != (t + 1) % L || ptrs[2 * B + b] != 0 || RSSM_PTR_HEAD(w) != 0u ||
+          RSSM_PTR_COUNT(w) != (uint32_t)ptrs[B + b] || RSSM_PTR_PENDING(w) != 0u) {
+        std::printf("step %d request %d: pointers head %d count %d pending %d, last head's record %u/%u/%u\n", t, b,
+                    ptrs[b], ptrs[B + b], ptrs[2 * B + b], RSSM_PTR_HEAD(w), RSSM_PTR_COUNT(w), RSSM_PTR_PENDING(w));
+        return 1;
+      }
     }
   }
   int32_t err_bits = -1;

@@ -33,7 +33,7 @@ def test_every_declared_function_is_exported_and_prototyped():
 
 def test_abi_version_and_strerror():
     lib = _lib.load()
-    assert lib.rssm_abi_version() == _lib.ABI_VERSION == 8
+    assert lib.rssm_abi_version() == _lib.ABI_VERSION == 9
     assert "invalid" in _lib.strerror(_lib.RSSM_EINVAL)
     assert "not compiled" in _lib.strerror(_lib.RSSM_ENOTSUP)
 
@@ -123,6 +123,10 @@ def test_host_validation_codes():
     r_odd.meta = FAKE.value + 64
     assert lib.replay_rollback(ctypes.byref(d), ctypes.byref(r_odd), P, None) == EINVAL
     assert lib.rssm_ring_reset(ctypes.byref(d), ctypes.byref(r_odd), None, None) == EINVAL
+    # the pointer view: an aligned record array, L within the build
+    assert lib.rssm_ring_pointers(ctypes.byref(d), ctypes.byref(r_odd), P, P, P, None) == EINVAL
+    assert lib.rssm_ring_pointers(ctypes.byref(d), None, P, P, P, None) == EINVAL
+    assert lib.rssm_ring_pointers(ctypes.byref(_dims(L=33)), ctypes.byref(r), P, P, P, None) == ENOTSUP
 
     # fused front-end: both conv buffers present and distinct
     assert lib.replay_append_decode_conv(ctypes.byref(d), P, ctypes.byref(r), P, P, P, P, P, P, P, P,

@@ -25,6 +25,7 @@ def test_cpu_baseline_single_core():
     res = bench._cpu_baseline(1)
     assert res["kind"] == "oracle" and res["cores"] == 1 and res["unit"] == "tokens/s"
     assert res["value"] > 0 and "256" in res["sample"]
+    assert res["cpu_model"] and res["cores_available"] == len(os.sched_getaffinity(0))
 
 
 @pytest.mark.timeout(300)
@@ -33,3 +34,14 @@ def test_cpu_baseline_all_cores_splits_the_batch():
     assert res["kind"] == "oracle" and res["unit"] == "tokens/s"
     assert res["cores"] == min(2, len(os.sched_getaffinity(0)))
     assert res["value"] > 0 and f"over {res['cores']} processes" in res["sample"]
+    assert res["cores_available"] == len(os.sched_getaffinity(0))
+    assert f"{res['cores']} of the {res['cores_available']} cores" in res["sample"]
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("cfg_id", [2, 4])
+def test_cpu_spec_baseline_runs_the_oracle(cfg_id):
+    res = bench._cpu_spec_baseline(cfg_id, 2, rounds=2)
+    assert res["kind"] == "oracle" and res["cores"] == 1 and res["unit"] == "verified positions/s"
+    assert res["value"] > 0 and res["accepted_tokens_per_s"] >= 0
+    assert "requests 0..1" in res["sample"] and "2 verify rounds" in res["sample"]

@@ -310,6 +310,7 @@ def test_config4_gdn_verify_full():
         if r < early.window:
             early.round(r, acc, y, state0, flushed)
         assert np.array_equal(flushed.cpu().numpy(), scheds[:, r, 1].astype(np.int32)), r
+        assert np.array_equal(ring.head.cpu().numpy(), scheds[:, r, 2]), r
         assert np.array_equal(ring.count.cpu().numpy(), scheds[:, r, 3]), r
         assert ring.copies_agree(), r
         rd.replay_rollback(dims, ring, dacc[r])

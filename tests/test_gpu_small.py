@@ -246,6 +246,34 @@ def test_pointer_anomalies_are_clamped_and_flagged():
     assert torch.all(ring.count == 0) and int(ring.err.item()) == 0
 
 
+def test_ring_pointers_view():
+    """rssm_ring_pointers: the int32 [B] view of the pointer words, through a slot
+    map (padding and out-of-pool entries read -1, the latter flagged), each output
+    optional, and a request whose head records disagree flagged as diverged."""
+    sh = synth.WORKLOADS[2].shape.with_(batch=4, nheads=4, capacity=16, T=4)
+    rows = 6
+    dims = _dims(sh)
+    ring = rd.Ring(dims, rows=rows)
+    ring.set_pointers(head=[1, 2, 3, 4, 5, 15], count=[0, 7, 12, 1, 3, 9], pending=[0, 0, 4, 0, 2, 1])
+    hd, ct, pd = (torch.full((4,), 99, dtype=torch.int32, device="cuda") for _ in range(3))
+    ring.use_slots(dev_i32(np.array([5, -1, 2, 9])))
+    rd.rssm_ring_pointers(dims, ring, hd, ct, pd)
+    assert hd.cpu().tolist() == [15, -1, 3, -1]
+    assert ct.cpu().tolist() == [9, -1, 12, -1]
+    assert pd.cpu().tolist() == [1, -1, 4, -1]
+    assert int(ring.err.item()) == 8                      # slot 9 is outside the pool
+    ct.fill_(99)
+    rd.rssm_ring_pointers(dims, ring, None, ct, None)      # outputs are optional
+    assert ct.cpu().tolist() == [9, -1, 12, -1]
+    ring.err.zero_()
+    ring.use_slots(None)
+    assert ring.count.cpu().tolist() == [0, 7, 12, 1, 3, 9]  # every pool row
+    assert int(ring.err.item()) == 0 and ring.copies_agree()
+    ring.meta.view(torch.int64)[4, 3, 0] += 1              # head 3 of row 4 moved alone
+    assert ring.head.cpu().tolist() == [1, 2, 3, 4, 5, 15]  # fields from head 0's record
+    assert int(ring.err.item()) == 16 and not ring.copies_agree()
+
+
 def test_gdn_decode_step_small():
     base = synth.WORKLOADS[4]
     sh = base.shape.with_(batch=4, T=1)
@@ -268,7 +296,8 @@ def test_gdn_decode_step_small():
 
 
 @pytest.mark.parametrize("d,G,L,T", [(128, 32, 16, 4), (64, 8, 8, 2), (128, 16, 16, 1),
-                                     (64, 8, 32, 8), (128, 32, 24, 5), (64, 4, 14, 7)])
+                                     (64, 8, 32, 8), (128, 32, 24, 5), (64, 4, 14, 7), (128, 8, 32, 3),
+                                     (128, 32, 32, 8)])
 def test_gdn_replay_verify_small(d, G, L, T):
     base = synth.WORKLOADS[4]
     sh = base.shape.with_(batch=3, head_dim=d, ngroups=G, capacity=L, T=T)
@@ -308,7 +337,8 @@ def test_gdn_replay_verify_small(d, G, L, T):
     assert es <= S_TOL, es
 
 
-@pytest.mark.parametrize("d,G,L", [(128, 32, 16), (64, 8, 8), (128, 16, 5), (64, 4, 32), (64, 8, 1), (128, 32, 2)])
+@pytest.mark.parametrize("d,G,L", [(128, 32, 16), (64, 8, 8), (128, 16, 5), (64, 4, 32), (64, 8, 1), (128, 32, 2),
+                                    (128, 32, 24), (128, 8, 32)])
 def test_gdn_replay_append_decode_small(d, G, L):
     """GDN standard decode through the ring: y every step, flush flags, pointers
     and the checkpoint at every flush against the oracle's flush-when-full
