@@ -120,7 +120,7 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
   __shared__ float s_fabar;
   __shared__ float s_dtn[T];  // the new entries' step sizes
   __shared__ __attribute__((aligned(16))) float s_y[T * D];  // outputs, stored whole lines at the end
-  __shared__ __attribute__((aligned(16))) uint16_t s_q[T * N];
+  __shared__ __attribute__((aligned(16))) uint16_t s_qk[2 * T * N];  // the drafts' q, then their k
   __shared__ __attribute__((aligned(16))) uint16_t s_k[LCAP * N];  // keys to fold by slot
   __shared__ __attribute__((aligned(16))) uint16_t s_v[LCAP * D];  // values by slot
   __shared__ __attribute__((aligned(16))) uint16_t s_conv[CONV ? NCONV : 8];  // v | k | q
@@ -138,7 +138,19 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
   const int MS = meta_words(L);
   float* rec = p.meta + bh * MS;  // this head's ring record
   const unsigned long long word = *reinterpret_cast<const unsigned long long*>(rec + kMetaPtr);
-  KC qm[T][KQC], kin[T][KQC];
+  // The token's query and key: each lane keeps the 16-lane slices it needs in
+  // registers (qm, kin).  Several drafts would hold 2T such slices per lane
+  // across the checkpoint load (a wave per SIMD fewer), so from T = 2 they are
+  // loaded one 16-byte chunk per thread and staged into LDS once the checkpoint
+  // loads are issued; the inner products read them from there (measured on the
+  // speculative workload, B = 512, T = 4: -5 % per round; at T = 1 the extra
+  // barrier costs 1 %).
+  constexpr bool kQkLds = T > 1;
+  constexpr int QKC = 2 * T * N / 8;
+  constexpr int QKP = kQkLds ? (QKC + kBlock - 1) / kBlock : 1;
+  constexpr int TQ = kQkLds ? 1 : T;  // register slices
+  uint4 qkc[QKP];
+  KC qm[TQ][KQC], kin[TQ][KQC];
   uint4 newc[NCP];  // chunks of the new entries: the head's v, then the group's k
   // conv operands of the four channels this thread computes (CONV only): state
   // 4 x 3 bf16 (three 8-byte words), the token 4 bf16, the taps 4 x 4 bf16
@@ -146,12 +158,18 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
   uint2 cst[3], cxv;
   uint4 cwv[2];
   if constexpr (!CONV) {
+    if constexpr (kQkLds) {
 #pragma unroll
-    for (int sd = 0; sd < T; ++sd) {
+      for (int i = 0; i < QKP; ++i) {
+        const int t = min(tid + i * kBlock, QKC - 1);
+        const int v = t / (N / 8), o = (t % (N / 8)) * 8;  // vector (q_0..q_{T-1}, k_0..k_{T-1}), column
+        qkc[i] = ld_u4((v < T ? p.q : p.k) + (((size_t)b * T + (v < T ? v : v - T)) * G + g) * N + o);
+      }
+    } else {
 #pragma unroll
       for (int ch = 0; ch < KQC; ++ch) {
-        qm[sd][ch] = *reinterpret_cast<const KC*>(p.q + (((size_t)b * T + sd) * G + g) * N + sub * KPL + ch * KQW);
-        kin[sd][ch] = *reinterpret_cast<const KC*>(p.k + (((size_t)b * T + sd) * G + g) * N + sub * KPL + ch * KQW);
+        qm[0][ch] = *reinterpret_cast<const KC*>(p.q + ((size_t)b * G + g) * N + sub * KPL + ch * KQW);
+        kin[0][ch] = *reinterpret_cast<const KC*>(p.k + ((size_t)b * G + g) * N + sub * KPL + ch * KQW);
       }
     }
 #pragma unroll
@@ -191,6 +209,13 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
   __builtin_amdgcn_sched_barrier(0);
   float4 st[RT][NCT];
   load_tiles<D, N, RT, NCT>(st, p.state0 + bh * D * N, wave, r, cq);
+  if constexpr (!CONV && kQkLds) {
+#pragma unroll
+    for (int i = 0; i < QKP; ++i) {
+      const int t = tid + i * kBlock;
+      if (t < QKC) *reinterpret_cast<uint4*>(&s_qk[t * 8]) = qkc[i];
+    }
+  }
 
   if constexpr (CONV) {
     // ---- 2b. the token's v, k, q from the conv (its operands arrive ahead of
@@ -343,16 +368,20 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
       if (lane == 0) s_fabar = all;
     }
     if (j >= c && j < E) s_dtn[j - c] = dl;  // the new entries' step sizes
-    if (lane < 16) {
+    if constexpr (!kQkLds && !CONV) {  // the query, for the output combine
+      if (lane < 16) {
 #pragma unroll
-      for (int sd = 0; sd < T; ++sd)
-#pragma unroll
-        for (int ch = 0; ch < KQC; ++ch) *reinterpret_cast<KC*>(&s_q[sd * N + sub * KPL + ch * KQW]) = qm[sd][ch];
+        for (int ch = 0; ch < KQC; ++ch) *reinterpret_cast<KC*>(&s_qk[sub * KPL + ch * KQW]) = qm[0][ch];
+      }
     }
   }
 
   // ---- 7. all waves: k . q_s for every physical slot (16 lanes per slot); keys
-  //      to fold staged by slot (zero rows for slots not folded)
+  //      to fold staged by slot (zero rows for slots not folded).  The drafts'
+  //      q and k come from registers at T = 1 and from LDS otherwise.
+  const uint16_t* s_qv = CONV ? &s_conv[D + N] : s_qk;
+  const uint16_t* s_kv = &s_qk[T * N];
+  if constexpr (kQkLds) __syncthreads();
 #pragma unroll
   for (int ps = 0; ps < PASSES; ++ps) {
     const int sl = ps * 16 + wave * 4 + (lane >> 4);
@@ -365,16 +394,18 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
     for (int sd = 0; sd < T; ++sd)
       if (in_ring && j == c + sd)
 #pragma unroll
-        for (int ch = 0; ch < KQC; ++ch) kv[ch] = kin[sd][ch];
+        for (int ch = 0; ch < KQC; ++ch)
+          kv[ch] = kQkLds ? *reinterpret_cast<const KC*>(&s_kv[sd * N + sub * KPL + ch * KQW]) : kin[0][ch];
     if (in_ring)
 #pragma unroll
       for (int ch = 0; ch < KQC; ++ch)
         *reinterpret_cast<KC*>(&s_k[sl * N + sub * KPL + ch * KQW]) = (j < F) ? kv[ch] : zero_chunk<KC>();
 #pragma unroll
     for (int sd = 0; sd < T; ++sd) {
-      float dd = KL::dot(kv[0], qm[sd][0]);
+      const KC* qs = kQkLds ? reinterpret_cast<const KC*>(&s_qv[sd * N + sub * KPL]) : qm[0];
+      float dd = KL::dot(kv[0], qs[0]);
 #pragma unroll
-      for (int ch = 1; ch < KQC; ++ch) dd += KL::dot(kv[ch], qm[sd][ch]);
+      for (int ch = 1; ch < KQC; ++ch) dd += KL::dot(kv[ch], qs[ch]);
       const float dv = reduce_quarter(dd);
       if (sub == 0) s_M[sd][sl] = dv;
     }
@@ -416,7 +447,7 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
     uint2 qb[NCT];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
-      qb[ct] = draft ? *reinterpret_cast<const uint2*>(&s_q[rd * N + ct * 16 + cq * 4]) : make_uint2(0, 0);
+      qb[ct] = draft ? *reinterpret_cast<const uint2*>(&s_qv[rd * N + ct * 16 + cq * 4]) : make_uint2(0, 0);
     float wm[VJ];
 #pragma unroll
     for (int m = 0; m < VJ; ++m) wm[m] = draft ? s_w[rd][cq + 4 * m] * s_M[rd][cq + 4 * m] : 0.f;
@@ -456,7 +487,7 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
         for (int sd = 0; sd < T; ++sd)
-          dots[sd] += dot4_bf16(st[rt][ct], *reinterpret_cast<const uint2*>(&s_q[sd * N + ct * 16 + cq * 4]));
+          dots[sd] += dot4_bf16(st[rt][ct], *reinterpret_cast<const uint2*>(&s_qv[sd * N + ct * 16 + cq * 4]));
 #pragma unroll
       for (int sd = 0; sd < T; ++sd) {
         float part = s_abar[sd] * dots[sd];
