@@ -63,8 +63,8 @@ extern "C" const char* rssm_strerror(int code) {
     case RSSM_OK: return "ok";
     case RSSM_EINVAL: return "invalid argument (null pointer, bad or inconsistent size)";
     case RSSM_ENOTSUP:
-      return "shape not compiled into this library (d in {64,128}; n in {64,128,256} for the Mamba-2 calls, "
-             "n = 128 for GDN and the fused front-end; L <= 32, T <= 8)";
+      return "shape not compiled into this library (d in {64,128}; n in {64,128,256}, n = 128 for the "
+             "fused front-end; L <= 32, T <= 8)";
     case RSSM_ELAUNCH: return "HIP kernel launch failed";
     default: return "unknown error code";
   }

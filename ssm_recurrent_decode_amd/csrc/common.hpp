@@ -298,24 +298,19 @@ inline bool dims_ok(const rssm_dims* d) {
   return true;
 }
 
-// Mamba-2 standard step, ReplaySSM append / verify / flush / rollback: state
-// sizes n in {64, 128, 256}.  The other calls (GDN, the snapshot route, the
-// fused front-end) are built for n = 128 only (shape_supported below).
-inline bool m2_shape_supported(const rssm_dims* d) {
+// Every decode call: head dims d in {64, 128}, state sizes n in {64, 128, 256};
+// the fused front-end is built for n = 128 only (conv_shape_supported).
+inline bool shape_supported(const rssm_dims* d) {
   return (d->head_dim == 64 || d->head_dim == 128) &&
          (d->state_dim == 64 || d->state_dim == 128 || d->state_dim == 256);
 }
 
-inline bool m2_ring_shape_supported(const rssm_dims* d) {
-  return m2_shape_supported(d) && d->capacity <= rssm::kMaxL;
-}
-
-inline bool shape_supported(const rssm_dims* d) {
-  return (d->head_dim == 64 || d->head_dim == 128) && d->state_dim == 128;
-}
-
 inline bool ring_shape_supported(const rssm_dims* d) {
   return shape_supported(d) && d->capacity <= rssm::kMaxL;
+}
+
+inline bool conv_shape_supported(const rssm_dims* d) {
+  return ring_shape_supported(d) && d->state_dim == 128;
 }
 
 inline bool meta_ok(const rssm_ring* r) {

@@ -196,8 +196,12 @@ extern "C" int gdn_decode_step(const rssm_dims* dims, float* state, const uint16
   if (!rssm_host::shape_supported(dims) || (dims->flags & RSSM_F_Y_BF16)) return RSSM_ENOTSUP;
   GdnStdParams p{state, v, k, q, g, beta, y, dims->nheads, dims->ngroups};
   const dim3 grid(dims->batch * dims->nheads);
-  if (dims->head_dim == 64) return launch(gdn_step_kernel<64, 128>, grid, dim3(kBlock), stream, p);
-  return launch(gdn_step_kernel<128, 128>, grid, dim3(kBlock), stream, p);
+  const bool d64 = dims->head_dim == 64;
+  switch (dims->state_dim) {
+    case 64: return launch(d64 ? gdn_step_kernel<64, 64> : gdn_step_kernel<128, 64>, grid, dim3(kBlock), stream, p);
+    case 256: return launch(d64 ? gdn_step_kernel<64, 256> : gdn_step_kernel<128, 256>, grid, dim3(kBlock), stream, p);
+    default: return launch(d64 ? gdn_step_kernel<64, 128> : gdn_step_kernel<128, 128>, grid, dim3(kBlock), stream, p);
+  }
 }
 
 extern "C" int gdn_replay_verify_T(const rssm_dims* dims, int32_t T, float* state0, rssm_ring* ring,
@@ -217,8 +221,11 @@ extern "C" int gdn_replay_verify_T(const rssm_dims* dims, int32_t T, float* stat
   p.beta = beta;
   p.y = y;
   p.flushed = flushed;
-  if (T <= 4) return rssm_host::launch_gdn_verify_lo(T, dims->head_dim, p, dims->batch, stream);
-  return rssm_host::launch_gdn_verify_hi(T, dims->head_dim, p, dims->batch, stream);
+  const int D = dims->head_dim;
+  if (dims->state_dim == 64) return rssm_host::launch_gdn_n64(T, D, p, dims->batch, stream);
+  if (dims->state_dim == 256) return rssm_host::launch_gdn_n256(T, D, p, dims->batch, stream);
+  if (T <= 4) return rssm_host::launch_gdn_verify_lo(T, D, p, dims->batch, stream);
+  return rssm_host::launch_gdn_verify_hi(T, D, p, dims->batch, stream);
 }
 
 extern "C" int gdn_replay_append_decode(const rssm_dims* dims, float* state0, rssm_ring* ring,
@@ -238,6 +245,8 @@ extern "C" int gdn_replay_append_decode(const rssm_dims* dims, float* state0, rs
   p.beta = beta;
   p.y = y;
   p.flushed = flushed;
+  if (dims->state_dim == 64) return rssm_host::launch_gdn_n64(0, dims->head_dim, p, dims->batch, stream);
+  if (dims->state_dim == 256) return rssm_host::launch_gdn_n256(0, dims->head_dim, p, dims->batch, stream);
   if (dims->head_dim == 64) return rssm_host::launch_gdn_window<64, 1, true>(p, dims->batch, stream);
   return rssm_host::launch_gdn_window<128, 1, true>(p, dims->batch, stream);
 }
@@ -250,6 +259,12 @@ extern "C" int gdn_replay_flush(const rssm_dims* dims, float* state0, rssm_ring*
   GdnReplayParams p = make_gdn_params(dims, state0, ring);
   p.mask = mask;
   const dim3 grid(dims->batch * dims->nheads);
-  if (dims->head_dim == 64) return launch(gdn_flush_kernel<64, 128>, grid, dim3(kBlock), stream, p);
-  return launch(gdn_flush_kernel<128, 128>, grid, dim3(kBlock), stream, p);
+  const bool d64 = dims->head_dim == 64;
+  switch (dims->state_dim) {
+    case 64: return launch(d64 ? gdn_flush_kernel<64, 64> : gdn_flush_kernel<128, 64>, grid, dim3(kBlock), stream, p);
+    case 256:
+      return launch(d64 ? gdn_flush_kernel<64, 256> : gdn_flush_kernel<128, 256>, grid, dim3(kBlock), stream, p);
+    default:
+      return launch(d64 ? gdn_flush_kernel<64, 128> : gdn_flush_kernel<128, 128>, grid, dim3(kBlock), stream, p);
+  }
 }

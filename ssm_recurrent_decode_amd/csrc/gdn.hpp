@@ -55,21 +55,25 @@ struct GdnReplayParams {
 // pointer word is in; the weights proceed while the checkpoint is in flight.  The 2T readouts S_0 x run on
 // the matrix cores from the state registers; the fold (when flushing) follows
 // from the same registers; the per-row solve runs one thread per row after that.
-// Waves per SIMD the register budget is sized for: four (128 registers) with a
-// ring of up to 16 slots; a 32-slot ring keeps twice the committed corrections
-// and fold operands live, so three (168) where that fits without spilling to
-// scratch, two (256) or one (512, accumulation registers included) for the
-// widest windows.  The build rejects any kernel that spills.
-template <int D, int T, int LCAP>
+// Waves per SIMD the register budget is sized for.  At n = 128: four (128
+// registers) with a ring of up to 16 slots; a 32-slot ring keeps twice the
+// committed corrections and fold operands live, so three (168) where that fits
+// without spilling to scratch, two (256) or one (512, accumulation registers
+// included) for the widest windows.  n = 64 halves the checkpoint registers, n =
+// 256 doubles them (d = 128, n = 256: 128 registers for the checkpoint alone).
+// The build rejects any kernel that spills.
+template <int D, int N, int T, int LCAP>
 constexpr int gdn_waves_per_simd() {
+  if (N == 64) return LCAP == 16 ? 5 : (D == 64 || T <= 2 ? 4 : 3);
+  if (N == 256) return D == 64 ? (LCAP == 16 ? 4 : 3) : 2;
   if (LCAP == 16) return 4;
   if (D == 64) return T <= 6 ? 3 : 2;
   return T <= 2 ? 3 : (T <= 6 ? 2 : 1);
 }
 
 template <int D, int N, int T, int LCAP, bool APPEND = false>
-__global__ __launch_bounds__(kBlock, (gdn_waves_per_simd<D, T, LCAP>())) void gdn_verify_kernel(GdnReplayParams p) {
-  static_assert(N == 128, "key staging assumes n = 128");
+__global__ __launch_bounds__(kBlock, (gdn_waves_per_simd<D, N, T, LCAP>())) void gdn_verify_kernel(GdnReplayParams p) {
+  static_assert(N == 64 || N == 128 || N == 256, "keys and queries: 16 lanes of n / 16 values");
   static_assert(!APPEND || T == 1, "append-decode is one token");
   static_assert(2 * T <= 16, "readout vectors must fit one MFMA M axis");
   static_assert(D <= kBlock, "one thread per state row in the solve");
@@ -84,6 +88,9 @@ __global__ __launch_bounds__(kBlock, (gdn_waves_per_simd<D, T, LCAP>())) void gd
   constexpr int XVP = (XC + VC + kBlock - 1) / kBlock;
   constexpr int UC = LCAP * D / 4;        // ... of the ring corrections (fp32)
   constexpr int UP = (UC + kBlock - 1) / kBlock;
+  using KL = KeyLanes<N>;  // a key or readout vector over 16 lanes, KQC chunks of KQW values each
+  using KC = typename KL::Chunk;
+  constexpr int KQC = KL::C, KQW = KL::W, KPL = N / 16;
   __shared__ float s_Z[NV][D];            // (S_0 x_v)[row]
   __shared__ float s_M[NV][LCAP];         // k_slot . x_v by physical slot
   __shared__ float s_w[LCAP];             // w_j by physical slot, zero if not committed
@@ -175,13 +182,18 @@ __global__ __launch_bounds__(kBlock, (gdn_waves_per_simd<D, T, LCAP>())) void gd
   // the committed entries' ring keys (slot ps*16 + wave*4 + lane/16, 8 columns per
   // lane) and corrections (16 bytes per lane, by logical entry), now that the
   // pointers are known: only the c entries in use, queued behind the checkpoint
-  uint4 kr[PASSES];
+  KC kr[PASSES][KQC];
 #pragma unroll
   for (int ps = 0; ps < PASSES; ++ps) {
     const int sl = ps * 16 + wave * 4 + (lane >> 4);
-    kr[ps] = make_uint4(0, 0, 0, 0);
-    if (sl < L && logical(min(sl, L - 1)) < c)
-      kr[ps] = ld_u4(p.ring_k + (((size_t)rb * G + g) * L + sl) * N + sub * 8);
+#pragma unroll
+    for (int ch = 0; ch < KQC; ++ch) kr[ps][ch] = zero_chunk<KC>();
+    if (sl < L && logical(min(sl, L - 1)) < c) {
+#pragma unroll
+      for (int ch = 0; ch < KQC; ++ch)
+        kr[ps][ch] = *reinterpret_cast<const KC*>(p.ring_k + (((size_t)rb * G + g) * L + sl) * N + sub * KPL +
+                                                  ch * KQW);
+    }
   }
   const int cpe = p.u_bf16 ? D / 8 : D / 4;  // 16-byte chunks per cached correction
   uint4 uc[UP];
@@ -228,15 +240,22 @@ __global__ __launch_bounds__(kBlock, (gdn_waves_per_simd<D, T, LCAP>())) void gd
     const int sl = ps * 16 + wave * 4 + (lane >> 4);
     const bool in_ring = sl < L;
     const int j = logical(min(sl, L - 1));
-    uint4 kv = (in_ring && j < c) ? kr[ps] : make_uint4(0, 0, 0, 0);
     const int sd = j - c;
-    if (in_ring && sd >= 0 && sd < T) kv = *reinterpret_cast<const uint4*>(&s_x[sd * N + sub * 8]);
-    if (in_ring)
-      *reinterpret_cast<uint4*>(&s_k[sl * N + sub * 8]) =
-          (j < F) ? kv : make_uint4(0, 0, 0, 0);
+    KC kv[KQC];
+#pragma unroll
+    for (int ch = 0; ch < KQC; ++ch) {
+      kv[ch] = (in_ring && j < c) ? kr[ps][ch] : zero_chunk<KC>();
+      if (in_ring && sd >= 0 && sd < T) kv[ch] = *reinterpret_cast<const KC*>(&s_x[sd * N + sub * KPL + ch * KQW]);
+      if (in_ring)
+        *reinterpret_cast<KC*>(&s_k[sl * N + sub * KPL + ch * KQW]) = (j < F) ? kv[ch] : zero_chunk<KC>();
+    }
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
-      const float d = reduce_quarter(dot8_bf16(kv, *reinterpret_cast<const uint4*>(&s_x[v * N + sub * 8])));
+      float dd = 0.f;
+#pragma unroll
+      for (int ch = 0; ch < KQC; ++ch)
+        dd += KL::dot(kv[ch], *reinterpret_cast<const KC*>(&s_x[v * N + sub * KPL + ch * KQW]));
+      const float d = reduce_quarter(dd);
       if (sub == 0) s_M[v][sl] = d;
     }
   }
@@ -421,15 +440,19 @@ namespace rssm_host {
 
 using rssm::GdnReplayParams;
 
-template <int D, int T, bool APPEND = false>
+template <int D, int T, bool APPEND = false, int N = 128>
 int launch_gdn_window(const GdnReplayParams& p, int B, void* stream) {
   const dim3 grid(B * p.H), block(rssm::kBlock);
-  if (p.L <= 16) return launch(rssm::gdn_verify_kernel<D, 128, T, 16, APPEND>, grid, block, stream, p);
-  return launch(rssm::gdn_verify_kernel<D, 128, T, 32, APPEND>, grid, block, stream, p);
+  if (p.L <= 16) return launch(rssm::gdn_verify_kernel<D, N, T, 16, APPEND>, grid, block, stream, p);
+  return launch(rssm::gdn_verify_kernel<D, N, T, 32, APPEND>, grid, block, stream, p);
 }
 
-// Verify launchers for T = 1..4 and T = 5..8 live in their own translation units.
+// Verify launchers for T = 1..4 and T = 5..8 (n = 128) live in their own
+// translation units, and so do the append and verify launchers of n = 64 and
+// n = 256 (T = 0 selects the append).
 __attribute__((visibility("hidden"))) int launch_gdn_verify_lo(int T, int D, const GdnReplayParams& p, int B, void* stream);
 __attribute__((visibility("hidden"))) int launch_gdn_verify_hi(int T, int D, const GdnReplayParams& p, int B, void* stream);
+__attribute__((visibility("hidden"))) int launch_gdn_n64(int T, int D, const GdnReplayParams& p, int B, void* stream);
+__attribute__((visibility("hidden"))) int launch_gdn_n256(int T, int D, const GdnReplayParams& p, int B, void* stream);
 
 }  // namespace rssm_host

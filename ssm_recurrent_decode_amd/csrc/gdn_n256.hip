@@ -1,0 +1,32 @@
+// Instantiations of the GDN ReplaySSM kernel for state size n = 256: the append
+// (T = 0 here) and the verify of T = 1..8 drafts, head dims 64 and 128 (own
+// translation unit so the kernel variants compile in parallel).
+#include "gdn.hpp"
+
+namespace rssm_host {
+
+int launch_gdn_n256(int T, int D, const GdnReplayParams& p, int B, void* stream) {
+  switch (T) {
+    case 0: return D == 64 ? launch_gdn_window<64, 1, true, 256>(p, B, stream)
+                           : launch_gdn_window<128, 1, true, 256>(p, B, stream);
+    case 1: return D == 64 ? launch_gdn_window<64, 1, false, 256>(p, B, stream)
+                           : launch_gdn_window<128, 1, false, 256>(p, B, stream);
+    case 2: return D == 64 ? launch_gdn_window<64, 2, false, 256>(p, B, stream)
+                           : launch_gdn_window<128, 2, false, 256>(p, B, stream);
+    case 3: return D == 64 ? launch_gdn_window<64, 3, false, 256>(p, B, stream)
+                           : launch_gdn_window<128, 3, false, 256>(p, B, stream);
+    case 4: return D == 64 ? launch_gdn_window<64, 4, false, 256>(p, B, stream)
+                           : launch_gdn_window<128, 4, false, 256>(p, B, stream);
+    case 5: return D == 64 ? launch_gdn_window<64, 5, false, 256>(p, B, stream)
+                           : launch_gdn_window<128, 5, false, 256>(p, B, stream);
+    case 6: return D == 64 ? launch_gdn_window<64, 6, false, 256>(p, B, stream)
+                           : launch_gdn_window<128, 6, false, 256>(p, B, stream);
+    case 7: return D == 64 ? launch_gdn_window<64, 7, false, 256>(p, B, stream)
+                           : launch_gdn_window<128, 7, false, 256>(p, B, stream);
+    case 8: return D == 64 ? launch_gdn_window<64, 8, false, 256>(p, B, stream)
+                           : launch_gdn_window<128, 8, false, 256>(p, B, stream);
+    default: return RSSM_ENOTSUP;
+  }
+}
+
+}  // namespace rssm_host

@@ -287,7 +287,7 @@ extern "C" int ssm_decode_step(const rssm_dims* dims, float* state, const uint16
                                const float* dt_bias, const float* A, float* y, void* stream) {
   if (!rssm_host::dims_ok(dims) || !state || !v || !k || !q || !dt || !dt_bias || !A || !y)
     return RSSM_EINVAL;
-  if (!rssm_host::m2_shape_supported(dims) || (dims->flags & RSSM_F_Y_BF16)) return RSSM_ENOTSUP;
+  if (!rssm_host::shape_supported(dims) || (dims->flags & RSSM_F_Y_BF16)) return RSSM_ENOTSUP;
   StdParams p{state, v, k, q, dt, dt_bias, A, y, dims->nheads, dims->ngroups};
   const dim3 grid(dims->batch * dims->nheads);
   const bool d64 = dims->head_dim == 64;
@@ -309,7 +309,7 @@ extern "C" int replay_append_decode(const rssm_dims* dims, float* state0, rssm_r
       !dt || !dt_bias || !A || !y)
     return RSSM_EINVAL;
   if (dims->capacity < 1) return RSSM_EINVAL;
-  if (!rssm_host::m2_ring_shape_supported(dims)) return RSSM_ENOTSUP;
+  if (!rssm_host::ring_shape_supported(dims)) return RSSM_ENOTSUP;
   ReplayParams p = make_replay_params(dims, state0, ring);
   p.v = v;
   p.k = k;
@@ -334,7 +334,7 @@ extern "C" int replay_append_decode_conv(const rssm_dims* dims, float* state0, r
       !conv_state_out || !xbc || !conv_w || !dt || !dt_bias || !A || !y)
     return RSSM_EINVAL;
   if (conv_state_in == conv_state_out || dims->capacity < 1) return RSSM_EINVAL;
-  if (!rssm_host::ring_shape_supported(dims)) return RSSM_ENOTSUP;
+  if (!rssm_host::conv_shape_supported(dims)) return RSSM_ENOTSUP;
   ReplayParams p = make_replay_params(dims, state0, ring);
   p.conv_in = conv_state_in;
   p.conv_out = conv_state_out;
@@ -353,7 +353,7 @@ extern "C" int replay_flush(const rssm_dims* dims, float* state0, rssm_ring* rin
                             const int32_t* mask, void* stream) {
   if (!rssm_host::dims_ok(dims) || !rssm_host::ring_ok(ring) || !state0) return RSSM_EINVAL;
   if (dims->capacity < 1) return RSSM_EINVAL;
-  if (!rssm_host::m2_ring_shape_supported(dims)) return RSSM_ENOTSUP;
+  if (!rssm_host::ring_shape_supported(dims)) return RSSM_ENOTSUP;
   ReplayParams p = make_replay_params(dims, state0, ring);
   p.mask = mask;
   const dim3 grid(dims->batch * dims->nheads);
@@ -378,7 +378,7 @@ extern "C" int replay_verify_T(const rssm_dims* dims, int32_t T, float* state0, 
       !dt || !dt_bias || !A || !y)
     return RSSM_EINVAL;
   if (T < 1 || dims->capacity < 2 * T) return RSSM_EINVAL;
-  if (!rssm_host::m2_ring_shape_supported(dims) || T > kMaxT) return RSSM_ENOTSUP;
+  if (!rssm_host::ring_shape_supported(dims) || T > kMaxT) return RSSM_ENOTSUP;
   ReplayParams p = make_replay_params(dims, state0, ring);
   p.v = v;
   p.k = k;

@@ -189,9 +189,8 @@ int snapshot_common(const rssm_dims* dims, int32_t T, int32_t nslots, float* poo
                     bool gdn, SnapParams& p) {
   if (!rssm_host::dims_ok(dims) || !pool || !slot || !v || !k || !q) return RSSM_EINVAL;
   if (T < 1 || nslots < T + 1) return RSSM_EINVAL;
-  // Mamba-2: n in {64, 128, 256}; GDN: n = 128, as the other calls of each family
-  const bool shape = gdn ? rssm_host::shape_supported(dims) : rssm_host::m2_shape_supported(dims);
-  if (!shape || T > kMaxT || (dims->flags & RSSM_F_Y_BF16)) return RSSM_ENOTSUP;
+  (void)gdn;
+  if (!rssm_host::shape_supported(dims) || T > kMaxT || (dims->flags & RSSM_F_Y_BF16)) return RSSM_ENOTSUP;
   p.pool = pool;
   p.slot = slot;
   p.v = v;
@@ -240,8 +239,12 @@ extern "C" int gdn_snapshot_verify_T(const rssm_dims* dims, int32_t T, int32_t n
   p.y = y;
   p.err = err;
   const dim3 grid(dims->batch * dims->nheads);
-  if (dims->head_dim == 64) return launch_snapshot<64, 128, true>(T, p, grid, stream);
-  return launch_snapshot<128, 128, true>(T, p, grid, stream);
+  const bool d64 = dims->head_dim == 64;
+  switch (dims->state_dim) {
+    case 64: return d64 ? launch_snapshot<64, 64, true>(T, p, grid, stream) : launch_snapshot<128, 64, true>(T, p, grid, stream);
+    case 256: return d64 ? launch_snapshot<64, 256, true>(T, p, grid, stream) : launch_snapshot<128, 256, true>(T, p, grid, stream);
+    default: return d64 ? launch_snapshot<64, 128, true>(T, p, grid, stream) : launch_snapshot<128, 128, true>(T, p, grid, stream);
+  }
 }
 
 extern "C" int snapshot_commit(int32_t batch, int32_t T, int32_t nslots, int32_t* slot,

@@ -74,7 +74,7 @@ def test_host_validation_codes():
     # H % G != 0
     bad = _dims(H=6, G=4)
     assert lib.ssm_decode_step(ctypes.byref(bad), P, P, P, P, P, P, P, P, None) == EINVAL
-    # unsupported head/state dims (Mamba-2 calls: d in {64, 128}, n in {64, 128, 256})
+    # unsupported head/state dims (every call: d in {64, 128}, n in {64, 128, 256})
     for dd in (_dims(d=96), _dims(n=96), _dims(n=32), _dims(n=512), _dims(d=256)):
         assert lib.ssm_decode_step(ctypes.byref(dd), P, P, P, P, P, P, P, P, None) == ENOTSUP
         assert lib.replay_append_decode(ctypes.byref(dd), P, ctypes.byref(r), P, P, P, P, P, P, P,
@@ -84,9 +84,6 @@ def test_host_validation_codes():
         assert lib.replay_flush(ctypes.byref(dd), P, ctypes.byref(r), None, None) == ENOTSUP
         assert lib.ssm_snapshot_verify_T(ctypes.byref(dd), 2, 3, P, P, P, P, P, P, P, P, P, P,
                                          None) == ENOTSUP
-    # GDN (its snapshot route included) and the fused front-end are built for n = 128 only
-    for n in (64, 256):
-        dd = _dims(n=n)
         assert lib.gdn_decode_step(ctypes.byref(dd), P, P, P, P, P, P, P, None) == ENOTSUP
         assert lib.gdn_replay_verify_T(ctypes.byref(dd), 2, P, ctypes.byref(r), P, P, P, P, P, P,
                                        None, None) == ENOTSUP
@@ -95,6 +92,9 @@ def test_host_validation_codes():
                                             None, None) == ENOTSUP
         assert lib.gdn_snapshot_verify_T(ctypes.byref(dd), 2, 3, P, P, P, P, P, P, P, P, P,
                                          None) == ENOTSUP
+    # the fused front-end is built for n = 128 only
+    for n in (64, 256):
+        dd = _dims(n=n)
         assert lib.replay_append_decode_conv(ctypes.byref(dd), P, ctypes.byref(r), P, FAKE2, P, P, P, P,
                                              P, P, None, None) == ENOTSUP
     # capacity limits
