@@ -654,12 +654,14 @@ def _row_sweep(torch, np, rd, synth, traffic, dev, stream, capacities=(4, 8, 16,
     return res
 
 
-def _row_gdn_append(torch, np, rd, synth, traffic, dev, stream):
+def _row_gdn_append(torch, np, rd, synth, traffic, dev, stream, n=None):
     """GDN standard decode through the ring (gdn_replay_append_decode) at the GDN
-    workload's shape, flush and non-flush steps reported separately, against the
-    standard GDN step; two layer instances rotated."""
+    workload's shape (state size n if given), flush and non-flush steps reported
+    separately, against the standard GDN step; two layer instances rotated."""
     wl = synth.WORKLOADS[4]
     sh, seed = wl.shape.with_(T=1), wl.cfg_seed
+    if n is not None:
+        sh = sh.with_(state_dim=n)
     B, H, D, N, G, L = sh.batch, sh.nheads, sh.head_dim, sh.state_dim, sh.ngroups, sh.capacity
     NLs, P = 2, 4
     dims = rd.Dims(B, H, D, N, G, L)
@@ -701,7 +703,7 @@ def _row_gdn_append(torch, np, rd, synth, traffic, dev, stream):
     fl = h == L - 1
     byts = np.array([traffic.gdn_append(B, H, D, N, G, int(x), bool(x == L - 1)) for x in h])
     every = [traffic.gdn_append(B, H, D, N, G, (t // NLs) % L, (t // NLs) % L == L - 1) for t in range(warm + K)]
-    std = _standard_step_row(torch, np, rd, synth, traffic, dev, stream, 4, True, S0s)
+    std = _standard_step_row(torch, np, rd, synth, traffic, dev, stream, 4, True, S0s, shape=sh)
     return {"workload": f"Gated DeltaNet append-decode (flush when full), batch {B}, {H} heads, head dim {D}, "
                         f"state {N}, {G} groups, ring capacity {L}; two layer instances rotated",
             "kernel": "gdn_replay_append_decode", "steps_timed": K,
@@ -714,6 +716,21 @@ def _row_gdn_append(torch, np, rd, synth, traffic, dev, stream):
             "tokens_per_s": round(float(B / (us.mean() * 1e-6)), 1),
             "alg_bytes_avg_all_launches": round(float(np.mean(every))), "launches": warm + K,
             "standard_step": std, "speedup": round(std["us"] / float(us.mean()), 3)}
+
+
+def _row_gdn_state_sizes(torch, np, rd, synth, traffic, dev, stream):
+    """GDN append-decode at the GDN workload's shape with state size n = 64, 128
+    and 256, each against the standard GDN step at the same n."""
+    res = {"workload": "Gated DeltaNet append-decode (flush when full), batch 256, 32 heads, head dim 128, "
+                       "32 groups, ring capacity 16, state size n in (64, 128, 256); two layer instances rotated",
+           "kernel": "gdn_replay_append_decode"}
+    for n in (64, 128, 256):
+        r = _row_gdn_append(torch, np, rd, synth, traffic, dev, stream, n=n)
+        res[f"n{n}"] = {k_: r[k_] for k_ in ("nonflush_us", "flush_us", "avg_us", "avg_GBs", "tokens_per_s",
+                                             "speedup")}
+        res[f"n{n}"]["frac_of_peak"] = round(r["avg_GBs"] / HBM_PEAK_GBS, 4)
+        res[f"n{n}"]["standard_step_us"] = r["standard_step"]["us"]
+    return res
 
 
 def _row_fused_conv(torch, np, rd, synth, traffic, dev, stream):
@@ -1058,6 +1075,7 @@ def _rows(torch, np, rd, synth, traffic, dev, stream, only=None):
         ("pooled_append_decode", lambda: _row_pooled(torch, np, rd, synth, traffic, dev, stream)),
         ("staggered_append_decode", lambda: _row_staggered(torch, np, rd, synth, traffic, dev, stream)),
         ("state_sizes", lambda: _row_state_sizes(torch, np, rd, synth, traffic, dev, stream)),
+        ("gdn_state_sizes", lambda: _row_gdn_state_sizes(torch, np, rd, synth, traffic, dev, stream)),
         ("fused_front_end", lambda: _row_fused_conv(torch, np, rd, synth, traffic, dev, stream)),
         ("storage_precision", lambda: _row_precision(torch, np, rd, synth, traffic, dev, stream)),
         ("window_sweep", lambda: {"mamba2": _row_window(torch, np, rd, synth, traffic, dev, stream, 2, False),

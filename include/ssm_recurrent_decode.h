@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define RSSM_ABI_VERSION 9
+#define RSSM_ABI_VERSION 10
 
 #define RSSM_OK 0
 #define RSSM_EINVAL (-22)
@@ -95,6 +95,12 @@ typedef struct rssm_dims {
  * from `head`, so a rollback only moves a pointer.  Physical slot of logical
  * entry j (0 = oldest) of request b is (head + j) % L.
  *
+ * Values (Mamba-2 v) and corrections (GDN u) are stored in blocks of hb
+ * consecutive heads, vu[B][H / hb][L][hb][d] with hb = RSSM_RING_HEAD_BLOCK(H)
+ * (4 when H % 4 == 0, else 2 when H is even, else 1): entry `slot` of head h of
+ * request b starts at element (((b * (H / hb) + h / hb) * L + slot) * hb + h % hb) * d.
+ * The entries a call caches for the heads of a block are adjacent in memory.
+ *
  * Everything else a call needs about request b's ring as head h sees it sits in
  * one record (rssm_ring_record below) of RSSM_META_WORDS(L) 32-bit words: one
  * 128-byte line for L <= 29, two for larger L.  The records of a ring are
@@ -130,6 +136,7 @@ typedef struct rssm_dims {
  * slots[b] >= rows: skipped, RSSM_ERR_SLOT flagged.  Two entries of one call
  * must not name the same row.  Sizes: rssm_ring_sizes with dims->batch = rows.
  */
+#define RSSM_RING_HEAD_BLOCK(H) ((H) % 4 == 0 ? 4 : ((H) % 2 == 0 ? 2 : 1))
 #define RSSM_META_WORDS(L) ((L) + 3 <= 32 ? 32 : 64)
 #define RSSM_RECORD_LINES(L) (RSSM_META_WORDS(L) / 32)
 #define RSSM_PTR_HEAD(w) ((uint32_t)((w) & 0xFFFFu))
@@ -150,7 +157,8 @@ typedef struct rssm_ring_record {
 #define RSSM_RECORD_SLOT(rec, s) (((float*)(rec))[3 + (s)])
 
 typedef struct rssm_ring {
-  void* vu;          /* Mamba-2: v  bf16 [B, H, L, d];  GDN: u fp32 [B, H, L, d]     */
+  void* vu;          /* Mamba-2: v bf16, GDN: u fp32 (or bf16, RSSM_F_U_BF16),
+                        [B, H / hb, L, hb, d] (see above)                            */
   uint16_t* k;       /* bf16 [B, G, L, n]                                           */
   rssm_ring_record* meta;  /* [B, H, RSSM_RECORD_LINES(L)] records (see above)     */
   int32_t* err;      /* [1] anomaly bits (RSSM_ERR_*), may be NULL                  */

@@ -23,7 +23,7 @@ RSSM_ERR_SLOT = 8
 RSSM_ERR_DIVERGED = 16
 RSSM_F_Y_BF16 = 1
 RSSM_F_U_BF16 = 2
-ABI_VERSION = 9  # RSSM_ABI_VERSION of the header this binding follows
+ABI_VERSION = 10  # RSSM_ABI_VERSION of the header this binding follows
 
 
 class rssm_dims(ctypes.Structure):

@@ -74,11 +74,17 @@ def meta_words(L: int) -> int:
     return 32 if L + 3 <= 32 else 64
 
 
+def ring_head_block(H: int) -> int:
+    """Heads whose ring entries of one slot are stored side by side (RSSM_RING_HEAD_BLOCK)."""
+    return 4 if H % 4 == 0 else (2 if H % 2 == 0 else 1)
+
+
 class Ring:
     """Device arrays of one layer's ReplaySSM ring (see rssm_ring in the header).
 
     Allocated zero-filled with torch on ``device``; ``gdn`` selects fp32
-    corrections u instead of bf16 values v.  ``meta`` holds one record per
+    corrections u instead of bf16 values v, stored [rows, H / hb, L, hb, d]
+    (``entries()`` gives the [rows, H, L, d] view).  ``meta`` holds one record per
     (request, head): the packed pointer word (head in bits 0-15, count 16-31,
     pending 32-47) in words 0-1, then A and the per-slot step sizes (Mamba-2) or
     decays (GDN).  ``head``, ``count`` and ``pending`` are int32 [rows] tensors
@@ -97,7 +103,8 @@ class Ring:
         self.dims, self.gdn, self.rows, self.slots = dims, gdn, B, None
         z = dict(device=device)
         u32 = gdn and not (dims.flags & _lib.RSSM_F_U_BF16)
-        self.vu = torch.zeros((B, H, L, D), dtype=torch.float32 if u32 else torch.bfloat16, **z)
+        hb = ring_head_block(H)
+        self.vu = torch.zeros((B, H // hb, L, hb, D), dtype=torch.float32 if u32 else torch.bfloat16, **z)
         self.k = torch.zeros((B, G, L, N), dtype=torch.bfloat16, **z)
         self.meta = torch.zeros((B, H, meta_words(L)), dtype=torch.float32, **z)
         self.err = torch.zeros((1,), dtype=torch.int32, **z)
@@ -106,6 +113,12 @@ class Ring:
     def ptr(self):
         """Pointer words [B, H] (int64 view into the records)."""
         return self.meta.view(torch.int64)[:, :, 0]
+
+    def entries(self):
+        """The cached values (Mamba-2) or corrections (GDN) as a [rows, H, L, d]
+        copy, head-major (``vu`` holds them in blocks of heads per slot)."""
+        B, Hb, L, hb, D = self.vu.shape
+        return self.vu.permute(0, 1, 3, 2, 4).reshape(B, Hb * hb, L, D)
 
     def pointers(self, stream=None):
         """(head, count, pending) of every pool row as int32 device tensors, from

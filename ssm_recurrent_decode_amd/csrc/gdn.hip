@@ -132,7 +132,7 @@ __global__ __launch_bounds__(kBlock) void gdn_flush_kernel(GdnReplayParams p) {
 #pragma unroll
     for (int m = 0; m < kVJ; ++m) {
       const int j = cq + 4 * m;
-      const size_t ua = (bh * L + (head + j) % L) * D + row;
+      const size_t ua = ring_entry(rb, h, H, L, (head + j) % L, D) + row;
       uf[rt][m] = (j < F) ? (p.u_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(p.ring_u)[ua]) : p.ring_u[ua])
                           : 0.f;
     }

@@ -202,7 +202,7 @@ __global__ __launch_bounds__(kBlock, (gdn_waves_per_simd<D, N, T, LCAP>())) void
     const int t = tid + i * kBlock;
     uc[i] = make_uint4(0, 0, 0, 0);
     if (t < c * cpe) {
-      const size_t e = (bh * L + ring_slot(head, t / cpe, L)) * D;
+      const size_t e = ring_entry(rb, h, H, L, ring_slot(head, t / cpe, L), D);
       uc[i] = p.u_bf16 ? ld_u4(reinterpret_cast<const uint16_t*>(p.ring_u) + e + (t % cpe) * 8)
                        : *reinterpret_cast<const uint4*>(p.ring_u + e + (t % cpe) * 4);
     }
@@ -385,7 +385,7 @@ __global__ __launch_bounds__(kBlock, (gdn_waves_per_simd<D, N, T, LCAP>())) void
       // the correction as cached (rounded when the ring holds bf16); this call's
       // outputs above used it unrounded
       const uint32_t ub = bf16_rne(u[sd]);
-      const size_t ua = (bh * L + dslot[sd]) * D + rho;
+      const size_t ua = ring_entry(rb, h, H, L, dslot[sd], D) + rho;
       if (write_new) {
         if (p.u_bf16) reinterpret_cast<uint16_t*>(p.ring_u)[ua] = (uint16_t)ub;
         else p.ring_u[ua] = u[sd];

@@ -131,7 +131,7 @@ __global__ __launch_bounds__(kBlock) void replay_flush_kernel(ReplayParams p) {
 #pragma unroll
     for (int m = 0; m < kVJ; ++m) {
       const int j = cq + 4 * m;
-      vj[rt][m] = (j < F) ? bf16_to_f32(p.ring_v[(bh * L + (head + j) % L) * D + row]) : 0.f;
+      vj[rt][m] = (j < F) ? bf16_to_f32(p.ring_v[ring_entry(rb, h, H, L, (head + j) % L, D) + row]) : 0.f;
     }
   }
   if (wave == 0) {

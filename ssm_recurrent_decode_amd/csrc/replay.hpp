@@ -324,7 +324,7 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
   for (int i = 0; i < RVP; ++i) {
     const int t = tid + i * kBlock;
     rv[i] = make_uint4(0, 0, 0, 0);
-    if (t < c * (D / 8)) rv[i] = ld_u4(p.ring_v + (bh * L + ring_slot(head, t / (D / 8), L)) * D + (t % (D / 8)) * 8);
+    if (t < c * (D / 8)) rv[i] = ld_u4(p.ring_v + ring_entry(rb, h, H, L, ring_slot(head, t / (D / 8), L), D) + (t % (D / 8)) * 8);
   }
 
   // ---- 5. the new entries' values into their LDS slots (they are cached in the
@@ -528,7 +528,7 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
       const int t = tid + i * kBlock;
       if (t < NEWV) {
         const int sd = t / (D / 8), o = (t % (D / 8)) * 8;
-        *reinterpret_cast<uint4*>(p.ring_v + (bh * L + ring_slot(head, c + sd, L)) * D + o) = newc[i];
+        *reinterpret_cast<uint4*>(p.ring_v + ring_entry(rb, h, H, L, ring_slot(head, c + sd, L), D) + o) = newc[i];
       } else if (k_owner && t < NCH) {
         const int tk = t - NEWV;
         const int sd = tk / (N / 8), o = (tk % (N / 8)) * 8;

@@ -33,7 +33,7 @@ def test_every_declared_function_is_exported_and_prototyped():
 
 def test_abi_version_and_strerror():
     lib = _lib.load()
-    assert lib.rssm_abi_version() == _lib.ABI_VERSION == 9
+    assert lib.rssm_abi_version() == _lib.ABI_VERSION == 10
     assert "invalid" in _lib.strerror(_lib.RSSM_EINVAL)
     assert "not compiled" in _lib.strerror(_lib.RSSM_ENOTSUP)
 

@@ -106,7 +106,7 @@ def test_gdn_verify_bf16_ring(flags, d, G, L, T):
         rd.gdn_replay_verify_T(dims, T, state0, ring, dev_bf16(st["v"]), dev_bf16(st["k"]), dev_bf16(st["q"]),
                                dev_f32(st["g"]), dev_f32(st["beta"]), y)
         yh = _y_f64(y)
-        ring_u = ring.vu.float().cpu().numpy()
+        ring_u = ring.entries().float().cpu().numpy()
         for b in range(sh.batch):
             yb, ub, fb = reqs[b].verify_round(s64["v"][b], s64["k"][b], s64["q"][b], s64["g"][b], s64["beta"][b])
             assert rel_err(yh[b], yb) <= ytol, (r, b)

@@ -101,7 +101,8 @@ def test_replay_append_decode_small(d, G, L, ring_dominant):
 def test_ring_record_contents():
     """The per-head ring record after a few appends: every head's pointer word
     equal, word 2 the head's A, word 3 + slot the step size of the entry cached in
-    that slot (against the oracle's softplus, at fp32 rounding)."""
+    that slot (against the oracle's softplus, at fp32 rounding); and the values
+    cached in each slot, bit-exact."""
     base = synth.WORKLOADS[0]
     sh = base.shape.with_(capacity=8)
     A, dt_bias, S0, seq = _mamba2_case(sh, base.cfg_seed, 0, 13, False)
@@ -122,6 +123,10 @@ def test_ring_record_contents():
         delta, _ = o_m2.step_size_and_decay(seq[8 + j]["dt"], dt_bias, A)
         got = meta[:, :, 3 + (head + j) % sh.capacity].astype(np.float64)
         assert np.max(np.abs(got - delta) / np.abs(delta)) <= 2e-6, j
+    # the cached values, bit for bit, through the head-blocked layout
+    vals = ring.entries().view(torch.int16).cpu().numpy().view(np.uint16)
+    for j in range(count):
+        assert np.array_equal(vals[:, :, (head + j) % sh.capacity], seq[8 + j]["v"]), j
     assert int(ring.err.item()) == 0
 
 
@@ -321,7 +326,7 @@ def test_gdn_replay_verify_small(d, G, L, T):
         y_ref, S = o_gdn.spec_round_snapshot(S, s64, G, acc[r])
         e = rel_err(y.cpu().numpy(), y_ref)
         assert e <= Y_TOL, (r, e)
-        ring_u = ring.vu.cpu().numpy()
+        ring_u = ring.entries().cpu().numpy()
         for b in range(sh.batch):
             yb, ub, fb = reqs[b].verify_round(s64["v"][b], s64["k"][b], s64["q"][b], s64["g"][b],
                                               s64["beta"][b])
@@ -370,7 +375,7 @@ def test_gdn_replay_append_decode_small(d, G, L):
             if fb:
                 assert rel_err(state0[b].cpu().numpy(), reqs[b].S0) <= S_TOL, (t, b)
         assert ring.copies_agree(), t
-    ring_u = ring.vu.cpu().numpy()
+    ring_u = ring.entries().cpu().numpy()
     for b in range(sh.batch):
         for j in range(reqs[b].count):
             sl = (reqs[b].head + j) % L
