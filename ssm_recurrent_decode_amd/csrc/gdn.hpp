@@ -289,11 +289,16 @@ __global__ __launch_bounds__(kBlock, (gdn_waves_per_simd<D, N, T, LCAP>())) void
   //      A[m][k] = x_m[col] (bf16 as stored), B[k][nn] = S_0[row nn][col] split into
   //      bf16 hi + lo (two MFMAs per pair of column tiles; K index 8cq + e <->
   //      column 32jj + 4cq + e, 8cq + 4 + e <-> 32jj + 16 + 4cq + e); lane (r, cq)
-  //      ends with Z[4cq+i][row r of the tile]
+  //      ends with Z[4cq+i][row r of the tile].  The committed entries' part of
+  //      the committed-state readouts accumulates on top in fp32
+  //      (v_mfma_f32_16x16x4_f32, K = ring slots): Z <- abar Z + (W o M) U, with
+  //      A[v][slot] = w_slot (k_slot . x_v) and B[slot][row] = u_slot[row], so the
+  //      per-row phase below starts from S_c x_v directly.
   uint2 xq[NCT];  // this lane's readout vector x_r at the columns of each tile
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct)
     xq[ct] = (r < NV) ? *reinterpret_cast<const uint2*>(&s_x[r * N + ct * 16 + cq * 4]) : make_uint2(0, 0);
+  const float abar = s_abar;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     v4f acc = {0.f, 0.f, 0.f, 0.f};
@@ -308,7 +313,16 @@ __global__ __launch_bounds__(kBlock, (gdn_waves_per_simd<D, N, T, LCAP>())) void
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xbf, __builtin_bit_cast(bf16x8_t, hi), acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xbf, __builtin_bit_cast(bf16x8_t, lo), acc, 0, 0, 0);
     }
+    acc *= abar;
     const int row = (wave * RT + rt) * 16 + r;
+#pragma unroll
+    for (int m = 0; m < VJ; ++m) {
+      if (4 * m >= L) break;  // physical slots; uniform across the work-group
+      const int sl = 4 * m + cq;  // A: w_sl (k_sl . x_r), B: u_sl at this lane's row
+      const bool cm = sl < L && logical(min(sl, L - 1)) < c;
+      const float a = (cm && r < NV) ? s_w[sl] * s_M[min(r, NV - 1)][sl] : 0.f;
+      acc = mfma4(a, cm ? s_u[sl * D + row] : 0.f, acc);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (4 * cq + i < NV) s_Z[4 * cq + i][row] = acc[i];
@@ -329,22 +343,14 @@ __global__ __launch_bounds__(kBlock, (gdn_waves_per_simd<D, N, T, LCAP>())) void
   }
   __syncthreads();
 
-  // ---- 8. per row: committed-state readouts, corrections by forward
-  //      substitution, outputs, the corrections cached in the ring
+  // ---- 8. per row: the committed-state readouts S_c x_v (from step 6),
+  //      corrections by forward substitution, outputs, the corrections cached
+  //      in the ring
   const int rho = tid;
   if (rho < D) {
-    const float abar = s_abar;
     float sh[NV];
 #pragma unroll
-    for (int v = 0; v < NV; ++v) sh[v] = abar * s_Z[v][rho];
-#pragma unroll
-    for (int sl = 0; sl < LCAP; ++sl) {
-      if (sl < L && logical(sl) < c) {
-        const float wu = s_w[sl] * s_u[sl * D + rho];
-#pragma unroll
-        for (int v = 0; v < NV; ++v) sh[v] += wu * s_M[v][sl];
-      }
-    }
+    for (int v = 0; v < NV; ++v) sh[v] = s_Z[v][rho];
     int dslot[T];  // physical slots of the drafts
 #pragma unroll
     for (int sd = 0; sd < T; ++sd) dslot[sd] = ring_slot(head, c + sd, L);
