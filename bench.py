@@ -1192,15 +1192,26 @@ def main(argv=None) -> int:
     # the dominant kernel alone over whole ring cycles of every layer, whatever
     # K is: K_kern launches back to back on its stream (a multiple of NL * L, so
     # every layer folds its ring once per cycle and the bytes are the L-cycle
-    # average exactly), HIP events around the whole run
-    # (at least four cycles, after four untimed ones whatever --warmup was: the
-    # first cycles of back-to-back launches run 2-10 % slower on this part)
-    K_kern = cyc * max(4, math.ceil(K / cyc))
-    t_kern = a.warmup + K + 4 * cyc
-    for i in range(4 * cyc):
-        step_calls(a.warmup + K + i)[1]()
+    # average exactly), HIP events around the whole run.  It follows eight
+    # untimed cycles and two cycles with an event pair around every launch (the
+    # launches that fold the ring and those that do not, separately), all
+    # enqueued without a host synchronisation in between: after the GPU idles,
+    # even briefly, the first cycles of back-to-back launches run 1-40 % slower
+    # on this part (measured 78, 61, 56, 55, 55 and 55 us against 54.4 after).
+    K_kern = cyc * max(8, math.ceil(K / cyc))
+    t_warm = a.warmup + K
+    t_cls = t_warm + 8 * cyc
+    n_cls = 2 * cyc
+    t_kern = t_cls + n_cls
+    ev_cls = _events(torch, n_cls)
     ev_cyc = _events(torch, K_kern // cyc)
     torch.cuda.synchronize()
+    for i in range(8 * cyc):
+        step_calls(t_warm + i)[1]()
+    for i in range(n_cls):
+        ev_cls[i][0].record(stream)
+        step_calls(t_cls + i)[1]()
+        ev_cls[i][1].record(stream)
     start.record(stream)
     for i in range(K_kern):
         if i % cyc == 0:
@@ -1212,17 +1223,6 @@ def main(argv=None) -> int:
     end.synchronize()
     kern_avg_ms = start.elapsed_time(end) / K_kern
     cycle_us = [round(1e3 * a_.elapsed_time(b_) / cyc, 3) for a_, b_ in ev_cyc]
-    # the same launches one cycle further on, each between its own events: the
-    # launches that fold the ring and those that do not, separately
-    t_cls = t_kern + K_kern
-    n_cls = 2 * cyc
-    ev_cls = _events(torch, n_cls)
-    torch.cuda.synchronize()
-    for i in range(n_cls):
-        ev_cls[i][0].record(stream)
-        step_calls(t_cls + i)[1]()
-        ev_cls[i][1].record(stream)
-    torch.cuda.synchronize()
     cls_us = {False: [], True: []}
     for i in range(n_cls):
         cls_us[cached_before(t_cls + i) == L - 1].append(1e3 * ev_cls[i][0].elapsed_time(ev_cls[i][1]))
@@ -1250,9 +1250,9 @@ def main(argv=None) -> int:
         R = max(20, math.ceil(K / cyc))
         ev_g = _events(torch, R)
         with torch.cuda.stream(side):
-            for _ in range(5):
-                g.replay()
             torch.cuda.synchronize()
+            for _ in range(5):            # untimed, and no host synchronisation before the timed ones
+                g.replay()
             for i in range(R):
                 ev_g[i][0].record(side)
                 g.replay()

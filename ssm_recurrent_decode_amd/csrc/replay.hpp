@@ -55,6 +55,33 @@ __device__ __forceinline__ uint32_t f64_to_bf16_rne(double x) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// SiLU of one channel's 4-tap conv sum, rounded to bf16 exactly as the float64
+// value rounds (nearest, ties to even).  fp32 first: the products of bf16 values
+// are exact in fp32, the three additions err by at most 3 u S (S = sum of
+// |products|, u = 2^-24) and SiLU's slope is below 1.1, while expf (within one
+// ulp), the addition and the division add at most 4 u |s|; so a value farther
+// than 8 u |s| + 4 u S from the midpoint between its two bf16 neighbours rounds
+// as the exact one does.  The few that are not (about 1 in 2 * 10^3; also every
+// |z| >= 64) take the float64 route, where the sum of the exact products is
+// exact and SiLU is evaluated in float64 before one rounding.
+__device__ __forceinline__ uint32_t conv_silu_bf16(const uint32_t* w, const uint32_t* x) {
+  float p[4], S = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    p[k] = bf16_to_f32(w[k]) * bf16_to_f32(x[k]);
+    S += fabsf(p[k]);
+  }
+  const float z = ((p[0] + p[1]) + p[2]) + p[3];  // oldest tap first
+  const float sf = z / (1.f + expf(-z));
+  const float mid = __uint_as_float((__float_as_uint(sf) & 0xFFFF0000u) | 0x8000u);
+  const float err = 0x1p-21f * fabsf(sf) + 0x1p-22f * S + 0x1p-126f;
+  if (fabsf(sf - mid) > err && fabsf(z) < 64.f) return bf16_rne(sf);
+  double zd = (double)bf16_to_f32(w[0]) * (double)bf16_to_f32(x[0]);
+#pragma unroll
+  for (int k = 1; k < 4; ++k) zd = zd + (double)bf16_to_f32(w[k]) * (double)bf16_to_f32(x[k]);
+  return f64_to_bf16_rne(zd / (1.0 + exp(-zd)));
+}
+
 // Load the checkpoint tiles of one head (tile layout) into registers.
 template <int D, int N, int RT, int NCT>
 __device__ __forceinline__ void load_tiles(float4 (&s)[RT][NCT], const float* S0, int wave, int r,
@@ -91,8 +118,18 @@ __device__ __forceinline__ void load_tiles(float4 (&s)[RT][NCT], const float* S0
 //    rounded to bf16 (the precision of the ring); the conv states of the x
 //    channels are written by their head, those of B and C by the group's first
 //    head, into a second buffer (the group's other heads still read the first).
+// Waves per SIMD the fused front-end is held to at d = 64: with the ring loads
+// issued before the conv, the conv's operands and the ring registers are live
+// together, and left alone the compiler takes 108 registers (four waves per
+// SIMD, +6 % per launch); bounded to five it fits in 96 without spilling and
+// runs 1 % faster than the conv before the ring loads.  Other instances: no bound.
+template <int D, bool CONV, int LCAP>
+constexpr int window_waves_per_simd() {
+  return (CONV && D == 64 && LCAP == 16) ? 5 : 1;
+}
+
 template <int D, int N, int T, bool APPEND, int LCAP, bool CONV = false>
-__global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
+__global__ __launch_bounds__(kBlock, (window_waves_per_simd<D, CONV, LCAP>())) void replay_window_kernel(ReplayParams p) {
   static_assert(N == 64 || N == 128 || N == 256, "keys and queries: 16 lanes of n / 16 values");
   static_assert(!CONV || N == 128, "the fused front-end is built for n = 128");
   static_assert(LCAP == 16 || LCAP == 32, "ring capacity bound");
@@ -217,69 +254,6 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
     }
   }
 
-  if constexpr (CONV) {
-    // ---- 2b. the token's v, k, q from the conv (its operands arrive ahead of
-    //      the checkpoint): window [s0, s1, s2, x], SiLU, bf16; shifted states out
-    const int C = H * D + 2 * G * N;
-    const bool owner = (h % hpg) == 0;
-    if (tid < NCQ) {
-      const int lc = 4 * tid;
-      // the 12 state values (channel m owns 3m .. 3m + 2, oldest first), 4 tokens, 16 taps
-      uint32_t sv[12], xv[4], wv[16];
-#pragma unroll
-      for (int w = 0; w < 3; ++w) {
-        sv[4 * w] = cst[w].x & 0xffffu;
-        sv[4 * w + 1] = cst[w].x >> 16;
-        sv[4 * w + 2] = cst[w].y & 0xffffu;
-        sv[4 * w + 3] = cst[w].y >> 16;
-      }
-      xv[0] = cxv.x & 0xffffu;
-      xv[1] = cxv.x >> 16;
-      xv[2] = cxv.y & 0xffffu;
-      xv[3] = cxv.y >> 16;
-#pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        const uint32_t q4[4] = {cwv[w].x, cwv[w].y, cwv[w].z, cwv[w].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          wv[8 * w + 2 * e] = q4[e] & 0xffffu;
-          wv[8 * w + 2 * e + 1] = q4[e] >> 16;
-        }
-      }
-      uint32_t o[4], ns[12];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const uint32_t win[4] = {sv[3 * m], sv[3 * m + 1], sv[3 * m + 2], xv[m]};
-        // fp64 (as fast as fp32 on this part): the products of bf16 values are
-        // exact and the sum runs oldest tap first, so the value whose rounding to
-        // bf16 is decided here does not depend on contraction or library rounding
-        double z = (double)bf16_to_f32(wv[4 * m]) * (double)bf16_to_f32(win[0]);
-#pragma unroll
-        for (int k = 1; k < 4; ++k) z = z + (double)bf16_to_f32(wv[4 * m + k]) * (double)bf16_to_f32(win[k]);
-        o[m] = f64_to_bf16_rne(z / (1.0 + exp(-z)));
-        ns[3 * m] = win[1];
-        ns[3 * m + 1] = win[2];
-        ns[3 * m + 2] = win[3];
-      }
-      *reinterpret_cast<uint2*>(&s_conv[lc]) = make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16));
-      if (lc < D || owner) {
-        uint16_t* dp = p.conv_out + ((size_t)rb * C + cch) * 3;
-#pragma unroll
-        for (int w = 0; w < 3; ++w)
-          *reinterpret_cast<uint2*>(dp + 4 * w) = make_uint2(ns[4 * w] | (ns[4 * w + 1] << 16),
-                                                             ns[4 * w + 2] | (ns[4 * w + 3] << 16));
-      }
-    }
-    __syncthreads();
-    qm[0][0] = *reinterpret_cast<const KC*>(&s_conv[D + N + sub * 8]);
-    kin[0][0] = *reinterpret_cast<const KC*>(&s_conv[D + sub * 8]);
-#pragma unroll
-    for (int i = 0; i < NCP; ++i) {
-      const int t = min(tid + i * kBlock, NCH - 1);
-      newc[i] = *reinterpret_cast<const uint4*>(&s_conv[t < NEWV ? t * 8 : D + (t - NEWV) * 8]);
-    }
-  }
-
   // ---- 3. ring pointers (uniform per request), clamped into range
   const RingPtr rp = unpack_ptr(word);
   int head = rp.head, cnt = rp.count;
@@ -325,6 +299,64 @@ __global__ __launch_bounds__(kBlock) void replay_window_kernel(ReplayParams p) {
     const int t = tid + i * kBlock;
     rv[i] = make_uint4(0, 0, 0, 0);
     if (t < c * (D / 8)) rv[i] = ld_u4(p.ring_v + ring_entry(rb, h, H, L, ring_slot(head, t / (D / 8), L), D) + (t % (D / 8)) * 8);
+  }
+
+  if constexpr (CONV) {
+    // ---- 4b. the token's v, k, q from the conv (its operands arrive ahead of
+    //      the checkpoint, and the ring loads are already on their way): window
+    //      [s0, s1, s2, x], SiLU, bf16; shifted states out
+    const int C = H * D + 2 * G * N;
+    const bool owner = (h % hpg) == 0;
+    if (tid < NCQ) {
+      const int lc = 4 * tid;
+      // the 12 state values (channel m owns 3m .. 3m + 2, oldest first), 4 tokens, 16 taps
+      uint32_t sv[12], xv[4], wv[16];
+#pragma unroll
+      for (int w = 0; w < 3; ++w) {
+        sv[4 * w] = cst[w].x & 0xffffu;
+        sv[4 * w + 1] = cst[w].x >> 16;
+        sv[4 * w + 2] = cst[w].y & 0xffffu;
+        sv[4 * w + 3] = cst[w].y >> 16;
+      }
+      xv[0] = cxv.x & 0xffffu;
+      xv[1] = cxv.x >> 16;
+      xv[2] = cxv.y & 0xffffu;
+      xv[3] = cxv.y >> 16;
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const uint32_t q4[4] = {cwv[w].x, cwv[w].y, cwv[w].z, cwv[w].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          wv[8 * w + 2 * e] = q4[e] & 0xffffu;
+          wv[8 * w + 2 * e + 1] = q4[e] >> 16;
+        }
+      }
+      uint32_t o[4], ns[12];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t win[4] = {sv[3 * m], sv[3 * m + 1], sv[3 * m + 2], xv[m]};
+        o[m] = conv_silu_bf16(&wv[4 * m], win);
+        ns[3 * m] = win[1];
+        ns[3 * m + 1] = win[2];
+        ns[3 * m + 2] = win[3];
+      }
+      *reinterpret_cast<uint2*>(&s_conv[lc]) = make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16));
+      if (lc < D || owner) {
+        uint16_t* dp = p.conv_out + ((size_t)rb * C + cch) * 3;
+#pragma unroll
+        for (int w = 0; w < 3; ++w)
+          *reinterpret_cast<uint2*>(dp + 4 * w) = make_uint2(ns[4 * w] | (ns[4 * w + 1] << 16),
+                                                             ns[4 * w + 2] | (ns[4 * w + 3] << 16));
+      }
+    }
+    __syncthreads();
+    qm[0][0] = *reinterpret_cast<const KC*>(&s_conv[D + N + sub * 8]);
+    kin[0][0] = *reinterpret_cast<const KC*>(&s_conv[D + sub * 8]);
+#pragma unroll
+    for (int i = 0; i < NCP; ++i) {
+      const int t = min(tid + i * kBlock, NCH - 1);
+      newc[i] = *reinterpret_cast<const uint4*>(&s_conv[t < NEWV ? t * 8 : D + (t - NEWV) * 8]);
+    }
   }
 
   // ---- 5. the new entries' values into their LDS slots (they are cached in the

@@ -263,9 +263,12 @@ def mfma_summary(path: str, kernels, command: str, out_md: str):
 
 
 def trace_summary(trace_csv: str, command: str, out_md: str, title: str, match: str = "rssm",
-                  segment: str = ""):
+                  segment: str = "", last: int = 0):
     """Kernel durations of a rocprofv3 --kernel-trace CSV grouped by kernel name and
-    grid size (one template instance can serve several workload shapes)."""
+    grid size (one template instance can serve several workload shapes).  With
+    ``segment``, also the longest run of back-to-back dispatches of that kernel,
+    or only its last ``last`` dispatches (the bench's timed pass follows its
+    untimed warm-up launches without a pause)."""
     groups = {}
     for row in _counter_rows(trace_csv):
         name = row.get("Kernel_Name", "")
@@ -297,11 +300,15 @@ def trace_summary(trace_csv: str, command: str, out_md: str, title: str, match: 
             runs.append(cur)
         if runs:
             run = max(runs, key=len)
+            n_run = len(run)
+            what = "the bench's back-to-back timed pass"
+            if last and last < n_run:
+                run = run[-last:]
+                what = f"the last {last} of a run of {n_run}, the bench's timed pass after its warm-up"
             dur = [(e - s_) * 1e-3 for s_, e in run]
             gap = (run[-1][0] - run[0][0]) * 1e-3 / max(len(run) - 1, 1)
-            lines += ["", f"Longest run of consecutive `{segment}` dispatches (the bench's back-to-back "
-                          f"timed pass): {len(run)} launches, average duration {sum(dur) / len(dur):.2f} us, "
-                          f"average start-to-start spacing {gap:.2f} us."]
+            lines += ["", f"Consecutive `{segment}` dispatches ({what}): {len(run)} launches, average "
+                          f"duration {sum(dur) / len(dur):.2f} us, average start-to-start spacing {gap:.2f} us."]
     with open(out_md, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     return groups
@@ -343,6 +350,8 @@ def main(argv=None) -> int:
     t.add_argument("--out", required=True)
     t.add_argument("--title", required=True)
     t.add_argument("--command", required=True)
+    t.add_argument("--last", type=int, default=0,
+                   help="with --segment: only the last N dispatches of the longest run")
     t.add_argument("--segment", default="",
                    help="also report the longest run of consecutive dispatches of this kernel")
     rt = sub.add_parser("rows-traffic")
@@ -364,7 +373,7 @@ def main(argv=None) -> int:
         print(open(a.out).read())
         return 0
     if a.cmd == "trace":
-        trace_summary(a.csv, a.command, a.out, a.title, segment=a.segment)
+        trace_summary(a.csv, a.command, a.out, a.title, segment=a.segment, last=a.last)
         print(open(a.out).read())
         return 0
     if a.cmd == "mfma":

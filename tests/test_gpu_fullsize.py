@@ -436,8 +436,10 @@ def test_fused_front_end_full():
     """replay_append_decode_conv at the Nemotron-H-like size (B=256, H=32, d=64,
     G=8, L=16, C = H d + 2 G n = 4096 xBC channels), 48 steps (3 flushes): sampled
     y every step and the sampled checkpoint at every flush against the oracle's
-    conv -> bf16 -> recurrence on those (request, head) pairs' channels; the whole
-    written conv state bit-exact every 8 steps."""
+    conv -> bf16 -> recurrence on those (request, head) pairs' channels; every
+    request's new v and k, as cached in the ring, bit-exact against the oracle's
+    conv and bf16 rounding every step but the flush steps (786,432 rounding
+    decisions a step); the whole written conv state bit-exact every 8 steps."""
     wl = synth.WORKLOADS[1]
     sh = wl.shape
     B, H, D, N, G, L = sh.batch, sh.nheads, sh.head_dim, sh.state_dim, sh.ngroups, sh.capacity
@@ -486,6 +488,15 @@ def test_fused_front_end_full():
         S, y_ref = o_m2.standard_step(S, v, k, q, delta, a, 1)
         e = rel_err(y[tb, th].cpu().numpy(), y_ref[:, 0])
         assert e <= Y_TOL, (t, e)
+        if (t + 1) % L:
+            # every request's new v and k as cached in the ring: the conv's bf16
+            # rounding decisions, bit for bit (entry t mod L: head stays 0)
+            full = o_conv.round_bf16(o_conv.update(cs64_all, x64, W64)[0])
+            v_all, k_all, _ = o_conv.split_xbc(full, H, D, G, N)
+            sl = t % L
+            got_v = _f64(ring.entries()[:, :, sl].contiguous().view(torch.int16).cpu().numpy().view(np.uint16))
+            got_k = _f64(ring.k[:, :, sl].contiguous().view(torch.int16).cpu().numpy().view(np.uint16))
+            assert np.array_equal(got_v, v_all) and np.array_equal(got_k, k_all), t
         cs64_all = np.concatenate([cs64_all[:, :, 1:], x64[:, :, None]], axis=-1)   # the state shift
         if t % 8 == 7:
             got = _f64(cout.view(torch.int16).cpu().numpy().view(np.uint16))

@@ -129,3 +129,18 @@ def test_trace_reports_the_longest_back_to_back_run(tmp_path):
     pf.trace_summary(str(tr), "cmd", str(out), "title", match="", segment="replay_window_kernel")
     text = out.read_text()
     assert "4 launches, average duration 50.00 us, average start-to-start spacing 55.00 us" in text
+
+
+def test_trace_can_keep_the_last_dispatches_of_the_run(tmp_path):
+    tr = tmp_path / "trace.csv"
+    rows = [(APPEND, 55 * i, 55 * i + 80) for i in range(3)]                        # warm-up, slower
+    rows += [(APPEND, 165 + 55 * i, 165 + 55 * i + 50) for i in range(4)]          # timed pass
+    with open(tr, "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(["Kernel_Name", "Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z", "Start_Timestamp", "End_Timestamp"])
+        w.writerows([(n, 1, 1, 1, s * 1000, e * 1000) for n, s, e in rows])
+    out = tmp_path / "t.md"
+    pf.trace_summary(str(tr), "cmd", str(out), "title", match="", segment="replay_window_kernel", last=4)
+    text = out.read_text()
+    assert "the last 4 of a run of 7" in text
+    assert "4 launches, average duration 50.00 us, average start-to-start spacing 55.00 us" in text
