@@ -228,7 +228,9 @@ def test_config2_speculative_verify_full():
 
 @pytest.mark.parametrize("L", [4, 8, 16, 32])
 def test_config3_capacity_sweep_full(L):
-    """B=256, H=128, d=64, n=128, G=8, 2048 steps at ring capacity L."""
+    """B=256, H=128, d=64, n=128, G=8, 2048 steps at ring capacity L: sampled y
+    every step, every request's pointers and flush flag every step, the sampled
+    checkpoint at every flush."""
     wl = synth.WORKLOADS[3]
     sh = wl.shape.with_(capacity=L)
     B, H, D, N, G = sh.batch, sh.nheads, sh.head_dim, sh.state_dim, sh.ngroups
@@ -260,11 +262,11 @@ def test_config3_capacity_sweep_full(L):
         if t < early.window:
             early.step(t, y, state0, flushed)
         head, count, fl = sched[t]
+        assert bool(torch.all(ring.head == head)) and bool(torch.all(ring.count == count)), t
+        assert bool(torch.all(flushed == int(fl))), t
         if t % 64 == 0 or fl:
-            assert bool(torch.all(ring.head == head)) and bool(torch.all(ring.count == count)), t
             assert ring.copies_agree(), t
-            assert bool(torch.all(flushed == int(fl))), t
-        if fl and (t // L) % 8 == 0:
+        if fl:
             es = rel_err(state0[tb, th].cpu().numpy(), S[:, 0])
             assert es <= S_TOL, (t, es)
     assert int(ring.err.item()) == 0
