@@ -202,6 +202,33 @@ def _cpu_baseline_all_cores(steps: int, max_workers: int = CPU_WORKERS_MAX):
                       f"{steps} decode steps, {dt:.1f} s wall", **host}
 
 
+def _cpu_standard_baseline(cfg_id: int, requests: int, capacity: int = 16):
+    """The standard-mode ReplaySSM oracle (float64, one core) on a bounded sample
+    of a decode workload: the first `requests` requests over one ring cycle of
+    `capacity` steps (the fold included)."""
+    import numpy as np
+
+    from oracle import replay as o_rep
+    from ssm_recurrent_decode_amd import synth
+    wl = synth.WORKLOADS[cfg_id]
+    sh, seed = wl.shape.with_(capacity=capacity), wl.cfg_seed
+    n = min(requests, sh.batch)
+    A, bias = synth.mamba2_head_params(sh, seed, cfg_id)
+    S0 = np.stack([synth.state0_request(sh, seed, cfg_id, b) for b in range(n)]).astype(np.float64)
+    seq = []
+    for t in range(capacity):
+        st = synth.mamba2_step_inputs(sh, seed, cfg_id, t)
+        seq.append({"v": synth.bf16_bits_to_f64(st["v"][:n]), "k": synth.bf16_bits_to_f64(st["k"][:n]),
+                    "q": synth.bf16_bits_to_f64(st["q"][:n]), "dt": st["dt"][:n].astype(np.float64)})
+    t0 = time.perf_counter()
+    o_rep.run_standard(S0, seq, bias.astype(np.float64), A.astype(np.float64), capacity, sh.ngroups)
+    dt = time.perf_counter() - t0
+    return {"value": n * capacity / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"ReplaySSM standard-mode oracle, requests 0..{n - 1} of {sh.batch} ({sh.nheads} heads), "
+                      f"{capacity} decode steps (one ring cycle, L = {capacity}), float64 numpy, {dt:.1f} s",
+            **_host()}
+
+
 def _cpu_spec_baseline(cfg_id: int, requests: int, rounds: int = 16):
     """The speculative oracle (float64, one core) on a bounded sample of a verify
     workload: the first `requests` requests of the batch over `rounds` verify
@@ -1365,10 +1392,13 @@ def main(argv=None) -> int:
         out["cpu_baseline"] = _cpu_baseline(a.cpu_steps)
         out["cpu_baseline_all_cores"] = _cpu_baseline_all_cores(a.cpu_steps)
         rows = out.get("rows", {})
-        for name, cfg_id, nreq in (("speculative_verify", 2, 128), ("gdn_speculative_verify", 4, 32)):
+        for name, cfg_id, nreq in (("speculative_verify", 2, 512), ("gdn_speculative_verify", 4, 128)):
             if name in rows:
                 print(f"[bench] cpu oracle for {name}", file=sys.stderr, flush=True)
                 rows[name]["cpu_baseline"] = _cpu_spec_baseline(cfg_id, nreq)
+        if "capacity_sweep" in rows:
+            print("[bench] cpu oracle for capacity_sweep", file=sys.stderr, flush=True)
+            rows["capacity_sweep"]["cpu_baseline"] = _cpu_standard_baseline(3, 96)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -45,3 +45,11 @@ def test_cpu_spec_baseline_runs_the_oracle(cfg_id):
     assert res["kind"] == "oracle" and res["cores"] == 1 and res["unit"] == "verified positions/s"
     assert res["value"] > 0 and res["accepted_tokens_per_s"] >= 0
     assert "requests 0..1" in res["sample"] and "2 verify rounds" in res["sample"]
+
+
+@pytest.mark.timeout(300)
+def test_cpu_standard_baseline_runs_one_ring_cycle():
+    res = bench._cpu_standard_baseline(3, 2, capacity=4)
+    assert res["kind"] == "oracle" and res["cores"] == 1 and res["unit"] == "tokens/s"
+    assert res["value"] > 0 and "requests 0..1 of 256 (128 heads)" in res["sample"]
+    assert "4 decode steps" in res["sample"]

@@ -62,6 +62,6 @@ def _functions_importing_oracle(path):
 
 def test_only_the_allowed_legs_call_the_oracle():
     owners, top = _functions_importing_oracle(os.path.join(ROOT, "bench.py"))
-    assert not top and owners <= {"_cpu_baseline", "_cpu_worker", "_cpu_spec_baseline"}, (owners, top)
+    assert not top and owners <= {"_cpu_baseline", "_cpu_worker", "_cpu_spec_baseline", "_cpu_standard_baseline"}, (owners, top)
     owners, top = _functions_importing_oracle(os.path.join(ROOT, "__graft_entry__.py"))
     assert not top and owners <= {"smoke"}, (owners, top)
