@@ -372,7 +372,39 @@ def _row_verify(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, rounds=
     fl = np.array([counts[r] + 2 * T > L for r in range(warm, R)])
     round_s = (sum(v_us) + sum(r_us)) * 1e-6
     gbs = sum(byts) / (sum(v_us) * 1e-6) / 1e9
+    # the same rounds with each commit folded into the next verify launch
+    # (commit-and-verify: one launch per round; the last window's commit is the
+    # separate kernel, outside the timed rounds)
+    for Ly in layers:
+        rd.rssm_ring_reset(dims, Ly["ring"], stream=stream)
+    zero = torch.zeros((B,), dtype=torch.int32, device=dev)
+    ev_c = _events(torch, R)
+    torch.cuda.synchronize()
+    for r in range(R):
+        Ly, ip = layers[r % NLr], pool[r % P]
+        prev = dacc[r - NLr] if r >= NLr else zero       # this ring's previous window
+        ev_c[r][0].record(stream)
+        if gdn:
+            rd.gdn_replay_commit_verify_T(dims, T, Ly["S0"], Ly["ring"], prev, ip["v"], ip["k"], ip["q"], ip["g"],
+                                          ip["beta"], y, flushed, stream=stream)
+        else:
+            rd.replay_commit_verify_T(dims, T, Ly["S0"], Ly["ring"], prev, ip["v"], ip["k"], ip["q"], ip["dt"],
+                                      Ly["bias"], Ly["A"], y, flushed, stream=stream)
+        ev_c[r][1].record(stream)
+    for l in range(NLr):
+        rd.replay_rollback(dims, layers[(R - NLr + l) % NLr]["ring"], dacc[R - NLr + l], stream=stream)
+    torch.cuda.synchronize()
+    errs = [int(Ly["ring"].err.item()) for Ly in layers]
+    if any(errs):
+        raise RuntimeError(f"ring anomaly bits set in the commit-and-verify rounds: {errs}")
+    cv_us = [1e3 * ev_c[r][0].elapsed_time(ev_c[r][1]) for r in range(warm, R)]
+    cv_s = sum(cv_us) * 1e-6
     fixed = _fixed_pointer_rounds(torch, np, rd, traffic, stream, layers, pool, verify, y, dims, gdn, flags)
+    all_bytes = 3 * sum(_verify_bytes(traffic, gdn, H, D, N, G, T, L, counts[r], flags) for r in range(R))
+    all_launches = 3 * R
+    for f_ in (fixed or {}).values():
+        all_bytes += f_["launches"] * f_["alg_bytes"]
+        all_launches += f_["launches"]
     base = None
     if gdn and with_standard:
         # the baseline that rewrites the state every token, at the same shape
@@ -388,12 +420,17 @@ def _row_verify(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, rounds=
            "accepted_tokens_per_s": round(float(acc[warm:].sum()) / round_s, 1),
            "achieved_GBs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
            "alg_bytes_per_round": round(sum(byts) / rounds),
-           # over every launch of the kernel (both passes replay rounds 0..R-1): the
-           # figure hardware traffic counters over the whole run compare with
-           "alg_bytes_avg_all_launches": round(float(np.mean(
-               [_verify_bytes(traffic, gdn, H, D, N, G, T, L, counts[r], flags) for r in range(R)]))),
-           "launches": 2 * R,
+           # over every launch of the kernel (three passes replay rounds 0..R-1, then
+           # the fixed-pointer rounds): the figure hardware traffic counters over the
+           # whole run compare with
+           "alg_bytes_avg_all_launches": round(all_bytes / all_launches),
+           "launches": all_launches,
            "flush_rate": round(float(fl.mean()), 4),
+           "commit_verify": {"kernel": "gdn_replay_commit_verify_T" if gdn else "replay_commit_verify_T",
+                             "us_per_round": round(sum(cv_us) / rounds, 3),
+                             "verified_positions_per_s": round(B * T * rounds / cv_s, 1),
+                             "accepted_tokens_per_s": round(float(acc[warm:].sum()) / cv_s, 1),
+                             "achieved_GBs": round(sum(byts) / cv_s / 1e9, 1)},
            "mean_committed_before": round(float(np.mean([counts[r] for r in range(warm, R)])), 3)}
     if fixed is not None:
         res["fixed_pointer_rounds"] = fixed
@@ -432,7 +469,7 @@ def _fixed_pointer_rounds(torch, np, rd, traffic, stream, layers, pool, verify, 
         med = us[len(us) // 2]
         nbytes = _verify_bytes(traffic, gdn, H, D, N, G, T, L, np.full(B, c), flags)
         out[tag] = {"committed_count": c, "folds": c + 2 * T > L, "median_us": round(med, 3),
-                    "min_us": round(us[0], 3), "alg_bytes": nbytes,
+                    "min_us": round(us[0], 3), "alg_bytes": nbytes, "launches": reps,
                     "achieved_GBs": round(nbytes / (med * 1e-6) / 1e9, 1),
                     "frac_of_peak": round(nbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
     for Ly in layers:
@@ -586,6 +623,7 @@ def _row_window(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, Ts=(1, 
         sn = _snapshot_rounds(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, T, rounds, warm)
         out["T"].append({
             "T": T, "replay_verify_us": rv["verify_us"], "replay_rollback_us": rv["rollback_us"],
+            "replay_commit_verify_us": rv["commit_verify"]["us_per_round"],
             "replay_GBs": rv["achieved_GBs"], "replay_flush_rate": rv["flush_rate"],
             "snapshot_verify_us": sn["verify_us"], "snapshot_commit_us": sn["commit_us"],
             "snapshot_GBs": sn["achieved_GBs"],

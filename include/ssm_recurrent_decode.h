@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define RSSM_ABI_VERSION 10
+#define RSSM_ABI_VERSION 11
 
 #define RSSM_OK 0
 #define RSSM_EINVAL (-22)
@@ -303,6 +303,24 @@ int replay_verify_T(const rssm_dims* dims, int32_t T, float* state0, rssm_ring* 
 int replay_rollback(const rssm_dims* dims, rssm_ring* ring, const int32_t* accepted,
                     void* stream);
 
+/*
+ * replay_verify_T with the commit of the previous window folded in: for every
+ * request that holds pending drafts (left by the previous verify on this ring),
+ *     count += clamp(accepted[b], 0, pending);  pending = 0,
+ * exactly as replay_rollback would, then the verify of the T new drafts as
+ * replay_verify_T (the early-flush decision taken from the committed count).
+ * One launch per speculative round instead of two (CUDA-Graph notes,
+ * "device-side commit and rollback": the commit stays on the device; here it
+ * also shares the verify's launch).  Requests with no pending drafts ignore
+ * accepted[b].  The last window of a run is committed with replay_rollback.
+ *   accepted int32 [B] (device): the previous window's accepted drafts
+ *   other arguments as replay_verify_T
+ */
+int replay_commit_verify_T(const rssm_dims* dims, int32_t T, float* state0, rssm_ring* ring,
+                           const int32_t* accepted, const uint16_t* v, const uint16_t* k,
+                           const uint16_t* q, const float* dt, const float* dt_bias, const float* A,
+                           float* y, int32_t* flushed, void* stream);
+
 /* ---------------------------------------------------------- Gated DeltaNet */
 
 /*
@@ -335,6 +353,13 @@ int gdn_decode_step(const rssm_dims* dims, float* state, const uint16_t* v, cons
 int gdn_replay_verify_T(const rssm_dims* dims, int32_t T, float* state0, rssm_ring* ring,
                         const uint16_t* v, const uint16_t* k, const uint16_t* q, const float* g,
                         const float* beta, float* y, int32_t* flushed, void* stream);
+
+/* gdn_replay_verify_T with the previous window's commit folded in, as
+ * replay_commit_verify_T. */
+int gdn_replay_commit_verify_T(const rssm_dims* dims, int32_t T, float* state0, rssm_ring* ring,
+                               const int32_t* accepted, const uint16_t* v, const uint16_t* k,
+                               const uint16_t* q, const float* g, const float* beta, float* y,
+                               int32_t* flushed, void* stream);
 
 /*
  * ReplaySSM GDN standard decode, one token per request (appendix, "GDN standard

@@ -12,7 +12,8 @@ generators in ``synth`` can be used without torch or a GPU.
 
 _BINDING_NAMES = (
     "Dims", "Ring", "ring_sizes", "rssm_ring_reset", "rssm_ring_pointers", "ssm_decode_step", "replay_append_decode",
-    "replay_append_decode_conv", "replay_flush", "replay_verify_T", "replay_rollback", "gdn_decode_step",
+    "replay_append_decode_conv", "replay_flush", "replay_verify_T", "replay_commit_verify_T", "replay_rollback",
+    "gdn_decode_step", "gdn_replay_commit_verify_T",
     "gdn_replay_verify_T", "gdn_replay_append_decode", "gdn_replay_flush", "ssm_snapshot_verify_T", "gdn_snapshot_verify_T",
     "snapshot_commit", "causal_conv1d_update", "rssm_probe_copy",
     "rssm_probe_read", "probe_read_sink_floats", "Prepared", "prepare_replay_append_decode",

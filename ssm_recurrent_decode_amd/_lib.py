@@ -23,7 +23,7 @@ RSSM_ERR_SLOT = 8
 RSSM_ERR_DIVERGED = 16
 RSSM_F_Y_BF16 = 1
 RSSM_F_U_BF16 = 2
-ABI_VERSION = 10  # RSSM_ABI_VERSION of the header this binding follows
+ABI_VERSION = 11  # RSSM_ABI_VERSION of the header this binding follows
 
 
 class rssm_dims(ctypes.Structure):
@@ -53,6 +53,8 @@ SIGNATURES = {
     "replay_flush": (c_int, [_D, _P, _R, _P, _P]),
     "replay_verify_T": (c_int, [_D, c_int32, _P, _R, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "replay_rollback": (c_int, [_D, _R, _P, _P]),
+    "replay_commit_verify_T": (c_int, [_D, c_int32, _P, _R, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "gdn_replay_commit_verify_T": (c_int, [_D, c_int32, _P, _R, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "gdn_decode_step": (c_int, [_D, _P, _P, _P, _P, _P, _P, _P, _P]),
     "gdn_replay_verify_T": (c_int, [_D, c_int32, _P, _R, _P, _P, _P, _P, _P, _P, _P, _P]),
     "gdn_replay_append_decode": (c_int, [_D, _P, _R, _P, _P, _P, _P, _P, _P, _P, _P]),

@@ -275,6 +275,20 @@ def replay_verify_T(dims: Dims, T: int, state0, ring: Ring, v, k, q, dt, dt_bias
                "replay_verify_T")
 
 
+def replay_commit_verify_T(dims: Dims, T: int, state0, ring: Ring, accepted, v, k, q, dt, dt_bias, A, y,
+                           flushed=None, stream=None):
+    B, H, D, N, G = dims.batch, dims.nheads, dims.head_dim, dims.state_dim, dims.ngroups
+    d, rc = dims.c(), _ring_args(dims, ring, False)
+    args = (_p(state0, "state0", _F32, (ring.rows, H, D, N)), ctypes.byref(rc),
+            _p(accepted, "accepted", _I32, (B,)),
+            _p(v, "v", _BF16, (B, T, H, D)), _p(k, "k", _BF16, (B, T, G, N)),
+            _p(q, "q", _BF16, (B, T, G, N)), _p(dt, "dt", _F32, (B, T, H)),
+            _p(dt_bias, "dt_bias", _F32, (H,)), _p(A, "A", _F32, (H,)),
+            _p(y, "y", dims.y_dtypes, (B, T, H, D)), _p(flushed, "flushed", _I32, (B,), allow_none=True))
+    _lib.check(_lib.load().replay_commit_verify_T(ctypes.byref(d), int(T), *args, _stream(stream)),
+               "replay_commit_verify_T")
+
+
 def replay_rollback(dims: Dims, ring: Ring, accepted, stream=None):
     d, rc = dims.c(), _ring_args(dims, ring, ring.gdn)
     _lib.check(_lib.load().replay_rollback(
@@ -303,6 +317,20 @@ def gdn_replay_verify_T(dims: Dims, T: int, state0, ring: Ring, v, k, q, g, beta
             _p(flushed, "flushed", _I32, (B,), allow_none=True))
     _lib.check(_lib.load().gdn_replay_verify_T(ctypes.byref(d), int(T), *args, _stream(stream)),
                "gdn_replay_verify_T")
+
+
+def gdn_replay_commit_verify_T(dims: Dims, T: int, state0, ring: Ring, accepted, v, k, q, g, beta, y,
+                               flushed=None, stream=None):
+    B, H, D, N, G = dims.batch, dims.nheads, dims.head_dim, dims.state_dim, dims.ngroups
+    d, rc = dims.c(), _ring_args(dims, ring, True)
+    args = (_p(state0, "state0", _F32, (ring.rows, H, D, N)), ctypes.byref(rc),
+            _p(accepted, "accepted", _I32, (B,)),
+            _p(v, "v", _BF16, (B, T, H, D)), _p(k, "k", _BF16, (B, T, G, N)),
+            _p(q, "q", _BF16, (B, T, G, N)), _p(g, "g", _F32, (B, T, H)),
+            _p(beta, "beta", _F32, (B, T, H)), _p(y, "y", dims.y_dtypes, (B, T, H, D)),
+            _p(flushed, "flushed", _I32, (B,), allow_none=True))
+    _lib.check(_lib.load().gdn_replay_commit_verify_T(ctypes.byref(d), int(T), *args, _stream(stream)),
+               "gdn_replay_commit_verify_T")
 
 
 def gdn_replay_append_decode(dims: Dims, state0, ring: Ring, v, k, q, g, beta, y, flushed=None,

@@ -217,6 +217,27 @@ __device__ __forceinline__ void flag_error(int32_t* err, int bits) {
   if (err != nullptr && bits != 0) atomicOr(err, bits);
 }
 
+// Device-side commit of a draft window: count += clamp(accepted, 0, pending),
+// pending = 0; a pending or count out of range is clamped and flagged first.
+// Used by the commit kernel and, folded into the next verify, by the
+// commit-and-verify calls.
+__device__ __forceinline__ void commit_window(int L, int acc, int& cnt, int& pend, int& bad) {
+  if (pend > L) {
+    pend = L;
+    bad |= RSSM_ERR_POINTERS;
+  }
+  if (cnt + pend > L) {
+    cnt = L - pend;
+    bad |= RSSM_ERR_POINTERS;
+  }
+  if (acc < 0 || acc > pend) {
+    acc = acc < 0 ? 0 : pend;
+    bad |= RSSM_ERR_ACCEPTED;
+  }
+  cnt += acc;
+  pend = 0;
+}
+
 // Pool row of batch entry b: b itself without a slot map, else slots[b]; -1
 // when the entry is skipped (a negative slot marks padding; a slot past the
 // pool is also flagged).  Uniform per request.

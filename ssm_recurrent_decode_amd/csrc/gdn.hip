@@ -204,16 +204,18 @@ extern "C" int gdn_decode_step(const rssm_dims* dims, float* state, const uint16
   }
 }
 
-extern "C" int gdn_replay_verify_T(const rssm_dims* dims, int32_t T, float* state0, rssm_ring* ring,
-                                   const uint16_t* v, const uint16_t* k, const uint16_t* q,
-                                   const float* g, const float* beta, float* y, int32_t* flushed,
-                                   void* stream) {
+namespace {
+
+int gdn_verify_common(const rssm_dims* dims, int32_t T, float* state0, rssm_ring* ring, const int32_t* accepted,
+                      const uint16_t* v, const uint16_t* k, const uint16_t* q, const float* g,
+                      const float* beta, float* y, int32_t* flushed, void* stream) {
   if (!rssm_host::dims_ok(dims) || !rssm_host::ring_ok(ring) || !state0 || !v || !k || !q ||
       !g || !beta || !y)
     return RSSM_EINVAL;
   if (T < 1 || dims->capacity < 2 * T) return RSSM_EINVAL;
   if (!rssm_host::ring_shape_supported(dims) || T > kMaxT) return RSSM_ENOTSUP;
   GdnReplayParams p = make_gdn_params(dims, state0, ring);
+  p.accepted = accepted;
   p.v = v;
   p.k = k;
   p.q = q;
@@ -226,6 +228,23 @@ extern "C" int gdn_replay_verify_T(const rssm_dims* dims, int32_t T, float* stat
   if (dims->state_dim == 256) return rssm_host::launch_gdn_n256(T, D, p, dims->batch, stream);
   if (T <= 4) return rssm_host::launch_gdn_verify_lo(T, D, p, dims->batch, stream);
   return rssm_host::launch_gdn_verify_hi(T, D, p, dims->batch, stream);
+}
+
+}  // namespace
+
+extern "C" int gdn_replay_verify_T(const rssm_dims* dims, int32_t T, float* state0, rssm_ring* ring,
+                                   const uint16_t* v, const uint16_t* k, const uint16_t* q,
+                                   const float* g, const float* beta, float* y, int32_t* flushed,
+                                   void* stream) {
+  return gdn_verify_common(dims, T, state0, ring, nullptr, v, k, q, g, beta, y, flushed, stream);
+}
+
+extern "C" int gdn_replay_commit_verify_T(const rssm_dims* dims, int32_t T, float* state0, rssm_ring* ring,
+                                          const int32_t* accepted, const uint16_t* v, const uint16_t* k,
+                                          const uint16_t* q, const float* g, const float* beta, float* y,
+                                          int32_t* flushed, void* stream) {
+  if (!accepted) return RSSM_EINVAL;
+  return gdn_verify_common(dims, T, state0, ring, accepted, v, k, q, g, beta, y, flushed, stream);
 }
 
 extern "C" int gdn_replay_append_decode(const rssm_dims* dims, float* state0, rssm_ring* ring,

@@ -25,6 +25,7 @@ struct GdnReplayParams {
   float* y;            // [B, T, H, D]
   int32_t* flushed;
   const int32_t* mask;
+  const int32_t* accepted;  // commit-and-verify: the previous window's accepted drafts, or null
   const int32_t* slots;  // pool row per batch entry, or null
   int rows;
   int y_bf16;          // outputs stored as bf16
@@ -117,6 +118,7 @@ __global__ __launch_bounds__(kBlock, (gdn_waves_per_simd<D, N, T, LCAP>())) void
   const int MS = meta_words(L);
   float* rec = p.meta + bh * MS;  // this head's ring record
   const unsigned long long word = *reinterpret_cast<const unsigned long long*>(rec + kMetaPtr);
+  const int acc_prev = (!APPEND && p.accepted != nullptr) ? p.accepted[b] : 0;
   uint4 xvc[XVP];  // readout vectors (k drafts, then q drafts), then the draft values
 #pragma unroll
   for (int i = 0; i < XVP; ++i) {
@@ -158,18 +160,20 @@ __global__ __launch_bounds__(kBlock, (gdn_waves_per_simd<D, N, T, LCAP>())) void
     else if (t < XC + VC) *reinterpret_cast<uint4*>(&s_vd[(t - XC) * 8]) = xvc[i];
   }
   const RingPtr rp = unpack_ptr(word);
-  int head = rp.head, cnt = rp.count;
+  int head = rp.head, cnt = rp.count, pend = rp.pending;
   int bad = 0;
   if (head >= L) {
     head %= L;
     bad |= RSSM_ERR_POINTERS;
   }
+  // commit-and-verify: the previous window's accepted drafts are committed first
+  if (!APPEND && p.accepted != nullptr && pend > 0) commit_window(L, acc_prev, cnt, pend, bad);
   const int cmax = APPEND ? L - 1 : L - T;
   if (cnt > cmax) {
     cnt = cmax;
     bad |= RSSM_ERR_POINTERS;
   }
-  if (rp.pending != 0) bad |= RSSM_ERR_PENDING;
+  if (pend != 0) bad |= RSSM_ERR_PENDING;
   const int c = cnt;
   const int E = c + T;
   // verify: early flush of the c committed entries; append: flush when full

@@ -188,25 +188,14 @@ __global__ __launch_bounds__(kBlock) void rollback_kernel(PtrParams p) {
   if (rb < 0) return;
   unsigned long long* w = ptr_word(p, rb * p.H + h);
   const RingPtr rp = unpack_ptr(*w);
-  int head = rp.head, cnt = rp.count, pend = rp.pending, acc = p.accepted[b];
+  int head = rp.head, cnt = rp.count, pend = rp.pending;
   int bad = 0;
   if (head >= p.L) {
     head %= p.L;
     bad |= RSSM_ERR_POINTERS;
   }
-  if (pend > p.L) {
-    pend = p.L;
-    bad |= RSSM_ERR_POINTERS;
-  }
-  if (cnt + pend > p.L) {
-    cnt = p.L - pend;
-    bad |= RSSM_ERR_POINTERS;
-  }
-  if (acc < 0 || acc > pend) {
-    acc = acc < 0 ? 0 : pend;
-    bad |= RSSM_ERR_ACCEPTED;
-  }
-  *w = pack_ptr(head, cnt + acc, 0);
+  commit_window(p.L, p.accepted[b], cnt, pend, bad);
+  *w = pack_ptr(head, cnt, 0);
   flag_error(p.err, bad);
 }
 
@@ -370,16 +359,18 @@ extern "C" int replay_flush(const rssm_dims* dims, float* state0, rssm_ring* rin
   }
 }
 
-extern "C" int replay_verify_T(const rssm_dims* dims, int32_t T, float* state0, rssm_ring* ring,
-                               const uint16_t* v, const uint16_t* k, const uint16_t* q,
-                               const float* dt, const float* dt_bias, const float* A, float* y,
-                               int32_t* flushed, void* stream) {
+namespace {
+
+int verify_common(const rssm_dims* dims, int32_t T, float* state0, rssm_ring* ring, const int32_t* accepted,
+                  const uint16_t* v, const uint16_t* k, const uint16_t* q, const float* dt,
+                  const float* dt_bias, const float* A, float* y, int32_t* flushed, void* stream) {
   if (!rssm_host::dims_ok(dims) || !rssm_host::ring_ok(ring) || !state0 || !v || !k || !q ||
       !dt || !dt_bias || !A || !y)
     return RSSM_EINVAL;
   if (T < 1 || dims->capacity < 2 * T) return RSSM_EINVAL;
   if (!rssm_host::ring_shape_supported(dims) || T > kMaxT) return RSSM_ENOTSUP;
   ReplayParams p = make_replay_params(dims, state0, ring);
+  p.accepted = accepted;
   p.v = v;
   p.k = k;
   p.q = q;
@@ -393,6 +384,23 @@ extern "C" int replay_verify_T(const rssm_dims* dims, int32_t T, float* state0, 
   if (dims->state_dim == 256) return rssm_host::launch_replay_n256(T, D, p, dims->batch, stream);
   if (T <= 4) return rssm_host::launch_replay_verify_lo(T, D, p, dims->batch, stream);
   return rssm_host::launch_replay_verify_hi(T, D, p, dims->batch, stream);
+}
+
+}  // namespace
+
+extern "C" int replay_verify_T(const rssm_dims* dims, int32_t T, float* state0, rssm_ring* ring,
+                               const uint16_t* v, const uint16_t* k, const uint16_t* q,
+                               const float* dt, const float* dt_bias, const float* A, float* y,
+                               int32_t* flushed, void* stream) {
+  return verify_common(dims, T, state0, ring, nullptr, v, k, q, dt, dt_bias, A, y, flushed, stream);
+}
+
+extern "C" int replay_commit_verify_T(const rssm_dims* dims, int32_t T, float* state0, rssm_ring* ring,
+                                      const int32_t* accepted, const uint16_t* v, const uint16_t* k,
+                                      const uint16_t* q, const float* dt, const float* dt_bias,
+                                      const float* A, float* y, int32_t* flushed, void* stream) {
+  if (!accepted) return RSSM_EINVAL;
+  return verify_common(dims, T, state0, ring, accepted, v, k, q, dt, dt_bias, A, y, flushed, stream);
 }
 
 extern "C" int replay_rollback(const rssm_dims* dims, rssm_ring* ring, const int32_t* accepted,

@@ -33,6 +33,7 @@ struct ReplayParams {
   float* y;            // [B, T, H, D]
   int32_t* flushed;
   const int32_t* mask;  // explicit flush only
+  const int32_t* accepted;  // commit-and-verify: the previous window's accepted drafts, or null
   const int32_t* slots;  // pool row per batch entry, or null
   int rows;
   // fused front-end (append only): depthwise causal conv1d (width 4) + SiLU over
@@ -175,6 +176,7 @@ __global__ __launch_bounds__(kBlock, (window_waves_per_simd<D, CONV, LCAP>())) v
   const int MS = meta_words(L);
   float* rec = p.meta + bh * MS;  // this head's ring record
   const unsigned long long word = *reinterpret_cast<const unsigned long long*>(rec + kMetaPtr);
+  const int acc_prev = (!APPEND && p.accepted != nullptr) ? p.accepted[b] : 0;
   // The token's query and key: each lane keeps the 16-lane slices it needs in
   // registers (qm, kin).  Several drafts would hold 2T such slices per lane
   // across the checkpoint load (a wave per SIMD fewer), so from T = 2 they are
@@ -256,18 +258,20 @@ __global__ __launch_bounds__(kBlock, (window_waves_per_simd<D, CONV, LCAP>())) v
 
   // ---- 3. ring pointers (uniform per request), clamped into range
   const RingPtr rp = unpack_ptr(word);
-  int head = rp.head, cnt = rp.count;
+  int head = rp.head, cnt = rp.count, pend = rp.pending;
   int bad = 0;
   if (head >= L) {
     head %= L;
     bad |= RSSM_ERR_POINTERS;
   }
+  // commit-and-verify: the previous window's accepted drafts are committed first
+  if (!APPEND && p.accepted != nullptr && pend > 0) commit_window(L, acc_prev, cnt, pend, bad);
   const int cmax = APPEND ? L - 1 : L - T;
   if (cnt > cmax) {
     cnt = cmax;
     bad |= RSSM_ERR_POINTERS;
   }
-  if (rp.pending != 0) bad |= RSSM_ERR_PENDING;
+  if (pend != 0) bad |= RSSM_ERR_PENDING;
   const int c = cnt;
   const int E = c + T;
   const bool do_flush = APPEND ? (E == L) : (c + 2 * T > L);

@@ -33,7 +33,7 @@ def test_every_declared_function_is_exported_and_prototyped():
 
 def test_abi_version_and_strerror():
     lib = _lib.load()
-    assert lib.rssm_abi_version() == _lib.ABI_VERSION == 10
+    assert lib.rssm_abi_version() == _lib.ABI_VERSION == 11
     assert "invalid" in _lib.strerror(_lib.RSSM_EINVAL)
     assert "not compiled" in _lib.strerror(_lib.RSSM_ENOTSUP)
 
@@ -117,8 +117,14 @@ def test_host_validation_codes():
     assert lib.causal_conv1d_update(4, 3072, 3, P, P, P, P, None) == ENOTSUP
     assert lib.causal_conv1d_update(4, 3070, 4, P, P, P, P, None) == ENOTSUP
     assert lib.causal_conv1d_update(0, 3072, 4, P, P, P, P, None) == EINVAL
-    # rollback needs accepted
+    # rollback needs accepted, and so does commit-and-verify
     assert lib.replay_rollback(ctypes.byref(d), ctypes.byref(r), None, None) == EINVAL
+    assert lib.replay_commit_verify_T(ctypes.byref(d), 2, P, ctypes.byref(r), None, P, P, P, P, P, P, P,
+                                      None, None) == EINVAL
+    assert lib.gdn_replay_commit_verify_T(ctypes.byref(d), 2, P, ctypes.byref(r), None, P, P, P, P, P, P,
+                                          None, None) == EINVAL
+    assert lib.replay_commit_verify_T(ctypes.byref(d), 5, P, ctypes.byref(r), P, P, P, P, P, P, P, P,
+                                      None, None) == EINVAL       # L < 2T
     r_odd = _ring()
     r_odd.meta = FAKE.value + 64
     assert lib.replay_rollback(ctypes.byref(d), ctypes.byref(r_odd), P, None) == EINVAL
