@@ -903,8 +903,9 @@ def _row_staggered(torch, np, rd, synth, traffic, dev, stream):
             layers[i % NLs]()
         b_.record(stream)
         torch.cuda.synchronize()
-        if any(int(Ly.keep_alive[1].err.item()) for Ly in layers):
-            raise RuntimeError("ring anomaly bits set in the staggered row")
+        errs = [int(Ly.keep_alive[1].err.item()) for Ly in layers]
+        if any(errs):
+            raise RuntimeError(f"ring anomaly bits set in the staggered row: {errs}")
         us = 1e3 * a_.elapsed_time(b_) / K
         res[name] = {"avg_us": round(us, 3), "avg_GBs": round(byts / (us * 1e-6) / 1e9, 1),
                      "frac_of_peak": round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
@@ -1423,8 +1424,9 @@ def main(argv=None) -> int:
     if not a.no_rows:
         del calls, layers
         torch.cuda.empty_cache()
-        out["rows"] = _rows(torch, np, rd, synth, traffic, dev, stream,
-                            None if a.rows is None else [x for x in a.rows.split(",") if x])
+        with torch.cuda.stream(stream):       # the rows' own tensor fills on the kernels' stream
+            out["rows"] = _rows(torch, np, rd, synth, traffic, dev, stream,
+                                None if a.rows is None else [x for x in a.rows.split(",") if x])
 
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = _cpu_baseline(a.cpu_steps)

@@ -108,6 +108,9 @@ class Ring:
         self.k = torch.zeros((B, G, L, N), dtype=torch.bfloat16, **z)
         self.meta = torch.zeros((B, H, meta_words(L)), dtype=torch.float32, **z)
         self.err = torch.zeros((1,), dtype=torch.int32, **z)
+        # zero-filled by torch on its current stream: finish before a call on any
+        # other stream reads the records (their memory may have held another ring's)
+        torch.cuda.synchronize(self.meta.device)
 
     @property
     def ptr(self):
@@ -153,6 +156,9 @@ class Ring:
         words = [(h & 0xFFFF) | ((c & 0xFFFF) << 16) | ((p & 0xFFFF) << 32) for h, c, p in zip(*new)]
         col = torch.tensor(words, dtype=torch.int64).to(self.meta.device)
         self.meta.view(torch.int64)[:, :, 0] = col[:, None]
+        # written by torch on its current stream: finish before a call on any
+        # other stream reads the records
+        torch.cuda.synchronize(self.meta.device)
 
     def use_slots(self, slots):
         """Map the batch entries of the following calls to pool rows (int32 device
