@@ -249,7 +249,7 @@ int replay_append_decode(const rssm_dims* dims, float* state0, rssm_ring* ring,
  * as replay_append_decode.
  *   conv_state_in  bf16 [B, C, 3] (pooled: [rows, C, 3]) read
  *   conv_state_out bf16 [B, C, 3] written; must not be conv_state_in (the heads
- *                  of a group read B and C states while one of them writes them):
+ *                  of a group read B and C states while they write them):
  *                  swap the two buffers every step
  *   xbc bf16 [B, C];  conv_w bf16 [C, 4] (no bias);  other arguments as
  *   replay_append_decode.
@@ -439,7 +439,7 @@ int snapshot_commit(int32_t batch, int32_t T, int32_t nslots, int32_t* slot,
  *     out[b,c] = SiLU(sum_w weight[c,w] window[w]);  state[b,c,:] <- window[1..W-1].
  *   conv_state bf16 [B, C, W-1] in/out;  x bf16 [B, C];  weight bf16 [C, W]
  *   out fp32 [B, C]
- * Supported: W = 4.
+ * Supported: W = 4 and an even number of channels C; otherwise RSSM_ENOTSUP.
  */
 int causal_conv1d_update(int32_t batch, int32_t channels, int32_t width, uint16_t* conv_state,
                          const uint16_t* x, const uint16_t* weight, float* out, void* stream);

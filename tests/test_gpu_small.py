@@ -467,6 +467,25 @@ def test_single_request_single_head():
     assert int(ring.err.item()) == 0
 
 
+@pytest.mark.parametrize("B,C", [(1, 2), (3, 70), (5, 3070)])
+def test_causal_conv1d_update_ragged(B, C):
+    """Channel counts that are even but not a multiple of four, and grids whose last
+    work-group is partly empty: state shift bit for bit, outputs to 1e-5."""
+    st_bits, w_bits = synth.conv_layer(B, C, 4, 777, 1)
+    state = dev_bf16(st_bits)
+    w = dev_bf16(w_bits)
+    out = torch.full((B, C), float("nan"), device="cuda")
+    ref_state = synth.bf16_bits_to_f64(st_bits)
+    W = synth.bf16_bits_to_f64(w_bits)
+    for t in range(3):
+        x_bits = synth.conv_step_input(B, C, 777, 1, t)
+        rd.causal_conv1d_update(state, dev_bf16(x_bits), w, out)
+        o_ref, ref_state = o_conv.update(ref_state, synth.bf16_bits_to_f64(x_bits), W)
+        assert rel_err(out.cpu().numpy(), o_ref) <= 1e-5
+        got_bits = state.view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(synth.bf16_bits_to_f64(got_bits), ref_state)
+
+
 def test_causal_conv1d_update_config1_size():
     wl = synth.WORKLOADS[1]
     B, C = wl.shape.batch, wl.conv_channels
