@@ -65,11 +65,11 @@ struct GdnReplayParams {
 // The build rejects any kernel that spills.
 template <int D, int N, int T, int LCAP>
 constexpr int gdn_waves_per_simd() {
-  if (N == 64) return LCAP == 16 ? 5 : (D == 64 || T <= 2 ? 4 : 3);
+  if (N == 64) return LCAP == 16 ? (T <= 7 ? 5 : 4) : (D == 64 || T <= 2 ? 4 : 3);
   if (N == 256) return D == 64 ? (LCAP == 16 ? 4 : 3) : 2;
   if (LCAP == 16) return 4;
-  if (D == 64) return T <= 6 ? 3 : 2;
-  return T <= 2 ? 3 : (T <= 6 ? 2 : 1);
+  if (D == 64) return T <= 5 ? 3 : 2;
+  return T <= 1 ? 3 : (T <= 6 ? 2 : 1);
 }
 
 template <int D, int N, int T, int LCAP, bool APPEND = false>
@@ -117,8 +117,10 @@ __global__ __launch_bounds__(kBlock, (gdn_waves_per_simd<D, N, T, LCAP>())) void
   // ---- 1. this head's copy of the pointer word and every small operand
   const int MS = meta_words(L);
   float* rec = p.meta + bh * MS;  // this head's ring record
-  const unsigned long long word = *reinterpret_cast<const unsigned long long*>(rec + kMetaPtr);
-  const int acc_prev = (!APPEND && p.accepted != nullptr) ? p.accepted[b] : 0;
+  // (both read per lane, so that the checkpoint loads are issued before they arrive)
+  const int z0 = opaque_zero();
+  const unsigned long long word = *reinterpret_cast<const unsigned long long*>(rec + kMetaPtr + z0);
+  const int acc_prev = (!APPEND && p.accepted != nullptr) ? p.accepted[b + z0] : 0;
   uint4 xvc[XVP];  // readout vectors (k drafts, then q drafts), then the draft values
 #pragma unroll
   for (int i = 0; i < XVP; ++i) {
@@ -134,12 +136,13 @@ __global__ __launch_bounds__(kBlock, (gdn_waves_per_simd<D, N, T, LCAP>())) void
     }
     xvc[i] = ld_u4(src);
   }
-  float rec_l = 0.f, gd = 0.f, bt = 0.f;
-  if (wave == 0) {  // the whole record (decays of every slot), the drafts' gates and betas
-    rec_l = rec[min(lane, MS - 1)];
-    gd = p.g[((size_t)b * T + min(lane, T - 1)) * H + h];
-    bt = p.beta[((size_t)b * T + min(lane, T - 1)) * H + h];
-  }
+  // the whole record (decays of every slot), the drafts' gates and betas: read by
+  // every wave, though only wave 0 uses them (behind a wave-0 branch the compiler
+  // computed the gates' exponentials there, and wave 0 waited for them before
+  // issuing its checkpoint loads)
+  const float rec_l = rec[min(lane, MS - 1)];
+  const float gd = p.g[((size_t)b * T + min(lane, T - 1)) * H + h];
+  const float bt = p.beta[((size_t)b * T + min(lane, T - 1)) * H + h];
 
   // ---- 2. the checkpoint, last (the scheduler may not hoist it above the rest)
   __builtin_amdgcn_sched_barrier(0);

@@ -176,8 +176,10 @@ __global__ __launch_bounds__(kBlock, (window_waves_per_simd<D, CONV, LCAP>())) v
   // ---- 1. this head's ring record (pointer word, step sizes) and every small operand
   const int MS = meta_words(L);
   float* rec = p.meta + bh * MS;  // this head's ring record
-  const unsigned long long word = *reinterpret_cast<const unsigned long long*>(rec + kMetaPtr);
-  const int acc_prev = (!APPEND && p.accepted != nullptr) ? p.accepted[b] : 0;
+  // (both read per lane, so that the checkpoint loads are issued before they arrive)
+  const int z0 = opaque_zero();
+  const unsigned long long word = *reinterpret_cast<const unsigned long long*>(rec + kMetaPtr + z0);
+  const int acc_prev = (!APPEND && p.accepted != nullptr) ? p.accepted[b + z0] : 0;
   // The token's query and key: each lane keeps the 16-lane slices it needs in
   // registers (qm, kin).  Several drafts would hold 2T such slices per lane
   // across the checkpoint load (a wave per SIMD fewer), so from T = 2 they are
