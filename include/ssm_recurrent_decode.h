@@ -25,6 +25,9 @@
  *    NULL).  The caller reads that word whenever it chooses.
  *  - Dense row-major layouts, innermost index last.  bf16 is passed as its
  *    uint16_t bit pattern.  fp32 is IEEE binary32.
+ *  - Every array is 16-byte aligned (the kernels move 16-byte chunks; hipMalloc
+ *    returns 256-byte aligned memory), rssm_ring.meta 128-byte aligned and
+ *    rssm_ring.err 4-byte aligned; a misaligned pointer is RSSM_EINVAL.
  *  - Outputs must not alias inputs.  Different requests are independent, so two
  *    calls on disjoint buffers may run on different streams concurrently; two
  *    calls on the same ring must be ordered (same stream or events).

@@ -83,7 +83,8 @@ extern "C" int rssm_ring_sizes(const rssm_dims* d, int is_gdn, size_t out[4]) {
 }
 
 extern "C" int rssm_probe_copy(void* dst, const void* src, size_t bytes, void* stream) {
-  if (!dst || !src || bytes == 0 || bytes % 16 != 0) return RSSM_EINVAL;
+  if (!dst || !src || bytes == 0 || bytes % 16 != 0 || !rssm_host::aligned16(static_cast<const char*>(dst), static_cast<const char*>(src)))
+    return RSSM_EINVAL;
   rssm::CopyParams p{static_cast<float4*>(dst), static_cast<const float4*>(src), bytes / 16};
   const size_t per_block = (size_t)rssm::kBlock * rssm::kProbeUnroll;
   const size_t want = (p.n16 + per_block - 1) / per_block;
@@ -98,7 +99,8 @@ extern "C" size_t rssm_probe_read_sink_floats(size_t bytes) {
 }
 
 extern "C" int rssm_probe_read(const void* src, size_t bytes, float* sink, void* stream) {
-  if (!src || !sink || bytes == 0 || bytes % 16 != 0) return RSSM_EINVAL;
+  if (!src || !sink || bytes == 0 || bytes % 16 != 0 || !rssm_host::aligned16(static_cast<const char*>(src), sink))
+    return RSSM_EINVAL;
   rssm::ReadParams p{static_cast<const float4*>(src), sink, bytes / 16};
   const dim3 grid((unsigned)rssm_probe_read_sink_floats(bytes));
   return rssm_host::launch(rssm::probe_read_kernel, grid, dim3(rssm::kBlock), stream, p);

@@ -364,13 +364,23 @@ inline bool conv_shape_supported(const rssm_dims* d) {
   return ring_shape_supported(d) && d->state_dim == 128;
 }
 
+// Every array argument is 16-byte aligned (the kernels move 16-byte chunks;
+// hipMalloc returns 256-byte aligned memory); null pointers pass here and are
+// checked where they are required.
+inline bool aligned16() { return true; }
+template <typename T, typename... Rest>
+inline bool aligned16(const T* p, Rest... rest) {
+  return reinterpret_cast<uintptr_t>(p) % 16 == 0 && aligned16(rest...);
+}
+
 inline bool meta_ok(const rssm_ring* r) {
   return r != nullptr && r->meta != nullptr && reinterpret_cast<uintptr_t>(r->meta) % 128 == 0 &&
-         (r->slots == nullptr || r->rows >= 1);
+         (r->slots == nullptr || r->rows >= 1) && aligned16(r->slots) &&
+         reinterpret_cast<uintptr_t>(r->err) % 4 == 0;
 }
 
 inline bool ring_ok(const rssm_ring* r) {
-  return meta_ok(r) && r->vu != nullptr && r->k != nullptr;
+  return meta_ok(r) && r->vu != nullptr && r->k != nullptr && aligned16(r->vu, r->k);
 }
 
 }  // namespace rssm_host

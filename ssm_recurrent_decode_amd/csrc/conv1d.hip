@@ -63,7 +63,8 @@ __global__ __launch_bounds__(kBlock) void conv1d_update_w4_kernel(ConvParams p) 
 extern "C" int causal_conv1d_update(int32_t batch, int32_t channels, int32_t width,
                                     uint16_t* conv_state, const uint16_t* x, const uint16_t* weight,
                                     float* out, void* stream) {
-  if (batch < 1 || channels < 1 || width < 2 || !conv_state || !x || !weight || !out)
+  if (batch < 1 || channels < 1 || width < 2 || !conv_state || !x || !weight || !out ||
+      !rssm_host::aligned16(conv_state, x, weight, out))
     return RSSM_EINVAL;
   if (width != 4 || channels % 2 != 0) return RSSM_ENOTSUP;
   rssm::ConvParams p{conv_state, x, weight, out, batch, channels};

@@ -192,7 +192,9 @@ GdnReplayParams make_gdn_params(const rssm_dims* d, float* state0, rssm_ring* ri
 extern "C" int gdn_decode_step(const rssm_dims* dims, float* state, const uint16_t* v,
                                const uint16_t* k, const uint16_t* q, const float* g,
                                const float* beta, float* y, void* stream) {
-  if (!rssm_host::dims_ok(dims) || !state || !v || !k || !q || !g || !beta || !y) return RSSM_EINVAL;
+  if (!rssm_host::dims_ok(dims) || !state || !v || !k || !q || !g || !beta || !y ||
+      !rssm_host::aligned16(state, v, k, q, g, beta, y))
+    return RSSM_EINVAL;
   if (!rssm_host::shape_supported(dims) || (dims->flags & RSSM_F_Y_BF16)) return RSSM_ENOTSUP;
   GdnStdParams p{state, v, k, q, g, beta, y, dims->nheads, dims->ngroups};
   const dim3 grid(dims->batch * dims->nheads);
@@ -210,7 +212,7 @@ int gdn_verify_common(const rssm_dims* dims, int32_t T, float* state0, rssm_ring
                       const uint16_t* v, const uint16_t* k, const uint16_t* q, const float* g,
                       const float* beta, float* y, int32_t* flushed, void* stream) {
   if (!rssm_host::dims_ok(dims) || !rssm_host::ring_ok(ring) || !state0 || !v || !k || !q ||
-      !g || !beta || !y)
+      !g || !beta || !y || !rssm_host::aligned16(state0, v, k, q, g, beta, y, flushed))
     return RSSM_EINVAL;
   if (T < 1 || dims->capacity < 2 * T) return RSSM_EINVAL;
   if (!rssm_host::ring_shape_supported(dims) || T > kMaxT) return RSSM_ENOTSUP;
@@ -243,7 +245,7 @@ extern "C" int gdn_replay_commit_verify_T(const rssm_dims* dims, int32_t T, floa
                                           const int32_t* accepted, const uint16_t* v, const uint16_t* k,
                                           const uint16_t* q, const float* g, const float* beta, float* y,
                                           int32_t* flushed, void* stream) {
-  if (!accepted) return RSSM_EINVAL;
+  if (!accepted || !rssm_host::aligned16(accepted)) return RSSM_EINVAL;
   return gdn_verify_common(dims, T, state0, ring, accepted, v, k, q, g, beta, y, flushed, stream);
 }
 
@@ -252,7 +254,7 @@ extern "C" int gdn_replay_append_decode(const rssm_dims* dims, float* state0, rs
                                         const float* g, const float* beta, float* y, int32_t* flushed,
                                         void* stream) {
   if (!rssm_host::dims_ok(dims) || !rssm_host::ring_ok(ring) || !state0 || !v || !k || !q ||
-      !g || !beta || !y)
+      !g || !beta || !y || !rssm_host::aligned16(state0, v, k, q, g, beta, y, flushed))
     return RSSM_EINVAL;
   if (dims->capacity < 1) return RSSM_EINVAL;
   if (!rssm_host::ring_shape_supported(dims)) return RSSM_ENOTSUP;
@@ -272,7 +274,9 @@ extern "C" int gdn_replay_append_decode(const rssm_dims* dims, float* state0, rs
 
 extern "C" int gdn_replay_flush(const rssm_dims* dims, float* state0, rssm_ring* ring,
                                 const int32_t* mask, void* stream) {
-  if (!rssm_host::dims_ok(dims) || !rssm_host::ring_ok(ring) || !state0) return RSSM_EINVAL;
+  if (!rssm_host::dims_ok(dims) || !rssm_host::ring_ok(ring) || !state0 ||
+      !rssm_host::aligned16(state0, mask))
+    return RSSM_EINVAL;
   if (dims->capacity < 1) return RSSM_EINVAL;
   if (!rssm_host::ring_shape_supported(dims)) return RSSM_ENOTSUP;
   GdnReplayParams p = make_gdn_params(dims, state0, ring);

@@ -280,7 +280,8 @@ ReplayParams make_replay_params(const rssm_dims* d, float* state0, rssm_ring* ri
 extern "C" int ssm_decode_step(const rssm_dims* dims, float* state, const uint16_t* v,
                                const uint16_t* k, const uint16_t* q, const float* dt,
                                const float* dt_bias, const float* A, float* y, void* stream) {
-  if (!rssm_host::dims_ok(dims) || !state || !v || !k || !q || !dt || !dt_bias || !A || !y)
+  if (!rssm_host::dims_ok(dims) || !state || !v || !k || !q || !dt || !dt_bias || !A || !y ||
+      !rssm_host::aligned16(state, v, k, q, dt, dt_bias, A, y))
     return RSSM_EINVAL;
   if (!rssm_host::shape_supported(dims) || (dims->flags & RSSM_F_Y_BF16)) return RSSM_ENOTSUP;
   StdParams p{state, v, k, q, dt, dt_bias, A, y, dims->nheads, dims->ngroups};
@@ -301,7 +302,7 @@ extern "C" int replay_append_decode(const rssm_dims* dims, float* state0, rssm_r
                                     const float* dt, const float* dt_bias, const float* A,
                                     float* y, int32_t* flushed, void* stream) {
   if (!rssm_host::dims_ok(dims) || !rssm_host::ring_ok(ring) || !state0 || !v || !k || !q ||
-      !dt || !dt_bias || !A || !y)
+      !dt || !dt_bias || !A || !y || !rssm_host::aligned16(state0, v, k, q, dt, dt_bias, A, y, flushed))
     return RSSM_EINVAL;
   if (dims->capacity < 1) return RSSM_EINVAL;
   if (!rssm_host::ring_shape_supported(dims)) return RSSM_ENOTSUP;
@@ -326,7 +327,8 @@ extern "C" int replay_append_decode_conv(const rssm_dims* dims, float* state0, r
                                          const float* dt_bias, const float* A, float* y,
                                          int32_t* flushed, void* stream) {
   if (!rssm_host::dims_ok(dims) || !rssm_host::ring_ok(ring) || !state0 || !conv_state_in ||
-      !conv_state_out || !xbc || !conv_w || !dt || !dt_bias || !A || !y)
+      !conv_state_out || !xbc || !conv_w || !dt || !dt_bias || !A || !y ||
+      !rssm_host::aligned16(state0, conv_state_in, conv_state_out, xbc, conv_w, dt, dt_bias, A, y, flushed))
     return RSSM_EINVAL;
   if (conv_state_in == conv_state_out || dims->capacity < 1) return RSSM_EINVAL;
   if (!rssm_host::conv_shape_supported(dims)) return RSSM_ENOTSUP;
@@ -346,7 +348,9 @@ extern "C" int replay_append_decode_conv(const rssm_dims* dims, float* state0, r
 
 extern "C" int replay_flush(const rssm_dims* dims, float* state0, rssm_ring* ring,
                             const int32_t* mask, void* stream) {
-  if (!rssm_host::dims_ok(dims) || !rssm_host::ring_ok(ring) || !state0) return RSSM_EINVAL;
+  if (!rssm_host::dims_ok(dims) || !rssm_host::ring_ok(ring) || !state0 ||
+      !rssm_host::aligned16(state0, mask))
+    return RSSM_EINVAL;
   if (dims->capacity < 1) return RSSM_EINVAL;
   if (!rssm_host::ring_shape_supported(dims)) return RSSM_ENOTSUP;
   ReplayParams p = make_replay_params(dims, state0, ring);
@@ -371,7 +375,7 @@ int verify_common(const rssm_dims* dims, int32_t T, float* state0, rssm_ring* ri
                   const uint16_t* v, const uint16_t* k, const uint16_t* q, const float* dt,
                   const float* dt_bias, const float* A, float* y, int32_t* flushed, void* stream) {
   if (!rssm_host::dims_ok(dims) || !rssm_host::ring_ok(ring) || !state0 || !v || !k || !q ||
-      !dt || !dt_bias || !A || !y)
+      !dt || !dt_bias || !A || !y || !rssm_host::aligned16(state0, v, k, q, dt, dt_bias, A, y, flushed))
     return RSSM_EINVAL;
   if (T < 1 || dims->capacity < 2 * T) return RSSM_EINVAL;
   if (!rssm_host::ring_shape_supported(dims) || T > kMaxT) return RSSM_ENOTSUP;
@@ -405,13 +409,14 @@ extern "C" int replay_commit_verify_T(const rssm_dims* dims, int32_t T, float* s
                                       const int32_t* accepted, const uint16_t* v, const uint16_t* k,
                                       const uint16_t* q, const float* dt, const float* dt_bias,
                                       const float* A, float* y, int32_t* flushed, void* stream) {
-  if (!accepted) return RSSM_EINVAL;
+  if (!accepted || !rssm_host::aligned16(accepted)) return RSSM_EINVAL;
   return verify_common(dims, T, state0, ring, accepted, v, k, q, dt, dt_bias, A, y, flushed, stream);
 }
 
 extern "C" int replay_rollback(const rssm_dims* dims, rssm_ring* ring, const int32_t* accepted,
                                void* stream) {
-  if (!rssm_host::dims_ok(dims) || !rssm_host::meta_ok(ring) || !accepted) return RSSM_EINVAL;
+  if (!rssm_host::dims_ok(dims) || !rssm_host::meta_ok(ring) || !accepted || !rssm_host::aligned16(accepted))
+    return RSSM_EINVAL;
   if (dims->capacity < 1) return RSSM_EINVAL;
   if (dims->capacity > kMaxL) return RSSM_ENOTSUP;
   PtrParams p{reinterpret_cast<float*>(ring->meta), ring->err, accepted, nullptr, ring->slots, ring->rows,
@@ -422,7 +427,7 @@ extern "C" int replay_rollback(const rssm_dims* dims, rssm_ring* ring, const int
 
 extern "C" int rssm_ring_reset(const rssm_dims* dims, rssm_ring* ring, const int32_t* mask,
                                void* stream) {
-  if (!rssm_host::dims_ok(dims) || !rssm_host::meta_ok(ring)) return RSSM_EINVAL;
+  if (!rssm_host::dims_ok(dims) || !rssm_host::meta_ok(ring) || !rssm_host::aligned16(mask)) return RSSM_EINVAL;
   if (dims->capacity < 1) return RSSM_EINVAL;
   if (dims->capacity > kMaxL) return RSSM_ENOTSUP;
   PtrParams p{reinterpret_cast<float*>(ring->meta), ring->err, nullptr, mask, ring->slots, ring->rows,
@@ -433,7 +438,8 @@ extern "C" int rssm_ring_reset(const rssm_dims* dims, rssm_ring* ring, const int
 
 extern "C" int rssm_ring_pointers(const rssm_dims* dims, const rssm_ring* ring, int32_t* head,
                                   int32_t* count, int32_t* pending, void* stream) {
-  if (!rssm_host::dims_ok(dims) || !rssm_host::meta_ok(ring)) return RSSM_EINVAL;
+  if (!rssm_host::dims_ok(dims) || !rssm_host::meta_ok(ring) || !rssm_host::aligned16(head, count, pending))
+    return RSSM_EINVAL;
   if (dims->capacity < 1) return RSSM_EINVAL;
   if (dims->capacity > kMaxL) return RSSM_ENOTSUP;
   PtrViewParams p{reinterpret_cast<const float*>(ring->meta), ring->err, head, count, pending, ring->slots,

@@ -187,7 +187,8 @@ int launch_snapshot(int T, const SnapParams& p, const dim3& grid, void* stream) 
 int snapshot_common(const rssm_dims* dims, int32_t T, int32_t nslots, float* pool,
                     const int32_t* slot, const uint16_t* v, const uint16_t* k, const uint16_t* q,
                     bool gdn, SnapParams& p) {
-  if (!rssm_host::dims_ok(dims) || !pool || !slot || !v || !k || !q) return RSSM_EINVAL;
+  if (!rssm_host::dims_ok(dims) || !pool || !slot || !v || !k || !q || !rssm_host::aligned16(pool, slot, v, k, q))
+    return RSSM_EINVAL;
   if (T < 1 || nslots < T + 1) return RSSM_EINVAL;
   (void)gdn;
   if (!rssm_host::shape_supported(dims) || T > kMaxT || (dims->flags & RSSM_F_Y_BF16)) return RSSM_ENOTSUP;
@@ -211,7 +212,7 @@ extern "C" int ssm_snapshot_verify_T(const rssm_dims* dims, int32_t T, int32_t n
   SnapParams p{};
   const int rc = snapshot_common(dims, T, nslots, pool, slot, v, k, q, false, p);
   if (rc != RSSM_OK) return rc;
-  if (!dt || !dt_bias || !A || !y) return RSSM_EINVAL;
+  if (!dt || !dt_bias || !A || !y || !rssm_host::aligned16(dt, dt_bias, A, y)) return RSSM_EINVAL;
   p.gate = dt;
   p.dt_bias = dt_bias;
   p.A = A;
@@ -233,7 +234,7 @@ extern "C" int gdn_snapshot_verify_T(const rssm_dims* dims, int32_t T, int32_t n
   SnapParams p{};
   const int rc = snapshot_common(dims, T, nslots, pool, slot, v, k, q, true, p);
   if (rc != RSSM_OK) return rc;
-  if (!g || !beta || !y) return RSSM_EINVAL;
+  if (!g || !beta || !y || !rssm_host::aligned16(g, beta, y)) return RSSM_EINVAL;
   p.gate = g;
   p.beta = beta;
   p.y = y;
@@ -249,7 +250,9 @@ extern "C" int gdn_snapshot_verify_T(const rssm_dims* dims, int32_t T, int32_t n
 
 extern "C" int snapshot_commit(int32_t batch, int32_t T, int32_t nslots, int32_t* slot,
                                const int32_t* accepted, int32_t* err, void* stream) {
-  if (batch < 1 || T < 1 || nslots < T + 1 || !slot || !accepted) return RSSM_EINVAL;
+  if (batch < 1 || T < 1 || nslots < T + 1 || !slot || !accepted || !rssm_host::aligned16(slot, accepted) ||
+      reinterpret_cast<uintptr_t>(err) % 4 != 0)
+    return RSSM_EINVAL;
   CommitParams p{slot, accepted, err, batch, T, nslots};
   const dim3 grid((batch + kBlock - 1) / kBlock);
   return rssm_host::launch(snapshot_commit_kernel, grid, dim3(kBlock), stream, p);

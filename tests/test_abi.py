@@ -113,7 +113,7 @@ def test_host_validation_codes():
     r_nometa = _ring()
     r_nometa.meta = None
     assert lib.replay_flush(ctypes.byref(d), P, ctypes.byref(r_nometa), None, None) == EINVAL
-    # conv1d: only W = 4 and C % 4 == 0
+    # conv1d: only W = 4 and an even channel count
     assert lib.causal_conv1d_update(4, 3072, 3, P, P, P, P, None) == ENOTSUP
     assert lib.causal_conv1d_update(4, 3071, 4, P, P, P, P, None) == ENOTSUP
     assert lib.causal_conv1d_update(0, 3072, 4, P, P, P, P, None) == EINVAL
@@ -128,6 +128,31 @@ def test_host_validation_codes():
     r_odd = _ring()
     r_odd.meta = FAKE.value + 64
     assert lib.replay_rollback(ctypes.byref(d), ctypes.byref(r_odd), P, None) == EINVAL
+    # every array 16-byte aligned: a misaligned input, output, ring array or flag
+    # array is rejected before any launch
+    M = ctypes.c_void_p(FAKE.value + 8)
+    assert lib.ssm_decode_step(ctypes.byref(d), P, M, P, P, P, P, P, P, None) == EINVAL
+    assert lib.replay_append_decode(ctypes.byref(d), P, ctypes.byref(r), P, P, P, P, P, P, M, None, None) == EINVAL
+    assert lib.replay_append_decode(ctypes.byref(d), P, ctypes.byref(r), P, P, P, P, P, P, P, M, None) == EINVAL
+    assert lib.replay_verify_T(ctypes.byref(d), 2, M, ctypes.byref(r), P, P, P, P, P, P, P, None, None) == EINVAL
+    assert lib.replay_commit_verify_T(ctypes.byref(d), 2, P, ctypes.byref(r), M, P, P, P, P, P, P, P,
+                                      None, None) == EINVAL
+    assert lib.gdn_replay_verify_T(ctypes.byref(d), 2, P, ctypes.byref(r), P, P, M, P, P, P, None, None) == EINVAL
+    assert lib.gdn_replay_append_decode(ctypes.byref(d), P, ctypes.byref(r), P, P, P, P, M, P, None, None) == EINVAL
+    assert lib.replay_flush(ctypes.byref(d), P, ctypes.byref(r), M, None) == EINVAL
+    assert lib.replay_rollback(ctypes.byref(d), ctypes.byref(r), M, None) == EINVAL
+    assert lib.causal_conv1d_update(4, 3072, 4, P, P, M, P, None) == EINVAL
+    assert lib.snapshot_commit(4, 2, 3, M, P, None, None) == EINVAL
+    r_vu = _ring()
+    r_vu.vu = FAKE.value + 4
+    assert lib.replay_append_decode(ctypes.byref(d), P, ctypes.byref(r_vu), P, P, P, P, P, P, P, None,
+                                    None) == EINVAL
+    r_err = _ring()
+    r_err.err = FAKE.value + 2
+    assert lib.replay_rollback(ctypes.byref(d), ctypes.byref(r_err), P, None) == EINVAL
+    for fn, args in (("rssm_ring_pointers", (M, None, None)), ("rssm_ring_reset", (M,))):
+        assert getattr(lib, fn)(ctypes.byref(d), ctypes.byref(r), *args, None) == EINVAL
+    assert lib.rssm_probe_copy(M, P, 64, None) == EINVAL
     assert lib.rssm_ring_reset(ctypes.byref(d), ctypes.byref(r_odd), None, None) == EINVAL
     # the pointer view: an aligned record array, L within the build
     assert lib.rssm_ring_pointers(ctypes.byref(d), ctypes.byref(r_odd), P, P, P, None) == EINVAL
