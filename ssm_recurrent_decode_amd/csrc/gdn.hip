@@ -83,13 +83,14 @@ __global__ __launch_bounds__(kBlock) void gdn_step_kernel(GdnStdParams p) {
 
 // ======================================================= ReplaySSM GDN
 // Explicit GDN flush of the committed entries of masked requests.
-template <int D, int N>
+template <int D, int N, bool EAGER>
 __global__ __launch_bounds__(kBlock) void gdn_flush_kernel(GdnReplayParams p) {
   constexpr int NCT = N / 16;
   constexpr int RT = D / (16 * kWavesPerBlock);
   __shared__ float s_w[kMaxL];
   __shared__ float s_abar;
   __shared__ __attribute__((aligned(16))) uint16_t s_k[kMaxL * N];
+  __shared__ __attribute__((aligned(16))) float s_u[kMaxL * D];
 
   const int H = p.H, G = p.G, L = p.L;
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
@@ -102,7 +103,23 @@ __global__ __launch_bounds__(kBlock) void gdn_flush_kernel(GdnReplayParams p) {
   if (rb < 0) return;
   const size_t bh = (size_t)rb * H + h;
   float* rec = p.meta + bh * meta_words(L);  // this head's ring record
-  const RingPtr rp = unpack_ptr(*reinterpret_cast<const unsigned long long*>(rec + kMetaPtr));
+  // read per lane, so that the eager checkpoint loads below are issued before it arrives
+  const unsigned long long word = *reinterpret_cast<const unsigned long long*>(rec + kMetaPtr + opaque_zero());
+  // EAGER (no mask: every request that holds entries folds them): the checkpoint
+  // is requested before the pointer word is known, one memory round trip earlier
+  // (a request whose ring is empty reads it in vain).  With a mask it is requested
+  // only for requests that fold.
+  float* S0 = p.state0 + bh * D * N;
+  float4 s[RT][NCT];
+  if constexpr (EAGER) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int row = (wave * RT + rt) * 16 + r;
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) s[rt][ct] = ld_f4(S0 + row * N + ct * 16 + cq * 4);
+    }
+  }
+  const RingPtr rp = unpack_ptr(word);
   int head = rp.head, cnt = rp.count;
   int bad = 0;
   if (head >= L) {
@@ -115,9 +132,7 @@ __global__ __launch_bounds__(kBlock) void gdn_flush_kernel(GdnReplayParams p) {
   }
   if (cnt + rp.pending > L) bad |= RSSM_ERR_POINTERS;
   const int F = cnt;
-  float* S0 = p.state0 + bh * D * N;
-  float4 s[RT][NCT];
-  if (F > 0) {
+  if (!EAGER && F > 0) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const int row = (wave * RT + rt) * 16 + r;
@@ -125,21 +140,30 @@ __global__ __launch_bounds__(kBlock) void gdn_flush_kernel(GdnReplayParams p) {
       for (int ct = 0; ct < NCT; ++ct) s[rt][ct] = ld_f4(S0 + row * N + ct * 16 + cq * 4);
     }
   }
-  float uf[RT][kVJ];
+  // the F entries' corrections and keys into LDS by logical index, 16 bytes per
+  // thread, every load issued before the first one is waited for (one round trip)
+  constexpr int KCH = N / 8;  // 16-byte chunks of a key
+  constexpr int UP = (kMaxL * (D / 4) + kBlock - 1) / kBlock, KP = (kMaxL * KCH + kBlock - 1) / kBlock;
+  const int cpe = p.u_bf16 ? D / 8 : D / 4;  // 16-byte chunks of a cached correction
+  uint4 uc[UP], kc[KP];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int row = (wave * RT + rt) * 16 + r;
-#pragma unroll
-    for (int m = 0; m < kVJ; ++m) {
-      const int j = cq + 4 * m;
-      const size_t ua = ring_entry(rb, h, H, L, (head + j) % L, D) + row;
-      uf[rt][m] = (j < F) ? (p.u_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(p.ring_u)[ua]) : p.ring_u[ua])
-                          : 0.f;
+  for (int i = 0; i < UP; ++i) {
+    const int t = tid + i * kBlock, j = t / cpe;
+    if (j < F) {
+      const size_t e = ring_entry(rb, h, H, L, (head + j) % L, D);
+      uc[i] = p.u_bf16 ? ld_u4(reinterpret_cast<const uint16_t*>(p.ring_u) + e + (t % cpe) * 8)
+                       : *reinterpret_cast<const uint4*>(p.ring_u + e + (t % cpe) * 4);
     }
+  }
+#pragma unroll
+  for (int i = 0; i < KP; ++i) {
+    const int t = tid + i * kBlock, j = t / KCH;
+    if (j < F) kc[i] = ld_u4(p.ring_k + (((size_t)rb * G + g) * L + (head + j) % L) * N + (t % KCH) * 8);
   }
   if (wave == 0) {
     const int j = lane;
-    const float al = (j < F) ? rec[kMetaSlot + (head + j) % L] : 1.f;
+    const float al_rec = rec[kMetaSlot + (head + min(j, L - 1)) % L];  // read unconditionally
+    const float al = (j < F) ? al_rec : 1.f;
     float R = 1.f, P = 1.f;
     for (int m = 0; m < F; ++m) {
       const float am = __shfl(al, m, kWave);
@@ -149,12 +173,38 @@ __global__ __launch_bounds__(kBlock) void gdn_flush_kernel(GdnReplayParams p) {
     if (j < F) s_w[j] = R;
     if (lane == 0) s_abar = P;
   }
-  for (int t = tid; t < F * (N / 8); t += kBlock) {
-    const int j = t / (N / 8), o = (t % (N / 8)) * 8;
-    *reinterpret_cast<uint4*>(&s_k[j * N + o]) =
-        ld_u4(p.ring_k + (((size_t)rb * G + g) * L + (head + j) % L) * N + o);
+#pragma unroll
+  for (int i = 0; i < UP; ++i) {
+    const int t = tid + i * kBlock, j = t / cpe;
+    if (j < F) {
+      float* dst = &s_u[j * D];
+      if (p.u_bf16) {
+        const int o = (t % cpe) * 8;
+        *reinterpret_cast<float4*>(dst + o) =
+            make_float4(bf16_lo(uc[i].x), bf16_hi(uc[i].x), bf16_lo(uc[i].y), bf16_hi(uc[i].y));
+        *reinterpret_cast<float4*>(dst + o + 4) =
+            make_float4(bf16_lo(uc[i].z), bf16_hi(uc[i].z), bf16_lo(uc[i].w), bf16_hi(uc[i].w));
+      } else {
+        *reinterpret_cast<uint4*>(dst + (t % cpe) * 4) = uc[i];
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < KP; ++i) {
+    const int t = tid + i * kBlock, j = t / KCH;
+    if (j < F) *reinterpret_cast<uint4*>(&s_k[j * N + (t % KCH) * 8]) = kc[i];
   }
   __syncthreads();
+  float uf[RT][kVJ];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int row = (wave * RT + rt) * 16 + r;
+#pragma unroll
+    for (int m = 0; m < kVJ; ++m) {
+      const int j = cq + 4 * m;
+      uf[rt][m] = (j < F) ? s_u[j * D + row] : 0.f;
+    }
+  }
   if (F > 0) fold_and_store<D, N, RT, NCT, kVJ>(S0, s, s_abar, s_k, s_w, uf, F, wave, r, cq);
 
   if (tid == 0) {
@@ -272,6 +322,28 @@ extern "C" int gdn_replay_append_decode(const rssm_dims* dims, float* state0, rs
   return rssm_host::launch_gdn_window<128, 1, true>(p, dims->batch, stream);
 }
 
+namespace {
+
+// the flush instances of one mode: EAGER when no mask selects the requests
+template <bool EAGER>
+int launch_gdn_replay_flush(const rssm_dims* dims, const GdnReplayParams& p, void* stream) {
+  const dim3 grid(dims->batch * dims->nheads);
+  const bool d64 = dims->head_dim == 64;
+  switch (dims->state_dim) {
+    case 64:
+      return launch(d64 ? gdn_flush_kernel<64, 64, EAGER> : gdn_flush_kernel<128, 64, EAGER>, grid, dim3(kBlock),
+                    stream, p);
+    case 256:
+      return launch(d64 ? gdn_flush_kernel<64, 256, EAGER> : gdn_flush_kernel<128, 256, EAGER>, grid, dim3(kBlock),
+                    stream, p);
+    default:
+      return launch(d64 ? gdn_flush_kernel<64, 128, EAGER> : gdn_flush_kernel<128, 128, EAGER>, grid, dim3(kBlock),
+                    stream, p);
+  }
+}
+
+}  // namespace
+
 extern "C" int gdn_replay_flush(const rssm_dims* dims, float* state0, rssm_ring* ring,
                                 const int32_t* mask, void* stream) {
   if (!rssm_host::dims_ok(dims) || !rssm_host::ring_ok(ring) || !state0 ||
@@ -281,13 +353,6 @@ extern "C" int gdn_replay_flush(const rssm_dims* dims, float* state0, rssm_ring*
   if (!rssm_host::ring_shape_supported(dims)) return RSSM_ENOTSUP;
   GdnReplayParams p = make_gdn_params(dims, state0, ring);
   p.mask = mask;
-  const dim3 grid(dims->batch * dims->nheads);
-  const bool d64 = dims->head_dim == 64;
-  switch (dims->state_dim) {
-    case 64: return launch(d64 ? gdn_flush_kernel<64, 64> : gdn_flush_kernel<128, 64>, grid, dim3(kBlock), stream, p);
-    case 256:
-      return launch(d64 ? gdn_flush_kernel<64, 256> : gdn_flush_kernel<128, 256>, grid, dim3(kBlock), stream, p);
-    default:
-      return launch(d64 ? gdn_flush_kernel<64, 128> : gdn_flush_kernel<128, 128>, grid, dim3(kBlock), stream, p);
-  }
+  return mask == nullptr ? launch_gdn_replay_flush<true>(dims, p, stream)
+                         : launch_gdn_replay_flush<false>(dims, p, stream);
 }

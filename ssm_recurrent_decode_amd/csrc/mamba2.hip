@@ -82,13 +82,14 @@ __global__ __launch_bounds__(kBlock) void ssm_step_kernel(StdParams p) {
 }
 
 // Explicit flush of the committed entries of masked requests.
-template <int D, int N>
+template <int D, int N, bool EAGER>
 __global__ __launch_bounds__(kBlock) void replay_flush_kernel(ReplayParams p) {
   constexpr int NCT = N / 16;
   constexpr int RT = D / (16 * kWavesPerBlock);
   __shared__ float s_fw[kMaxL];
   __shared__ float s_fabar;
   __shared__ __attribute__((aligned(16))) uint16_t s_k[kMaxL * N];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v[kMaxL * D];
 
   const int H = p.H, G = p.G, L = p.L;
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
@@ -101,7 +102,23 @@ __global__ __launch_bounds__(kBlock) void replay_flush_kernel(ReplayParams p) {
   if (rb < 0) return;
   const size_t bh = (size_t)rb * H + h;
   float* rec = p.meta + bh * meta_words(L);  // this head's ring record
-  const RingPtr rp = unpack_ptr(*reinterpret_cast<const unsigned long long*>(rec + kMetaPtr));
+  // read per lane, so that the eager checkpoint loads below are issued before it arrives
+  const unsigned long long word = *reinterpret_cast<const unsigned long long*>(rec + kMetaPtr + opaque_zero());
+  // EAGER (no mask: every request that holds entries folds them): the checkpoint
+  // is requested before the pointer word is known, one memory round trip earlier
+  // (a request whose ring is empty reads it in vain).  With a mask it is requested
+  // only for requests that fold.
+  float* S0 = p.state0 + bh * D * N;
+  float4 s[RT][NCT];
+  if constexpr (EAGER) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int row = (wave * RT + rt) * 16 + r;
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) s[rt][ct] = ld_f4(S0 + row * N + ct * 16 + cq * 4);
+    }
+  }
+  const RingPtr rp = unpack_ptr(word);
   int head = rp.head, cnt = rp.count;
   int bad = 0;
   if (head >= L) {
@@ -114,9 +131,7 @@ __global__ __launch_bounds__(kBlock) void replay_flush_kernel(ReplayParams p) {
   }
   if (cnt + rp.pending > L) bad |= RSSM_ERR_POINTERS;
   const int F = cnt;
-  float* S0 = p.state0 + bh * D * N;
-  float4 s[RT][NCT];
-  if (F > 0) {
+  if (!EAGER && F > 0) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const int row = (wave * RT + rt) * 16 + r;
@@ -124,23 +139,26 @@ __global__ __launch_bounds__(kBlock) void replay_flush_kernel(ReplayParams p) {
       for (int ct = 0; ct < NCT; ++ct) s[rt][ct] = ld_f4(S0 + row * N + ct * 16 + cq * 4);
     }
   }
-  float vj[RT][kVJ];
+  // the F entries' values and keys into LDS by logical index, 16 bytes per thread,
+  // every load issued before the first one is waited for (one round trip)
+  constexpr int VCH = D / 8, KCH = N / 8;  // 16-byte chunks of a value, of a key
+  constexpr int VP = (kMaxL * VCH + kBlock - 1) / kBlock, KP = (kMaxL * KCH + kBlock - 1) / kBlock;
+  uint4 vc[VP], kc[KP];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int row = (wave * RT + rt) * 16 + r;
+  for (int i = 0; i < VP; ++i) {
+    const int t = tid + i * kBlock, j = t / VCH;
+    if (j < F) vc[i] = ld_u4(p.ring_v + ring_entry(rb, h, H, L, (head + j) % L, D) + (t % VCH) * 8);
+  }
 #pragma unroll
-    for (int m = 0; m < kVJ; ++m) {
-      const int j = cq + 4 * m;
-      vj[rt][m] = (j < F) ? bf16_to_f32(p.ring_v[ring_entry(rb, h, H, L, (head + j) % L, D) + row]) : 0.f;
-    }
+  for (int i = 0; i < KP; ++i) {
+    const int t = tid + i * kBlock, j = t / KCH;
+    if (j < F) kc[i] = ld_u4(p.ring_k + (((size_t)rb * G + g) * L + (head + j) % L) * N + (t % KCH) * 8);
   }
   if (wave == 0) {
     const int j = lane;
-    float dl = 0.f, al = 1.f;
-    if (j < F) {
-      dl = rec[kMetaSlot + (head + j) % L];
-      al = expf(rec[kMetaA] * dl);
-    }
+    const float dl_rec = rec[kMetaSlot + (head + min(j, L - 1)) % L];  // read unconditionally
+    const float dl = (j < F) ? dl_rec : 0.f;
+    const float al = (j < F) ? expf(rec[kMetaA] * dl) : 1.f;
     float R = 1.f, P = 1.f;
     for (int m = 0; m < F; ++m) {
       const float am = __shfl(al, m, kWave);
@@ -150,12 +168,27 @@ __global__ __launch_bounds__(kBlock) void replay_flush_kernel(ReplayParams p) {
     if (j < F) s_fw[j] = dl * R;
     if (lane == 0) s_fabar = P;
   }
-  for (int t = tid; t < F * (N / 8); t += kBlock) {
-    const int j = t / (N / 8), o = (t % (N / 8)) * 8;
-    *reinterpret_cast<uint4*>(&s_k[j * N + o]) =
-        ld_u4(p.ring_k + (((size_t)rb * G + g) * L + (head + j) % L) * N + o);
+#pragma unroll
+  for (int i = 0; i < VP; ++i) {
+    const int t = tid + i * kBlock, j = t / VCH;
+    if (j < F) *reinterpret_cast<uint4*>(&s_v[j * D + (t % VCH) * 8]) = vc[i];
+  }
+#pragma unroll
+  for (int i = 0; i < KP; ++i) {
+    const int t = tid + i * kBlock, j = t / KCH;
+    if (j < F) *reinterpret_cast<uint4*>(&s_k[j * N + (t % KCH) * 8]) = kc[i];
   }
   __syncthreads();
+  float vj[RT][kVJ];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int row = (wave * RT + rt) * 16 + r;
+#pragma unroll
+    for (int m = 0; m < kVJ; ++m) {
+      const int j = cq + 4 * m;
+      vj[rt][m] = (j < F) ? bf16_to_f32(s_v[j * D + row]) : 0.f;
+    }
+  }
   if (F > 0) fold_and_store<D, N, RT, NCT, kVJ>(S0, s, s_fabar, s_k, s_fw, vj, F, wave, r, cq);
 
   if (tid == 0) {
@@ -346,6 +379,28 @@ extern "C" int replay_append_decode_conv(const rssm_dims* dims, float* state0, r
   return rssm_host::launch_window<128, 1, true, true>(p, dims->batch, stream);
 }
 
+namespace {
+
+// the flush instances of one mode: EAGER when no mask selects the requests
+template <bool EAGER>
+int launch_replay_flush(const rssm_dims* dims, const ReplayParams& p, void* stream) {
+  const dim3 grid(dims->batch * dims->nheads);
+  const bool d64 = dims->head_dim == 64;
+  switch (dims->state_dim) {
+    case 64:
+      return launch(d64 ? replay_flush_kernel<64, 64, EAGER> : replay_flush_kernel<128, 64, EAGER>, grid, dim3(kBlock),
+                    stream, p);
+    case 256:
+      return launch(d64 ? replay_flush_kernel<64, 256, EAGER> : replay_flush_kernel<128, 256, EAGER>, grid, dim3(kBlock),
+                    stream, p);
+    default:
+      return launch(d64 ? replay_flush_kernel<64, 128, EAGER> : replay_flush_kernel<128, 128, EAGER>, grid, dim3(kBlock),
+                    stream, p);
+  }
+}
+
+}  // namespace
+
 extern "C" int replay_flush(const rssm_dims* dims, float* state0, rssm_ring* ring,
                             const int32_t* mask, void* stream) {
   if (!rssm_host::dims_ok(dims) || !rssm_host::ring_ok(ring) || !state0 ||
@@ -355,18 +410,7 @@ extern "C" int replay_flush(const rssm_dims* dims, float* state0, rssm_ring* rin
   if (!rssm_host::ring_shape_supported(dims)) return RSSM_ENOTSUP;
   ReplayParams p = make_replay_params(dims, state0, ring);
   p.mask = mask;
-  const dim3 grid(dims->batch * dims->nheads);
-  const bool d64 = dims->head_dim == 64;
-  switch (dims->state_dim) {
-    case 64:
-      return launch(d64 ? replay_flush_kernel<64, 64> : replay_flush_kernel<128, 64>, grid, dim3(kBlock), stream, p);
-    case 256:
-      return launch(d64 ? replay_flush_kernel<64, 256> : replay_flush_kernel<128, 256>, grid, dim3(kBlock), stream,
-                    p);
-    default:
-      return launch(d64 ? replay_flush_kernel<64, 128> : replay_flush_kernel<128, 128>, grid, dim3(kBlock), stream,
-                    p);
-  }
+  return mask == nullptr ? launch_replay_flush<true>(dims, p, stream) : launch_replay_flush<false>(dims, p, stream);
 }
 
 namespace {
