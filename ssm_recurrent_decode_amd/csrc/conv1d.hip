@@ -52,10 +52,15 @@ __global__ __launch_bounds__(kBlock) void conv1d_update_w4_kernel(ConvParams p) 
     ns[3 * m + 1] = win[2];
     ns[3 * m + 2] = win[3];
   }
-  *reinterpret_cast<float2*>(p.out + (size_t)b * p.C + c0) = make_float2(o[0], o[1]);
-  st[0] = ns[0] | (ns[1] << 16);
-  st[1] = ns[2] | (ns[3] << 16);
-  st[2] = ns[4] | (ns[5] << 16);
+  // written once and not read again by this launch: non-temporal stores, which keep
+  // them from displacing the following kernel's lines in L2 (3.60 vs 3.76 us for the
+  // update, 59.1 vs 59.7 us for the layer step with the append after it)
+  float* op = p.out + (size_t)b * p.C + c0;
+  __builtin_nontemporal_store(o[0], op);
+  __builtin_nontemporal_store(o[1], op + 1);
+  __builtin_nontemporal_store(ns[0] | (ns[1] << 16), st);
+  __builtin_nontemporal_store(ns[2] | (ns[3] << 16), st + 1);
+  __builtin_nontemporal_store(ns[4] | (ns[5] << 16), st + 2);
 }
 
 }  // namespace rssm
