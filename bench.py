@@ -298,14 +298,16 @@ def _draft_inputs(synth, sh, seed, cfg_id, r, gdn):
 
 
 def _row_verify(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, rounds=64, warm=16, T=None,
-                with_standard=True, flags=0):
+                with_standard=True, flags=0, G=None):
     """Speculative verify rounds (verify kernel + device-side rollback) on two
     rotated layer instances.  A first pass records the committed count every
     request had before each round; the rings are reset and the same sequence is
-    replayed with HIP events around every launch.  T overrides the workload's
-    draft window."""
+    replayed with HIP events around every launch.  T and G override the
+    workload's draft window and group count."""
     wl = synth.WORKLOADS[cfg_id]
     sh, seed = (wl.shape if T is None else wl.shape.with_(T=T)), wl.cfg_seed
+    if G is not None:
+        sh = sh.with_(ngroups=G)
     B, H, D, N, G, L, T = sh.batch, sh.nheads, sh.head_dim, sh.state_dim, sh.ngroups, sh.capacity, sh.T
     NLr, P, R = 2, 8, warm + rounds
     dims = rd.Dims(B, H, D, N, G, L, flags=flags)
@@ -1134,6 +1136,10 @@ def _rows(torch, np, rd, synth, traffic, dev, stream, only=None):
     rows = [
         ("speculative_verify", lambda: _row_verify(torch, np, rd, synth, traffic, dev, stream, 2, False)),
         ("gdn_speculative_verify", lambda: _row_verify(torch, np, rd, synth, traffic, dev, stream, 4, True)),
+        # the speculative workload with keys and queries shared by groups of four
+        # heads instead of all 32 (a sensitivity run of the group count)
+        ("speculative_verify_groups8", lambda: _row_verify(torch, np, rd, synth, traffic, dev, stream, 2, False,
+                                                           rounds=32, G=8)),
         ("capacity_sweep", lambda: _row_sweep(torch, np, rd, synth, traffic, dev, stream)),
         ("explicit_flush", lambda: _row_flush(torch, np, rd, synth, traffic, dev, stream)),
         ("gdn_append_decode", lambda: _row_gdn_append(torch, np, rd, synth, traffic, dev, stream)),
