@@ -385,7 +385,7 @@ def test_gdn_replay_append_decode_small(d, G, L):
     assert rel_err(state0.cpu().numpy(), S) <= S_TOL
 
 
-@pytest.mark.parametrize("d,G,L", [(64, 1, 8), (64, 2, 5), (128, 4, 16)])
+@pytest.mark.parametrize("d,G,L", [(64, 1, 8), (64, 2, 5), (128, 4, 16), (64, 8, 24), (128, 2, 32)])
 def test_replay_append_decode_conv_small(d, G, L):
     """Fused front-end: conv1d + SiLU over the xBC channels gives v, k, q (bf16),
     then the ReplaySSM step.  y every step against the oracle conv -> bf16 ->
