@@ -150,3 +150,78 @@ def test_gdn_append_bf16_ring():
             if fb:
                 assert rel_err(state0[b].cpu().numpy(), reqs[b].S0) <= GDN_TOL, (t, b)
     assert int(ring.err.item()) == 0
+
+
+def test_fused_front_end_bf16_y():
+    """The fused front-end with bf16 outputs: y within 1e-3 + 2^-8 of the oracle's
+    conv -> bf16 -> recurrence; the conv state still bit-exact; the checkpoint at
+    every flush within the fp32 bar (the outputs' precision does not reach it)."""
+    from oracle import conv1d as o_conv
+    base = synth.WORKLOADS[0]
+    d, G, L = 64, 2, 8
+    sh = base.shape.with_(head_dim=d, ngroups=G, capacity=L)
+    B, H, N = sh.batch, sh.nheads, sh.state_dim
+    C = H * d + 2 * G * N
+    seed, steps = base.cfg_seed, 2 * L + 3
+    A, dt_bias = synth.mamba2_head_params(sh, seed, 0)
+    S0 = synth.state0(sh, seed, 0)
+    cs_bits, w_bits = synth.conv_layer(B, C, 4, seed, 0)
+    dims = rd.Dims(B, H, d, N, G, L, flags=_lib.RSSM_F_Y_BF16)
+    ring = rd.Ring(dims)
+    state0 = dev_f32(S0)
+    cs = [dev_bf16(cs_bits), dev_bf16(cs_bits)]
+    w = dev_bf16(w_bits)
+    y = torch.empty(B, H, d, dtype=torch.bfloat16, device="cuda")
+    S = S0.astype(np.float64)
+    cs64, W64 = synth.bf16_bits_to_f64(cs_bits), synth.bf16_bits_to_f64(w_bits)
+    for t in range(steps):
+        x_bits = synth.conv_step_input(B, C, seed, 0, t)
+        dt = synth.mamba2_step_inputs(sh, seed, 0, t)["dt"]
+        cin, cout = cs[t % 2], cs[(t + 1) % 2]
+        rd.replay_append_decode_conv(dims, state0, ring, cin, cout, dev_bf16(x_bits), w, dev_f32(dt),
+                                     dev_f32(dt_bias), dev_f32(A), y)
+        out, cs64 = o_conv.update(cs64, synth.bf16_bits_to_f64(x_bits), W64)
+        v, k, q = o_conv.split_xbc(o_conv.round_bf16(out), H, d, G, N)
+        delta, a = o_m2.step_size_and_decay(dt.astype(np.float64), dt_bias.astype(np.float64),
+                                            A.astype(np.float64))
+        S, y_ref = o_m2.standard_step(S, v, k, q, delta, a, G)
+        assert rel_err(_y_f64(y), y_ref) <= Y_TOL_BF16, t
+        got = synth.bf16_bits_to_f64(cout.view(torch.int16).cpu().numpy().view(np.uint16))
+        assert np.array_equal(got, cs64), t
+        if (t + 1) % L == 0:
+            assert rel_err(state0.cpu().numpy(), S) <= S_TOL, t
+    assert int(ring.err.item()) == 0
+
+
+def test_commit_verify_bf16_y():
+    """One launch per round with bf16 outputs (Mamba-2, T = 4): every draft's y
+    within 1e-3 + 2^-8, the committed state after the final commit and flush
+    within the fp32 bar."""
+    from oracle import replay as o_rep
+    base = synth.WORKLOADS[2]
+    sh = base.shape.with_(batch=5, capacity=16, T=4)
+    B, H, D, N, G, L, T = sh.batch, sh.nheads, sh.head_dim, sh.state_dim, sh.ngroups, sh.capacity, sh.T
+    seed, R = base.cfg_seed, 14
+    A, dt_bias = synth.mamba2_head_params(sh, seed, 2)
+    S0 = synth.state0(sh, seed, 2)
+    acc = synth.accept_draws(seed, 2, R, B, T)
+    dims = rd.Dims(B, H, D, N, G, L, flags=_lib.RSSM_F_Y_BF16)
+    ring = rd.Ring(dims)
+    state0 = dev_f32(S0)
+    y = torch.empty(B, T, H, D, dtype=torch.bfloat16, device="cuda")
+    S = S0.astype(np.float64)
+    prev = dev_i32(np.zeros(B, int))
+    scheds = [o_rep.pointer_schedule_spec(L, T, acc[:, b]) for b in range(B)]
+    for r in range(R):
+        st = synth.mamba2_step_inputs(sh, seed, 2, r)
+        rd.replay_commit_verify_T(dims, T, state0, ring, prev, dev_bf16(st["v"]), dev_bf16(st["k"]),
+                                  dev_bf16(st["q"]), dev_f32(st["dt"]), dev_f32(dt_bias), dev_f32(A), y)
+        y_ref, S = o_m2.spec_round_snapshot(S, mamba2_step_f64(st), dt_bias.astype(np.float64),
+                                            A.astype(np.float64), G, acc[r])
+        assert rel_err(_y_f64(y), y_ref) <= Y_TOL_BF16, r
+        prev = dev_i32(acc[r])
+    rd.replay_rollback(dims, ring, prev)
+    assert ring.count.cpu().tolist() == [scheds[b][R - 1][4] for b in range(B)]
+    rd.replay_flush(dims, state0, ring)
+    assert rel_err(state0.cpu().numpy(), S) <= S_TOL
+    assert int(ring.err.item()) == 0
