@@ -316,7 +316,9 @@ int replay_rollback(const rssm_dims* dims, rssm_ring* ring, const int32_t* accep
  * "device-side commit and rollback": the commit stays on the device; here it
  * also shares the verify's launch).  Requests with no pending drafts ignore
  * accepted[b].  The last window of a run is committed with replay_rollback.
- *   accepted int32 [B] (device): the previous window's accepted drafts
+ *   accepted int32 [B] (device): the previous window's accepted drafts of the
+ *            request at batch entry b of this call (with a slot map: of row
+ *            slots[b], wherever that request sat in the previous call)
  *   other arguments as replay_verify_T
  */
 int replay_commit_verify_T(const rssm_dims* dims, int32_t T, float* state0, rssm_ring* ring,

@@ -208,3 +208,49 @@ def test_slot_outside_pool_is_skipped_and_flagged():
     ring.use_slots(None)
     assert ring.count.cpu().tolist() == [0, 0, 1, 0, 0, 0, 0]
     assert torch.equal(state0, before)
+
+
+def test_pooled_commit_verify():
+    """One launch per round on pooled rows whose batch positions change every call:
+    accepted[b] carries the previous window of the request now at position b."""
+    base = synth.WORKLOADS[2]
+    sh = base.shape.with_(batch=4, nheads=8, capacity=16, T=4)
+    seed, R, T = base.cfg_seed, 18, 4
+    A, dt_bias = synth.mamba2_head_params(sh, seed, 2)
+    S0 = _pool_state(sh, seed, 2)
+    acc = synth.accept_draws(seed, 2, R, sh.batch, T)
+    dims = _dims(sh)
+    ring = rd.Ring(dims, rows=ROWS)
+    state0 = dev_f32(S0)
+    untouched = state0.clone()
+    y = torch.empty(sh.batch, T, sh.nheads, sh.head_dim, device="cuda")
+    S = {r: S0[r:r + 1].astype(np.float64) for r in USED}
+    last = {r: 0 for r in USED}                   # each row's window awaiting its commit
+    for rnd in range(R):
+        mp = MAPS[rnd % len(MAPS)]
+        ring.use_slots(dev_i32(np.array(mp)))
+        prev = np.array([last[r] if r >= 0 else 0 for r in mp], dtype=np.int32)
+        st = synth.mamba2_step_inputs(sh, seed, 2, rnd)
+        y.fill_(float("nan"))
+        rd.replay_commit_verify_T(dims, T, state0, ring, dev_i32(prev), dev_bf16(st["v"]), dev_bf16(st["k"]),
+                                  dev_bf16(st["q"]), dev_f32(st["dt"]), dev_f32(dt_bias), dev_f32(A), y)
+        s64 = mamba2_step_f64(st)
+        yh = y.cpu().numpy()
+        for b, r in enumerate(mp):
+            if r < 0:
+                assert np.isnan(yh[b]).all()
+                continue
+            y_ref, S[r] = o_m2.spec_round_snapshot(S[r], _sub(s64, b, True), dt_bias.astype(np.float64),
+                                                   A.astype(np.float64), sh.ngroups, acc[rnd, b:b + 1])
+            assert rel_err(yh[b], y_ref[0]) <= Y_TOL, (rnd, b)
+            last[r] = int(acc[rnd, b])
+    mp = MAPS[0]
+    ring.use_slots(dev_i32(np.array(mp)))
+    rd.replay_rollback(dims, ring, dev_i32(np.array([last[r] if r >= 0 else 0 for r in mp], dtype=np.int32)))
+    rd.replay_flush(dims, state0, ring)
+    ring.use_slots(None)
+    assert int(ring.err.item()) == 0
+    for r in USED:
+        assert rel_err(state0[r].cpu().numpy(), S[r][0]) <= S_TOL
+    for r in set(range(ROWS)) - set(USED):
+        assert torch.equal(state0[r], untouched[r])
