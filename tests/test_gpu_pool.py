@@ -254,3 +254,54 @@ def test_pooled_commit_verify():
         assert rel_err(state0[r].cpu().numpy(), S[r][0]) <= S_TOL
     for r in set(range(ROWS)) - set(USED):
         assert torch.equal(state0[r], untouched[r])
+
+
+def test_pooled_fused_front_end():
+    """The fused front-end on pooled rows: the conv states live in the pool's rows
+    (ping-pong buffers), the tokens at the batch positions of each call."""
+    from oracle import conv1d as o_conv
+    base = synth.WORKLOADS[0]
+    sh = base.shape.with_(batch=4, nheads=8, ngroups=2, capacity=8)
+    B, H, D, N, G, L = sh.batch, sh.nheads, sh.head_dim, sh.state_dim, sh.ngroups, sh.capacity
+    C = H * D + 2 * G * N
+    seed, steps = base.cfg_seed, 2 * L + 3
+    A, dt_bias = synth.mamba2_head_params(sh, seed, 0)
+    S0 = _pool_state(sh, seed, 0)
+    cs_bits, w_bits = synth.conv_layer(ROWS, C, 4, seed, 0)
+    dims = _dims(sh)
+    ring = rd.Ring(dims, rows=ROWS)
+    state0 = dev_f32(S0)
+    untouched = state0.clone()
+    cs = [dev_bf16(cs_bits), dev_bf16(cs_bits)]
+    w = dev_bf16(w_bits)
+    y = torch.empty(B, H, D, device="cuda")
+    S = {r: S0[r:r + 1].astype(np.float64) for r in USED}
+    cs64 = {r: synth.bf16_bits_to_f64(cs_bits[r:r + 1]) for r in USED}
+    W64 = synth.bf16_bits_to_f64(w_bits)
+    for t in range(steps):
+        mp = MAPS[t % len(MAPS)]
+        ring.use_slots(dev_i32(np.array(mp)))
+        x_bits = synth.conv_step_input(B, C, seed, 0, t)
+        dt = synth.mamba2_step_inputs(sh, seed, 0, t)["dt"]
+        cin, cout = cs[t % 2], cs[(t + 1) % 2]
+        y.fill_(float("nan"))
+        rd.replay_append_decode_conv(dims, state0, ring, cin, cout, dev_bf16(x_bits), w, dev_f32(dt),
+                                     dev_f32(dt_bias), dev_f32(A), y)
+        yh = y.cpu().numpy()
+        got = cout.view(torch.int16).cpu().numpy().view(np.uint16)
+        x64 = synth.bf16_bits_to_f64(x_bits)
+        for b, r in enumerate(mp):
+            if r < 0:
+                assert np.isnan(yh[b]).all()
+                continue
+            out, cs64[r] = o_conv.update(cs64[r], x64[b:b + 1], W64)
+            v, k, q = o_conv.split_xbc(o_conv.round_bf16(out), H, D, G, N)
+            delta, a = o_m2.step_size_and_decay(dt[b:b + 1].astype(np.float64), dt_bias.astype(np.float64),
+                                                A.astype(np.float64))
+            S[r], y_ref = o_m2.standard_step(S[r], v, k, q, delta, a, G)
+            assert rel_err(yh[b], y_ref[0]) <= Y_TOL, (t, b)
+            assert np.array_equal(synth.bf16_bits_to_f64(got[r:r + 1]), cs64[r]), (t, r)
+    ring.use_slots(None)
+    assert int(ring.err.item()) == 0
+    for r in set(range(ROWS)) - set(USED):
+        assert torch.equal(state0[r], untouched[r])
