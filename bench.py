@@ -298,16 +298,20 @@ def _draft_inputs(synth, sh, seed, cfg_id, r, gdn):
 
 
 def _row_verify(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, rounds=64, warm=16, T=None,
-                with_standard=True, flags=0, G=None):
+                with_standard=True, flags=0, G=None, shape=None, light=False):
     """Speculative verify rounds (verify kernel + device-side rollback) on two
     rotated layer instances.  A first pass records the committed count every
     request had before each round; the rings are reset and the same sequence is
     replayed with HIP events around every launch.  T and G override the
-    workload's draft window and group count."""
+    workload's draft window and group count, `shape` any other of its sizes;
+    `light` times the verify rounds only (no commit-and-verify pass, no
+    fixed-pointer rounds, no standard step)."""
     wl = synth.WORKLOADS[cfg_id]
     sh, seed = (wl.shape if T is None else wl.shape.with_(T=T)), wl.cfg_seed
     if G is not None:
         sh = sh.with_(ngroups=G)
+    if shape:
+        sh = sh.with_(**shape)
     B, H, D, N, G, L, T = sh.batch, sh.nheads, sh.head_dim, sh.state_dim, sh.ngroups, sh.capacity, sh.T
     NLr, P, R = 2, 8, warm + rounds
     dims = rd.Dims(B, H, D, N, G, L, flags=flags)
@@ -374,6 +378,11 @@ def _row_verify(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, rounds=
     fl = np.array([counts[r] + 2 * T > L for r in range(warm, R)])
     round_s = (sum(v_us) + sum(r_us)) * 1e-6
     gbs = sum(byts) / (sum(v_us) * 1e-6) / 1e9
+    if light:
+        return {"batch": B, "nheads": H, "head_dim": D, "state_dim": N, "ngroups": G, "capacity": L, "T": T,
+                "verify_us": round(sum(v_us) / rounds, 3), "achieved_GBs": round(gbs, 1),
+                "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "alg_bytes_per_round": round(sum(byts) / rounds),
+                "flush_rate": round(float(fl.mean()), 4)}
     # the same rounds with each commit folded into the next verify launch
     # (commit-and-verify: one launch per round; the last window's commit is the
     # separate kernel, outside the timed rounds)
@@ -800,6 +809,25 @@ def _row_gdn_state_sizes(torch, np, rd, synth, traffic, dev, stream):
     return res
 
 
+def _row_verify_shapes(torch, np, rd, synth, traffic, dev, stream, rounds=24, warm=8):
+    """The speculative verify rows (T = 4, L = 16) at other head dims and state
+    sizes, the batch scaled so that every shape reads the same 512 MiB of
+    checkpoint per round: verify rounds only, two layer instances rotated."""
+    res = {"workload": "speculative verify, T=4, ring capacity 16, 32 heads, at head dim d and state size n "
+                       "(Mamba-2 with one group, Gated DeltaNet with one group per head), batch chosen so that "
+                       "B*32*d*n*4 bytes = 512 MiB; verify rounds only"}
+    cases = ((False, 2, 64, 64), (False, 2, 64, 128), (False, 2, 64, 256), (False, 2, 128, 128),
+             (False, 2, 128, 256), (True, 4, 128, 64), (True, 4, 64, 128), (True, 4, 128, 128),
+             (True, 4, 128, 256))
+    for gdn, cfg, d, n in cases:
+        B = (512 * 64 * 128) // (d * n)
+        print(f"[bench]   verify {'gdn' if gdn else 'mamba2'} d={d} n={n} B={B}", file=sys.stderr, flush=True)
+        res[f"{'gdn' if gdn else 'mamba2'}_d{d}_n{n}"] = _row_verify(
+            torch, np, rd, synth, traffic, dev, stream, cfg, gdn, rounds=rounds, warm=warm,
+            shape={"batch": B, "head_dim": d, "state_dim": n}, light=True)
+    return res
+
+
 def _row_fused_conv(torch, np, rd, synth, traffic, dev, stream):
     """The layer's front-end fused into the append: conv1d + SiLU over the xBC
     channels (C = H d + 2 G n = 4096 at the Nemotron-H-like shape) producing v, k, q
@@ -1148,6 +1176,7 @@ def _rows(torch, np, rd, synth, traffic, dev, stream, only=None):
         ("staggered_append_decode", lambda: _row_staggered(torch, np, rd, synth, traffic, dev, stream)),
         ("state_sizes", lambda: _row_state_sizes(torch, np, rd, synth, traffic, dev, stream)),
         ("gdn_state_sizes", lambda: _row_gdn_state_sizes(torch, np, rd, synth, traffic, dev, stream)),
+        ("verify_shapes", lambda: _row_verify_shapes(torch, np, rd, synth, traffic, dev, stream)),
         ("fused_front_end", lambda: _row_fused_conv(torch, np, rd, synth, traffic, dev, stream)),
         ("storage_precision", lambda: _row_precision(torch, np, rd, synth, traffic, dev, stream)),
         ("window_sweep", lambda: {"mamba2": _row_window(torch, np, rd, synth, traffic, dev, stream, 2, False),
