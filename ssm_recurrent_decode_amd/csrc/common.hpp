@@ -11,6 +11,10 @@
 // runs on the matrix cores straight from the registers the state was loaded into,
 // and a row's dot product with a vector needs only a two-step reduction over the
 // four lanes l, l^16, l^32, l^48 that share the row.
+//
+// Between HBM and that layout the state moves in the "line arrangement" (see
+// load_state_lines below): every load or store instruction covers whole 128-byte
+// lines, and it is non-temporal.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -148,6 +152,93 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
 __device__ __forceinline__ void st_f4(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
 __device__ __forceinline__ uint2 ld_u2(const uint16_t* p) { return *reinterpret_cast<const uint2*>(p); }
 __device__ __forceinline__ uint4 ld_u4(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// ---- a head's state between HBM and the tile layout
+// In the tile layout one instruction moves 16 rows x 64 bytes, half of every
+// 128-byte line it touches, and the other half comes with the next column tile.
+// The state is therefore moved in the line arrangement instead: each pair of
+// column tiles 2jj, 2jj + 1 (one 128-byte line per row) travels as two
+// instructions, A with rows 0..7 of the row tile and B with rows 8..15, each
+// covering its eight lines whole.  Lanes r < 8 carry the left halves (columns
+// 32jj + 4cq ..) of row r in A and of row r + 8 in B; lanes r >= 8 the right
+// halves (columns 32jj + 16 + 4cq ..) of row r - 8 in A and of row r in B.  One
+// exchange between lanes r and r ^ 8 (settle_pair) turns a pair into the tile
+// layout; the same exchange turns it back.  Loads and stores of the state are
+// non-temporal: a launch touches each state byte once.  Measured interleaved on
+// the same buffers, bit-identical results: append-decode -5.6 %, Mamba-2 verify
+// (B = 512, T = 4) -10 %, GDN verify (B = 256, d = 128, T = 4) -16 %, fused
+// front-end -4.7 % per launch against tile-layout transfers with plain loads and
+// stores; non-temporal loads in the tile layout were 8 % slower, and the line
+// arrangement with plain loads 1-4 % slower.
+__device__ __forceinline__ float4 ld_f4_nt(const float* p) {
+  const v4f t = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
+  return make_float4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ void st_f4_nt(float* p, float4 v) {
+  __builtin_nontemporal_store(v4f{v.x, v.y, v.z, v.w}, reinterpret_cast<v4f*>(p));
+}
+
+// old with the lanes of the banks in BANKS (groups of four lanes of each row of
+// 16: bank 0 = lanes 0..3, ...) replaced by src from the lane eight places away
+// in the same row
+template <int BANKS>
+__device__ __forceinline__ float ror8_into(float old, float src) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src), kDppRowRor8, 0xF,
+                                                    BANKS, false));
+}
+
+// A pair of column tiles between the line arrangement and the tile layout (the
+// map is its own inverse): lanes r >= 8 take b of lane r - 8 into a, lanes r < 8
+// take a of lane r + 8 into b.
+__device__ __forceinline__ void settle_pair(float4& a, float4& b) {
+  const float4 a0 = a, b0 = b;
+  a = make_float4(ror8_into<0xC>(a0.x, b0.x), ror8_into<0xC>(a0.y, b0.y), ror8_into<0xC>(a0.z, b0.z),
+                  ror8_into<0xC>(a0.w, b0.w));
+  b = make_float4(ror8_into<0x3>(b0.x, a0.x), ror8_into<0x3>(b0.y, a0.y), ror8_into<0x3>(b0.z, a0.z),
+                  ror8_into<0x3>(b0.w, a0.w));
+}
+
+// Row (within the row tile) and column of what lane (r, cq) moves in
+// instruction A of a pair; instruction B is eight rows further down.
+__device__ __forceinline__ int line_row(int r) { return r & 7; }
+__device__ __forceinline__ int line_col(int r, int cq) { return ((r & 8) ? 16 : 0) + cq * 4; }
+
+// Issue the loads of a head's d x n state (wave w: row tiles w * RT ..) in the
+// line arrangement; every pair must pass settle_pair before it is used.
+template <int N, int RT, int NCT>
+__device__ __forceinline__ void load_state_lines(float4 (&s)[RT][NCT], const float* S, int wave, int r, int cq) {
+  static_assert(NCT % 2 == 0, "pairs of column tiles");
+  // (addresses written as base + row offset + column offset: summing the two
+  // offsets first took more registers and made the GDN verify spill)
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int ra = (wave * RT + rt) * 16 + line_row(r), co = line_col(r, cq);
+#pragma unroll
+    for (int jj = 0; jj < NCT / 2; ++jj) {
+      s[rt][2 * jj] = ld_f4_nt(S + ra * N + 32 * jj + co);
+      s[rt][2 * jj + 1] = ld_f4_nt(S + (ra + 8) * N + 32 * jj + co);
+    }
+  }
+}
+
+// Every pair of a loaded state into the tile layout.
+template <int RT, int NCT>
+__device__ __forceinline__ void settle_state(float4 (&s)[RT][NCT]) {
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int jj = 0; jj < NCT / 2; ++jj) settle_pair(s[rt][2 * jj], s[rt][2 * jj + 1]);
+}
+
+// Store the pair of column tiles 2jj, 2jj + 1 of row tile `rowtile` given in the
+// tile layout (a = tile 2jj, b = tile 2jj + 1) as whole lines.
+template <int N>
+__device__ __forceinline__ void store_pair_lines(float* S, int rowtile, int jj, float4 a, float4 b, int r, int cq) {
+  settle_pair(a, b);
+  const int ra = rowtile * 16 + line_row(r), co = line_col(r, cq);
+  st_f4_nt(S + ra * N + 32 * jj + co, a);
+  st_f4_nt(S + (ra + 8) * N + 32 * jj + co, b);
+}
 
 __device__ __forceinline__ float dot4_bf16(float4 s, uint2 q) {
   return s.x * bf16_lo(q.x) + s.y * bf16_hi(q.x) + s.z * bf16_lo(q.y) + s.w * bf16_hi(q.y);
@@ -290,7 +381,8 @@ __device__ __forceinline__ void split_bf16x8(const float (&x)[8], u32x4_t& hi, u
 // (r, cq) handles entries j = cq + 4m, m < kMaxL / 4.
 constexpr int kVJ = kMaxL / 4;
 
-// Fold F cached entries into the checkpoint tiles held in registers and store them:
+// Fold F cached entries into the checkpoint tiles held in registers (tile layout)
+// and store them as whole lines:
 //   S_0 <- fabar S_0 + sum_{j<F} fw_j x_j k_j^T   (x = v for Mamba-2, u for GDN)
 // on the matrix cores (transposed tile product, K axis = ring entries).
 // sk: keys of entries 0..F-1 in LDS, row-major [j][N] bf16; fw: weights in LDS;
@@ -302,7 +394,6 @@ __device__ __forceinline__ void fold_and_store(float* S0, float4 (&s)[RT][NCT], 
                                                int r, int cq) {
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const int rowbase = (wave * RT + rt) * 16;
     float bop[VJ];
 #pragma unroll
     for (int ks = 0; ks < VJ; ++ks) {
@@ -310,16 +401,22 @@ __device__ __forceinline__ void fold_and_store(float* S0, float4 (&s)[RT][NCT], 
       bop[ks] = (j < F) ? fw[j] * vj[rt][ks] : 0.f;
     }
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      v4f acc = {fab * s[rt][ct].x, fab * s[rt][ct].y, fab * s[rt][ct].z, fab * s[rt][ct].w};
+    for (int jj = 0; jj < NCT / 2; ++jj) {
+      float4 o[2];
 #pragma unroll
-      for (int ks = 0; ks < VJ; ++ks) {
-        if (4 * ks >= F) break;  // uniform across the work-group
-        const int j = 4 * ks + cq;
-        const float aop = (j < F) ? bf16_to_f32(sk[j * N + ct * 16 + r]) : 0.f;
-        acc = mfma4(aop, bop[ks], acc);
+      for (int half = 0; half < 2; ++half) {
+        const int ct = 2 * jj + half;
+        v4f acc = {fab * s[rt][ct].x, fab * s[rt][ct].y, fab * s[rt][ct].z, fab * s[rt][ct].w};
+#pragma unroll
+        for (int ks = 0; ks < VJ; ++ks) {
+          if (4 * ks >= F) break;  // uniform across the work-group
+          const int j = 4 * ks + cq;
+          const float aop = (j < F) ? bf16_to_f32(sk[j * N + ct * 16 + r]) : 0.f;
+          acc = mfma4(aop, bop[ks], acc);
+        }
+        o[half] = make_float4(acc[0], acc[1], acc[2], acc[3]);
       }
-      st_f4(S0 + (rowbase + r) * N + ct * 16 + cq * 4, make_float4(acc[0], acc[1], acc[2], acc[3]));
+      store_pair_lines<N>(S0, wave * RT + rt, jj, o[0], o[1], r, cq);
     }
   }
 }

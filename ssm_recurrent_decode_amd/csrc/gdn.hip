@@ -36,13 +36,8 @@ __global__ __launch_bounds__(kBlock) void gdn_step_kernel(GdnStdParams p) {
   const int r = lane & 15, cq = lane >> 4;
 
   float* S = p.state + (size_t)wg * D * N;
-  float4 s[RT][NCT];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int row = (wave * RT + rt) * 16 + r;
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) s[rt][ct] = ld_f4(S + row * N + ct * 16 + cq * 4);
-  }
+  float4 s[RT][NCT];  // line arrangement until each pair is settled
+  load_state_lines<N, RT, NCT>(s, S, wave, r, cq);
   const uint16_t* kp = p.k + ((size_t)b * p.G + g) * N + cq * 4;
   const uint16_t* qp = p.q + ((size_t)b * p.G + g) * N + cq * 4;
   uint2 kk[NCT], qq[NCT];
@@ -62,19 +57,28 @@ __global__ __launch_bounds__(kBlock) void gdn_step_kernel(GdnStdParams p) {
     const int row = (wave * RT + rt) * 16 + r;
     float sk = 0.f;
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) sk += dot4_bf16(s[rt][ct], kk[ct]);
+    for (int jj = 0; jj < NCT / 2; ++jj) {
+      settle_pair(s[rt][2 * jj], s[rt][2 * jj + 1]);
+      sk += dot4_bf16(s[rt][2 * jj], kk[2 * jj]) + dot4_bf16(s[rt][2 * jj + 1], kk[2 * jj + 1]);
+    }
     sk = reduce_row4(sk);
     const float u = beta * (vr[rt] - alpha * sk);
     float acc = 0.f;
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      float4 x = s[rt][ct];
-      x.x = alpha * x.x + u * bf16_lo(kk[ct].x);
-      x.y = alpha * x.y + u * bf16_hi(kk[ct].x);
-      x.z = alpha * x.z + u * bf16_lo(kk[ct].y);
-      x.w = alpha * x.w + u * bf16_hi(kk[ct].y);
-      acc += dot4_bf16(x, qq[ct]);
-      st_f4(S + row * N + ct * 16 + cq * 4, x);
+    for (int jj = 0; jj < NCT / 2; ++jj) {
+      float4 xo[2];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int ct = 2 * jj + half;
+        float4 x = s[rt][ct];
+        x.x = alpha * x.x + u * bf16_lo(kk[ct].x);
+        x.y = alpha * x.y + u * bf16_hi(kk[ct].x);
+        x.z = alpha * x.z + u * bf16_lo(kk[ct].y);
+        x.w = alpha * x.w + u * bf16_hi(kk[ct].y);
+        acc += dot4_bf16(x, qq[ct]);
+        xo[half] = x;
+      }
+      store_pair_lines<N>(S, wave * RT + rt, jj, xo[0], xo[1], r, cq);
     }
     acc = reduce_row4(acc);
     if (cq == 0) p.y[(size_t)wg * D + row] = acc;
@@ -111,14 +115,7 @@ __global__ __launch_bounds__(kBlock) void gdn_flush_kernel(GdnReplayParams p) {
   // only for requests that fold.
   float* S0 = p.state0 + bh * D * N;
   float4 s[RT][NCT];
-  if constexpr (EAGER) {
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const int row = (wave * RT + rt) * 16 + r;
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) s[rt][ct] = ld_f4(S0 + row * N + ct * 16 + cq * 4);
-    }
-  }
+  if constexpr (EAGER) load_state_lines<N, RT, NCT>(s, S0, wave, r, cq);
   const RingPtr rp = unpack_ptr(word);
   int head = rp.head, cnt = rp.count;
   int bad = 0;
@@ -132,14 +129,7 @@ __global__ __launch_bounds__(kBlock) void gdn_flush_kernel(GdnReplayParams p) {
   }
   if (cnt + rp.pending > L) bad |= RSSM_ERR_POINTERS;
   const int F = cnt;
-  if (!EAGER && F > 0) {
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const int row = (wave * RT + rt) * 16 + r;
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) s[rt][ct] = ld_f4(S0 + row * N + ct * 16 + cq * 4);
-    }
-  }
+  if (!EAGER && F > 0) load_state_lines<N, RT, NCT>(s, S0, wave, r, cq);
   // the F entries' corrections and keys into LDS by logical index, 16 bytes per
   // thread, every load issued before the first one is waited for (one round trip)
   constexpr int KCH = N / 8;  // 16-byte chunks of a key
@@ -205,7 +195,10 @@ __global__ __launch_bounds__(kBlock) void gdn_flush_kernel(GdnReplayParams p) {
       uf[rt][m] = (j < F) ? s_u[j * D + row] : 0.f;
     }
   }
-  if (F > 0) fold_and_store<D, N, RT, NCT, kVJ>(S0, s, s_abar, s_k, s_w, uf, F, wave, r, cq);
+  if (F > 0) {
+    settle_state<RT, NCT>(s);
+    fold_and_store<D, N, RT, NCT, kVJ>(S0, s, s_abar, s_k, s_w, uf, F, wave, r, cq);
+  }
 
   if (tid == 0) {
     if (h == 0) flag_error(p.err, bad);

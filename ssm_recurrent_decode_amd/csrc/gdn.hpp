@@ -147,13 +147,8 @@ __global__ __launch_bounds__(kBlock, (gdn_waves_per_simd<D, N, T, LCAP>())) void
   // ---- 2. the checkpoint, last (the scheduler may not hoist it above the rest)
   __builtin_amdgcn_sched_barrier(0);
   float* S0 = p.state0 + bh * D * N;
-  float4 st[RT][NCT];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int row = (wave * RT + rt) * 16 + r;
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) st[rt][ct] = ld_f4(S0 + row * N + ct * 16 + cq * 4);
-  }
+  float4 st[RT][NCT];  // line arrangement; each pair settled where the readouts first use it
+  load_state_lines<N, RT, NCT>(st, S0, wave, r, cq);
 
   // ---- 3. small operands into LDS; pointers, clamped into range
 #pragma unroll
@@ -311,6 +306,7 @@ __global__ __launch_bounds__(kBlock, (gdn_waves_per_simd<D, N, T, LCAP>())) void
     v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int jj = 0; jj < NCT / 2; ++jj) {
+      settle_pair(st[rt][2 * jj], st[rt][2 * jj + 1]);
       const float4 s0 = st[rt][2 * jj], s1 = st[rt][2 * jj + 1];
       const float xs[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
       u32x4_t hi, lo;

@@ -7,9 +7,10 @@
 // kernel design (shared inner products, ring indexed in-kernel).
 //
 // Work decomposition: one work-group of four waves per (request b, head h).  Each
-// wave streams D/64 row tiles of the head's d x n fp32 state in the tile layout
-// described in common.hpp (one float4 per lane per 16x16 tile, all loads issued
-// before any dependent arithmetic).  Work-groups are renumbered so that the heads
+// wave streams D/64 row tiles of the head's d x n fp32 state, moved in the line
+// arrangement and computed on in the tile layout described in common.hpp (one
+// float4 per lane per 16x16 tile, all loads issued before any dependent
+// arithmetic).  Work-groups are renumbered so that the heads
 // of a request land on one XCD.
 #include "replay.hpp"
 
@@ -40,13 +41,8 @@ __global__ __launch_bounds__(kBlock) void ssm_step_kernel(StdParams p) {
   const int r = lane & 15, cq = lane >> 4;
 
   float* S = p.state + (size_t)wg * D * N;
-  float4 s[RT][NCT];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int row = (wave * RT + rt) * 16 + r;
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) s[rt][ct] = ld_f4(S + row * N + ct * 16 + cq * 4);
-  }
+  float4 s[RT][NCT];  // line arrangement until each pair is settled
+  load_state_lines<N, RT, NCT>(s, S, wave, r, cq);
   const uint16_t* kp = p.k + ((size_t)b * p.G + g) * N + cq * 4;
   const uint16_t* qp = p.q + ((size_t)b * p.G + g) * N + cq * 4;
   uint2 kk[NCT], qq[NCT];
@@ -67,14 +63,21 @@ __global__ __launch_bounds__(kBlock) void ssm_step_kernel(StdParams p) {
     const float dv = delta * vr[rt];
     float acc = 0.f;
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      float4 x = s[rt][ct];
-      x.x = a * x.x + dv * bf16_lo(kk[ct].x);
-      x.y = a * x.y + dv * bf16_hi(kk[ct].x);
-      x.z = a * x.z + dv * bf16_lo(kk[ct].y);
-      x.w = a * x.w + dv * bf16_hi(kk[ct].y);
-      acc += dot4_bf16(x, qq[ct]);
-      st_f4(S + row * N + ct * 16 + cq * 4, x);
+    for (int jj = 0; jj < NCT / 2; ++jj) {
+      settle_pair(s[rt][2 * jj], s[rt][2 * jj + 1]);
+      float4 xo[2];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int ct = 2 * jj + half;
+        float4 x = s[rt][ct];
+        x.x = a * x.x + dv * bf16_lo(kk[ct].x);
+        x.y = a * x.y + dv * bf16_hi(kk[ct].x);
+        x.z = a * x.z + dv * bf16_lo(kk[ct].y);
+        x.w = a * x.w + dv * bf16_hi(kk[ct].y);
+        acc += dot4_bf16(x, qq[ct]);
+        xo[half] = x;
+      }
+      store_pair_lines<N>(S, wave * RT + rt, jj, xo[0], xo[1], r, cq);
     }
     acc = reduce_row4(acc);
     if (cq == 0) p.y[(size_t)wg * D + row] = acc;
@@ -110,14 +113,7 @@ __global__ __launch_bounds__(kBlock) void replay_flush_kernel(ReplayParams p) {
   // only for requests that fold.
   float* S0 = p.state0 + bh * D * N;
   float4 s[RT][NCT];
-  if constexpr (EAGER) {
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const int row = (wave * RT + rt) * 16 + r;
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) s[rt][ct] = ld_f4(S0 + row * N + ct * 16 + cq * 4);
-    }
-  }
+  if constexpr (EAGER) load_state_lines<N, RT, NCT>(s, S0, wave, r, cq);
   const RingPtr rp = unpack_ptr(word);
   int head = rp.head, cnt = rp.count;
   int bad = 0;
@@ -131,14 +127,7 @@ __global__ __launch_bounds__(kBlock) void replay_flush_kernel(ReplayParams p) {
   }
   if (cnt + rp.pending > L) bad |= RSSM_ERR_POINTERS;
   const int F = cnt;
-  if (!EAGER && F > 0) {
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const int row = (wave * RT + rt) * 16 + r;
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) s[rt][ct] = ld_f4(S0 + row * N + ct * 16 + cq * 4);
-    }
-  }
+  if (!EAGER && F > 0) load_state_lines<N, RT, NCT>(s, S0, wave, r, cq);
   // the F entries' values and keys into LDS by logical index, 16 bytes per thread,
   // every load issued before the first one is waited for (one round trip)
   constexpr int VCH = D / 8, KCH = N / 8;  // 16-byte chunks of a value, of a key
@@ -189,7 +178,10 @@ __global__ __launch_bounds__(kBlock) void replay_flush_kernel(ReplayParams p) {
       vj[rt][m] = (j < F) ? bf16_to_f32(s_v[j * D + row]) : 0.f;
     }
   }
-  if (F > 0) fold_and_store<D, N, RT, NCT, kVJ>(S0, s, s_fabar, s_k, s_fw, vj, F, wave, r, cq);
+  if (F > 0) {
+    settle_state<RT, NCT>(s);
+    fold_and_store<D, N, RT, NCT, kVJ>(S0, s, s_fabar, s_k, s_fw, vj, F, wave, r, cq);
+  }
 
   if (tid == 0) {
     if (h == 0) flag_error(p.err, bad);

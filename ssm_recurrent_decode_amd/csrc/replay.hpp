@@ -83,18 +83,6 @@ __device__ __forceinline__ uint32_t conv_silu_bf16(const uint32_t* w, const uint
   return f64_to_bf16_rne(zd / (1.0 + exp(-zd)));
 }
 
-// Load the checkpoint tiles of one head (tile layout) into registers.
-template <int D, int N, int RT, int NCT>
-__device__ __forceinline__ void load_tiles(float4 (&s)[RT][NCT], const float* S0, int wave, int r,
-                                           int cq) {
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int row = (wave * RT + rt) * 16 + r;
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) s[rt][ct] = ld_f4(S0 + row * N + ct * 16 + cq * 4);
-  }
-}
-
 // One kernel for both decode modes, one work-group of four waves per (request,
 // head).
 //  APPEND (T == 1): append the token; it is entry c of E = c + 1; flush all E
@@ -103,7 +91,7 @@ __device__ __forceinline__ void load_tiles(float4 (&s)[RT][NCT], const float* S0
 //    entries; if c + 2T > L fold the c committed entries only.  pending <- T.
 //
 // Issue order: this head's ring record (pointer word and step sizes), the
-// queries, drafts and new entries, then the checkpoint tiles, then -- once the
+// queries, drafts and new entries, then the checkpoint (line arrangement), then -- once the
 // pointer word is in -- the ring keys and values of the c committed entries only
 // (on average half the ring).  Loads complete in issue order, so the weights
 // (wave 0) go ahead while the checkpoint streams in; the inner products k . q,
@@ -247,10 +235,12 @@ __global__ __launch_bounds__(kBlock, (window_waves_per_simd<D, CONV, LCAP>())) v
     A_h = p.A[h];
   }
 
-  // ---- 2. the checkpoint (the scheduler may not hoist it above the rest)
+  // ---- 2. the checkpoint (the scheduler may not hoist it above the rest), in the
+  //      line arrangement: each pair of column tiles is settled into the tile
+  //      layout where the combine first uses it
   __builtin_amdgcn_sched_barrier(0);
   float4 st[RT][NCT];
-  load_tiles<D, N, RT, NCT>(st, p.state0 + bh * D * N, wave, r, cq);
+  load_state_lines<N, RT, NCT>(st, p.state0 + bh * D * N, wave, r, cq);
   if constexpr (!CONV && kQkLds) {
 #pragma unroll
     for (int i = 0; i < QKP; ++i) {
@@ -543,6 +533,7 @@ __global__ __launch_bounds__(kBlock, (window_waves_per_simd<D, CONV, LCAP>())) v
       v4f z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int jj = 0; jj < NCT / 2; ++jj) {
+        settle_pair(st[rt][2 * jj], st[rt][2 * jj + 1]);
         const float4 s0 = st[rt][2 * jj], s1 = st[rt][2 * jj + 1];
         const float xs[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
         u32x4_t hi, lo;
@@ -570,10 +561,14 @@ __global__ __launch_bounds__(kBlock, (window_waves_per_simd<D, CONV, LCAP>())) v
 #pragma unroll
       for (int sd = 0; sd < T; ++sd) dots[sd] = 0.f;
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
+      for (int jj = 0; jj < NCT / 2; ++jj) {
+        settle_pair(st[rt][2 * jj], st[rt][2 * jj + 1]);
 #pragma unroll
-        for (int sd = 0; sd < T; ++sd)
-          dots[sd] += dot4_bf16(st[rt][ct], *reinterpret_cast<const uint2*>(&s_qv[sd * N + ct * 16 + cq * 4]));
+        for (int ct = 2 * jj; ct < 2 * jj + 2; ++ct)
+#pragma unroll
+          for (int sd = 0; sd < T; ++sd)
+            dots[sd] += dot4_bf16(st[rt][ct], *reinterpret_cast<const uint2*>(&s_qv[sd * N + ct * 16 + cq * 4]));
+      }
 #pragma unroll
       for (int sd = 0; sd < T; ++sd) {
         float part = s_abar[sd] * dots[sd];

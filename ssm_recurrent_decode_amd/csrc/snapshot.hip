@@ -66,16 +66,8 @@ __global__ __launch_bounds__(kBlock) void snapshot_verify_kernel(SnapParams p) {
   const size_t slot_floats = (size_t)H * D * N;    // one slot of one request
   float* base = p.pool + (size_t)b * P * slot_floats + (size_t)h * D * N;
 
-  float4 s[RT][NCT];
-  {
-    const float* S = base + (size_t)cur * slot_floats;
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const int row = (wave * RT + rt) * 16 + r;
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) s[rt][ct] = ld_f4(S + row * N + ct * 16 + cq * 4);
-    }
-  }
+  float4 s[RT][NCT];  // line arrangement until each pair is settled (first draft)
+  load_state_lines<N, RT, NCT>(s, base + (size_t)cur * slot_floats, wave, r, cq);
 
 #pragma unroll
   for (int sd = 0; sd < T; ++sd) {
@@ -110,7 +102,10 @@ __global__ __launch_bounds__(kBlock) void snapshot_verify_kernel(SnapParams p) {
       if constexpr (GDN) {
         float sk = 0.f;
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) sk += dot4_bf16(s[rt][ct], kk[ct]);
+        for (int jj = 0; jj < NCT / 2; ++jj) {
+          if (sd == 0) settle_pair(s[rt][2 * jj], s[rt][2 * jj + 1]);
+          sk += dot4_bf16(s[rt][2 * jj], kk[2 * jj]) + dot4_bf16(s[rt][2 * jj + 1], kk[2 * jj + 1]);
+        }
         sk = reduce_row4(sk);
         coef = scale * (vr[rt] - decay * sk);
       } else {
@@ -118,15 +113,20 @@ __global__ __launch_bounds__(kBlock) void snapshot_verify_kernel(SnapParams p) {
       }
       float acc = 0.f;
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        float4 x = s[rt][ct];
-        x.x = decay * x.x + coef * bf16_lo(kk[ct].x);
-        x.y = decay * x.y + coef * bf16_hi(kk[ct].x);
-        x.z = decay * x.z + coef * bf16_lo(kk[ct].y);
-        x.w = decay * x.w + coef * bf16_hi(kk[ct].y);
-        s[rt][ct] = x;
-        acc += dot4_bf16(x, qq[ct]);
-        st_f4(Sd + row * N + ct * 16 + cq * 4, x);
+      for (int jj = 0; jj < NCT / 2; ++jj) {
+        if (!GDN && sd == 0) settle_pair(s[rt][2 * jj], s[rt][2 * jj + 1]);
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int ct = 2 * jj + half;
+          float4 x = s[rt][ct];
+          x.x = decay * x.x + coef * bf16_lo(kk[ct].x);
+          x.y = decay * x.y + coef * bf16_hi(kk[ct].x);
+          x.z = decay * x.z + coef * bf16_lo(kk[ct].y);
+          x.w = decay * x.w + coef * bf16_hi(kk[ct].y);
+          s[rt][ct] = x;
+          acc += dot4_bf16(x, qq[ct]);
+        }
+        store_pair_lines<N>(Sd, wave * RT + rt, jj, s[rt][2 * jj], s[rt][2 * jj + 1], r, cq);
       }
       acc = reduce_row4(acc);
       if (cq == 0) p.y[(bt * H + h) * D + row] = acc;
