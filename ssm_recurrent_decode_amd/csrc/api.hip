@@ -13,17 +13,18 @@ struct CopyParams {
 // Loads in flight per thread per pass of the probes (issued before any use).
 constexpr int kProbeUnroll = 4;
 
-// Grid-stride float4 copy: one read and one write of every byte.
+// Grid-stride float4 copy: one read and one write of every byte, non-temporal
+// like the decode kernels' state transfers (each wave instruction covers 1 KB).
 __global__ __launch_bounds__(kBlock) void probe_copy_kernel(CopyParams p) {
   const size_t stride = (size_t)gridDim.x * kBlock * kProbeUnroll;
   for (size_t i = (size_t)blockIdx.x * kBlock * kProbeUnroll + threadIdx.x; i < p.n16; i += stride) {
     float4 v[kProbeUnroll];
 #pragma unroll
     for (int u = 0; u < kProbeUnroll; ++u)
-      if (i + (size_t)u * kBlock < p.n16) v[u] = p.src[i + (size_t)u * kBlock];
+      if (i + (size_t)u * kBlock < p.n16) v[u] = ld_f4_nt(reinterpret_cast<const float*>(p.src + i + (size_t)u * kBlock));
 #pragma unroll
     for (int u = 0; u < kProbeUnroll; ++u)
-      if (i + (size_t)u * kBlock < p.n16) p.dst[i + (size_t)u * kBlock] = v[u];
+      if (i + (size_t)u * kBlock < p.n16) st_f4_nt(reinterpret_cast<float*>(p.dst + i + (size_t)u * kBlock), v[u]);
   }
 }
 
@@ -35,7 +36,8 @@ struct ReadParams {
 
 constexpr int kProbeBlocks = 4096;
 
-// Grid-stride float4 read; one checksum per work-group keeps the loads live.
+// Grid-stride float4 read (non-temporal); one checksum per work-group keeps the
+// loads live.
 __global__ __launch_bounds__(kBlock) void probe_read_kernel(ReadParams p) {
   __shared__ float red[kBlock / kWave];
   const size_t stride = (size_t)gridDim.x * kBlock * kProbeUnroll;
@@ -44,7 +46,8 @@ __global__ __launch_bounds__(kBlock) void probe_read_kernel(ReadParams p) {
     float4 v[kProbeUnroll];
 #pragma unroll
     for (int u = 0; u < kProbeUnroll; ++u)
-      v[u] = (i + (size_t)u * kBlock < p.n16) ? p.src[i + (size_t)u * kBlock] : make_float4(0.f, 0.f, 0.f, 0.f);
+      v[u] = (i + (size_t)u * kBlock < p.n16) ? ld_f4_nt(reinterpret_cast<const float*>(p.src + i + (size_t)u * kBlock))
+                                              : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int u = 0; u < kProbeUnroll; ++u) acc += (v[u].x + v[u].y) + (v[u].z + v[u].w);
   }

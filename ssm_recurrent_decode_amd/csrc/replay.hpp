@@ -112,14 +112,19 @@ __device__ __forceinline__ uint32_t conv_silu_bf16(const uint32_t* w, const uint
 // issued before the conv, the conv's operands and the ring registers are live
 // together, and left alone the compiler takes 108 registers (four waves per
 // SIMD, +6 % per launch); bounded to five it fits in 96 without spilling and
-// runs 1 % faster than the conv before the ring loads.  Other instances: no bound.
-template <int D, bool CONV, int LCAP>
+// runs 1 % faster than the conv before the ring loads.  The append-decode at
+// d = 64, n = 128 with a ring of up to 32 entries is held to five as well: left
+// alone they took 100 vector and 4 accumulator registers (four waves per SIMD),
+// and bounded they fit in 96 without spilling and run 7 % faster (append-decode
+// at L = 32, 32 and 128 heads, interleaved; at L = 16 the same bound changed
+// nothing).  Other instances: no bound.
+template <int D, int N, bool APPEND, bool CONV, int LCAP>
 constexpr int window_waves_per_simd() {
-  return (CONV && D == 64 && LCAP == 16) ? 5 : 1;
+  return ((CONV && D == 64 && LCAP == 16) || (APPEND && !CONV && D == 64 && N == 128 && LCAP == 32)) ? 5 : 1;
 }
 
 template <int D, int N, int T, bool APPEND, int LCAP, bool CONV = false>
-__global__ __launch_bounds__(kBlock, (window_waves_per_simd<D, CONV, LCAP>())) void replay_window_kernel(ReplayParams p) {
+__global__ __launch_bounds__(kBlock, (window_waves_per_simd<D, N, APPEND, CONV, LCAP>())) void replay_window_kernel(ReplayParams p) {
   static_assert(N == 64 || N == 128 || N == 256, "keys and queries: 16 lanes of n / 16 values");
   static_assert(!CONV || N == 128, "the fused front-end is built for n = 128");
   static_assert(LCAP == 16 || LCAP == 32, "ring capacity bound");
