@@ -26,6 +26,7 @@
 namespace rssm {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t v3u __attribute__((ext_vector_type(3)));
 
 constexpr int kWave = 64;
 constexpr int kBlock = 256;          // four waves per work-group
