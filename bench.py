@@ -833,7 +833,8 @@ def _row_fused_conv(torch, np, rd, synth, traffic, dev, stream):
     channels (C = H d + 2 G n = 4096 at the Nemotron-H-like shape) producing v, k, q
     in the same launch, against the conv kernel followed by the append kernel (its
     v, k, q already in bf16: the cast between them is not counted); two layer
-    instances rotated, per-step HIP-event times."""
+    instances rotated, per-step HIP-event times of eager launches and, under
+    `graph`, the median over replays of the same steps captured in HIP graphs."""
     wl = synth.WORKLOADS[1]
     sh, seed = wl.shape, wl.cfg_seed
     B, H, D, N, G, L = sh.batch, sh.nheads, sh.head_dim, sh.state_dim, sh.ngroups, sh.capacity
@@ -886,6 +887,41 @@ def _row_fused_conv(torch, np, rd, synth, traffic, dev, stream):
                      "tokens_per_s": round(B / (us * 1e-6), 1)}
     res["alg_bytes_per_step"] = round(byts)
     res["speedup"] = round(res["unfused_conv_then_append"]["us_per_step"] / res["fused"]["us_per_step"], 3)
+    # the same two step sequences captured in HIP graphs (one ring cycle of both
+    # layers per graph), no launch gaps or per-step events: 5 untimed replays,
+    # then 12 timed ones, median
+    graphs = {}
+    for name, fn in (("unfused_conv_then_append", unfused), ("fused", fused)):
+        for Ly in layers:
+            rd.rssm_ring_reset(dims, Ly["ring"], stream=stream)
+        for t in range(NLs * L):
+            fn(t)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for t in range(NLs * L):
+                fn(t)
+        graphs[name] = g
+    reps = {name: [] for name in graphs}
+    with torch.cuda.stream(stream):
+        torch.cuda.synchronize()
+        for _ in range(5):
+            for g in graphs.values():
+                g.replay()
+        for _ in range(12):
+            for name, g in graphs.items():
+                a_, b_ = _events(torch, 1)[0]
+                a_.record(stream)
+                g.replay()
+                b_.record(stream)
+                reps[name].append((a_, b_))
+    torch.cuda.synchronize()
+    gr = {}
+    for name, evs in reps.items():
+        us = sorted(1e3 * a_.elapsed_time(b_) / (NLs * L) for a_, b_ in evs)
+        gr[name] = {"us_per_step": round(us[len(us) // 2], 3), "GBs": round(byts / (us[len(us) // 2] * 1e-6) / 1e9, 1)}
+    gr["speedup"] = round(gr["unfused_conv_then_append"]["us_per_step"] / gr["fused"]["us_per_step"], 3)
+    res["graph"] = gr
     return res
 
 

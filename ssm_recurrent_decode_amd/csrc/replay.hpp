@@ -117,10 +117,15 @@ __device__ __forceinline__ uint32_t conv_silu_bf16(const uint32_t* w, const uint
 // alone they took 100 vector and 4 accumulator registers (four waves per SIMD),
 // and bounded they fit in 96 without spilling and run 7 % faster (append-decode
 // at L = 32, 32 and 128 heads, interleaved; at L = 16 the same bound changed
-// nothing).  Other instances: no bound.
+// nothing).  At d = 64, n = 64 (16 KB of checkpoint per work-group) and L <= 16,
+// seven waves per SIMD (67 registers, from 72 + 4 accumulator registers at six):
+// append -1.0 %, verify -1.2 % per launch, interleaved; eight spilled in the
+// verify.  Other instances: no bound.
 template <int D, int N, bool APPEND, bool CONV, int LCAP>
 constexpr int window_waves_per_simd() {
-  return ((CONV && D == 64 && LCAP == 16) || (APPEND && !CONV && D == 64 && N == 128 && LCAP == 32)) ? 5 : 1;
+  return ((CONV && D == 64 && LCAP == 16) || (APPEND && !CONV && D == 64 && N == 128 && LCAP == 32))
+             ? 5
+             : ((D == 64 && N == 64 && LCAP == 16) ? 7 : 1);
 }
 
 template <int D, int N, int T, bool APPEND, int LCAP, bool CONV = false>
