@@ -34,8 +34,7 @@
  *
  * Symbols: B batch, H nheads, d head_dim, n state_dim, G ngroups (head h reads
  * the k/q of group h / (H / G)), L ring capacity, T draft window.
- * Supported: d in {64, 128}; n in {64, 128, 256} for every call except the
- * fused front-end (replay_append_decode_conv: n = 128), RSSM_ENOTSUP
+ * Supported: d in {64, 128}; n in {64, 128, 256} for every call, RSSM_ENOTSUP
  * otherwise; 1 <= L <= 32; 1 <= T <= 8 with 2T <= L for
  * the verify calls; any B >= 1, H >= 1 with H % G == 0 and B * H < 2^24 (one
  * 256-thread work-group per (request, head); larger: RSSM_EINVAL).

@@ -66,8 +66,7 @@ extern "C" const char* rssm_strerror(int code) {
     case RSSM_OK: return "ok";
     case RSSM_EINVAL: return "invalid argument (null pointer, bad or inconsistent size)";
     case RSSM_ENOTSUP:
-      return "shape not compiled into this library (d in {64,128}; n in {64,128,256}, n = 128 for the "
-             "fused front-end; L <= 32, T <= 8)";
+      return "shape not compiled into this library (d in {64,128}; n in {64,128,256}; L <= 32, T <= 8)";
     case RSSM_ELAUNCH: return "HIP kernel launch failed";
     default: return "unknown error code";
   }

@@ -447,8 +447,8 @@ inline bool dims_ok(const rssm_dims* d) {
   return true;
 }
 
-// Every decode call: head dims d in {64, 128}, state sizes n in {64, 128, 256};
-// the fused front-end is built for n = 128 only (conv_shape_supported).
+// Every decode call, the fused front-end included: head dims d in {64, 128},
+// state sizes n in {64, 128, 256}.
 inline bool shape_supported(const rssm_dims* d) {
   return (d->head_dim == 64 || d->head_dim == 128) &&
          (d->state_dim == 64 || d->state_dim == 128 || d->state_dim == 256);
@@ -458,9 +458,7 @@ inline bool ring_shape_supported(const rssm_dims* d) {
   return shape_supported(d) && d->capacity <= rssm::kMaxL;
 }
 
-inline bool conv_shape_supported(const rssm_dims* d) {
-  return ring_shape_supported(d) && d->state_dim == 128;
-}
+inline bool conv_shape_supported(const rssm_dims* d) { return ring_shape_supported(d); }
 
 // Every array argument is 16-byte aligned (the kernels move 16-byte chunks;
 // hipMalloc returns 256-byte aligned memory); null pointers pass here and are

@@ -367,6 +367,8 @@ extern "C" int replay_append_decode_conv(const rssm_dims* dims, float* state0, r
   p.A = A;
   p.y = y;
   p.flushed = flushed;
+  if (dims->state_dim == 64) return rssm_host::launch_replay_conv_n64(dims->head_dim, p, dims->batch, stream);
+  if (dims->state_dim == 256) return rssm_host::launch_replay_conv_n256(dims->head_dim, p, dims->batch, stream);
   if (dims->head_dim == 64) return rssm_host::launch_window<64, 1, true, true>(p, dims->batch, stream);
   return rssm_host::launch_window<128, 1, true, true>(p, dims->batch, stream);
 }

@@ -123,7 +123,7 @@ __device__ __forceinline__ uint32_t conv_silu_bf16(const uint32_t* w, const uint
 // verify.  Other instances: no bound.
 template <int D, int N, bool APPEND, bool CONV, int LCAP>
 constexpr int window_waves_per_simd() {
-  return ((CONV && D == 64 && LCAP == 16) || (APPEND && !CONV && D == 64 && N == 128 && LCAP == 32))
+  return ((CONV && D == 64 && N == 128 && LCAP == 16) || (APPEND && !CONV && D == 64 && N == 128 && LCAP == 32))
              ? 5
              : ((D == 64 && N == 64 && LCAP == 16) ? 7 : 1);
 }
@@ -131,11 +131,13 @@ constexpr int window_waves_per_simd() {
 template <int D, int N, int T, bool APPEND, int LCAP, bool CONV = false>
 __global__ __launch_bounds__(kBlock, (window_waves_per_simd<D, N, APPEND, CONV, LCAP>())) void replay_window_kernel(ReplayParams p) {
   static_assert(N == 64 || N == 128 || N == 256, "keys and queries: 16 lanes of n / 16 values");
-  static_assert(!CONV || N == 128, "the fused front-end is built for n = 128");
   static_assert(LCAP == 16 || LCAP == 32, "ring capacity bound");
   static_assert(!CONV || (APPEND && T == 1), "the fused front-end is one token");
   constexpr int NCONV = D + 2 * N;  // channels of one head: its x, the group's B and C
-  constexpr int NCQ = NCONV / 2;     // threads of the conv, two channels each
+  // conv channels per thread: two, or four where two would need more threads
+  // than the work-group has (n = 256)
+  constexpr int CPT = NCONV / 2 <= kBlock ? 2 : 4;
+  constexpr int NCQ = NCONV / CPT;   // threads of the conv
   static_assert(!CONV || NCQ <= kBlock, "one pass of the conv");
   constexpr int NCT = N / 16;
   constexpr int RT = D / (16 * kWavesPerBlock);
@@ -192,15 +194,17 @@ __global__ __launch_bounds__(kBlock, (window_waves_per_simd<D, N, APPEND, CONV, 
   uint4 qkc[QKP];
   KC qm[TQ][KQC], kin[TQ][KQC];
   uint4 newc[NCP];  // chunks of the new entries: the head's v, then the group's k
-  // conv operands of the two channels this thread computes (CONV only): state
-  // 2 x 3 bf16 (one 12-byte load), the token 2 bf16, the taps 2 x 4 bf16.  Two
-  // channels per thread over 160 threads instead of four over 80: every state
-  // load and store instruction covers its bytes whole, and each thread's SiLU
-  // chain is half as long (-2.3 % per launch, interleaved; bit-identical)
+  // conv operands of the channels this thread computes (CONV only), per pair of
+  // channels: state 2 x 3 bf16 (one 12-byte load), the token 2 bf16, the taps
+  // 2 x 4 bf16.  Two channels per thread (160 threads at d = 64, n = 128)
+  // instead of four over 80: every state load and store instruction covers its
+  // bytes whole, and each thread's SiLU chain is half as long (-2.3 % per
+  // launch, interleaved; bit-identical)
+  constexpr int CPR = CPT / 2;  // pairs of channels per thread
   int cch = 0;
-  v3u cst = {0u, 0u, 0u};
-  uint32_t cxv = 0;
-  uint4 cwv = make_uint4(0, 0, 0, 0);
+  v3u cst[CPR];
+  uint32_t cxv[CPR];
+  uint4 cwv[CPR];
   if constexpr (!CONV) {
     if constexpr (kQkLds) {
 #pragma unroll
@@ -231,11 +235,14 @@ __global__ __launch_bounds__(kBlock, (window_waves_per_simd<D, N, APPEND, CONV, 
   } else {
     if (tid < NCQ) {
       const int C = H * D + 2 * G * N;
-      const int lc = 2 * tid;  // first local channel: x | B | C
+      const int lc = CPT * tid;  // first local channel: x | B | C (never straddling two)
       cch = lc < D ? h * D + lc : (lc < D + N ? H * D + g * N + (lc - D) : H * D + G * N + g * N + (lc - D - N));
-      cst = __builtin_nontemporal_load(reinterpret_cast<const v3u*>(p.conv_in + ((size_t)rb * C + cch) * 3));
-      cxv = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p.xbc + (size_t)b * C + cch));
-      cwv = *reinterpret_cast<const uint4*>(p.conv_w + (size_t)cch * 4);
+#pragma unroll
+      for (int i = 0; i < CPR; ++i) {
+        cst[i] = __builtin_nontemporal_load(reinterpret_cast<const v3u*>(p.conv_in + ((size_t)rb * C + cch + 2 * i) * 3));
+        cxv[i] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p.xbc + (size_t)b * C + cch + 2 * i));
+        cwv[i] = *reinterpret_cast<const uint4*>(p.conv_w + (size_t)(cch + 2 * i) * 4);
+      }
     }
   }
   float rec_l = 0.f, dt_draft = 0.f, dt_bias = 0.f, A_h = 0.f;
@@ -315,32 +322,42 @@ __global__ __launch_bounds__(kBlock, (window_waves_per_simd<D, N, APPEND, CONV, 
     //      [s0, s1, s2, x], SiLU, bf16; shifted states out
     const int C = H * D + 2 * G * N;
     if (tid < NCQ) {
-      const int lc = 2 * tid;
-      // the 6 state values (channel m owns 3m .. 3m + 2, oldest first), 2 tokens, 8 taps
-      const uint32_t sv[6] = {cst.x & 0xffffu, cst.x >> 16, cst.y & 0xffffu, cst.y >> 16, cst.z & 0xffffu, cst.z >> 16};
-      const uint32_t xv[2] = {cxv & 0xffffu, cxv >> 16};
-      const uint32_t wv[8] = {cwv.x & 0xffffu, cwv.x >> 16, cwv.y & 0xffffu, cwv.y >> 16,
-                              cwv.z & 0xffffu, cwv.z >> 16, cwv.w & 0xffffu, cwv.w >> 16};
-      uint32_t o[2], ns[6];
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const uint32_t win[4] = {sv[3 * m], sv[3 * m + 1], sv[3 * m + 2], xv[m]};
-        o[m] = conv_silu_bf16(&wv[4 * m], win);
-        ns[3 * m] = win[1];
-        ns[3 * m + 1] = win[2];
-        ns[3 * m + 2] = win[3];
-      }
-      *reinterpret_cast<uint32_t*>(&s_conv[lc]) = o[0] | (o[1] << 16);
+      const int lc = CPT * tid;
       // x states by their head; the group's B and C states spread over its heads
-      // (1/hpg of them each: the group's first head writing them all ran 0.5 %
-      // slower); non-temporal, nothing in this launch reads them again
-      if (lc < D || ((tid - D / 2) * hpg) / N == h % hpg)
-        __builtin_nontemporal_store(v3u{ns[0] | (ns[1] << 16), ns[2] | (ns[3] << 16), ns[4] | (ns[5] << 16)},
-                                    reinterpret_cast<v3u*>(p.conv_out + ((size_t)rb * C + cch) * 3));
+      // (1/hpg of them each, by the thread's first channel: the group's first
+      // head writing them all ran 0.5 % slower); non-temporal, nothing in this
+      // launch reads them again
+      const bool owner = lc < D || ((lc - D) * hpg) / (2 * N) == h % hpg;
+#pragma unroll
+      for (int i = 0; i < CPR; ++i) {
+        // the 6 state values of a pair (channel m owns 3m .. 3m + 2, oldest first), 2 tokens, 8 taps
+        const v3u sp = cst[i];
+        const uint32_t sv[6] = {sp.x & 0xffffu, sp.x >> 16, sp.y & 0xffffu, sp.y >> 16, sp.z & 0xffffu, sp.z >> 16};
+        const uint32_t xv[2] = {cxv[i] & 0xffffu, cxv[i] >> 16};
+        const uint4 wq = cwv[i];
+        const uint32_t wv[8] = {wq.x & 0xffffu, wq.x >> 16, wq.y & 0xffffu, wq.y >> 16,
+                                wq.z & 0xffffu, wq.z >> 16, wq.w & 0xffffu, wq.w >> 16};
+        uint32_t o[2], ns[6];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const uint32_t win[4] = {sv[3 * m], sv[3 * m + 1], sv[3 * m + 2], xv[m]};
+          o[m] = conv_silu_bf16(&wv[4 * m], win);
+          ns[3 * m] = win[1];
+          ns[3 * m + 1] = win[2];
+          ns[3 * m + 2] = win[3];
+        }
+        *reinterpret_cast<uint32_t*>(&s_conv[lc + 2 * i]) = o[0] | (o[1] << 16);
+        if (owner)
+          __builtin_nontemporal_store(v3u{ns[0] | (ns[1] << 16), ns[2] | (ns[3] << 16), ns[4] | (ns[5] << 16)},
+                                      reinterpret_cast<v3u*>(p.conv_out + ((size_t)rb * C + cch + 2 * i) * 3));
+      }
     }
     __syncthreads();
-    qm[0][0] = *reinterpret_cast<const KC*>(&s_conv[D + N + sub * 8]);
-    kin[0][0] = *reinterpret_cast<const KC*>(&s_conv[D + sub * 8]);
+#pragma unroll
+    for (int ch = 0; ch < KQC; ++ch) {
+      qm[0][ch] = *reinterpret_cast<const KC*>(&s_conv[D + N + sub * KPL + ch * KQW]);
+      kin[0][ch] = *reinterpret_cast<const KC*>(&s_conv[D + sub * KPL + ch * KQW]);
+    }
 #pragma unroll
     for (int i = 0; i < NCP; ++i) {
       const int t = min(tid + i * kBlock, NCH - 1);
@@ -604,11 +621,13 @@ int launch_window(const ReplayParams& p, int B, void* stream) {
 }
 
 // Verify launchers for T = 1..4 and T = 5..8 (n = 128) live in their own
-// translation units, and so do the append and verify launchers of n = 64 and
-// n = 256 (T = 0 selects the append).
+// translation units, and so do the append, verify and fused front-end launchers
+// of n = 64 and n = 256 (T = 0 selects the append).
 __attribute__((visibility("hidden"))) int launch_replay_verify_lo(int T, int D, const ReplayParams& p, int B, void* stream);
 __attribute__((visibility("hidden"))) int launch_replay_verify_hi(int T, int D, const ReplayParams& p, int B, void* stream);
 __attribute__((visibility("hidden"))) int launch_replay_n64(int T, int D, const ReplayParams& p, int B, void* stream);
 __attribute__((visibility("hidden"))) int launch_replay_n256(int T, int D, const ReplayParams& p, int B, void* stream);
+__attribute__((visibility("hidden"))) int launch_replay_conv_n64(int D, const ReplayParams& p, int B, void* stream);
+__attribute__((visibility("hidden"))) int launch_replay_conv_n256(int D, const ReplayParams& p, int B, void* stream);
 
 }  // namespace rssm_host

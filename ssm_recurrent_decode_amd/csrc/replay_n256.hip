@@ -1,5 +1,6 @@
 // Instantiations of the ReplaySSM window kernel for state size n = 256: the
-// append (T = 0 here) and the verify of T = 1..8 drafts, head dims 64 and 128
+// append (T = 0 here), the verify of T = 1..8 drafts and the fused front-end,
+// head dims 64 and 128
 // (own translation unit so the kernel variants compile in parallel).
 #include "replay.hpp"
 
@@ -27,6 +28,10 @@ int launch_replay_n256(int T, int D, const ReplayParams& p, int B, void* stream)
                            : launch_window<128, 8, false, false, 256>(p, B, stream);
     default: return RSSM_ENOTSUP;
   }
+}
+
+int launch_replay_conv_n256(int D, const ReplayParams& p, int B, void* stream) {
+  return D == 64 ? launch_window<64, 1, true, true, 256>(p, B, stream) : launch_window<128, 1, true, true, 256>(p, B, stream);
 }
 
 }  // namespace rssm_host

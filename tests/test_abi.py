@@ -92,9 +92,9 @@ def test_host_validation_codes():
                                             None, None) == ENOTSUP
         assert lib.gdn_snapshot_verify_T(ctypes.byref(dd), 2, 3, P, P, P, P, P, P, P, P, P,
                                          None) == ENOTSUP
-    # the fused front-end is built for n = 128 only
-    for n in (64, 256):
-        dd = _dims(n=n)
+    # the fused front-end takes the same shapes as every other call
+    for hd, sn in ((64, 96), (96, 128), (128, 32)):
+        dd = _dims(d=hd, n=sn)
         assert lib.replay_append_decode_conv(ctypes.byref(dd), P, ctypes.byref(r), P, FAKE2, P, P, P, P,
                                              P, P, None, None) == ENOTSUP
     # capacity limits

@@ -385,14 +385,19 @@ def test_gdn_replay_append_decode_small(d, G, L):
     assert rel_err(state0.cpu().numpy(), S) <= S_TOL
 
 
-@pytest.mark.parametrize("d,G,L", [(64, 1, 8), (64, 2, 5), (128, 4, 16), (64, 8, 24), (128, 2, 32)])
-def test_replay_append_decode_conv_small(d, G, L):
+@pytest.mark.parametrize("d,G,L,H,n", [(64, 1, 8, 8, 128), (64, 2, 5, 8, 128), (128, 4, 16, 8, 128),
+                                       (64, 8, 24, 8, 128), (128, 2, 32, 8, 128), (64, 2, 8, 6, 128),
+                                       (128, 4, 4, 12, 128), (64, 2, 8, 8, 64), (128, 8, 16, 8, 64),
+                                       (64, 4, 8, 8, 256), (128, 1, 32, 8, 256), (64, 2, 6, 6, 256)])
+def test_replay_append_decode_conv_small(d, G, L, H, n):
     """Fused front-end: conv1d + SiLU over the xBC channels gives v, k, q (bf16),
     then the ReplaySSM step.  y every step against the oracle conv -> bf16 ->
     recurrence; the written conv state bit-exact every step (buffers swapped);
-    the checkpoint at every flush."""
+    the checkpoint at every flush.  Three heads per group (H = 6, G = 2 and
+    H = 12, G = 4) split a group's B and C conv states in unequal shares; at
+    n = 256 a thread takes four conv channels instead of two."""
     base = synth.WORKLOADS[0]
-    sh = base.shape.with_(head_dim=d, ngroups=G, capacity=L)
+    sh = base.shape.with_(head_dim=d, ngroups=G, capacity=L, nheads=H, state_dim=n)
     B, H, N = sh.batch, sh.nheads, sh.state_dim
     C = H * d + 2 * G * N
     seed, steps = base.cfg_seed, 2 * L + 3
