@@ -297,7 +297,7 @@ def _draft_inputs(synth, sh, seed, cfg_id, r, gdn):
     return {k_: v_[:, None] for k_, v_ in st.items()} if sh.T == 1 else st
 
 
-def _row_verify(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, rounds=64, warm=16, T=None,
+def _row_verify(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, rounds=64, warm=48, T=None,
                 with_standard=True, flags=0, G=None, shape=None, light=False):
     """Speculative verify rounds (verify kernel + device-side rollback) on two
     rotated layer instances.  A first pass records the committed count every
@@ -305,7 +305,11 @@ def _row_verify(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, rounds=
     replayed with HIP events around every launch.  T and G override the
     workload's draft window and group count, `shape` any other of its sizes;
     `light` times the verify rounds only (no commit-and-verify pass, no
-    fixed-pointer rounds, no standard step)."""
+    fixed-pointer rounds, no standard step).  The first `warm` rounds of each
+    pass are not timed: after a pause of the stream (the host reading the
+    pointers, the rings reset between passes) the first few milliseconds of
+    rounds run up to 15 % slower on this part.
+    """
     wl = synth.WORKLOADS[cfg_id]
     sh, seed = (wl.shape if T is None else wl.shape.with_(T=T)), wl.cfg_seed
     if G is not None:
