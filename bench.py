@@ -414,9 +414,34 @@ def _row_verify(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, rounds=
         raise RuntimeError(f"ring anomaly bits set in the commit-and-verify rounds: {errs}")
     cv_us = [1e3 * ev_c[r][0].elapsed_time(ev_c[r][1]) for r in range(warm, R)]
     cv_s = sum(cv_us) * 1e-6
+    # the same rounds once more, one event pair around the timed rounds (no events
+    # between launches)
+    for Ly in layers:
+        rd.rssm_ring_reset(dims, Ly["ring"], stream=stream)
+    blk = _events(torch, 1)[0]
+    torch.cuda.synchronize()
+    for r in range(R):
+        Ly, ip = layers[r % NLr], pool[r % P]
+        prev = dacc[r - NLr] if r >= NLr else zero
+        if r == warm:
+            blk[0].record(stream)
+        if gdn:
+            rd.gdn_replay_commit_verify_T(dims, T, Ly["S0"], Ly["ring"], prev, ip["v"], ip["k"], ip["q"], ip["g"],
+                                          ip["beta"], y, flushed, stream=stream)
+        else:
+            rd.replay_commit_verify_T(dims, T, Ly["S0"], Ly["ring"], prev, ip["v"], ip["k"], ip["q"], ip["dt"],
+                                      Ly["bias"], Ly["A"], y, flushed, stream=stream)
+    blk[1].record(stream)
+    for l in range(NLr):
+        rd.replay_rollback(dims, layers[(R - NLr + l) % NLr]["ring"], dacc[R - NLr + l], stream=stream)
+    torch.cuda.synchronize()
+    cv_block_us = 1e3 * blk[0].elapsed_time(blk[1]) / rounds
     fixed = _fixed_pointer_rounds(torch, np, rd, traffic, stream, layers, pool, verify, y, dims, gdn, flags)
-    all_bytes = 3 * sum(_verify_bytes(traffic, gdn, H, D, N, G, T, L, counts[r], flags) for r in range(R))
-    all_launches = 3 * R
+    # every launch of the kernel in this row: the counting pass, the timed verify
+    # pass and the two commit-and-verify passes replay rounds 0..R-1, then the
+    # fixed-pointer rounds
+    all_bytes = 4 * sum(_verify_bytes(traffic, gdn, H, D, N, G, T, L, counts[r], flags) for r in range(R))
+    all_launches = 4 * R
     for f_ in (fixed or {}).values():
         all_bytes += f_["launches"] * f_["alg_bytes"]
         all_launches += f_["launches"]
@@ -435,7 +460,7 @@ def _row_verify(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, rounds=
            "accepted_tokens_per_s": round(float(acc[warm:].sum()) / round_s, 1),
            "achieved_GBs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
            "alg_bytes_per_round": round(sum(byts) / rounds),
-           # over every launch of the kernel (three passes replay rounds 0..R-1, then
+           # over every launch of the kernel (four passes replay rounds 0..R-1, then
            # the fixed-pointer rounds): the figure hardware traffic counters over the
            # whole run compare with
            "alg_bytes_avg_all_launches": round(all_bytes / all_launches),
@@ -445,7 +470,9 @@ def _row_verify(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, rounds=
                              "us_per_round": round(sum(cv_us) / rounds, 3),
                              "verified_positions_per_s": round(B * T * rounds / cv_s, 1),
                              "accepted_tokens_per_s": round(float(acc[warm:].sum()) / cv_s, 1),
-                             "achieved_GBs": round(sum(byts) / cv_s / 1e9, 1)},
+                             "achieved_GBs": round(sum(byts) / cv_s / 1e9, 1),
+                             "us_per_round_block": round(cv_block_us, 3),
+                             "achieved_GBs_block": round(sum(byts) / (cv_block_us * rounds * 1e-6) / 1e9, 1)},
            "mean_committed_before": round(float(np.mean([counts[r] for r in range(warm, R)])), 3)}
     if fixed is not None:
         res["fixed_pointer_rounds"] = fixed
