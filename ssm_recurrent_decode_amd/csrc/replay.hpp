@@ -13,10 +13,12 @@ namespace rssm {
 
 // ======================================================= ReplaySSM
 // Draft windows from this size up combine on the matrix cores (measured against
-// the vector-ALU dot products, interleaved on the same buffers at B = 512:
-// T = 2 equal, T = 3 -0.8 %, T = 4 -2.2 %, and at T = 5, 6 the vector path
-// also costs a wave per SIMD in registers).
-constexpr int kMfmaCombineMinT = 3;
+// the vector-ALU dot products, interleaved on the same buffers at B = 512: T = 3
+// -0.8 %, T = 4 -2.2 %, and at T = 5, 6 the vector path also costs a wave per
+// SIMD in registers; T = 2 was even before the state moved as whole lines and
+// -5.8 % after; a one-token call on the matrix cores, 15 of 16 columns unused:
+// +3.3 %).
+constexpr int kMfmaCombineMinT = 2;
 
 struct ReplayParams {
   float* state0;
