@@ -51,12 +51,18 @@ __device__ __forceinline__ float softplus_f32(float x) { return x > 20.f ? x : l
 // buffers: chunks of 4 were fastest for the append (-6 %), GDN verify (-3.8 %)
 // and standard step (-2.5 %); the Mamba-2 verify was 1 % faster still with the
 // plain order.  Blocks past the largest multiple of 8 * kXcdChunk keep their id.
+// The Mamba-2 append-decode takes chunks of 8 (two head blocks per XCD): -1.2 to
+// -1.8 % per launch in two interleaved runs after the state moved as whole lines,
+// fused front-end -0.5 %; chunks of 16: -0.3 %.  The verify kernels stay at 4
+// (chunks of 8: Mamba-2 verify +0.5 %, GDN verify +1.7 %).
 constexpr int kXcdChunk = 4;
+constexpr int kXcdChunkAppend = 8;
+template <int CH = kXcdChunk>
 __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
-  const int full = (nblocks / (kNumXcd * kXcdChunk)) * (kNumXcd * kXcdChunk);
+  const int full = (nblocks / (kNumXcd * CH)) * (kNumXcd * CH);
   if (bid >= full) return bid;
   const int x = bid % kNumXcd, i = bid / kNumXcd;  // XCD, and dispatch order within it
-  return ((i / kXcdChunk) * kNumXcd + x) * kXcdChunk + i % kXcdChunk;
+  return ((i / CH) * kNumXcd + x) * CH + i % CH;
 }
 
 // Ring values (Mamba-2 v) and corrections (GDN u) of one slot are kept side by

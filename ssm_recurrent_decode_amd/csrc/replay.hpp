@@ -167,7 +167,7 @@ __global__ __launch_bounds__(kBlock, (window_waves_per_simd<D, N, APPEND, CONV, 
   __shared__ __attribute__((aligned(16))) uint16_t s_conv[CONV ? NCONV : 8];  // v | k | q
 
   const int H = p.H, G = p.G, L = p.L;
-  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int wg = xcd_remap<(APPEND ? kXcdChunkAppend : kXcdChunk)>(blockIdx.x, gridDim.x);
   const int b = wg / H, h = wg - b * H, hpg = H / G, g = h / hpg;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, cq = lane >> 4, sub = lane & 15;
