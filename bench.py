@@ -731,7 +731,9 @@ def _row_window(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, Ts=(1, 
 
 def _row_sweep(torch, np, rd, synth, traffic, dev, stream, capacities=(4, 8, 16, 32)):
     """Append-decode at every ring capacity of the large-layer workload, flush
-    and non-flush steps reported separately, plus the standard step."""
+    and non-flush steps reported separately (an event pair per launch), the
+    average over whole ring cycles from HIP-graph replays as well, plus the
+    standard step."""
     wl = synth.WORKLOADS[3]
     base, seed = wl.shape, wl.cfg_seed
     B, H, D, N, G = base.batch, base.nheads, base.head_dim, base.state_dim, base.ngroups
@@ -788,6 +790,34 @@ def _row_sweep(torch, np, rd, synth, traffic, dev, stream, capacities=(4, 8, 16,
             "avg_us": round(float(us.mean()), 3),
             "avg_GBs": round(float(byts.sum() / (us.sum() * 1e-6) / 1e9), 1),
             "tokens_per_s": round(float(B / (us.mean() * 1e-6)), 1), "steps_timed": K}
+        # the survey's graph protocol: lcm(L, 16) steps of both layers (whole ring
+        # cycles, flushes included) captured once, 5 untimed and 20 timed replays
+        steps = NLs * (L * 16 // math.gcd(L, 16))
+        t0 = warm + K
+        for t in range(t0, t0 + (-t0) % (NLs * L)):   # start the graph on a cycle boundary
+            calls[t % NLs][(t // NLs) % P]()
+        t0 += (-t0) % (NLs * L)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for t in range(t0, t0 + steps):
+                calls[t % NLs][(t // NLs) % P]()
+        ev_g = _events(torch, 20)
+        with torch.cuda.stream(stream):
+            torch.cuda.synchronize()
+            for _ in range(5):
+                graph.replay()
+            for i in range(20):
+                ev_g[i][0].record(stream)
+                graph.replay()
+                ev_g[i][1].record(stream)
+        torch.cuda.synchronize()
+        g_us = sorted(1e3 * a_.elapsed_time(b_) / steps for a_, b_ in ev_g)
+        cyc_bytes = float(np.mean([traffic.replay_append(B, H, D, N, G, x, x == L - 1) for x in range(L)]))
+        res[f"L{L}"]["graph"] = {"steps_per_replay": steps, "replays_timed": 20, "warmup_replays": 5,
+                                 "us_per_step_median": round(g_us[10], 3), "us_per_step_min": round(g_us[0], 3),
+                                 "GBs": round(cyc_bytes / (g_us[10] * 1e-6) / 1e9, 1),
+                                 "tokens_per_s": round(B / (g_us[10] * 1e-6), 1)}
         errs = [int(r.err.item()) for r in rings]
         if any(errs):
             raise RuntimeError(f"ring anomaly bits set: {errs}")
