@@ -314,6 +314,33 @@ def trace_summary(trace_csv: str, command: str, out_md: str, title: str, match: 
     return groups
 
 
+def counter_table(csvs, match: str, command: str, title: str, out_md: str, note: str = ""):
+    """Mean value per dispatch of every counter in one or more rocprofv3 --pmc
+    CSVs (one per pass), for the dispatches whose kernel name contains
+    ``match``, as a markdown table."""
+    rows = []
+    for path in csvs:
+        per = {}
+        for row in _counter_rows(path):
+            if match not in row.get("Kernel_Name", ""):
+                continue
+            key = row.get("Dispatch_Id") or row.get("Correlation_Id")
+            c = row["Counter_Name"]
+            per.setdefault(c, {}).setdefault(key, 0.0)
+            per[c][key] += float(row["Counter_Value"])
+        for c, d in sorted(per.items()):
+            rows.append((c, len(d), sum(d.values()) / len(d)))
+    lines = [f"# {title}", "", "Commands (repository root on one MI355X; `<repo>` is its path):", "",
+             "```", command, "```", "", f"Kernel: `{match}`.  Kernel sources: hash `{kernel_source_hash()}`.", ""]
+    if note:
+        lines += [note, ""]
+    lines += ["| counter | dispatches | mean per dispatch |", "|---|---|---|"]
+    lines += [f"| {c} | {n} | {v:,.0f} |" for c, n, v in rows]
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    return rows
+
+
 def stored_traffic(kernel: str):
     """(traffic bytes per launch, note) from the stored counter summary, or
     (None, reason) when there is none or the kernel sources changed since."""
@@ -363,10 +390,21 @@ def main(argv=None) -> int:
     rt.add_argument("--title", required=True)
     rt.add_argument("--command", required=True)
     rt.add_argument("--out", required=True)
+    ct = sub.add_parser("counters")
+    ct.add_argument("--csv", required=True, nargs="+", help="counter_collection.csv of each --pmc pass")
+    ct.add_argument("--match", required=True)
+    ct.add_argument("--title", required=True)
+    ct.add_argument("--command", required=True)
+    ct.add_argument("--note", default="")
+    ct.add_argument("--out", required=True)
     sub.add_parser("hash")
     a = ap.parse_args(argv)
     if a.cmd == "hash":
         print(kernel_source_hash())
+        return 0
+    if a.cmd == "counters":
+        counter_table(a.csv, a.match, a.command, a.title, a.out, a.note)
+        print(open(a.out).read())
         return 0
     if a.cmd == "rows-traffic":
         rows_traffic(a.fetch, a.write, a.calib_fetch, a.calib_write, a.bench_log, a.command, a.title, a.out)
