@@ -30,6 +30,7 @@ import math
 import os
 import sys
 import time
+import traceback
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -1336,9 +1337,18 @@ def _rows(torch, np, rd, synth, traffic, dev, stream, only=None):
             raise SystemExit(f"unknown rows: {sorted(unknown)}")
         rows = [(name, fn) for name, fn in rows if name in only]
     out = {}
+    failed = None
     for name, fn in rows:
+        if failed is not None:   # after a failure the device may be unusable: stop there
+            out[name] = {"skipped": f"row {failed} failed"}
+            continue
         print(f"[bench] row {name}", file=sys.stderr, flush=True)
-        out[name] = fn()
+        try:
+            out[name] = fn()
+        except Exception as e:  # recorded in the line (and the traceback on stderr); the headline stays
+            traceback.print_exc(file=sys.stderr)
+            out[name] = {"error": f"{type(e).__name__}: {e}"}
+            failed = name
     return out
 
 

@@ -53,3 +53,15 @@ def test_cpu_standard_baseline_runs_one_ring_cycle():
     assert res["kind"] == "oracle" and res["cores"] == 1 and res["unit"] == "tokens/s"
     assert res["value"] > 0 and "requests 0..1 of 256 (128 heads)" in res["sample"]
     assert "4 decode steps" in res["sample"]
+
+
+def test_a_failing_row_is_recorded_and_the_rest_skipped(monkeypatch):
+    def boom(*args, **kwargs):
+        raise ValueError("planted")
+
+    monkeypatch.setattr(bench, "_row_verify", boom)
+    out = bench._rows(None, None, None, None, None, None, None,
+                      ["speculative_verify", "gdn_speculative_verify", "max_concurrency"])
+    assert out["speculative_verify"] == {"error": "ValueError: planted"}
+    assert out["gdn_speculative_verify"] == {"skipped": "row speculative_verify failed"}
+    assert out["max_concurrency"] == {"skipped": "row speculative_verify failed"}
