@@ -80,7 +80,9 @@ def _ceiling_probes(torch, rd, dev, stream, launch_bytes):
     """This part's streaming ceilings, measured in the same process: the read probe
     over one launch's checkpoint bytes (four buffers rotated, so nothing stays in
     the 256 MB Infinity Cache) and over 1 GiB, and the 1 GiB copy probe (read +
-    write); mean of 16 back-to-back launches timed with HIP events."""
+    write).  16 back-to-back launches under one HIP event pair, as the kernels
+    are timed; then the same 16 with an event pair around each launch (the mean,
+    `us_event_pair_each`: that adds the gap between launches to every one)."""
     res = {}
     for name, nbytes, nbuf, copy in (("read_one_launch", launch_bytes, 4, False),
                                      ("read_1GiB", 1 << 30, 1, False), ("copy_1GiB", 1 << 30, 1, True)):
@@ -98,16 +100,24 @@ def _ceiling_probes(torch, rd, dev, stream, launch_bytes):
                 rd.rssm_probe_read(bufs[i % nbuf], sink, stream=stream)
         for i in range(4):
             run(i)
-        ev = _events(torch, 16)
+        ev = _events(torch, 17)
         torch.cuda.synchronize()
+        ev[16][0].record(stream)
+        for i in range(16):
+            run(i)
+        ev[16][1].record(stream)
+        torch.cuda.synchronize()
+        us = 1e3 * ev[16][0].elapsed_time(ev[16][1]) / 16
         for i in range(16):
             ev[i][0].record(stream)
             run(i)
             ev[i][1].record(stream)
         torch.cuda.synchronize()
-        us = sum(1e3 * a_.elapsed_time(b_) for a_, b_ in ev) / 16
+        us_each = sum(1e3 * a_.elapsed_time(b_) for a_, b_ in ev[:16]) / 16
         moved = nbytes * (2 if copy else 1)
-        res[name] = {"bytes": moved, "us": round(us, 2), "GBs": round(moved / (us * 1e-6) / 1e9, 1)}
+        res[name] = {"bytes": moved, "us": round(us, 2), "GBs": round(moved / (us * 1e-6) / 1e9, 1),
+                     "us_event_pair_each": round(us_each, 2),
+                     "GBs_event_pair_each": round(moved / (us_each * 1e-6) / 1e9, 1)}
         del bufs, dst, sink
     return res
 
