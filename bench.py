@@ -50,7 +50,9 @@ def _args(argv=None):
     ap.add_argument("--no-standard", action="store_true", help="skip the standard-step comparator")
     ap.add_argument("--cpu-steps", type=int, default=96,
                     help="decode steps of the CPU oracle sample (96: about 10 s on one core)")
-    ap.add_argument("--no-graph", action="store_true", help="time the step eagerly only")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="no HIP graphs: the step eagerly only, and the rows without their graph passes "
+                         "(so that hardware counters see only launches whose bytes the rows account exactly)")
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the other measured rows (verify, GDN verify, capacity sweep)")
     ap.add_argument("--rows", default=None,
@@ -308,6 +310,10 @@ def _draft_inputs(synth, sh, seed, cfg_id, r, gdn):
     return {k_: v_[:, None] for k_, v_ in st.items()} if sh.T == 1 else st
 
 
+# Whether the rows also time their HIP-graph passes (off under --no-graph).
+ROW_GRAPHS = True
+
+
 def _row_verify(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, rounds=64, warm=48, T=None,
                 with_standard=True, flags=0, G=None, shape=None, light=False):
     """Speculative verify rounds (verify kernel + device-side rollback) on two
@@ -452,6 +458,68 @@ def _row_verify(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, rounds=
     # 5 untimed replays, then 20 timed ones (median and minimum per round); the
     # graph keeps replaying the same accepted counts while the rings move on
     GR = 16
+    g_us = _verify_graph_pass(torch, rd, dims, T, gdn, layers, pool, dacc, y, flushed, stream, NLr, P, GR) \
+        if ROW_GRAPHS else None
+    fixed = _fixed_pointer_rounds(torch, np, rd, traffic, stream, layers, pool, verify, y, dims, gdn, flags)
+    # every launch of the kernel in this row: the counting pass, the timed verify
+    # pass and the two commit-and-verify passes replay rounds 0..R-1, then the
+    # fixed-pointer rounds
+    all_bytes = 4 * sum(_verify_bytes(traffic, gdn, H, D, N, G, T, L, counts[r], flags) for r in range(R))
+    all_launches = 4 * R
+    if g_us is not None:
+        # the graph pass (counts not recorded): its launches at the timed pass's mean bytes
+        all_bytes += (GR + GR * 25) * sum(byts) / rounds
+        all_launches += GR + GR * 25
+    for f_ in (fixed or {}).values():
+        all_bytes += f_["launches"] * f_["alg_bytes"]
+        all_launches += f_["launches"]
+    base = None
+    if gdn and with_standard:
+        # the baseline that rewrites the state every token, at the same shape
+        base = _standard_step_row(torch, np, rd, synth, traffic, dev, stream, cfg_id, True,
+                                  [Ly["S0"] for Ly in layers])
+    cv = {"kernel": "gdn_replay_commit_verify_T" if gdn else "replay_commit_verify_T",
+          "us_per_round": round(sum(cv_us) / rounds, 3),
+          "verified_positions_per_s": round(B * T * rounds / cv_s, 1),
+          "accepted_tokens_per_s": round(float(acc[warm:].sum()) / cv_s, 1),
+          "achieved_GBs": round(sum(byts) / cv_s / 1e9, 1),
+          "us_per_round_block": round(cv_block_us, 3),
+          "achieved_GBs_block": round(sum(byts) / (cv_block_us * rounds * 1e-6) / 1e9, 1)}
+    if g_us is not None:
+        cv["graph"] = {"rounds_per_replay": GR, "replays_timed": 20, "warmup_replays": 5,
+                       "us_per_round_median": round(g_us[10], 3),
+                       "us_per_round_min": round(g_us[0], 3),
+                       "verified_positions_per_s": round(B * T / (g_us[10] * 1e-6), 1),
+                       "achieved_GBs": round(sum(byts) / rounds / (g_us[10] * 1e-6) / 1e9, 1),
+                       "bytes_note": "mean algorithmic bytes per round of the timed pass"}
+    res = {"workload": ("Gated DeltaNet" if gdn else "Mamba-2") +
+                       f" speculative verify, batch {B}, {H} heads, head dim {D}, state {N}, "
+                       f"{G} group(s), ring capacity {L}, T={T}; two layer instances rotated",
+           "kernel": "gdn_replay_verify_T" if gdn else "replay_verify_T",
+           "rounds_timed": rounds, "verify_us": round(sum(v_us) / rounds, 3),
+           "rollback_us": round(sum(r_us) / rounds, 3),
+           "verified_positions_per_s": round(B * T * rounds / round_s, 1),
+           "accepted_tokens_per_s": round(float(acc[warm:].sum()) / round_s, 1),
+           "achieved_GBs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+           "alg_bytes_per_round": round(sum(byts) / rounds),
+           # over every launch of the kernel (four passes replay rounds 0..R-1, the
+           # graph pass, then the fixed-pointer rounds): the figure hardware traffic
+           # counters over the whole run compare with
+           "alg_bytes_avg_all_launches": round(all_bytes / all_launches),
+           "launches": all_launches,
+           "flush_rate": round(float(fl.mean()), 4),
+           "commit_verify": cv,
+           "mean_committed_before": round(float(np.mean([counts[r] for r in range(warm, R)])), 3)}
+    if fixed is not None:
+        res["fixed_pointer_rounds"] = fixed
+    if base is not None:
+        res["standard_step"] = base
+    return res
+
+
+def _verify_graph_pass(torch, rd, dims, T, gdn, layers, pool, dacc, y, flushed, stream, NLr, P, GR):
+    """The commit-and-verify rounds under the graph protocol; per-round times of
+    the 20 timed replays, sorted."""
     for Ly in layers:
         rd.rssm_ring_reset(dims, Ly["ring"], stream=stream)
     torch.cuda.synchronize()
@@ -489,58 +557,7 @@ def _row_verify(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, rounds=
     for Ly in layers:
         rd.rssm_ring_reset(dims, Ly["ring"], stream=stream)
     torch.cuda.synchronize()
-    fixed = _fixed_pointer_rounds(torch, np, rd, traffic, stream, layers, pool, verify, y, dims, gdn, flags)
-    # every launch of the kernel in this row: the counting pass, the timed verify
-    # pass and the two commit-and-verify passes replay rounds 0..R-1, then the
-    # fixed-pointer rounds
-    all_bytes = 4 * sum(_verify_bytes(traffic, gdn, H, D, N, G, T, L, counts[r], flags) for r in range(R))
-    all_launches = 4 * R
-    # the graph pass (counts not recorded): its launches at the timed pass's mean bytes
-    all_bytes += (GR + GR * 25) * sum(byts) / rounds
-    all_launches += GR + GR * 25
-    for f_ in (fixed or {}).values():
-        all_bytes += f_["launches"] * f_["alg_bytes"]
-        all_launches += f_["launches"]
-    base = None
-    if gdn and with_standard:
-        # the baseline that rewrites the state every token, at the same shape
-        base = _standard_step_row(torch, np, rd, synth, traffic, dev, stream, cfg_id, True,
-                                  [Ly["S0"] for Ly in layers])
-    res = {"workload": ("Gated DeltaNet" if gdn else "Mamba-2") +
-                       f" speculative verify, batch {B}, {H} heads, head dim {D}, state {N}, "
-                       f"{G} group(s), ring capacity {L}, T={T}; two layer instances rotated",
-           "kernel": "gdn_replay_verify_T" if gdn else "replay_verify_T",
-           "rounds_timed": rounds, "verify_us": round(sum(v_us) / rounds, 3),
-           "rollback_us": round(sum(r_us) / rounds, 3),
-           "verified_positions_per_s": round(B * T * rounds / round_s, 1),
-           "accepted_tokens_per_s": round(float(acc[warm:].sum()) / round_s, 1),
-           "achieved_GBs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
-           "alg_bytes_per_round": round(sum(byts) / rounds),
-           # over every launch of the kernel (four passes replay rounds 0..R-1, then
-           # the fixed-pointer rounds): the figure hardware traffic counters over the
-           # whole run compare with
-           "alg_bytes_avg_all_launches": round(all_bytes / all_launches),
-           "launches": all_launches,
-           "flush_rate": round(float(fl.mean()), 4),
-           "commit_verify": {"kernel": "gdn_replay_commit_verify_T" if gdn else "replay_commit_verify_T",
-                             "us_per_round": round(sum(cv_us) / rounds, 3),
-                             "verified_positions_per_s": round(B * T * rounds / cv_s, 1),
-                             "accepted_tokens_per_s": round(float(acc[warm:].sum()) / cv_s, 1),
-                             "achieved_GBs": round(sum(byts) / cv_s / 1e9, 1),
-                             "us_per_round_block": round(cv_block_us, 3),
-                             "achieved_GBs_block": round(sum(byts) / (cv_block_us * rounds * 1e-6) / 1e9, 1),
-                             "graph": {"rounds_per_replay": GR, "replays_timed": 20, "warmup_replays": 5,
-                                       "us_per_round_median": round(g_us[10], 3),
-                                       "us_per_round_min": round(g_us[0], 3),
-                                       "verified_positions_per_s": round(B * T / (g_us[10] * 1e-6), 1),
-                                       "achieved_GBs": round(sum(byts) / rounds / (g_us[10] * 1e-6) / 1e9, 1),
-                                       "bytes_note": "mean algorithmic bytes per round of the timed pass"}},
-           "mean_committed_before": round(float(np.mean([counts[r] for r in range(warm, R)])), 3)}
-    if fixed is not None:
-        res["fixed_pointer_rounds"] = fixed
-    if base is not None:
-        res["standard_step"] = base
-    return res
+    return g_us
 
 
 def _fixed_pointer_rounds(torch, np, rd, traffic, stream, layers, pool, verify, y, dims, gdn, flags,
@@ -801,34 +818,35 @@ def _row_sweep(torch, np, rd, synth, traffic, dev, stream, capacities=(4, 8, 16,
             "avg_us": round(float(us.mean()), 3),
             "avg_GBs": round(float(byts.sum() / (us.sum() * 1e-6) / 1e9), 1),
             "tokens_per_s": round(float(B / (us.mean() * 1e-6)), 1), "steps_timed": K}
-        # the survey's graph protocol: lcm(L, 16) steps of both layers (whole ring
-        # cycles, flushes included) captured once, 5 untimed and 20 timed replays
-        steps = NLs * (L * 16 // math.gcd(L, 16))
-        t0 = warm + K
-        for t in range(t0, t0 + (-t0) % (NLs * L)):   # start the graph on a cycle boundary
-            calls[t % NLs][(t // NLs) % P]()
-        t0 += (-t0) % (NLs * L)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
-            for t in range(t0, t0 + steps):
+        if ROW_GRAPHS:
+            # the survey's graph protocol: lcm(L, 16) steps of both layers (whole ring
+            # cycles, flushes included) captured once, 5 untimed and 20 timed replays
+            steps = NLs * (L * 16 // math.gcd(L, 16))
+            t0 = warm + K
+            for t in range(t0, t0 + (-t0) % (NLs * L)):   # start the graph on a cycle boundary
                 calls[t % NLs][(t // NLs) % P]()
-        ev_g = _events(torch, 20)
-        with torch.cuda.stream(stream):
+            t0 += (-t0) % (NLs * L)
             torch.cuda.synchronize()
-            for _ in range(5):
-                graph.replay()
-            for i in range(20):
-                ev_g[i][0].record(stream)
-                graph.replay()
-                ev_g[i][1].record(stream)
-        torch.cuda.synchronize()
-        g_us = sorted(1e3 * a_.elapsed_time(b_) / steps for a_, b_ in ev_g)
-        cyc_bytes = float(np.mean([traffic.replay_append(B, H, D, N, G, x, x == L - 1) for x in range(L)]))
-        res[f"L{L}"]["graph"] = {"steps_per_replay": steps, "replays_timed": 20, "warmup_replays": 5,
-                                 "us_per_step_median": round(g_us[10], 3), "us_per_step_min": round(g_us[0], 3),
-                                 "GBs": round(cyc_bytes / (g_us[10] * 1e-6) / 1e9, 1),
-                                 "tokens_per_s": round(B / (g_us[10] * 1e-6), 1)}
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                for t in range(t0, t0 + steps):
+                    calls[t % NLs][(t // NLs) % P]()
+            ev_g = _events(torch, 20)
+            with torch.cuda.stream(stream):
+                torch.cuda.synchronize()
+                for _ in range(5):
+                    graph.replay()
+                for i in range(20):
+                    ev_g[i][0].record(stream)
+                    graph.replay()
+                    ev_g[i][1].record(stream)
+            torch.cuda.synchronize()
+            g_us = sorted(1e3 * a_.elapsed_time(b_) / steps for a_, b_ in ev_g)
+            cyc_bytes = float(np.mean([traffic.replay_append(B, H, D, N, G, x, x == L - 1) for x in range(L)]))
+            res[f"L{L}"]["graph"] = {"steps_per_replay": steps, "replays_timed": 20, "warmup_replays": 5,
+                                     "us_per_step_median": round(g_us[10], 3), "us_per_step_min": round(g_us[0], 3),
+                                     "GBs": round(cyc_bytes / (g_us[10] * 1e-6) / 1e9, 1),
+                                     "tokens_per_s": round(B / (g_us[10] * 1e-6), 1)}
         errs = [int(r.err.item()) for r in rings]
         if any(errs):
             raise RuntimeError(f"ring anomaly bits set: {errs}")
@@ -1013,38 +1031,39 @@ def _row_fused_conv(torch, np, rd, synth, traffic, dev, stream):
     # the same two step sequences captured in HIP graphs (one ring cycle of both
     # layers per graph), no launch gaps or per-step events: 5 untimed replays,
     # then 12 timed ones, median
-    graphs = {}
-    for name, fn in (("unfused_conv_then_append", unfused), ("fused", fused)):
-        for Ly in layers:
-            rd.rssm_ring_reset(dims, Ly["ring"], stream=stream)
-        for t in range(NLs * L):
-            fn(t)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
+    if ROW_GRAPHS:
+        graphs = {}
+        for name, fn in (("unfused_conv_then_append", unfused), ("fused", fused)):
+            for Ly in layers:
+                rd.rssm_ring_reset(dims, Ly["ring"], stream=stream)
             for t in range(NLs * L):
                 fn(t)
-        graphs[name] = g
-    reps = {name: [] for name in graphs}
-    with torch.cuda.stream(stream):
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for t in range(NLs * L):
+                    fn(t)
+            graphs[name] = g
+        reps = {name: [] for name in graphs}
+        with torch.cuda.stream(stream):
+            torch.cuda.synchronize()
+            for _ in range(5):
+                for g in graphs.values():
+                    g.replay()
+            for _ in range(12):
+                for name, g in graphs.items():
+                    a_, b_ = _events(torch, 1)[0]
+                    a_.record(stream)
+                    g.replay()
+                    b_.record(stream)
+                    reps[name].append((a_, b_))
         torch.cuda.synchronize()
-        for _ in range(5):
-            for g in graphs.values():
-                g.replay()
-        for _ in range(12):
-            for name, g in graphs.items():
-                a_, b_ = _events(torch, 1)[0]
-                a_.record(stream)
-                g.replay()
-                b_.record(stream)
-                reps[name].append((a_, b_))
-    torch.cuda.synchronize()
-    gr = {}
-    for name, evs in reps.items():
-        us = sorted(1e3 * a_.elapsed_time(b_) / (NLs * L) for a_, b_ in evs)
-        gr[name] = {"us_per_step": round(us[len(us) // 2], 3), "GBs": round(byts / (us[len(us) // 2] * 1e-6) / 1e9, 1)}
-    gr["speedup"] = round(gr["unfused_conv_then_append"]["us_per_step"] / gr["fused"]["us_per_step"], 3)
-    res["graph"] = gr
+        gr = {}
+        for name, evs in reps.items():
+            us = sorted(1e3 * a_.elapsed_time(b_) / (NLs * L) for a_, b_ in evs)
+            gr[name] = {"us_per_step": round(us[len(us) // 2], 3), "GBs": round(byts / (us[len(us) // 2] * 1e-6) / 1e9, 1)}
+        gr["speedup"] = round(gr["unfused_conv_then_append"]["us_per_step"] / gr["fused"]["us_per_step"], 3)
+        res["graph"] = gr
     return res
 
 
@@ -1624,6 +1643,8 @@ def main(argv=None) -> int:
                                 "alg_bytes": std_bytes,
                                 "replay_speedup": round(std_us / (1e3 * kern_avg_ms), 3)}
 
+    global ROW_GRAPHS
+    ROW_GRAPHS = not a.no_graph
     if not a.no_rows:
         del calls, layers
         torch.cuda.empty_cache()
