@@ -8,12 +8,19 @@
 // arrays, and cross-checked against the typed record of the last head of every
 // request.  Exit status 0 and "ok" on success.  Built next to the library by
 // ssm_recurrent_decode_amd.build.
+//
+// With a directory as the only argument, the program also writes what it fed the
+// library and what came back, as raw little-endian arrays, for a comparison with
+// the float64 oracle: S0.f32 [B,H,d,n], A.f32 [H], dt_bias.f32 [H], and per step,
+// appended in step order, v.bf16 [B,H,d], k.bf16 / q.bf16 [B,G,n], dt.f32 [B,H],
+// y_replay.f32 and y_standard.f32 [B,H,d].
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <string>
 #include <vector>
 
 #include "ssm_recurrent_decode.h"
@@ -52,9 +59,27 @@ struct Lcg {  // uniform on [lo, hi), 64-bit linear congruential generator
   }
 };
 
+// Appends n elements of T to dir/name (no-op when dir is empty); false on error.
+template <typename T>
+bool dump(const std::string& dir, const char* name, const T* data, size_t n, bool first) {
+  if (dir.empty()) return true;
+  FILE* f = std::fopen((dir + "/" + name).c_str(), first ? "wb" : "ab");
+  if (f == nullptr) return false;
+  const bool ok = std::fwrite(data, sizeof(T), n, f) == n;
+  return std::fclose(f) == 0 && ok;
+}
+
 }  // namespace
 
-int main() {
+int main(int argc, char** argv) {
+  const std::string out_dir = argc > 1 ? argv[1] : "";
+#define CHECK_DUMP(x)                              \
+  do {                                             \
+    if (!(x)) {                                    \
+      std::printf("cannot write %s\n", #x);        \
+      return 1;                                    \
+    }                                              \
+  } while (0)
   const int B = 4, H = 8, D = 64, N = 128, G = 2, L = 8, steps = 2 * L + 3;
   rssm_dims dims{B, H, D, N, G, L, 0};
   if (rssm_abi_version() != RSSM_ABI_VERSION) {
@@ -97,6 +122,9 @@ int main() {
   CHECK_HIP(hipMemcpy(state0, S.data(), ns * 4, hipMemcpyHostToDevice));
   CHECK_HIP(hipMemcpy(dA, A.data(), H * 4, hipMemcpyHostToDevice));
   CHECK_HIP(hipMemcpy(dbias, bias.data(), H * 4, hipMemcpyHostToDevice));
+  CHECK_DUMP(dump(out_dir, "S0.f32", S.data(), S.size(), true));
+  CHECK_DUMP(dump(out_dir, "A.f32", A.data(), A.size(), true));
+  CHECK_DUMP(dump(out_dir, "dt_bias.f32", bias.data(), bias.size(), true));
   rssm_ring ring{ring_mem[0], static_cast<uint16_t*>(ring_mem[1]), static_cast<rssm_ring_record*>(ring_mem[2]),
                  static_cast<int32_t*>(ring_mem[3]), nullptr, 0};
   const size_t lines = RSSM_RECORD_LINES(L);  // 128-byte lines per (request, head) record
@@ -127,6 +155,12 @@ int main() {
       CHECK_HIP(hipMemcpyAsync(&last[b], ring.meta + ((size_t)b * H + H - 1) * lines, sizeof(rssm_ring_record),
                                hipMemcpyDeviceToHost, stream));
     CHECK_HIP(hipStreamSynchronize(stream));
+    CHECK_DUMP(dump(out_dir, "v.bf16", v.data(), v.size(), t == 0));
+    CHECK_DUMP(dump(out_dir, "k.bf16", k.data(), k.size(), t == 0));
+    CHECK_DUMP(dump(out_dir, "q.bf16", q.data(), q.size(), t == 0));
+    CHECK_DUMP(dump(out_dir, "dt.f32", dt.data(), dt.size(), t == 0));
+    CHECK_DUMP(dump(out_dir, "y_replay.f32", hr.data(), hr.size(), t == 0));
+    CHECK_DUMP(dump(out_dir, "y_standard.f32", hs.data(), hs.size(), t == 0));
     double mx = 0.0, err = 0.0;
     for (size_t i = 0; i < hs.size(); ++i) {
       mx = std::fmax(mx, std::fabs((double)hs[i]));
