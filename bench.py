@@ -453,7 +453,7 @@ def _row_verify(torch, np, rd, synth, traffic, dev, stream, cfg_id, gdn, rounds=
         rd.replay_rollback(dims, layers[(R - NLr + l) % NLr]["ring"], dacc[R - NLr + l], stream=stream)
     torch.cuda.synchronize()
     cv_block_us = 1e3 * blk[0].elapsed_time(blk[1]) / rounds
-    # the timing protocol of the survey for the speculative workloads: 16 rounds
+    # the graph timing protocol for the speculative workloads: 16 rounds
     # of commit-and-verify (both layers alternating) captured once in a HIP graph,
     # 5 untimed replays, then 20 timed ones (median and minimum per round); the
     # graph keeps replaying the same accepted counts while the rings move on
@@ -819,7 +819,7 @@ def _row_sweep(torch, np, rd, synth, traffic, dev, stream, capacities=(4, 8, 16,
             "avg_GBs": round(float(byts.sum() / (us.sum() * 1e-6) / 1e9), 1),
             "tokens_per_s": round(float(B / (us.mean() * 1e-6)), 1), "steps_timed": K}
         if ROW_GRAPHS:
-            # the survey's graph protocol: lcm(L, 16) steps of both layers (whole ring
+            # the graph timing protocol: lcm(L, 16) steps of both layers (whole ring
             # cycles, flushes included) captured once, 5 untimed and 20 timed replays
             steps = NLs * (L * 16 // math.gcd(L, 16))
             t0 = warm + K
